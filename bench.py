@@ -1,0 +1,211 @@
+"""Benchmark of the packed varlen RoPE-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload single_1024]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+mf_modulate_rope -> mf_varlen_attn_fwd -> mf_gated_residual, with the inputs
+already resident in HBM.  Steps rotate over several copies of the batch so
+that each step starts from inputs that are not in the 256 MB Infinity Cache.
+Prints one JSON line:
+  value       attention FLOPs (4 * d * H * sum L^2) per step / step time,
+              i.e. the whole hot path's throughput in attention TFLOP/s;
+  roofline    the attention kernel alone against the bf16 dense MFMA peak,
+              timed with HIP events on the stream it runs on;
+  kernels     per-kernel average durations, algorithmic bytes and GB/s
+              against the HBM peak (the two elementwise kernels are
+              HBM-bound);
+  cpu_baseline the fp64 oracle's attention on a bounded sample of the same
+              workload, timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "packed varlen RoPE-attention fwd TFLOP/s + % bf16 MFMA peak, 1024² pack"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_fwd_single_1024_counters.json")
+
+
+def algorithmic_bytes(w):
+    """Bytes each kernel must move at least once per launch."""
+    T, C, n_rows = w.T, w.C, w.n_seq
+    mod = T * (2 * 2 * C * 2) + T * 16 + (2 * n_rows * C * 2 if w.modulate else 0)
+    attn = 4 * T * C * 2 + 4 * w.H * T + 4 * (w.n_seq + 1)
+    gres = (T * (4 * C * 2 + 4) + 3 * n_rows * C * 2) if w.x is not None else 0
+    return dict(modulate_rope=mod, varlen_attn_fwd=attn, gated_residual=gres)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("varlen_attn_fwd.hip", "mf_device.h"):
+        with open(os.path.join(ROOT, "packed_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_hash") != source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle's attention over whole heads of the workload, head by
+    head, until about `budget_s` seconds have passed (at least one head)."""
+    import numpy as np
+    from oracle import reference as R
+    from packed_attention_amd.workloads import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cu, pos, _, mr = R.pack_tables(w.descs)
+    q, k, v = bf16_bits_to_f64(w.q), bf16_bits_to_f64(w.k), bf16_bits_to_f64(w.v)
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < w.H and (time.perf_counter() - t0) < budget_s:
+        h = heads
+        R.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], cu)
+        heads += 1
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * heads * w.sum_sq_len
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle attention of {w.name} (T={w.T}), heads 0..{heads - 1} of "
+                      f"{w.H}, all query rows; {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="single_1024")
+    ap.add_argument("--sets", type=int, default=4, help="input copies rotated over (defeats MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the packed attention path runs on a single "
+              "MI355X and has no multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from packed_attention_amd import native, runner, workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    native.lib()
+    make = W.NAMED[args.workload]
+    w = make()
+    sets = [runner.to_device(w) for _ in range(max(1, args.sets))]
+    stream = torch.cuda.current_stream()
+
+    def step(b):
+        runner.run_chain(b)
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    # Whole-step timing: K steps bracketed by device synchronisation.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(sets[i % len(sets)])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # Per-kernel durations: HIP events on the stream the kernels run on.
+    names = ("modulate_rope", "varlen_attn_fwd", "gated_residual")
+    fns = (runner.run_modulate_rope, runner.run_attention, runner.run_gated_residual)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        b = sets[i % len(sets)]
+        evs[i][0].record(stream)
+        for j, fn in enumerate(fns):
+            fn(b)
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
+               for j, n in enumerate(names)}
+
+    if args.copy_calib_mb:
+        n = args.copy_calib_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    flops = w.attn_flops()
+    abytes = algorithmic_bytes(w)
+    attn_tflops = flops / (kern_ms["varlen_attn_fwd"] * 1e-3) / 1e12
+    kernels = {}
+    for n in names:
+        ms = kern_ms[n]
+        e = {"ms": round(ms, 5), "algorithmic_bytes": abytes[n]}
+        if abytes[n] and ms > 0:
+            gbs = abytes[n] / (ms * 1e-3) / 1e9
+            e["GB/s"] = round(gbs, 1)
+            e["frac_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+        kernels[n] = e
+    kernels["varlen_attn_fwd"]["TFLOP/s"] = round(attn_tflops, 2)
+    kernels["varlen_attn_fwd"]["frac_bf16_peak"] = round(attn_tflops / PEAK_BF16_TFLOPS, 4)
+
+    traffic = measured_traffic() if args.workload == "single_1024" else None
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v/x, N(0,0.1) adaLN rows; no weights)",
+        "config": {"workload": w.name, "T": w.T, "n_seq": w.n_seq, "H": w.H, "D": w.D,
+                   "rope_dims": list(w.rope_dims), "sum_L2": w.sum_sq_len,
+                   "attn_gflop": round(flops / 1e9, 3), "input_sets": len(sets)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * mf.h -- C ABI of the packed varlen RoPE joint-attention forward (libmf.so).
+ *
+ * The method: a native-resolution multimodal diffusion transformer packs the
+ * text tokens and the flattened image-latent tokens of several samples into
+ * one buffer, delimits the samples by cumulative offsets and runs joint
+ * self-attention that never crosses samples; rotary position embeddings are
+ * per sample (2D, or 3D with a frame axis for editing), and adaptive
+ * normalisation, rotary embedding and the gated residual are fused kernels.
+ * Sources: picx.dev summary of Mage-Flow, Methodology > Native-Resolution
+ * MMDiT (packing under a token budget, per-sample cumulative offsets, packed
+ * CFG, frame coordinate of the 3D rotary embedding) and Methodology >
+ * Training Infrastructure (fused adaptive normalisation / RoPE / gating);
+ * gist.science "Resumo Tecnico: Mage-Flow", Metodologia > 2. NR-MMDiT
+ * (variable-length attention kernels with per-sample 2D rotary embeddings)
+ * and > 3. Otimizacao de Nivel de Sistema (fused kernels).
+ *
+ * Conventions for every call below.
+ *  - Plain C: no C++ exceptions cross this boundary, no torch or HIP types.
+ *    A stream argument is a hipStream_t passed as void* (NULL = the null
+ *    stream of the current device).
+ *  - Ownership: the caller allocates and frees every buffer, device or host,
+ *    including the attention workspace (size from the query call).  The
+ *    library allocates no device memory.
+ *  - Device calls validate their scalar arguments and pointer alignment on
+ *    the host before any HIP call; on failure they return a negative status
+ *    and enqueue nothing.  On success the work is enqueued on `stream` and
+ *    the call returns without synchronising.  A launch error reported by
+ *    the runtime is returned as MF_ERR_HIP.  T == 0 is a successful no-op.
+ *  - Contents of device tables (cu_seqlens, pos, mod_row) are the caller's
+ *    contract and are not read on the host, except when the environment
+ *    variable MF_DEBUG=1 is set: then each device call copies its tables to
+ *    the host, checks them (MF_ERR_TABLE) and synchronises after launching.
+ *  - bf16 tensors are row-major with the last dimension contiguous; their
+ *    pointers must be 16-byte aligned and their row strides multiples of 8
+ *    elements.  int32 tables must be 4-byte aligned.
+ *  - Calls are re-entrant; concurrent calls on different streams are safe.
+ */
+#ifndef MF_H
+#define MF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mf_status;
+
+enum {
+    MF_OK = 0,
+    MF_ERR_NULL = -1,        /* a required pointer is NULL                     */
+    MF_ERR_SHAPE = -2,       /* sizes, strides or rope dims out of range       */
+    MF_ERR_ALIGN = -3,       /* pointer or stride misaligned                   */
+    MF_ERR_UNSUPPORTED = -4, /* head dim or configuration not implemented      */
+    MF_ERR_WORKSPACE = -5,   /* workspace missing or smaller than the query    */
+    MF_ERR_TABLE = -6,       /* table contents invalid (checked on the host)   */
+    MF_ERR_HIP = -7          /* the HIP runtime reported an error              */
+};
+
+#define MF_ABI_VERSION 1
+
+/* Human-readable name of a status code; static storage, never NULL. */
+const char* mf_status_string(mf_status s);
+
+/* MF_ABI_VERSION of the built library. */
+int32_t mf_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Host-side integer pack tables (CPU only; no device needed).
+ *
+ * One descriptor per packed sample: text_len text tokens followed by
+ * n_frames frames of a grid_h x grid_w latent grid (frame 0 is the generation
+ * target or the edit source, frame 1 the edit target).  A 1024x1024 image at
+ * 16x downsampling is a 64x64 grid.  mod_row_text / mod_row_image select the
+ * adaLN table row used by that sample's text / image tokens.
+ * ---------------------------------------------------------------------- */
+typedef struct mf_sample_desc {
+    int32_t text_len;
+    int32_t n_frames;
+    int32_t grid_h;
+    int32_t grid_w;
+    int32_t mod_row_text;
+    int32_t mod_row_image;
+} mf_sample_desc;
+
+/* Total packed tokens T = sum_s (text_len + n_frames * grid_h * grid_w).
+ * Errors: MF_ERR_NULL (descs NULL with n > 0, or total NULL), MF_ERR_SHAPE
+ * (n < 0, a negative field, or T > INT32_MAX). */
+mf_status mf_pack_count(const mf_sample_desc* descs, int32_t n, int64_t* total_tokens);
+
+/* Fill caller-allocated host arrays:
+ *   cu_seqlens[n+1]: cu[0] = 0, cu[s+1] = cu[s] + L_s (per-sample cumulative
+ *                    offsets that delimit the block-diagonal attention);
+ *   pos[T][3]      : (frame, row, col) of every token; text tokens (0,0,0);
+ *                    image token i of a sample (0-based, after its text) at
+ *                    (i / (h*w), (i % (h*w)) / w, i % w);
+ *   seq_id[T]      : sample index of every token (may be NULL);
+ *   mod_row[T]     : adaLN row of every token (may be NULL).
+ * Per-sample positions restart at every sample, as the per-sample 2D/3D
+ * rotary embedding requires.  Errors as mf_pack_count, plus MF_ERR_NULL if
+ * cu_seqlens or pos is NULL. */
+mf_status mf_pack_tables(const mf_sample_desc* descs, int32_t n, int32_t* cu_seqlens,
+                         int32_t* pos, int32_t* seq_id, int32_t* mod_row);
+
+/* ------------------------------------------------------------------------
+ * Fused adaLN modulation + multi-axis rotary embedding of q and k.
+ *
+ * For X in {q, k} and every token t (row of C = H*D channels, c = h*D + e):
+ *   if shift != NULL:  u = LN(X[t]) * (1 + scale[m(t)]) + shift[m(t)]
+ *                      (LayerNorm without affine, population variance, fp32
+ *                      statistics, m(t) = mod_row[t]);
+ *   else               u = X[t];
+ *   then in every head the dims are split in contiguous blocks of rope_f
+ *   (frame), rope_r (row) and rope_c (col) dims; pair j of an axis block
+ *   (dims o+2j, o+2j+1) is rotated counter-clockwise by
+ *   pos[t][axis] * rope_base^(-2j / D_axis).
+ * Output is rounded to bf16 (round-to-nearest-even).
+ *
+ * q_in, k_in, q_out, k_out: bf16 [T][H][D] with token strides ld_in / ld_out
+ *   (elements, >= H*D, multiple of 8).  q_out may equal q_in and k_out may
+ *   equal k_in (in place); other overlaps are undefined.
+ * shift, scale: bf16 [n_rows][H*D], both NULL (RoPE only) or both set.
+ * mod_row: int32 [T]; required when shift/scale are set, ignored otherwise.
+ * pos: int32 [T][3] (frame, row, col).
+ * rope_f + rope_r + rope_c == D, each a multiple of 8.  D in {64, 128},
+ * H*D <= 8192.
+ * eps > 0 when modulating.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
+ * MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+mf_status mf_modulate_rope(void* stream,
+                           const void* q_in, const void* k_in, void* q_out, void* k_out,
+                           int64_t T, int32_t H, int32_t D, int64_t ld_in, int64_t ld_out,
+                           const void* shift, const void* scale, const int32_t* mod_row,
+                           const int32_t* pos, int32_t rope_f, int32_t rope_r, int32_t rope_c,
+                           float rope_base, float eps);
+
+/* ------------------------------------------------------------------------
+ * Block-diagonal (varlen) joint softmax attention forward.
+ *
+ * For every packed sequence s (tokens cu_seqlens[s] .. cu_seqlens[s+1]-1)
+ * and head h, with Q, K, V that sequence's L_s x D slices:
+ *   O = softmax(softmax_scale * Q K^T) V, row-wise, no mask inside the
+ *   sequence (joint text + image attention) and nothing across sequences;
+ *   lse[h][t] = natural-log sum-exp of row t of softmax_scale * Q K^T.
+ * bf16 MFMA products with fp32 accumulation; fp32 online softmax; O rounded
+ * to bf16.
+ *
+ * q, k, v: bf16 [T][H][D], token stride ld_qkv (elements, >= H*D,
+ *   multiple of 8), so q/k/v may be slices of one fused [T][3][H][D] buffer.
+ * o: bf16 [T][H][D], token stride ld_o; must not overlap q, k or v.
+ * lse: NULL or fp32 [H][T].
+ * cu_seqlens: device int32 [n_seq+1], cu[0] = 0, non-decreasing,
+ *   cu[n_seq] = T.  Empty sequences are allowed.
+ * max_seqlen: an upper bound of the sequence lengths (0 < max_seqlen <= T
+ *   when T > 0); it sizes the work decomposition.  A value below the true
+ *   maximum is a contract violation (MF_ERR_TABLE under MF_DEBUG).
+ * softmax_scale: > 0, normally 1/sqrt(D).
+ * workspace: device memory of at least mf_varlen_attn_workspace_bytes(...)
+ *   bytes, 256-byte aligned; it holds the work-tile schedule built on the
+ *   device at the start of every call, so concurrent calls need distinct
+ *   workspaces.
+ * D in {64, 128}.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
+ * MF_ERR_WORKSPACE, MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+size_t mf_varlen_attn_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D);
+
+mf_status mf_varlen_attn_fwd(void* stream,
+                             const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* cu_seqlens, int32_t n_seq, int32_t max_seqlen,
+                             int64_t T, int32_t H, int32_t D, int64_t ld_qkv, int64_t ld_o,
+                             float softmax_scale, void* workspace, size_t workspace_bytes);
+
+/* ------------------------------------------------------------------------
+ * Gated residual, optionally fused with the next sub-layer's adaLN.
+ *
+ *   y[t] = x[t] + gate[m(t)] * o[t]                        (fp32, then bf16)
+ *   z[t] = LN(y[t]) * (1 + scale2[m(t)]) + shift2[m(t)]    (from fp32 y)
+ * x, o, y, z: bf16 [T][C], contiguous rows (o is the attention output viewed
+ *   as [T][H*D]).  y may equal x (in place); z must not overlap x, o or y.
+ * gate, shift2, scale2: bf16 [n_rows][C]; mod_row: int32 [T].
+ * shift2, scale2 and z are all NULL (no fused adaLN) or all set.
+ * C a multiple of 64 and at most 8192; eps > 0 when z is produced.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_TABLE (MF_DEBUG
+ * only), MF_ERR_HIP. */
+mf_status mf_gated_residual(void* stream,
+                            const void* x, const void* o, void* y,
+                            const void* gate, const int32_t* mod_row,
+                            const void* shift2, const void* scale2, void* z,
+                            int64_t T, int32_t C, float eps);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MF_H */

@@ -1,0 +1,202 @@
+// C-ABI entry points of libmf.so: argument validation on the host, optional
+// table checks (MF_DEBUG=1), and launches on the caller's stream.  Every
+// check runs before the first HIP call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "mf.h"
+#include "mf_internal.h"
+
+namespace {
+
+bool debug_mode() {
+    static const bool on = [] {
+        const char* e = std::getenv("MF_DEBUG");
+        return e != nullptr && std::strcmp(e, "1") == 0;
+    }();
+    return on;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline mf_status from_hip(hipError_t e) { return e == hipSuccess ? MF_OK : MF_ERR_HIP; }
+
+// Copy a device int32 array to the host (debug checks only).
+bool fetch(const int32_t* dev, size_t n, std::vector<int32_t>& out, hipStream_t stream) {
+    out.resize(n);
+    if (n == 0) return true;
+    if (hipStreamSynchronize(stream) != hipSuccess) return false;
+    return hipMemcpy(out.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+mf_status check_rows(const int32_t* mod_row, int64_t T, hipStream_t stream) {
+    std::vector<int32_t> h;
+    if (!fetch(mod_row, size_t(T), h, stream)) return MF_ERR_HIP;
+    for (int32_t m : h)
+        if (m < 0) return MF_ERR_TABLE;
+    return MF_OK;
+}
+
+mf_status finish(hipError_t e, hipStream_t stream) {
+    if (e != hipSuccess) return MF_ERR_HIP;
+    if (debug_mode()) return from_hip(hipStreamSynchronize(stream));
+    return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mf_status_string(mf_status s) {
+    switch (s) {
+        case MF_OK: return "MF_OK";
+        case MF_ERR_NULL: return "MF_ERR_NULL: a required pointer is NULL";
+        case MF_ERR_SHAPE: return "MF_ERR_SHAPE: sizes, strides or rope dims out of range";
+        case MF_ERR_ALIGN: return "MF_ERR_ALIGN: pointer or stride misaligned";
+        case MF_ERR_UNSUPPORTED: return "MF_ERR_UNSUPPORTED: configuration not implemented";
+        case MF_ERR_WORKSPACE: return "MF_ERR_WORKSPACE: workspace missing or too small";
+        case MF_ERR_TABLE: return "MF_ERR_TABLE: invalid table contents";
+        case MF_ERR_HIP: return "MF_ERR_HIP: the HIP runtime reported an error";
+        default: return "MF_ERR_UNKNOWN";
+    }
+}
+
+int32_t mf_abi_version(void) { return MF_ABI_VERSION; }
+
+mf_status mf_modulate_rope(void* stream, const void* q_in, const void* k_in, void* q_out, void* k_out,
+                           int64_t T, int32_t H, int32_t D, int64_t ld_in, int64_t ld_out,
+                           const void* shift, const void* scale, const int32_t* mod_row,
+                           const int32_t* pos, int32_t rope_f, int32_t rope_r, int32_t rope_c,
+                           float rope_base, float eps) {
+    if (T < 0 || T > INT32_MAX || H <= 0) return MF_ERR_SHAPE;
+    if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
+    if (int64_t(H) * D > 8192) return MF_ERR_UNSUPPORTED;
+    if (rope_f < 0 || rope_r < 0 || rope_c < 0 || rope_f % 8 || rope_r % 8 || rope_c % 8 ||
+        rope_f + rope_r + rope_c != D)
+        return MF_ERR_SHAPE;
+    if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return MF_ERR_SHAPE;
+    if (ld_in < int64_t(H) * D || ld_out < int64_t(H) * D) return MF_ERR_SHAPE;
+    if ((shift == nullptr) != (scale == nullptr)) return MF_ERR_NULL;
+    const bool modulate = shift != nullptr;
+    if (modulate && !(eps > 0.f)) return MF_ERR_SHAPE;
+    if (T == 0) return MF_OK;
+    if (!q_in || !k_in || !q_out || !k_out || !pos) return MF_ERR_NULL;
+    if (modulate && !mod_row) return MF_ERR_NULL;
+    if (ld_in % 8 || ld_out % 8) return MF_ERR_ALIGN;
+    if (!aligned(q_in, 16) || !aligned(k_in, 16) || !aligned(q_out, 16) || !aligned(k_out, 16) ||
+        !aligned(pos, 4))
+        return MF_ERR_ALIGN;
+    if (modulate && (!aligned(shift, 16) || !aligned(scale, 16) || !aligned(mod_row, 4)))
+        return MF_ERR_ALIGN;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        std::vector<int32_t> hp;
+        if (!fetch(pos, size_t(T) * 3, hp, s)) return MF_ERR_HIP;
+        for (int32_t v : hp)
+            if (v < 0) return MF_ERR_TABLE;
+        if (modulate) {
+            mf_status st = check_rows(mod_row, T, s);
+            if (st != MF_OK) return st;
+        }
+    }
+    mf::ModRopeArgs a;
+    a.q_in = static_cast<const uint16_t*>(q_in);
+    a.k_in = static_cast<const uint16_t*>(k_in);
+    a.q_out = static_cast<uint16_t*>(q_out);
+    a.k_out = static_cast<uint16_t*>(k_out);
+    a.T = T; a.H = H; a.D = D; a.ld_in = ld_in; a.ld_out = ld_out;
+    a.shift = static_cast<const uint16_t*>(shift);
+    a.scale = static_cast<const uint16_t*>(scale);
+    a.mod_row = mod_row; a.pos = pos;
+    a.rope_f = rope_f; a.rope_r = rope_r; a.rope_c = rope_c;
+    a.rope_base = rope_base; a.eps = eps;
+    return finish(mf::launch_modulate_rope(a, s), s);
+}
+
+size_t mf_varlen_attn_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D) {
+    return mf::attn_workspace_bytes(n_seq, T, H, D);
+}
+
+mf_status mf_varlen_attn_fwd(void* stream, const void* q, const void* k, const void* v, void* o,
+                             float* lse, const int32_t* cu_seqlens, int32_t n_seq, int32_t max_seqlen,
+                             int64_t T, int32_t H, int32_t D, int64_t ld_qkv, int64_t ld_o,
+                             float softmax_scale, void* workspace, size_t workspace_bytes) {
+    if (T < 0 || T > INT32_MAX || H <= 0 || H > 4096) return MF_ERR_SHAPE;
+    if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
+    if (n_seq < 0 || (T > 0 && n_seq < 1) || n_seq > (1 << 24)) return MF_ERR_SHAPE;
+    if (max_seqlen < 0 || max_seqlen > T || (T > 0 && max_seqlen == 0)) return MF_ERR_SHAPE;
+    if (ld_qkv < int64_t(H) * D || ld_o < int64_t(H) * D) return MF_ERR_SHAPE;
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MF_ERR_SHAPE;
+    // work units must fit a 1D grid
+    if (int64_t(H) * (T / 128 + 1 + n_seq) > (int64_t(1) << 30)) return MF_ERR_SHAPE;
+    if (T == 0) return MF_OK;
+    if (!q || !k || !v || !o || !cu_seqlens) return MF_ERR_NULL;
+    if (ld_qkv % 8 || ld_o % 8) return MF_ERR_ALIGN;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4)))
+        return MF_ERR_ALIGN;
+    const size_t need = mf::attn_workspace_bytes(n_seq, T, H, D);
+    if (workspace == nullptr || workspace_bytes < need) return MF_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MF_ERR_ALIGN;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        std::vector<int32_t> cu;
+        if (!fetch(cu_seqlens, size_t(n_seq) + 1, cu, s)) return MF_ERR_HIP;
+        if (cu[0] != 0 || cu[n_seq] != T) return MF_ERR_TABLE;
+        for (int32_t i = 0; i < n_seq; ++i) {
+            const int64_t L = int64_t(cu[i + 1]) - cu[i];
+            if (L < 0 || L > max_seqlen) return MF_ERR_TABLE;
+        }
+    }
+    mf::AttnArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse; a.cu_seqlens = cu_seqlens; a.n_seq = n_seq; a.max_seqlen = max_seqlen;
+    a.T = T; a.H = H; a.D = D; a.ld_qkv = ld_qkv; a.ld_o = ld_o;
+    a.softmax_scale = softmax_scale; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return finish(mf::launch_varlen_attn_fwd(a, s), s);
+}
+
+mf_status mf_gated_residual(void* stream, const void* x, const void* o, void* y, const void* gate,
+                            const int32_t* mod_row, const void* shift2, const void* scale2, void* z,
+                            int64_t T, int32_t C, float eps) {
+    if (T < 0 || T > INT32_MAX || C <= 0 || C % 64 || C > 8192) return MF_ERR_SHAPE;
+    const int n_fused = (shift2 != nullptr) + (scale2 != nullptr) + (z != nullptr);
+    if (n_fused != 0 && n_fused != 3) return MF_ERR_NULL;
+    if (n_fused == 3 && !(eps > 0.f)) return MF_ERR_SHAPE;
+    if (T == 0) return MF_OK;
+    if (!x || !o || !y || !gate || !mod_row) return MF_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(o, 16) || !aligned(y, 16) || !aligned(gate, 16) ||
+        !aligned(mod_row, 4))
+        return MF_ERR_ALIGN;
+    if (n_fused == 3 && (!aligned(shift2, 16) || !aligned(scale2, 16) || !aligned(z, 16)))
+        return MF_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        mf_status st = check_rows(mod_row, T, s);
+        if (st != MF_OK) return st;
+    }
+    mf::GatedResArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.o = static_cast<const uint16_t*>(o);
+    a.y = static_cast<uint16_t*>(y);
+    a.gate = static_cast<const uint16_t*>(gate);
+    a.mod_row = mod_row;
+    a.shift2 = static_cast<const uint16_t*>(shift2);
+    a.scale2 = static_cast<const uint16_t*>(scale2);
+    a.z = static_cast<uint16_t*>(z);
+    a.T = T; a.C = C; a.eps = eps;
+    return finish(mf::launch_gated_residual(a, s), s);
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Device-side helpers for the gfx950 kernels of libmf.so: vector types,
+// bf16 <-> fp32 conversion and wavefront (64-lane) reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace mf {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// 16-byte global load/store of 8 bf16 values held as 4 packed dwords.
+__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void st16(uint16_t* p, u32x4_t v) {
+    *reinterpret_cast<u32x4_t*>(p) = v;
+}
+
+// Exact widening of the two bf16 halves of a dword.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Unpack 8 bf16 (4 dwords) to fp32, element order preserved.
+__device__ __forceinline__ void unpack8(u32x4_t v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf_lo(v[i]);
+        f[2 * i + 1] = bf_hi(v[i]);
+    }
+}
+
+// Round two fp32 values to bf16 (round-to-nearest-even, v_cvt_pk_bf16_f32)
+// and pack them into one dword, `a` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2_t v = {a, b};
+    bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ u32x4_t pack8(const float* f) {
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return r;
+}
+
+// Sum over the 64 lanes of a wavefront; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+}  // namespace mf

@@ -1,0 +1,70 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels of
+// libmf.so.  Not part of the public interface (include/mf.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace mf {
+
+// ---------------------------------------------------------------------------
+// Launchers (one per kernel family).  Arguments are already validated by the
+// C-ABI layer; each returns the hipError_t of its launches.
+// ---------------------------------------------------------------------------
+
+struct ModRopeArgs {
+    const uint16_t* q_in;
+    const uint16_t* k_in;
+    uint16_t* q_out;
+    uint16_t* k_out;
+    int64_t T;
+    int32_t H, D;
+    int64_t ld_in, ld_out;
+    const uint16_t* shift;   // nullptr: RoPE only
+    const uint16_t* scale;
+    const int32_t* mod_row;
+    const int32_t* pos;
+    int32_t rope_f, rope_r, rope_c;
+    float rope_base, eps;
+    // Rotation frequency of every pair of a head (index = dim / 2), filled by
+    // the launcher in double precision: base^(-2j / D_axis).
+    double theta[64];
+};
+hipError_t launch_modulate_rope(const ModRopeArgs& a, hipStream_t stream);
+
+struct GatedResArgs {
+    const uint16_t* x;
+    const uint16_t* o;
+    uint16_t* y;
+    const uint16_t* gate;
+    const int32_t* mod_row;
+    const uint16_t* shift2;  // nullptr: no fused adaLN
+    const uint16_t* scale2;
+    uint16_t* z;
+    int64_t T;
+    int32_t C;
+    float eps;
+};
+hipError_t launch_gated_residual(const GatedResArgs& a, hipStream_t stream);
+
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    const int32_t* cu_seqlens;
+    int32_t n_seq, max_seqlen;
+    int64_t T;
+    int32_t H, D;
+    int64_t ld_qkv, ld_o;
+    float softmax_scale;
+    void* workspace;
+    size_t workspace_bytes;
+};
+size_t attn_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D);
+hipError_t launch_varlen_attn_fwd(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace mf

@@ -1,0 +1,209 @@
+"""ctypes binding of libmf.so (include/mf.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module only
+turns torch tensors into device pointers, strides and the current stream.
+If libmf.so is missing the first call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmf.so")
+
+MF_OK = 0
+STATUS_NAMES = {0: "MF_OK", -1: "MF_ERR_NULL", -2: "MF_ERR_SHAPE", -3: "MF_ERR_ALIGN",
+                -4: "MF_ERR_UNSUPPORTED", -5: "MF_ERR_WORKSPACE", -6: "MF_ERR_TABLE",
+                -7: "MF_ERR_HIP"}
+
+# Every symbol include/mf.h declares.
+EXPORTS = ("mf_status_string", "mf_abi_version", "mf_pack_count", "mf_pack_tables",
+           "mf_modulate_rope", "mf_varlen_attn_workspace_bytes", "mf_varlen_attn_fwd",
+           "mf_gated_residual")
+
+
+class MFError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{message} (status {code})")
+        self.code = code
+
+
+class SampleDesc(ctypes.Structure):
+    _fields_ = [("text_len", ctypes.c_int32), ("n_frames", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("mod_row_text", ctypes.c_int32), ("mod_row_image", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmf.so (built in-tree by packed_attention_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run packed_attention_amd.build.build() "
+                           "(there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    L.mf_status_string.argtypes = [i32]
+    L.mf_status_string.restype = ctypes.c_char_p
+    L.mf_abi_version.argtypes = []
+    L.mf_abi_version.restype = i32
+    L.mf_pack_count.argtypes = [vp, i32, ctypes.POINTER(i64)]
+    L.mf_pack_count.restype = i32
+    L.mf_pack_tables.argtypes = [vp, i32, vp, vp, vp, vp]
+    L.mf_pack_tables.restype = i32
+    L.mf_modulate_rope.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, vp, vp, vp, vp,
+                                   i32, i32, i32, f32, f32]
+    L.mf_modulate_rope.restype = i32
+    L.mf_varlen_attn_workspace_bytes.argtypes = [i32, i64, i32, i32]
+    L.mf_varlen_attn_workspace_bytes.restype = sz
+    L.mf_varlen_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i64, i64,
+                                     f32, vp, sz]
+    L.mf_varlen_attn_fwd.restype = i32
+    L.mf_gated_residual.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, f32]
+    L.mf_gated_residual.restype = i32
+    _lib = L
+    return L
+
+
+def check(code: int) -> None:
+    if code != MF_OK:
+        msg = lib().mf_status_string(code).decode()
+        raise MFError(code, msg)
+
+
+# ---------------------------------------------------------------------------
+# Host tables
+# ---------------------------------------------------------------------------
+
+def _desc_array(descs: Sequence[Tuple[int, ...]]):
+    arr = (SampleDesc * max(1, len(descs)))()
+    for i, d in enumerate(descs):
+        arr[i] = SampleDesc(*[int(x) for x in d])
+    return arr
+
+
+def pack_count(descs) -> int:
+    out = ctypes.c_int64(0)
+    check(lib().mf_pack_count(_desc_array(descs), len(descs), ctypes.byref(out)))
+    return int(out.value)
+
+
+def pack_tables(descs):
+    """Host C++ tables: (cu_seqlens[n+1], pos[T][3], seq_id[T], mod_row[T]) as int32 numpy."""
+    n = len(descs)
+    T = pack_count(descs)
+    cu = np.zeros(n + 1, dtype=np.int32)
+    pos = np.zeros((T, 3), dtype=np.int32)
+    sid = np.zeros(T, dtype=np.int32)
+    mr = np.zeros(T, dtype=np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    check(lib().mf_pack_tables(_desc_array(descs), n, p(cu), p(pos), p(sid), p(mr)))
+    return cu, pos, sid, mr
+
+
+# ---------------------------------------------------------------------------
+# Device calls (torch tensors)
+# ---------------------------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check_bf16_rows(name, t, cols):
+    import torch
+    if t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name}: expected a bfloat16 CUDA tensor")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous")
+
+
+def _token_stride(t, inner):
+    """Token stride (elements) of a [T][H][D] or [T][C] view whose inner dims are packed."""
+    if t.dim() == 3:
+        if t.stride(1) != t.shape[2]:
+            raise ValueError("head dimension must be packed (stride(1) == D)")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), inner)
+
+
+def modulate_rope(q_in, k_in, q_out, k_out, pos, rope_dims, rope_base=10000.0,
+                  shift=None, scale=None, mod_row=None, eps=1e-6, stream=None):
+    """mf_modulate_rope on [T][H][D] bf16 tensors (q_out/k_out may alias the inputs)."""
+    T, H, D = q_in.shape
+    for n, t in (("q_in", q_in), ("k_in", k_in), ("q_out", q_out), ("k_out", k_out)):
+        _check_bf16_rows(n, t, H * D)
+        if tuple(t.shape) != (T, H, D):
+            raise ValueError(f"{n}: shape {tuple(t.shape)} != {(T, H, D)}")
+    ld_in = _token_stride(q_in, H * D)
+    if _token_stride(k_in, H * D) != ld_in:
+        raise ValueError("q_in and k_in must share a token stride")
+    ld_out = _token_stride(q_out, H * D)
+    if _token_stride(k_out, H * D) != ld_out:
+        raise ValueError("q_out and k_out must share a token stride")
+    f, r, c = (int(x) for x in rope_dims)
+    check(lib().mf_modulate_rope(_stream(stream), _ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out),
+                                 T, H, D, ld_in, ld_out, _ptr(shift), _ptr(scale), _ptr(mod_row),
+                                 _ptr(pos), f, r, c, float(rope_base), float(eps)))
+
+
+def attn_workspace_bytes(n_seq: int, T: int, H: int, D: int) -> int:
+    return int(lib().mf_varlen_attn_workspace_bytes(n_seq, T, H, D))
+
+
+def varlen_attn_fwd(q, k, v, o, cu_seqlens, max_seqlen, lse=None, softmax_scale=None,
+                    workspace=None, stream=None):
+    """mf_varlen_attn_fwd on [T][H][D] bf16 q, k, v (sharing one token stride) into o."""
+    import torch
+    T, H, D = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bf16_rows(n, t, H * D)
+        if tuple(t.shape) != (T, H, D):
+            raise ValueError(f"{n}: shape {tuple(t.shape)} != {(T, H, D)}")
+    ld = _token_stride(q, H * D)
+    if _token_stride(k, H * D) != ld or _token_stride(v, H * D) != ld:
+        raise ValueError("q, k and v must share a token stride")
+    ld_o = _token_stride(o, H * D)
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+        raise TypeError("cu_seqlens: expected an int32 CUDA tensor")
+    n_seq = cu_seqlens.numel() - 1
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (H, T)):
+        raise ValueError("lse: expected float32 [H][T]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    need = attn_workspace_bytes(n_seq, T, H, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    check(lib().mf_varlen_attn_fwd(_stream(stream), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   _ptr(cu_seqlens), n_seq, int(max_seqlen), T, H, D, ld, ld_o,
+                                   float(softmax_scale), _ptr(workspace), workspace.numel()))
+
+
+def gated_residual(x, o, y, gate, mod_row, shift2=None, scale2=None, z=None, eps=1e-6, stream=None):
+    """mf_gated_residual on contiguous [T][C] bf16 rows (o may be given as [T][H][D])."""
+    T = x.shape[0]
+    C = x.numel() // max(T, 1) if T else x.shape[-1]
+    for n, t in (("x", x), ("o", o), ("y", y), ("z", z)):
+        if t is None:
+            continue
+        _check_bf16_rows(n, t, C)
+        if not t.is_contiguous() or t.numel() != T * C:
+            raise ValueError(f"{n}: expected a contiguous [T][C] tensor")
+    check(lib().mf_gated_residual(_stream(stream), _ptr(x), _ptr(o), _ptr(y), _ptr(gate),
+                                  _ptr(mod_row), _ptr(shift2), _ptr(scale2), _ptr(z), T, C,
+                                  float(eps)))

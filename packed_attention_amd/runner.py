@@ -1,0 +1,107 @@
+"""Run the hot path of a workload on one GPU through the C-ABI binding.
+
+Moves a seeded workload (bf16 bit patterns from ``workloads``) into HBM,
+builds the integer tables with the library's host table builder, and chains
+mf_modulate_rope -> mf_varlen_attn_fwd -> mf_gated_residual on the current
+stream.  Used by the GPU tests, the smoke check and the benchmark.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+from . import native
+from .workloads import Workload
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def bf16_to_f64(t) -> np.ndarray:
+    """Exact widening of a bf16 torch tensor (any device) to float64 numpy."""
+    import torch
+    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+@dataclasses.dataclass
+class DeviceBatch:
+    w: Workload
+    cu_host: np.ndarray
+    pos_host: np.ndarray
+    mod_row_host: np.ndarray
+    cu: object
+    pos: object
+    mod_row: object
+    q: object
+    k: object
+    v: object
+    x: Optional[object]
+    shift: Optional[object]
+    scale: Optional[object]
+    gate: Optional[object]
+    shift2: Optional[object]
+    scale2: Optional[object]
+    # outputs / intermediates
+    qr: object
+    kr: object
+    o: object
+    lse: object
+    y: Optional[object]
+    z: Optional[object]
+    workspace: object
+    max_seqlen: int
+
+
+def to_device(w: Workload, device="cuda", with_lse=True) -> DeviceBatch:
+    import torch
+    cu, pos, _sid, mr = native.pack_tables(w.descs)
+    T, H, D = w.T, w.H, w.D
+    dev = lambda a: None if a is None else bf16_tensor(a, device)  # noqa: E731
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    lens = np.diff(cu)
+    max_seqlen = int(lens.max()) if len(lens) else 0
+    return DeviceBatch(
+        w=w, cu_host=cu, pos_host=pos, mod_row_host=mr,
+        cu=torch.from_numpy(cu).to(device), pos=torch.from_numpy(pos).to(device),
+        mod_row=torch.from_numpy(mr).to(device),
+        q=q, k=k, v=v, x=dev(w.x), shift=dev(w.shift), scale=dev(w.scale), gate=dev(w.gate),
+        shift2=dev(w.shift2), scale2=dev(w.scale2),
+        qr=torch.empty_like(q), kr=torch.empty_like(k), o=torch.empty_like(q),
+        lse=torch.empty((H, T), dtype=torch.float32, device=device) if with_lse else None,
+        y=torch.empty((T, H * D), dtype=torch.bfloat16, device=device) if w.x is not None else None,
+        z=torch.empty((T, H * D), dtype=torch.bfloat16, device=device) if w.x is not None else None,
+        workspace=torch.empty(native.attn_workspace_bytes(len(w.descs), T, H, D), dtype=torch.uint8,
+                              device=device),
+        max_seqlen=max_seqlen,
+    )
+
+
+def run_modulate_rope(b: DeviceBatch, stream=None):
+    w = b.w
+    native.modulate_rope(b.q, b.k, b.qr, b.kr, b.pos, w.rope_dims, w.rope_base,
+                         b.shift, b.scale, b.mod_row if b.shift is not None else None, w.eps,
+                         stream=stream)
+
+
+def run_attention(b: DeviceBatch, stream=None):
+    native.varlen_attn_fwd(b.qr, b.kr, b.v, b.o, b.cu, b.max_seqlen, lse=b.lse,
+                           workspace=b.workspace, stream=stream)
+
+
+def run_gated_residual(b: DeviceBatch, stream=None):
+    if b.x is None:
+        return
+    native.gated_residual(b.x, b.o.view(b.w.T, -1), b.y, b.gate, b.mod_row, b.shift2, b.scale2,
+                          b.z, b.w.eps, stream=stream)
+
+
+def run_chain(b: DeviceBatch, stream=None):
+    """One pass of the whole hot path."""
+    run_modulate_rope(b, stream)
+    run_attention(b, stream)
+    run_gated_residual(b, stream)

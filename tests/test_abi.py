@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports every symbol include/mf.h declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed: every
+call here fails validation, so nothing reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from packed_attention_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+NULL, SHAPE, ALIGN, UNSUP, WS = -1, -2, -3, -4, -5
+P = 0x10000          # a 16-byte-aligned stand-in address; never dereferenced
+PODD = 0x10002       # misaligned
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "mf.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mf_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    syms = header_symbols()
+    assert syms == sorted(native.EXPORTS)
+    lib = native.lib()
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_version_and_strings():
+    lib = native.lib()
+    assert lib.mf_abi_version() == 1
+    for code in range(-7, 1):
+        s = lib.mf_status_string(code).decode()
+        assert s.startswith(native.STATUS_NAMES[code])
+    assert lib.mf_status_string(-99).decode() == "MF_ERR_UNKNOWN"
+
+
+def modrope(**kw):
+    a = dict(stream=None, q_in=P, k_in=P, q_out=P, k_out=P, T=4, H=2, D=64, ld_in=128, ld_out=128,
+             shift=None, scale=None, mod_row=None, pos=P, f=0, r=32, c=32, base=10000.0, eps=1e-6)
+    a.update(kw)
+    return native.lib().mf_modulate_rope(*a.values())
+
+
+def test_modulate_rope_validation():
+    assert modrope(D=96) == UNSUP
+    assert modrope(H=0) == SHAPE
+    assert modrope(T=-1) == SHAPE
+    assert modrope(H=128, D=128, ld_in=16384, ld_out=16384, r=64, c=64) == UNSUP   # C > 8192
+    assert modrope(r=20, c=44) == SHAPE          # not multiples of 8
+    assert modrope(r=32, c=24) == SHAPE          # sum != D
+    assert modrope(f=-8, r=40, c=32) == SHAPE
+    assert modrope(base=0.0) == SHAPE
+    assert modrope(ld_in=120) == SHAPE
+    assert modrope(shift=P) == NULL              # shift without scale
+    assert modrope(shift=P, scale=P, mod_row=P, eps=0.0) == SHAPE
+    assert modrope(q_in=None) == NULL
+    assert modrope(pos=None) == NULL
+    assert modrope(shift=P, scale=P, mod_row=None) == NULL
+    assert modrope(ld_in=132, ld_out=136) == ALIGN
+    assert modrope(k_out=PODD) == ALIGN
+    assert modrope(shift=PODD, scale=P, mod_row=P) == ALIGN
+    assert modrope(T=0, q_in=None, k_in=None, q_out=None, k_out=None, pos=None) == 0   # no-op
+
+
+def attn(**kw):
+    a = dict(stream=None, q=P, k=P, v=P, o=P, lse=None, cu=P, n_seq=1, max_seqlen=4, T=4, H=2,
+             D=128, ld=256, ld_o=256, scale=0.088, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    return native.lib().mf_varlen_attn_fwd(*a.values())
+
+
+def test_attention_validation():
+    assert attn(D=96) == UNSUP
+    assert attn(H=0) == SHAPE
+    assert attn(n_seq=0) == SHAPE
+    assert attn(max_seqlen=5) == SHAPE
+    assert attn(max_seqlen=0) == SHAPE
+    assert attn(ld=200) == SHAPE
+    assert attn(scale=0.0) == SHAPE
+    assert attn(scale=float("inf")) == SHAPE
+    assert attn(q=None) == NULL
+    assert attn(cu=None) == NULL
+    assert attn(ld=264, ld_o=260) == ALIGN
+    assert attn(v=PODD) == ALIGN
+    assert attn(lse=PODD) == ALIGN
+    assert attn(ws=None) == WS
+    assert attn(ws_bytes=8) == WS
+    assert attn(ws=P + 16) == ALIGN
+    assert attn(T=0, n_seq=0, max_seqlen=0, q=None, k=None, v=None, o=None, cu=None) == 0
+
+
+def test_workspace_query():
+    lib = native.lib()
+    a = lib.mf_varlen_attn_workspace_bytes(1, 4352, 24, 128)
+    b = lib.mf_varlen_attn_workspace_bytes(1000, 4352, 24, 128)
+    assert a > 0 and a % 256 == 0 and b % 256 == 0 and b >= (3 + 3 * 1000) * 4
+
+
+def gres(**kw):
+    a = dict(stream=None, x=P, o=P, y=P, gate=P, mod_row=P, shift2=None, scale2=None, z=None, T=4,
+             C=256, eps=1e-6)
+    a.update(kw)
+    return native.lib().mf_gated_residual(*a.values())
+
+
+def test_gated_residual_validation():
+    assert gres(C=100) == SHAPE
+    assert gres(C=16384) == SHAPE
+    assert gres(T=-3) == SHAPE
+    assert gres(shift2=P) == NULL
+    assert gres(shift2=P, scale2=P, z=P, eps=-1.0) == SHAPE
+    assert gres(x=None) == NULL
+    assert gres(mod_row=None) == NULL
+    assert gres(o=PODD) == ALIGN
+    assert gres(shift2=P, scale2=P, z=PODD) == ALIGN
+    assert gres(T=0, x=None, o=None, y=None, gate=None, mod_row=None) == 0
+
+
+def test_library_has_no_oracle_dependency():
+    """The product path never touches the oracle: no module of the package
+    imports it, and the native sources do not mention it."""
+    pkg = os.path.join(ROOT, "packed_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

@@ -1,0 +1,240 @@
+"""HIP path vs the fp64 oracle on small packs (full oracle, every element).
+
+Each case runs the three kernels through the C-ABI binding and checks
+  * the integer tables the library built: exactly equal to the oracle's;
+  * per kernel: the oracle fed that kernel's own bf16 inputs;
+  * end to end: the oracle chain in fp64 from the same seeded bf16 inputs.
+Bar: max-abs <= 2e-2 and mean-abs <= 2e-3 on every bf16 output, plus the
+internal checks (one bf16 ulp for the elementwise kernels, relative RMS and
+LSE for attention).
+"""
+import numpy as np
+import pytest
+
+import gpu_common as G
+from oracle import reference as R
+from packed_attention_amd import native, runner, workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    native.lib()
+
+
+def run_and_check(w, e2e=True, qk_sigma=1.0):
+    import torch
+    G.say(w.name, "T", w.T, "H", w.H, "D", w.D, "descs", w.descs)
+    b = runner.to_device(w)
+    # tables: exact
+    cu, pos, sid, mr = R.pack_tables(w.descs)
+    np.testing.assert_array_equal(b.cu_host, cu)
+    np.testing.assert_array_equal(b.pos_host, pos)
+    np.testing.assert_array_equal(b.mod_row_host, mr)
+    runner.run_chain(b)
+    torch.cuda.synchronize()
+    a = G.wl_f64(w)
+    T, H, D = w.T, w.H, w.D
+    # per kernel: modulate + rope
+    qr_ref, kr_ref = R.modulate_rope(a["q"], a["k"], pos, w.rope_dims, w.rope_base, a["shift"],
+                                     a["scale"], mr, w.eps)
+    qr, kr = G.f64(b.qr), G.f64(b.kr)
+    # the absolute bar is stated for unit-scale rows; stress rows of scale
+    # sigma carry sigma times the bf16 rounding, so it scales with sigma there
+    G.check_bar(qr, qr_ref, w.name + ".q'", G.MAX_ABS * qk_sigma, G.MEAN_ABS * qk_sigma)
+    G.check_bar(kr, kr_ref, w.name + ".k'", G.MAX_ABS * qk_sigma, G.MEAN_ABS * qk_sigma)
+    G.check_rounded(qr, qr_ref, w.name + ".q'")
+    G.check_rounded(kr, kr_ref, w.name + ".k'")
+    # per kernel: attention on the kernel's own bf16 inputs
+    O_ref, L_ref = R.attention(qr, kr, a["v"], cu)
+    O = G.f64(b.o)
+    lse = b.lse.cpu().numpy().astype(np.float64)
+    G.check_attention(O, O_ref, w.name, lse, L_ref)
+    # per kernel: gated residual on the kernel's own O
+    if w.x is not None:
+        y_ref, z_ref = R.gated_residual(a["x"], O, a["gate"], mr, a["shift2"], a["scale2"], w.eps)
+        y, z = G.f64(b.y), G.f64(b.z)
+        G.check_bar(y, y_ref, w.name + ".y")
+        G.check_rounded(y, y_ref, w.name + ".y")
+        G.check_bar(z, z_ref, w.name + ".z")
+        G.check_rounded(z, z_ref, w.name + ".z", slack=1e-5)
+    # end to end, fp64 throughout
+    if e2e:
+        r = R.forward(w.descs, a["q"], a["k"], a["v"], w.rope_dims, w.rope_base, a["shift"],
+                      a["scale"], a["x"], a["gate"], a["shift2"], a["scale2"], w.eps)
+        G.check_attention(O, r["O"], w.name + ".e2e", lse, r["LSE"], G.LSE_ABS_E2E * qk_sigma ** 2)
+        if w.x is not None:
+            G.check_bar(G.f64(b.y), r["y"], w.name + ".e2e.y")
+            G.check_bar(G.f64(b.z), r["z"], w.name + ".e2e.z")
+    return b
+
+
+def test_tiny_pack():
+    run_and_check(W.tiny())
+
+
+def test_tiny_pack_modulated():
+    run_and_check(W.tiny_mod())
+
+
+# Sequence lengths around the 64-key and 128-query tile edges, an empty
+# sequence and a single token; text + latent grid mixes.
+RAGGED = [(1, 1, 0, 0), (1, 1, 1, 1), (3, 1, 6, 10), (0, 1, 8, 8), (1, 1, 8, 8), (0, 1, 0, 0),
+          (7, 1, 8, 15), (0, 1, 8, 16), (1, 1, 8, 16), (12, 1, 16, 18), (5, 2, 4, 6)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_ragged_pack(D):
+    descs = [(t, f, h, ww, s, s) for s, (t, f, h, ww) in enumerate(RAGGED)]
+    assert [W.sample_len(d) for d in descs] == [1, 2, 63, 64, 65, 0, 127, 128, 129, 300, 53]
+    dims = (0, D // 2, D // 2) if D == 64 else (16, 56, 56)
+    w = W.custom(descs, H=3, D=D, rope_dims=dims, modulate=True, residual=True, seed=77,
+                 name=f"ragged_d{D}")
+    run_and_check(w)
+
+
+@pytest.mark.parametrize("sigma", [4.0, 8.0])
+def test_peaky_softmax(sigma):
+    descs = [(40, 1, 12, 12, 0, 0), (9, 1, 7, 5, 1, 1)]
+    w = W.custom(descs, H=2, D=128, rope_dims=(0, 64, 64), modulate=False, residual=False,
+                 seed=int(sigma), qk_sigma=sigma, name=f"peaky_x{sigma:g}")
+    # per kernel only: with scores of standard deviation ~sigma^2 the softmax is
+    # near one-hot, and the bf16 rounding of q'/k' (part of the kernel chain,
+    # absent from an fp64-throughout chain) can swap near-tied maxima
+    run_and_check(w, e2e=False, qk_sigma=sigma)
+
+
+def test_leak_probe():
+    """V = +100 in one sequence and 0 elsewhere: no other sequence sees it."""
+    import torch
+    descs = [(10, 1, 9, 9, 0, 0), (3, 1, 5, 7, 1, 1), (0, 1, 11, 13, 2, 2)]
+    w = W.custom(descs, H=2, D=128, seed=5, name="leak")
+    b = runner.to_device(w)
+    cu = b.cu_host
+    for s in range(len(descs)):
+        G.say("leak probe, hot sequence", s)
+        b.v.zero_()
+        b.v[cu[s]:cu[s + 1]] = 100.0
+        runner.run_modulate_rope(b)
+        runner.run_attention(b)
+        torch.cuda.synchronize()
+        O = G.f64(b.o)
+        for s2 in range(len(descs)):
+            blk = O[cu[s2]:cu[s2 + 1]]
+            if s2 == s:
+                # P is rounded to bf16 before PV while the normaliser sums the
+                # fp32 probabilities: within a few bf16 ulps of 100.
+                assert np.abs(blk - 100.0).max() <= 1.0
+            else:
+                np.testing.assert_array_equal(blk, 0.0)
+
+
+def test_packed_equals_alone_and_determinism():
+    import torch
+    descs = [(17, 1, 10, 14, 0, 0), (2, 1, 3, 3, 1, 1), (0, 1, 16, 20, 2, 2)]
+    w = W.custom(descs, H=2, D=128, seed=9, name="alone")
+    b = runner.to_device(w)
+    G.say("packed vs alone")
+    runner.run_modulate_rope(b)
+    runner.run_attention(b)
+    torch.cuda.synchronize()
+    O1 = b.o.clone()
+    L1 = b.lse.clone()
+    runner.run_attention(b)
+    torch.cuda.synchronize()
+    assert torch.equal(O1.view(torch.int16), b.o.view(torch.int16)), "not deterministic"
+    assert torch.equal(L1, b.lse)
+    for s in range(len(descs)):
+        a0, a1 = int(b.cu_host[s]), int(b.cu_host[s + 1])
+        L = a1 - a0
+        o = torch.empty((L, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.H, L), dtype=torch.float32, device="cuda")
+        cu1 = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        native.varlen_attn_fwd(b.qr[a0:a1], b.kr[a0:a1], b.v[a0:a1], o, cu1, L, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), O1[a0:a1].view(torch.int16)), s
+        assert torch.equal(lse, L1[:, a0:a1]), s
+
+
+def test_guard_bands_and_strides():
+    """Outputs written exactly where they belong: canary bands around every
+    output stay intact; q/k/v as slices of one fused [T][3][H][D] buffer;
+    q'/k' written in place."""
+    import torch
+    descs = [(13, 1, 9, 10, 0, 0), (4, 1, 6, 6, 1, 1)]
+    w = W.custom(descs, H=2, D=128, modulate=True, residual=True, seed=21, name="guards")
+    b = runner.to_device(w)
+    T, H, D = w.T, w.H, w.D
+    g = 64
+    CANARY = 0x4B1D   # a finite bf16 bit pattern
+
+    def banded(shape):
+        buf = torch.full((shape[0] + 2 * g,) + tuple(shape[1:]), CANARY, dtype=torch.int16,
+                         device="cuda").view(torch.bfloat16)
+        return buf, buf[g:g + shape[0]]
+
+    qkv = torch.empty((T, 3, H, D), dtype=torch.bfloat16, device="cuda")
+    qkv[:, 0] = b.q
+    qkv[:, 1] = b.k
+    qkv[:, 2] = b.v
+    q, k, v = qkv[:, 0], qkv[:, 1], qkv[:, 2]
+    G.say("in-place modulate_rope on fused qkv")
+    native.modulate_rope(q, k, q, k, b.pos, w.rope_dims, w.rope_base, b.shift, b.scale, b.mod_row,
+                         w.eps)
+    runner.run_modulate_rope(b)          # reference: separate buffers
+    torch.cuda.synchronize()
+    assert torch.equal(q.contiguous().view(torch.int16), b.qr.view(torch.int16))
+    assert torch.equal(k.contiguous().view(torch.int16), b.kr.view(torch.int16))
+    ob, o = banded((T, H, D))
+    lse_buf = torch.full((H * T + 2 * g,), 12345.0, dtype=torch.float32, device="cuda")
+    lse = lse_buf[g:g + H * T].view(H, T)
+    G.say("attention with fused-qkv strides and banded outputs")
+    native.varlen_attn_fwd(q, k, v, o, b.cu, b.max_seqlen, lse=lse)
+    runner.run_attention(b)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), b.o.view(torch.int16))
+    assert torch.equal(lse, b.lse)
+    assert torch.all(ob[:g].view(torch.int16) == CANARY) and torch.all(ob[-g:].view(torch.int16) == CANARY)
+    assert torch.all(lse_buf[:g] == 12345.0) and torch.all(lse_buf[-g:] == 12345.0)
+    yb, y = banded((T, H * D))
+    zb, z = banded((T, H * D))
+    G.say("gated residual with banded outputs")
+    native.gated_residual(b.x, o.view(T, -1), y, b.gate, b.mod_row, b.shift2, b.scale2, z, w.eps)
+    runner.run_gated_residual(b)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), b.y.view(torch.int16))
+    assert torch.equal(z.view(torch.int16), b.z.view(torch.int16))
+    for buf in (yb, zb):
+        assert torch.all(buf[:g].view(torch.int16) == CANARY)
+        assert torch.all(buf[-g:].view(torch.int16) == CANARY)
+    # gated residual in place (y == x) and without the fused norm
+    x2 = b.x.clone()
+    native.gated_residual(x2, o.view(T, -1), x2, b.gate, b.mod_row)
+    torch.cuda.synchronize()
+    assert torch.equal(x2.view(torch.int16), b.y.view(torch.int16))
+
+
+def test_zero_tokens_is_noop():
+    import torch
+    q = torch.empty((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    cu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pos = torch.empty((0, 3), dtype=torch.int32, device="cuda")
+    native.modulate_rope(q, q, q, q, pos, (0, 32, 32))
+    native.varlen_attn_fwd(q, q, q, q, cu, 0)
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    native.gated_residual(x, x, x, x, cu)
+    torch.cuda.synchronize()
+
+
+def test_gate_zero_is_exact_residual():
+    """gate = 0: y equals x bit for bit."""
+    import torch
+    w = W.custom([(5, 1, 6, 6, 0, 0)], H=2, D=64, modulate=True, residual=True, seed=3, name="g0")
+    b = runner.to_device(w)
+    b.gate.zero_()
+    runner.run_chain(b)
+    torch.cuda.synchronize()
+    assert torch.equal(b.y.view(torch.int16), b.x.view(torch.int16))
