@@ -134,6 +134,8 @@ mf_status mf_varlen_attn_fwd(void* stream, const void* q, const void* k, const v
     if (max_seqlen < 0 || max_seqlen > T || (T > 0 && max_seqlen == 0)) return MF_ERR_SHAPE;
     if (ld_qkv < int64_t(H) * D || ld_o < int64_t(H) * D) return MF_ERR_SHAPE;
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MF_ERR_SHAPE;
+    // 32-bit buffer offsets inside one sequence's rows (plus a ragged tile)
+    if ((int64_t(max_seqlen) + 256) * ld_qkv * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
     // work units must fit a 1D grid
     if (int64_t(H) * (T / 128 + 1 + n_seq) > (int64_t(1) << 30)) return MF_ERR_SHAPE;
     if (T == 0) return MF_OK;

@@ -27,6 +27,18 @@ __device__ __forceinline__ void st16(uint16_t* p, u32x4_t v) {
     *reinterpret_cast<u32x4_t*>(p) = v;
 }
 
+// Raw buffer resource over [base, base + bytes): a buffer load whose offset
+// falls outside the range returns zeros instead of touching memory, which
+// lets ragged tiles load without branches.  The range is clamped to 4 GiB-1,
+// so every in-range offset is an address inside the caller's tensor.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : uint32_t(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // Exact widening of the two bf16 halves of a dword.
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

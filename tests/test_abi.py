@@ -91,6 +91,8 @@ def test_attention_validation():
     assert attn(ws=None) == WS
     assert attn(ws_bytes=8) == WS
     assert attn(ws=P + 16) == ALIGN
+    # one sequence's rows must be addressable with 32-bit byte offsets
+    assert attn(T=2_000_000, max_seqlen=2_000_000, ld=4096, ld_o=256) == UNSUP
     assert attn(T=0, n_seq=0, max_seqlen=0, q=None, k=None, v=None, o=None, cu=None) == 0
 
 

@@ -238,3 +238,20 @@ def test_gate_zero_is_exact_residual():
     runner.run_chain(b)
     torch.cuda.synchronize()
     assert torch.equal(b.y.view(torch.int16), b.x.view(torch.int16))
+
+
+def test_many_sequences_prologue_schedule():
+    """More sequences than the in-kernel scheduler takes: the schedule comes
+    from the prologue kernel through the workspace (lengths 0..150, shuffled)."""
+    rng = np.random.default_rng(314)
+    descs = []
+    for s in range(100):
+        t = int(rng.integers(0, 20))
+        h = int(rng.integers(0, 12))
+        ww = int(rng.integers(0, 12)) if h else 0
+        if s % 10 == 7:
+            t, h, ww = 0, 0, 0          # empty sequences in the middle of the pack
+        descs.append((t, 1, h, ww, s, s))
+    w = W.custom(descs, H=2, D=128, modulate=True, residual=True, seed=315, name="many_seqs")
+    assert w.n_seq > 64 and min(w.seq_lens) == 0
+    run_and_check(w)
