@@ -16,6 +16,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
@@ -37,6 +39,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane
+// group, lane j points at a row of 4 consecutive 16-bit elements; lane i
+// receives element i%4 of the rows pointed at by lanes i/4, 4+i/4, 8+i/4 and
+// 12+i/4 (in that order).
+__device__ __forceinline__ s16x4_t lds_read_tr16_b64(const void* p) {
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// Direct global->LDS load of 16 bytes per lane through a buffer resource:
+// lane i's bytes land at lds + 16*i (lds must be the same for the whole
+// wavefront); out-of-range offsets deposit zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16, voff,
+                                             soff, 0, 0);
 }
 
 // Exact widening of the two bf16 halves of a dword.

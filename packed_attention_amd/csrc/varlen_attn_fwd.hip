@@ -9,35 +9,42 @@
 // "Resumo Tecnico: Mage-Flow", Metodologia > 2. NR-MMDiT.
 //
 // Design (MI355X, CDNA4):
-//  * Work unit = (sequence, head, 128-query tile).  A one-workgroup prologue
-//    kernel orders the sequences longest first and writes the unit ranges
-//    into the caller's workspace; the main grid maps blockIdx to units with
-//    an XCD-aware permutation so that consecutive units (same sequence and
-//    head, hence the same K/V) land on the same XCD and share its L2.
-//  * 256 threads = 4 wavefronts; each wavefront owns 32 query rows.  The Q
-//    rows live in VGPRs for the whole tile as MFMA B operands.
-//  * K/V advance in 64-key tiles, double-buffered in LDS: the next tile's
-//    global loads are issued before the current tile's MFMAs and written to
-//    the other LDS buffer after them, one barrier per tile.
+//  * Work unit = (sequence, head, 128-query tile).  Sequences are ordered
+//    longest first (in-kernel for packs of up to 64 sequences, otherwise by a
+//    one-workgroup prologue kernel writing into the caller's workspace), and
+//    blockIdx maps to units through an XCD-aware permutation so consecutive
+//    units (same sequence and head, hence the same K/V) share one XCD's L2.
+//  * One workgroup of 8 wavefronts per CU (two per SIMD, 256 registers
+//    each) sharing every K/V tile; each wavefront owns 32 query rows, held
+//    in VGPRs as MFMA B operands for the whole tile.  Two waves per SIMD
+//    because one wavefront alone cannot stream LDS operands fast enough to
+//    feed its MFMAs (about 1 KiB per 32-cycle MFMA).
 //  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: every lane then holds 16 keys of one query
-//    row, so the online-softmax max/sum need one cross-half exchange and
-//    the rescale of the output accumulator is a per-lane scalar.
-//  * The fp32 probabilities are rounded to bf16 in registers and used
-//    directly as the B operand of O^T += V^T P^T: the MFMA accumulator
-//    layout of S^T gives each lane keys {4h..4h+3, 8+4h..8+4h+3} of every
-//    16-key chunk, so V^T is stored in LDS with that key order inside each
-//    16-key chunk and read with one 16-byte access per MFMA.
-//  * V is transposed on the way into LDS: each thread loads 4 keys x 8 dims
-//    (4 16-byte loads), transposes the 4x8 bf16 block with byte permutes and
-//    writes 8 x 8 bytes.  LDS layouts are bank-conflict free for the 16 lanes
-//    a 16-byte access serves per cycle (32 lanes for 8-byte writes) over 64
-//    banks, by padding rows (K: 256 -> 272 bytes, V^T: 128 -> 144 bytes)
-//    rather than swizzling, so all operand addresses are affine.
-//  * Full tiles run an unguarded path; only the ragged last tile of a
-//    sequence masks keys and zero-fills its loads.
-//  * exp2 with the softmax scale folded into one FMA (scale * log2 e);
-//    all softmax state in fp32.
+//    v_mfma_f32_32x32x16_bf16: every lane holds 16 keys of one query row, so
+//    the online-softmax max/sum need one v_permlane32_swap and the rescale of
+//    the output accumulator is a per-lane scalar.  The fp32 probabilities are
+//    rounded to bf16 in registers and used directly as the B operand of
+//    O^T += V^T P^T: V^T is stored in LDS with the key order that the S^T
+//    accumulator layout gives each lane ({4h..4h+3, 8+4h..8+4h+3} of every
+//    16-key chunk), read with one 16-byte access per MFMA.
+//  * Per 64-key tile a wavefront runs S^T = K Q^T (2*D/16 MFMAs), the
+//    online softmax (VALU), then O^T += V^T P^T (D/8 MFMAs); with two waves
+//    per SIMD one wave's softmax runs while the other's MFMAs execute.
+//    Operand fragments are read from LDS four MFMAs ahead, pinned with
+//    sched_barrier so the scheduler does not sink them next to their use.
+//  * K and V arrive by direct global->LDS buffer loads (no staging
+//    registers, no LDS stores), double-buffered: tile t+1 is fetched while
+//    tile t is consumed, one barrier per tile.  V stays row-major and is
+//    read transposed (ds_read_b64_tr_b16) into the V^T operand.  Rows are
+//    padded (K: 2D -> 2D+16 bytes, V: 2D -> 2D+64) so every LDS read cycle
+//    hits distinct banks of the 64, with affine addresses.
+//  * Q/K/V are read through raw buffer resources that end at the sequence's
+//    last row, so ragged tiles read zeros without branches; only the last
+//    tile of a sequence masks its scores.
+//  * exp2 with the softmax scale folded into one FMA (scale * log2 e); the
+//    reference max is raised lazily (only when a row max grows by more than
+//    2^8), so the output accumulator is rarely rescaled; all softmax state
+//    in fp32.
 #include <cmath>
 
 #include "mf_device.h"
@@ -46,33 +53,43 @@
 namespace mf {
 namespace {
 
-constexpr int kBM = 128;        // query rows per workgroup
+constexpr int kWaves = 8;       // wavefronts per workgroup: 2 per SIMD
+constexpr int kBM = 32 * kWaves; // query rows per workgroup (32 per wavefront)
 constexpr int kBN = 64;         // keys per K/V tile
-constexpr int kThreads = 256;   // 4 wavefronts
+constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;        // XCDs of an MI355X; blockIdx round-robins over them
-constexpr int kXcdGroup = 8;    // consecutive work units kept on one XCD
+constexpr int kXcdGroup = 32;   // consecutive work units kept on one XCD (its 32 CUs)
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int kInlineSeqs = 64;  // packs up to this many sequences schedule in-kernel
+constexpr int kPrefetch = 4;     // MFMA operand fragments read ahead from LDS
 
 template <int D>
 struct Tile {
     static constexpr int KK = D / 16;            // QK^T MFMA steps along d
     static constexpr int EB = D / 32;            // 32-wide blocks of the output dim
-    static constexpr int KCH = D / 8;            // 16-byte chunks per K row
+    static constexpr int KCH = D / 8;            // 16-byte chunks per K or V row
+    static constexpr int NQK = 2 * KK;           // MFMAs of one S tile
+    static constexpr int NPV = 4 * EB;           // MFMAs of one PV tile
     // K rows padded by one 16-byte unit: the 16 lanes one LDS cycle serves
-    // (rows r..r+15, same chunk) then start 17 units apart, i.e. on 16
-    // distinct 4-bank groups of the 64 banks, and every MFMA operand address
-    // is the lane's base plus a compile-time offset.
-    static constexpr int K_ROW_BYTES = D * 2 + 16;
+    // (rows r..r+15, same chunk) start 17 units apart, i.e. on 16 distinct
+    // 4-bank groups of the 64 banks, with affine addresses.
+    static constexpr int K_UNITS = KCH + 1;
+    static constexpr int K_ROW_BYTES = 16 * K_UNITS;
     static constexpr int K_BYTES = kBN * K_ROW_BYTES;
-    // V^T rows: 64 keys = 128 bytes (8 units of 16 bytes) padded to 144, so
-    // that rows e and e+1 start 36 banks apart.
-    static constexpr int VT_ROW_BYTES = kBN * 2 + 16;
-    static constexpr int VT_BYTES = D * VT_ROW_BYTES;
-    static constexpr int BUF_BYTES = K_BYTES + VT_BYTES;
-    static constexpr int K_ROWS_PER_PASS = kThreads / KCH;
-    static constexpr int K_PASSES = kBN / K_ROWS_PER_PASS;
-    static constexpr int V_THREADS = (D / 8) * (kBN / 4);   // 8 dims x 4 keys per thread
+    // V rows stay row-major (keys x dims) and are read transposed; rows are
+    // padded to 80 dwords (D=128) / 48 dwords (D=64) so that the 4 rows x 2
+    // column blocks one 32-lane transposed read touches map to all 64 banks.
+    static constexpr int V_UNITS = KCH + 4;
+    static constexpr int V_ROW_BYTES = 16 * V_UNITS;
+    static constexpr int V_BYTES = kBN * V_ROW_BYTES;
+    static constexpr int LDS_BYTES = 2 * K_BYTES + 2 * V_BYTES;   // K0 K1 V0 V1
+    // Direct global->LDS loads: one wave instruction fills 64 consecutive
+    // 16-byte units, so a tile takes K_UNITS (V_UNITS) instructions, dealt
+    // round-robin to the wavefronts.
+    static constexpr int K_DMA = K_UNITS;
+    static constexpr int V_DMA = V_UNITS;
+    static constexpr int K_DMA_PER_WAVE = (K_DMA + kWaves - 1) / kWaves;
+    static constexpr int V_DMA_PER_WAVE = (V_DMA + kWaves - 1) / kWaves;
 };
 
 // Workspace layout (int32): [0] number of work units, [1] n_seq,
@@ -128,23 +145,27 @@ struct KParams {
     float scale_log2;   // softmax_scale * log2(e)
 };
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-    // low bf16 of a in the low half, low bf16 of b in the high half
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+// Wait until this wavefront's direct global->LDS loads have landed
+// (vmcnt(0); expcnt and lgkmcnt left unconstrained).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Lanes l and l+32 hold the two halves of one query row's keys: combine them
+// with one v_permlane32_swap (each lane ends with {own, partner} in some order).
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
     using TL = Tile<D>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     // ---- decode the work unit -------------------------------------------
-    // Packs of up to kInlineSeqs sequences are scheduled here, by every
-    // workgroup (cheaper than a prologue launch); larger ones read the
-    // schedule the prologue kernel wrote into the workspace.
     __shared__ int32_t sched[3 * kInlineSeqs + 2];
     const int w = xcd_remap(blockIdx.x);
     const int n = p.n_seq;
@@ -214,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     // Buffer resources over this sequence's rows of the head: loads of rows
     // at or past L return zeros (ragged q-tile and last K/V tile).
     const uint64_t seq_bytes = uint64_t(L) * uint64_t(ld) * 2u;
-    const int64_t head_off = (tok0 * ld + int64_t(head) * D);
+    const int64_t head_off = tok0 * ld + int64_t(head) * D;
     const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(p.q + head_off, seq_bytes);
     const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(p.k + head_off, seq_bytes);
     const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(p.v + head_off, seq_bytes);
@@ -230,62 +251,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
             qf[kk] = __builtin_bit_cast(bf16x8_t, bload16(q_rs, qoff, 32u * kk));
     }
 
-    // ---- per-thread K/V load offsets and LDS addresses --------------------
-    // K: thread -> (row k_row0 + 16*i, 16-byte chunk k_chunk).
-    const int k_chunk = tid % TL::KCH;
-    const int k_row0 = tid / TL::KCH;
-    // V: thread -> (4-key group v_kg, 8-dim chunk v_ec); key group fastest so
-    // the 32 lanes of one LDS write cycle cover two whole V^T rows 8 apart.
-    const int v_kg = tid % (kBN / 4);
-    const int v_ec = tid / (kBN / 4);
-    const bool v_active = (TL::V_THREADS == kThreads) || tid < TL::V_THREADS;
-    const uint32_t k_voff = uint32_t(k_row0) * row_bytes + 16u * k_chunk;
-    const uint32_t v_voff = uint32_t(4 * v_kg) * row_bytes + 16u * v_ec;
-    // LDS byte offsets inside one buffer
-    const int k_wr = k_row0 * TL::K_ROW_BYTES + k_chunk * 16;
-    const int v_wr = (8 * v_ec) * TL::VT_ROW_BYTES + (2 * (v_kg >> 2) + (v_kg & 1)) * 16 +
-                     ((v_kg >> 1) & 1) * 8;
-    const int k_rd = l32 * TL::K_ROW_BYTES + hlf * 16;                    // + b*32 rows + kk*32 B
-    const int v_rd = TL::K_BYTES + l32 * TL::VT_ROW_BYTES + hlf * 16;     // + m*32 rows + cc*32 B
-
-    u32x4_t kreg[TL::K_PASSES];
-    u32x4_t vreg[4];
-
-    // Global -> registers for the tile starting at key kv0 (rows past the end
-    // of the sequence read as zeros).
-    auto gload = [&](int kv0) {
-        const uint32_t base = uint32_t(kv0) * row_bytes;
+    // ---- direct-load offsets and LDS read addresses -----------------------
+    // DMA instruction n of a tile covers units [64n, 64n+64); lane i fetches
+    // unit 64n+i = (row, chunk) of the padded LDS image.  Pad units fetch a
+    // duplicate of the row's last chunk (never read back).
+    uint32_t k_dma_off[TL::K_DMA_PER_WAVE], v_dma_off[TL::V_DMA_PER_WAVE];
 #pragma unroll
-        for (int i = 0; i < TL::K_PASSES; ++i)
-            kreg[i] = bload16(k_rs, k_voff, base + uint32_t(i * TL::K_ROWS_PER_PASS) * row_bytes);
-        if (v_active) {
+    for (int j = 0; j < TL::K_DMA_PER_WAVE; ++j) {
+        const int u = 64 * (wave + kWaves * j) + lane;
+        const int c = u % TL::K_UNITS;
+        k_dma_off[j] = uint32_t(u / TL::K_UNITS) * row_bytes + 16u * uint32_t(c < TL::KCH ? c : TL::KCH - 1);
+    }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vreg[r] = bload16(v_rs, v_voff, base + uint32_t(r) * row_bytes);
+    for (int j = 0; j < TL::V_DMA_PER_WAVE; ++j) {
+        const int u = 64 * (wave + kWaves * j) + lane;
+        const int c = u % TL::V_UNITS;
+        v_dma_off[j] = uint32_t(u / TL::V_UNITS) * row_bytes + 16u * uint32_t(c < TL::KCH ? c : TL::KCH - 1);
+    }
+    // K fragment of lane: row l32 (+32 per key block), bytes 16*hlf (+32 per kk).
+    const int k_rd = l32 * TL::K_ROW_BYTES + hlf * 16;
+    // V^T fragment via two transposed reads: in each 16-lane group lane j
+    // addresses row (4h + j/4) of the 16-key chunk (+8 rows for the second
+    // read) at dims 32m + 16*(group&1) + 4*(j&3); lane i then receives dim
+    // 32m + (lane&31) for 4 consecutive keys.
+    const int v_rd = (4 * hlf + ((lane & 15) >> 2)) * TL::V_ROW_BYTES +
+                     2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    auto kbuf = [&](int b) { return smem + b * TL::K_BYTES; };
+    auto vbuf = [&](int b) { return smem + 2 * TL::K_BYTES + b * TL::V_BYTES; };
+
+    // Direct loads of K/V tile `tile` into an LDS buffer (rows past the end
+    // of the sequence read as zeros through the buffer range check).
+    auto dma_k = [&](int tile, unsigned char* kb) {
+        const uint32_t base = uint32_t(tile) * kBN * row_bytes;
+#pragma unroll
+        for (int j = 0; j < TL::K_DMA_PER_WAVE; ++j) {
+            const int nidx = wave + kWaves * j;
+            if (TL::K_DMA % kWaves == 0 || nidx < TL::K_DMA)
+                dma16(k_rs, kb + 1024 * nidx, k_dma_off[j], base);
         }
     };
-
-    // Registers -> LDS buffer `buf`; V is transposed on the way (4 keys x 8
-    // dims -> 8 rows of V^T, 4 keys each, in the MFMA key order).
-    auto swrite = [&](int buf) {
-        unsigned char* b = smem + buf * TL::BUF_BYTES;
+    auto dma_v = [&](int tile, unsigned char* vb) {
+        const uint32_t base = uint32_t(tile) * kBN * row_bytes;
 #pragma unroll
-        for (int i = 0; i < TL::K_PASSES; ++i)
-            *reinterpret_cast<u32x4_t*>(b + k_wr + i * TL::K_ROWS_PER_PASS * TL::K_ROW_BYTES) = kreg[i];
-        if (v_active) {
-            unsigned char* vt = b + TL::K_BYTES + v_wr;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int wd = i >> 1;
-                u32x2_t val;
-                if ((i & 1) == 0) {
-                    val[0] = lo_pair(vreg[0][wd], vreg[1][wd]);
-                    val[1] = lo_pair(vreg[2][wd], vreg[3][wd]);
-                } else {
-                    val[0] = hi_pair(vreg[0][wd], vreg[1][wd]);
-                    val[1] = hi_pair(vreg[2][wd], vreg[3][wd]);
-                }
-                *reinterpret_cast<u32x2_t*>(vt + i * TL::VT_ROW_BYTES) = val;
-            }
+        for (int j = 0; j < TL::V_DMA_PER_WAVE; ++j) {
+            const int nidx = wave + kWaves * j;
+            if (TL::V_DMA % kWaves == 0 || nidx < TL::V_DMA)
+                dma16(v_rs, vb + 1024 * nidx, v_dma_off[j], base);
         }
     };
 
@@ -297,33 +308,55 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     float m_run = -INFINITY;
     float l_run = 0.f;
     const float c = p.scale_log2;
-
     const int nkv = (L + kBN - 1) / kBN;
-    const int nfull = L / kBN;                     // tiles needing no key mask
+    const bool ragged = (L % kBN) != 0;
 
-    // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  `cur` is the
-    // LDS buffer holding this tile; the next tile (if any) is fetched into
-    // registers at the start and stored into the other buffer at the end.
-    auto step = [&](int it, const int cur, bool masked) {
-        const unsigned char* b = smem + cur * TL::BUF_BYTES;
-        const int nxt = it + 1;
-        if (nxt < nkv) gload(nxt * kBN);
+    // Operand fragment of MFMA op `i`: S ops read K fragment i (key block
+    // i&1, d-step i>>1); PV ops read the V^T fragment of (chunk i/EB, output
+    // block i%EB) with two transposed reads (keys 4h..4h+3, 8+4h..8+4h+3).
+    auto kfrag = [&](int i, const unsigned char* kb) -> bf16x8_t {
+        return *reinterpret_cast<const bf16x8_t*>(kb + k_rd + (i & 1) * 32 * TL::K_ROW_BYTES + (i >> 1) * 32);
+    };
+    auto vfrag = [&](int j, const unsigned char* vb) -> bf16x8_t {
+        const unsigned char* a = vb + v_rd + (j / TL::EB) * 16 * TL::V_ROW_BYTES + (j % TL::EB) * 64;
+        const s16x4_t lo = lds_read_tr16_b64(a);
+        const s16x4_t hi = lds_read_tr16_b64(a + 8 * TL::V_ROW_BYTES);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
+    // One K/V tile t in buffers `cur`: S^T = K Q^T, online softmax,
+    // O^T += V^T P^T.  The direct loads of tile t+1 into the other buffers
+    // are issued first and land during this tile's work.
+    auto step = [&](int t, const int cur, bool masked) {
+        const unsigned char* kb = kbuf(cur);
+        const unsigned char* vb = vbuf(cur);
+        if (t + 1 < nkv) {
+            dma_k(t + 1, kbuf(cur ^ 1));
+            dma_v(t + 1, vbuf(cur ^ 1));
+        }
+
+        // S^T for the 64 keys: two 32-key accumulators; fragments read from
+        // LDS kPrefetch MFMAs ahead (sched_barrier keeps them ahead).
         f32x16_t s[2];
+        {
+            bf16x8_t fr[kPrefetch];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
+            for (int i = 0; i < kPrefetch; ++i) fr[i] = kfrag(i, kb);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[bb][r] = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < TL::KK; ++kk) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-                    b + k_rd + bb * 32 * TL::K_ROW_BYTES + kk * 32);
-                s[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[bb], 0, 0, 0);
+            for (int i = 0; i < TL::NQK; ++i) {
+                const bf16x8_t f = fr[i % kPrefetch];
+                if (i < 2)
+                    s[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[0], f32x16_t{}, 0, 0, 0);
+                else
+                    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[i >> 1], s[i & 1], 0, 0, 0);
+                if (i + kPrefetch < TL::NQK) fr[i % kPrefetch] = kfrag(i + kPrefetch, kb);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
         if (masked) {
-            const int kv0 = it * kBN;
+            const int kv0 = t * kBN;
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -344,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int r = (bb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c;
+        mx = half_max(mx) * c;
         const bool raise = mx > m_run + kRescaleLog2;
         if (__any(raise)) {
             const float m_new = raise ? mx : m_run;
@@ -357,58 +390,60 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
                 for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
         }
         float lsum = 0.f;
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], c, -m_run));
-                s[bb][r] = e;
-                lsum += e;
-            }
-        l_run += lsum;
-
-        // P^T fragments (bf16) for the four 16-key chunks.
         bf16x8_t pf[4];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            const int bb = cc >> 1;
-            const int r0 = 8 * (cc & 1);
+            const int bb = cc >> 1, r0 = 8 * (cc & 1);
+            float e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r0 + i], c, -m_run));
+                lsum += e[i];
+            }
             u32x4_t u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) u[i] = pack_bf16x2(s[bb][r0 + 2 * i], s[bb][r0 + 2 * i + 1]);
+            for (int i = 0; i < 4; ++i) u[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
             pf[cc] = __builtin_bit_cast(bf16x8_t, u);
         }
+        l_run += lsum;
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T over EB independent accumulators, chunk outer.
+        {
+            bf16x8_t fr[kPrefetch];
 #pragma unroll
-        for (int m = 0; m < TL::EB; ++m)
+            for (int i = 0; i < kPrefetch; ++i) fr[i] = vfrag(i, vb);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
-                    b + v_rd + m * 32 * TL::VT_ROW_BYTES + cc * 32);
-                oacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[cc], oacc[m], 0, 0, 0);
+            for (int i = 0; i < TL::NPV; ++i) {
+                const bf16x8_t f = fr[i % kPrefetch];
+                oacc[i % TL::EB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[i / TL::EB],
+                                                                          oacc[i % TL::EB], 0, 0, 0);
+                if (i + kPrefetch < TL::NPV) fr[i % kPrefetch] = vfrag(i + kPrefetch, vb);
+                __builtin_amdgcn_sched_barrier(0);
             }
-
-        if (nxt < nkv) swrite(cur ^ 1);
+        }
+        wait_dma();
         __syncthreads();
     };
 
-    gload(0);
-    swrite(0);
+    dma_k(0, kbuf(0));
+    dma_v(0, vbuf(0));
+    wait_dma();
     __syncthreads();
-    int it = 0;
-    for (; it + 2 <= nfull; it += 2) {       // unrolled pair: buffers 0 then 1
-        step(it, 0, false);
-        step(it + 1, 1, false);
+    const int nfull = ragged ? nkv - 1 : nkv;
+    int t = 0;
+    for (; t + 2 <= nfull; t += 2) {       // unrolled pair: buffers 0 then 1
+        step(t, 0, false);
+        step(t + 1, 1, false);
     }
-    if (it < nfull) {
-        step(it, 0, false);
-        ++it;
+    if (t < nfull) {
+        step(t, 0, false);
+        ++t;
     }
-    if (it < nkv) step(it, it & 1, true);
+    if (t < nkv) step(t, t & 1, true);
 
     // ---- epilogue -------------------------------------------------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+    const float l_tot = half_sum(l_run);
     if (qrow < L) {
         const float inv = 1.0f / l_tot;
         uint16_t* op = p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 4 * hlf;
@@ -444,7 +479,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
     const int64_t units = int64_t(a.H) * ((a.T + kBM - 1) / kBM + a.n_seq);
     const int64_t quantum = int64_t(kXcds) * kXcdGroup;
     const int64_t grid = (units + quantum - 1) / quantum * quantum;
-    const size_t smem = 2 * Tile<D>::BUF_BYTES;
+    const size_t smem = Tile<D>::LDS_BYTES;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&attn_fwd_kernel<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
         int(smem));

@@ -132,3 +132,9 @@ def test_library_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_library_resolves_every_symbol():
+    """Load with immediate binding: an undefined symbol (e.g. a kernel stub the
+    host pass failed to emit) fails here instead of at the first GPU call."""
+    ctypes.CDLL(native.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
