@@ -69,7 +69,7 @@ def test_modulate_rope_validation():
 
 def attn(**kw):
     a = dict(stream=None, q=P, k=P, v=P, o=P, lse=None, cu=P, n_seq=1, max_seqlen=4, T=4, H=2,
-             D=128, ld=256, ld_o=256, scale=0.088, ws=P, ws_bytes=1 << 20)
+             D=128, ld=256, ld_o=256, scale=0.088, ws=P, ws_bytes=1 << 31)
     a.update(kw)
     return native.lib().mf_varlen_attn_fwd(*a.values())
 
