@@ -34,15 +34,17 @@
 //    two transposed LDS reads (ds_read_b64_tr_b16) of the row-major V tile
 //    deliver as the V^T operand.
 //  * Per 64-key tile a wavefront runs S^T = K Q^T (2*D/16 MFMAs), the online
-//    softmax (VALU), then O^T += V^T P^T (D/8 MFMAs); with two waves per
-//    SIMD one wave's softmax runs while the other's MFMAs execute.  Operand
+//    softmax (VALU), then O^T += V^T P^T (D/8 MFMAs).  The two wavefronts of
+//    a SIMD are half a tile apart: waves 0..3 run S, softmax, PV of tile i
+//    between two barriers while waves 4..7 run softmax, PV of tile i and S
+//    of tile i+1, so one wave's softmax overlaps the other's MFMAs.  Operand
 //    fragments are read from LDS four MFMAs ahead, pinned with
 //    sched_barrier so the scheduler does not sink them next to their use.
 //  * K and V arrive by direct global->LDS buffer loads (no staging
-//    registers, no LDS stores), double-buffered: tile t+1 is fetched while
-//    tile t is consumed, one barrier per tile.  Rows are padded (K: 2D ->
-//    2D+16 bytes, V: 2D -> 2D+64) so every LDS read cycle hits distinct
-//    banks of the 64, with affine addresses.
+//    registers, no LDS stores) issued by waves 0..3, two K tiles and one V
+//    tile ahead of use (3 K buffers, 2 V buffers), one barrier per tile.
+//    Rows are padded (K: 2D -> 2D+16 bytes, V: 2D -> 2D+64) so every LDS
+//    read cycle hits distinct banks of the 64, with affine addresses.
 //  * Q/K/V are read through raw buffer resources that end at the sequence's
 //    last row, so ragged tiles read zeros without branches; only the last
 //    key tile of a sequence masks its scores.
@@ -66,6 +68,7 @@ constexpr int kXcds = 8;         // XCDs of an MI355X; blockIdx round-robins ove
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr int kInlineSeqs = 64;  // packs up to this many sequences schedule in-kernel
 constexpr int kPrefetch = 4;     // MFMA operand fragments read ahead from LDS
+constexpr int kLoaders = kWaves / 2;  // leading wavefronts, which issue the K/V loads
 
 template <int D>
 struct Tile {
@@ -86,14 +89,16 @@ struct Tile {
     static constexpr int V_UNITS = KCH + 4;
     static constexpr int V_ROW_BYTES = 16 * V_UNITS;
     static constexpr int V_BYTES = kBN * V_ROW_BYTES;
-    static constexpr int LDS_BYTES = 2 * K_BYTES + 2 * V_BYTES;   // K0 K1 V0 V1
+    static constexpr int K_STAGES = 3;           // K of tiles i, i+1, i+2
+    static constexpr int V_STAGES = 2;           // V of tiles i, i+1
+    static constexpr int LDS_BYTES = K_STAGES * K_BYTES + V_STAGES * V_BYTES;
     // Direct global->LDS loads: one wave instruction fills 64 consecutive
     // 16-byte units, so a tile takes K_UNITS (V_UNITS) instructions, dealt
-    // round-robin to the wavefronts.
+    // round-robin to the leading wavefronts.
     static constexpr int K_DMA = K_UNITS;
     static constexpr int V_DMA = V_UNITS;
-    static constexpr int K_DMA_PER_WAVE = (K_DMA + kWaves - 1) / kWaves;
-    static constexpr int V_DMA_PER_WAVE = (V_DMA + kWaves - 1) / kWaves;
+    static constexpr int K_DMA_PER_WAVE = (K_DMA + kLoaders - 1) / kLoaders;
+    static constexpr int V_DMA_PER_WAVE = (V_DMA + kLoaders - 1) / kLoaders;
     // One partial-result slot of the workspace: unnormalised O (fp32,
     // kBM x D), then the reference max (log2 units) and sum of each row.
     static constexpr size_t SLOT_BYTES = size_t(kBM) * D * 4 + size_t(kBM) * 8;
@@ -259,10 +264,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
     unsigned char* const partials = p.ws + sched_bytes(p.n_seq);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hlf = lane >> 5;
+    // Waves 0..3 (one per SIMD) lead and issue the direct loads; waves 4..7
+    // trail them by one softmax phase (see the step loop below).
+    const bool lead = wave < kLoaders;
+    const int lw = wave & (kLoaders - 1);
     const int64_t ld = p.ld_qkv;
     const uint32_t row_bytes = uint32_t(ld) * 2u;
     const float c = p.scale_log2;
@@ -270,17 +279,18 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
     // ---- direct-load offsets and LDS read addresses (same for every tile) --
     // DMA instruction n of a tile covers units [64n, 64n+64); lane i fetches
     // unit 64n+i = (row, chunk) of the padded LDS image.  Pad units fetch a
-    // duplicate of the row's last chunk (never read back).
+    // duplicate of the row's last chunk (never read back).  Instruction n is
+    // issued by leading wave n % kLoaders.
     uint32_t k_dma_off[TL::K_DMA_PER_WAVE], v_dma_off[TL::V_DMA_PER_WAVE];
 #pragma unroll
     for (int j = 0; j < TL::K_DMA_PER_WAVE; ++j) {
-        const int u = 64 * (wave + kWaves * j) + lane;
+        const int u = 64 * (lw + kLoaders * j) + lane;
         const int cc = u % TL::K_UNITS;
         k_dma_off[j] = uint32_t(u / TL::K_UNITS) * row_bytes + 16u * uint32_t(cc < TL::KCH ? cc : TL::KCH - 1);
     }
 #pragma unroll
     for (int j = 0; j < TL::V_DMA_PER_WAVE; ++j) {
-        const int u = 64 * (wave + kWaves * j) + lane;
+        const int u = 64 * (lw + kLoaders * j) + lane;
         const int cc = u % TL::V_UNITS;
         v_dma_off[j] = uint32_t(u / TL::V_UNITS) * row_bytes + 16u * uint32_t(cc < TL::KCH ? cc : TL::KCH - 1);
     }
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
     const int v_rd = (4 * hlf + ((lane & 15) >> 2)) * TL::V_ROW_BYTES +
                      2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     auto kbuf = [&](int b) { return smem + b * TL::K_BYTES; };
-    auto vbuf = [&](int b) { return smem + 2 * TL::K_BYTES + b * TL::V_BYTES; };
+    auto vbuf = [&](int b) { return smem + TL::K_STAGES * TL::K_BYTES + b * TL::V_BYTES; };
 
     bool first_segment = true;
     for (int64_t it = range_begin(sch.W, g, p.G); it < it_end;) {
@@ -307,12 +317,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
         const int nkv = __builtin_amdgcn_readfirstlane(sch.nkv[rank]);
         const int tile = __builtin_amdgcn_readfirstlane(at.tile);
         const int kv0 = __builtin_amdgcn_readfirstlane(at.step);
-        const int kv1 = int(min(int64_t(nkv), int64_t(kv0) + (it_end - it)));
+        const int kv1 = __builtin_amdgcn_readfirstlane(int(min(int64_t(nkv), int64_t(kv0) + (it_end - it))));
         const int head = tile / nt;
         const int qtile = tile - head * nt;
         const int64_t tok0 = __builtin_amdgcn_readfirstlane(p.cu[seq]);
         const int L = __builtin_amdgcn_readfirstlane(p.cu[seq + 1]) - int(tok0);
-        const bool ragged = (L % kBN) != 0;
+        // the last key tile of a sequence whose length is not a multiple of
+        // kBN has keys past the end: those scores are masked
+        const int masked_tile = (L % kBN) != 0 ? nkv - 1 : nkv;
         it += kv1 - kv0;
 
         // Buffer resources over this sequence's rows of the head: loads of
@@ -323,23 +335,30 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
         const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(p.k + head_off, seq_bytes);
         const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(p.v + head_off, seq_bytes);
 
-        // Direct loads of key tile `t` into LDS buffer b.
-        auto dma = [&](int t, int b) {
+        // Direct loads of key tile `t` into K buffer kb / V buffer vb
+        // (leading waves only).
+        auto dma_k = [&](int t, int kb) {
             const uint32_t base = uint32_t(t) * kBN * row_bytes;
 #pragma unroll
             for (int j = 0; j < TL::K_DMA_PER_WAVE; ++j) {
-                const int nidx = wave + kWaves * j;
-                if (TL::K_DMA % kWaves == 0 || nidx < TL::K_DMA)
-                    dma16(k_rs, kbuf(b) + 1024 * nidx, k_dma_off[j], base);
-            }
-#pragma unroll
-            for (int j = 0; j < TL::V_DMA_PER_WAVE; ++j) {
-                const int nidx = wave + kWaves * j;
-                if (TL::V_DMA % kWaves == 0 || nidx < TL::V_DMA)
-                    dma16(v_rs, vbuf(b) + 1024 * nidx, v_dma_off[j], base);
+                const int nidx = lw + kLoaders * j;
+                if (TL::K_DMA % kLoaders == 0 || nidx < TL::K_DMA)
+                    dma16(k_rs, kbuf(kb) + 1024 * nidx, k_dma_off[j], base);
             }
         };
-        dma(kv0, 0);
+        auto dma_v = [&](int t, int vb) {
+            const uint32_t base = uint32_t(t) * kBN * row_bytes;
+#pragma unroll
+            for (int j = 0; j < TL::V_DMA_PER_WAVE; ++j) {
+                const int nidx = lw + kLoaders * j;
+                if (TL::V_DMA % kLoaders == 0 || nidx < TL::V_DMA)
+                    dma16(v_rs, vbuf(vb) + 1024 * nidx, v_dma_off[j], base);
+            }
+        };
+        auto dma = [&](int t, int kb, int vb) {
+            dma_k(t, kb);
+            dma_v(t, vb);
+        };
 
         // Q^T fragments (B operand), kept in registers.
         const int qrow = qtile * kBM + wave * 32 + l32;    // row inside the sequence
@@ -372,33 +391,34 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
             return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
 
-        // One key tile t in buffers `cur`: S^T = K Q^T, online softmax,
-        // O^T += V^T P^T.  The direct loads of tile t+1 into the other
-        // buffers are issued first and land during this tile's work.
-        auto step = [&](int t, const int cur, bool masked) {
-            const unsigned char* kb = kbuf(cur);
-            const unsigned char* vb = vbuf(cur);
-            if (t + 1 < kv1) dma(t + 1, cur ^ 1);
-
-            f32x16_t s[2];
-            {
-                bf16x8_t fr[kPrefetch];
+        // S^T = K Q^T for one key tile held in K buffer kb.
+        f32x16_t s[2];
+        auto qk = [&](const unsigned char* kb) {
+            bf16x8_t fr[kPrefetch];
 #pragma unroll
-                for (int i = 0; i < kPrefetch; ++i) fr[i] = kfrag(i, kb);
+            for (int i = 0; i < kPrefetch; ++i) fr[i] = kfrag(i, kb);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TL::NQK; ++i) {
+                const bf16x8_t f = fr[i % kPrefetch];
+                if (i < 2)
+                    s[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[0], f32x16_t{}, 0, 0, 0);
+                else
+                    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[i >> 1], s[i & 1], 0, 0, 0);
+                if (i + kPrefetch < TL::NQK) fr[i % kPrefetch] = kfrag(i + kPrefetch, kb);
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < TL::NQK; ++i) {
-                    const bf16x8_t f = fr[i % kPrefetch];
-                    if (i < 2)
-                        s[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[0], f32x16_t{}, 0, 0, 0);
-                    else
-                        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[i >> 1], s[i & 1], 0, 0, 0);
-                    if (i + kPrefetch < TL::NQK) fr[i % kPrefetch] = kfrag(i + kPrefetch, kb);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
             }
+        };
 
-            if (masked) {
+        // Online softmax of key tile t (scores in s) for this lane's query
+        // row, then O^T += V^T P^T with the tile's V in buffer vb.  The
+        // exponentials use a reference max m_run that is only raised when a
+        // row's block max exceeds it by more than kRescaleLog2 (so p <=
+        // 2^kRescaleLog2); numerator and denominator share m_run, so the
+        // result is the same softmax, and the output accumulator is rescaled
+        // only on those (rare, wave-uniform) occasions.
+        auto softmax_pv = [&](int t, const unsigned char* vb) {
+            if (t == masked_tile) {
                 const int key0 = t * kBN;
 #pragma unroll
                 for (int bb = 0; bb < 2; ++bb)
@@ -408,13 +428,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
                         if (key >= L) s[bb][r] = -INFINITY;
                     }
             }
-
-            // Online softmax for this lane's query row.  The exponentials use
-            // a reference max m_run that is only raised when a row's block
-            // max exceeds it by more than kRescaleLog2 (so p <= 2^kRescaleLog2);
-            // numerator and denominator share m_run, so the result is the same
-            // softmax, and the output accumulator is rescaled only on those
-            // (rare, wave-uniform) occasions.
             float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
@@ -451,37 +464,59 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
             l_run += lsum;
 
             // O^T += V^T P^T over EB independent accumulators, chunk outer.
-            {
-                bf16x8_t fr[kPrefetch];
+            bf16x8_t fr[kPrefetch];
 #pragma unroll
-                for (int i = 0; i < kPrefetch; ++i) fr[i] = vfrag(i, vb);
+            for (int i = 0; i < kPrefetch; ++i) fr[i] = vfrag(i, vb);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TL::NPV; ++i) {
+                const bf16x8_t f = fr[i % kPrefetch];
+                oacc[i % TL::EB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[i / TL::EB],
+                                                                          oacc[i % TL::EB], 0, 0, 0);
+                if (i + kPrefetch < TL::NPV) fr[i % kPrefetch] = vfrag(i + kPrefetch, vb);
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < TL::NPV; ++i) {
-                    const bf16x8_t f = fr[i % kPrefetch];
-                    oacc[i % TL::EB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[i / TL::EB],
-                                                                              oacc[i % TL::EB], 0, 0, 0);
-                    if (i + kPrefetch < TL::NPV) fr[i % kPrefetch] = vfrag(i + kPrefetch, vb);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
             }
-            wait_dma();
-            __syncthreads();
         };
 
+        // ---- key steps -----------------------------------------------------
+        // Iteration i (0 <= i <= n) runs softmax + PV of tile i-1, then S of
+        // tile i; the leading waves pass the step barrier between the two,
+        // the trailing waves after both.  Between two barriers a leading wave
+        // thus runs S(i), softmax(i), PV(i) while a trailing wave runs
+        // softmax(i), PV(i), S(i+1): on each SIMD one wave's softmax (VALU)
+        // overlaps the other wave's MFMAs instead of both alternating in
+        // lockstep.  In that interval K of tiles i and i+1 and V of tile i
+        // are read, so K of tile i+2 and V of tile i+1 are fetched into the
+        // third K buffer and the second V buffer (K of tile i in buffer i%3,
+        // V in buffer i%2).  Only the leading waves load; each barrier
+        // follows its wave's own loads landing.
+        const int n = kv1 - kv0;
+        if (lead) {
+            dma(kv0, 0, 0);
+            if (n > 1) dma_k(kv0 + 1, 1);
+        }
         wait_dma();
         __syncthreads();
-        const int kfull = (ragged && kv1 == nkv) ? kv1 - 1 : kv1;   // steps needing no mask
-        int t = kv0;
-        for (; t + 2 <= kfull; t += 2) {     // unrolled pair: buffers 0 then 1
-            step(t, 0, false);
-            step(t + 1, 1, false);
+        int k0 = 0, k1 = 1, k2 = 2, v0 = 0;     // K buffers of tiles i, i+1, i+2; V of tile i
+        for (int i = 0; i <= n; ++i) {
+            if (i > 0) softmax_pv(kv0 + i - 1, vbuf(v0 ^ 1));
+            if (lead) {
+                wait_dma();
+                __syncthreads();
+                if (i + 2 < n) dma_k(kv0 + i + 2, k2);
+                if (i + 1 < n) dma_v(kv0 + i + 1, v0 ^ 1);
+            }
+            if (i < n) qk(kbuf(k0));
+            if (!lead) {
+                wait_dma();
+                __syncthreads();
+            }
+            const int kt = k0;
+            k0 = k1;
+            k1 = k2;
+            k2 = kt;
+            v0 ^= 1;
         }
-        if (t < kfull) {
-            step(t, 0, false);
-            ++t;
-        }
-        if (t < kv1) step(t, (t - kv0) & 1, true);
 
         // ---- epilogue ----------------------------------------------------
         const float l_tot = half_sum(l_run);
