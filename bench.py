@@ -4,7 +4,10 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 mf_modulate_rope -> mf_varlen_attn_fwd -> mf_gated_residual, with the inputs
-already resident in HBM.  Steps rotate over several copies of the batch so
+already resident in HBM.  The timed steps replay one captured HIP graph per
+input set (the same kernels as the eager calls, submitted at once; --eager
+times the three Python calls instead, and the eager step time is reported
+beside it).  Steps rotate over several copies of the batch so
 that each step starts from inputs that are not in the 256 MB Infinity Cache.
 Prints one JSON line:
   value       attention FLOPs (4 * d * H * sum L^2) per step / step time,
@@ -101,11 +104,13 @@ def cpu_baseline(w, budget_s=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="single_1024")
     ap.add_argument("--sets", type=int, default=4, help="input copies rotated over (defeats MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as three eager calls instead of a captured HIP graph")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -134,18 +139,32 @@ def main():
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
 
-    # Whole-step timing: K steps bracketed by device synchronisation.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(sets[i % len(sets)])
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    def timed(fn):
+        """K calls of fn(i) bracketed by device synchronisation and events on
+        the current stream; returns (ms per call, wall seconds)."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / args.steps, time.perf_counter() - t0
+
+    # Whole step, eager: three library calls per step from Python.
+    ms_step_eager, _ = timed(lambda i: step(sets[i % len(sets)]))
+    # Whole step as one HIP graph per input set (the same kernels, submitted
+    # at once): the reported value.
+    graphs = None
+    if not args.eager:
+        graphs = [runner.capture_chain(b) for b in sets]
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        ms_step, wall = timed(lambda i: graphs[i % len(graphs)].replay())
+    else:
+        ms_step, wall = timed(lambda i: step(sets[i % len(sets)]))
 
     # Per-kernel durations: HIP events on the stream the kernels run on.
     names = ("modulate_rope", "varlen_attn_fwd", "gated_residual")
@@ -192,6 +211,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_eager": round(ms_step_eager, 5),
+        "step_submission": "eager" if args.eager else "hip_graph",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

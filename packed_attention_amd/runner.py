@@ -105,3 +105,16 @@ def run_chain(b: DeviceBatch, stream=None):
     run_modulate_rope(b, stream)
     run_attention(b, stream)
     run_gated_residual(b, stream)
+
+
+def capture_chain(b: DeviceBatch):
+    """Record one pass of the hot path on `b` into a HIP graph (torch's
+    CUDAGraph wrapper); ``g.replay()`` then re-runs the three calls with one
+    submission.  The path enqueues kernels only (no memsets, no allocation),
+    so the graph holds exactly the eager kernels.  Run the chain eagerly once
+    before capturing so that one-time set-up happens outside the capture."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_chain(b)
+    return g

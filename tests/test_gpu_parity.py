@@ -261,3 +261,40 @@ def test_many_sequences_prologue_schedule():
     w = W.custom(descs, H=2, D=128, modulate=True, residual=True, seed=315, name="many_seqs")
     assert w.n_seq > 64 and min(w.seq_lens) == 0
     run_and_check(w)
+
+
+@pytest.mark.parametrize("which", ["modulated_pack", "many_sequences"])
+def test_graph_replay_matches_eager(which):
+    """The whole chain captured in a HIP graph: every replay (with eager work
+    and synchronisation between replays) reproduces the eager outputs bit for
+    bit, for the in-kernel schedule and for the prologue-kernel schedule."""
+    import torch
+    if which == "modulated_pack":
+        w = W.custom([(40, 1, 12, 20, 0, 0), (7, 1, 9, 5, 1, 1)], H=2, D=128, modulate=True,
+                     residual=True, seed=77, name="graph_pack")
+    else:
+        descs = [(s % 9, 1, s % 5, (s % 7) if s % 5 else 0, s, s) for s in range(80)]
+        w = W.custom(descs, H=2, D=64, modulate=True, residual=True, seed=78, name="graph_many")
+        assert w.n_seq > 64
+    G.say("graph replay", w.name, "T", w.T, "n_seq", w.n_seq)
+    b = runner.to_device(w)
+    other = runner.to_device(W.custom([(5, 1, 6, 6, 0, 0)], H=2, D=128, modulate=True,
+                                      residual=True, seed=79, name="graph_other"))
+    outs = lambda: (b.qr, b.kr, b.o, b.lse, b.y, b.z)  # noqa: E731
+    runner.run_chain(b)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs()]
+    g = runner.capture_chain(b)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs():
+            t.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, r in zip(("q'", "k'", "O", "LSE", "y", "z"), outs(), ref):
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                               r.view(torch.int32) if r.dtype == torch.float32 else r.view(torch.int16)), \
+                f"replay {rep}: {name} differs from the eager result"
+        runner.run_chain(other)          # unrelated eager work between replays
+        torch.cuda.synchronize()
