@@ -20,37 +20,50 @@ namespace {
 
 constexpr int kTokensPerBlock = 4;
 
+// Up to C = 3072: five wavefronts per SIMD (<= 96 VGPRs), so that all
+// tokens of a 1024^2 pack (17 per CU) are resident at once.
 template <int NCH, bool kFusedNorm>
-__global__ __launch_bounds__(256) void gated_residual_kernel(GatedResArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH <= 6 ? 5 : 1))) void
+gated_residual_kernel(GatedResArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t t = int64_t(blockIdx.x) * kTokensPerBlock + (threadIdx.x >> 6);
+    // wave-uniform (readfirstlane): the buffer resources below live in SGPRs
+    const int64_t t = int64_t(blockIdx.x) * kTokensPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t >= a.T) return;
     const int C = a.C;
     const int nch = C >> 3;
-    const int64_t m = a.mod_row[t];
-    const uint16_t* xr = a.x + t * C;
-    const uint16_t* orow = a.o + t * C;
-    const uint16_t* gr = a.gate + m * C;
-    uint16_t* yr = a.y + t * C;
+    const int64_t m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
+    // Raw buffer resources over the rows: chunks past the row (C not a
+    // multiple of 512) read zeros and their stores are dropped, so no load or
+    // store sits behind a branch and all loads of the row are in flight at once.
+    const uint32_t row_bytes = uint32_t(C) * 2u;
+    const __amdgpu_buffer_rsrc_t x_rs = make_rsrc(a.x + t * C, row_bytes);
+    const __amdgpu_buffer_rsrc_t o_rs = make_rsrc(a.o + t * C, row_bytes);
+    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(a.gate + m * C, row_bytes);
+    const __amdgpu_buffer_rsrc_t y_rs = make_rsrc(a.y + t * C, row_bytes);
 
+    u32x4_t px[NCH], po[NCH], pg[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const uint32_t off = 16u * uint32_t(lane + kWave * i);
+        px[i] = bload16(x_rs, off, 0);
+        po[i] = bload16(o_rs, off, 0);
+        pg[i] = bload16(g_rs, off, 0);
+    }
     float y[NCH][8];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-        const int ci = lane + kWave * i;
-        if (ci < nch) {
-            float fx[8], fo[8], fg[8];
-            unpack8(ld16(xr + 8 * ci), fx);
-            unpack8(ld16(orow + 8 * ci), fo);
-            unpack8(ld16(gr + 8 * ci), fg);
+        float fx[8], fo[8], fg[8];
+        unpack8(px[i], fx);
+        unpack8(po[i], fo);
+        unpack8(pg[i], fg);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) y[i][j] = fx[j] + fg[j] * fo[j];
-            st16(yr + 8 * ci, pack8(y[i]));
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) y[i][j] = 0.f;
-        }
+        for (int j = 0; j < 8; ++j) y[i][j] = fx[j] + fg[j] * fo[j];
+        bstore16(y_rs, 16u * uint32_t(lane + kWave * i), 0, pack8(y[i]));
     }
     if constexpr (kFusedNorm) {
+        // LayerNorm of the fp32 y (population variance), two passes; the
+        // zero-filled chunks past the row hold y = 0 and are left out of the
+        // variance.
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < NCH; ++i)
@@ -61,29 +74,26 @@ __global__ __launch_bounds__(256) void gated_residual_kernel(GatedResArgs a) {
         float v = 0.f;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            if (lane + kWave * i < nch) {
+            const bool in = lane + kWave * i < nch;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float d = y[i][j] - mean;
-                    v += d * d;
-                }
+            for (int j = 0; j < 8; ++j) {
+                const float d = y[i][j] - mean;
+                v += in ? d * d : 0.f;
             }
         }
         const float rstd = rsqrtf(wave_sum(v) * invC + a.eps);
-        const uint16_t* sh = a.shift2 + m * C;
-        const uint16_t* sc = a.scale2 + m * C;
-        uint16_t* zr = a.z + t * C;
+        const __amdgpu_buffer_rsrc_t sh_rs = make_rsrc(a.shift2 + m * C, row_bytes);
+        const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(a.scale2 + m * C, row_bytes);
+        const __amdgpu_buffer_rsrc_t z_rs = make_rsrc(a.z + t * C, row_bytes);
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const int ci = lane + kWave * i;
-            if (ci < nch) {
-                float fs[8], fc[8], r[8];
-                unpack8(ld16(sh + 8 * ci), fs);
-                unpack8(ld16(sc + 8 * ci), fc);
+            const uint32_t off = 16u * uint32_t(lane + kWave * i);
+            float fs[8], fc[8], r[8];
+            unpack8(bload16(sh_rs, off, 0), fs);
+            unpack8(bload16(sc_rs, off, 0), fc);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) r[j] = (y[i][j] - mean) * rstd * (1.0f + fc[j]) + fs[j];
-                st16(zr + 8 * ci, pack8(r));
-            }
+            for (int j = 0; j < 8; ++j) r[j] = (y[i][j] - mean) * rstd * (1.0f + fc[j]) + fs[j];
+            bstore16(z_rs, off, 0, pack8(r));
         }
     }
 }

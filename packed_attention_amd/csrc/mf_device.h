@@ -40,6 +40,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// 16-byte store through a buffer resource; stores whose offset falls
+// outside the resource's range are dropped.
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, u32x4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                          r, voff, soff, 0);
+}
 
 // gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane
 // group, lane j points at a row of 4 consecutive 16-bit elements; lane i
@@ -86,11 +92,27 @@ __device__ __forceinline__ u32x4_t pack8(const float* f) {
     return r;
 }
 
-// Sum over the 64 lanes of a wavefront; every lane receives the total.
+// DPP lane permutation within rows of 16 lanes (all rows and banks enabled).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront; every lane receives the same total
+// (bitwise: each step adds two values in an order-independent way).  A
+// butterfly inside each row of 16 lanes with DPP (swap neighbours, swap
+// pairs, mirror within 8, mirror within 16), then v_permlane16_swap adds row
+// pairs and v_permlane32_swap the two halves: eight VALU instructions, no
+// LDS traffic.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);   // row_half_mirror
+    v += dpp<0x140>(v);   // row_mirror
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
 }
 
 }  // namespace mf

@@ -28,9 +28,10 @@ struct ModRopeArgs {
     const int32_t* pos;
     int32_t rope_f, rope_r, rope_c;
     float rope_base, eps;
-    // Rotation frequency of every pair of a head (index = dim / 2), filled by
-    // the launcher in double precision: base^(-2j / D_axis).
-    double theta[64];
+    // Rotation frequency of every pair of a head (index = dim / 2) in turns
+    // per position, filled by the launcher in double precision:
+    // base^(-2j / D_axis) / (2 pi).
+    double theta_turns[64];
 };
 hipError_t launch_modulate_rope(const ModRopeArgs& a, hipStream_t stream);
 
