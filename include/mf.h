@@ -173,6 +173,44 @@ mf_status mf_varlen_attn_fwd(void* stream,
                              float softmax_scale, void* workspace, size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
+ * Backward of the block-diagonal attention (training).
+ *
+ * Gradients of O = softmax(softmax_scale * Q K^T) V per packed sequence and
+ * head, given dO = dout and the forward's lse:
+ *   P = exp(softmax_scale * Q K^T - lse) (row-wise, recomputed),
+ *   D_i = sum_e dO[i,e] O[i,e]  (from the bf16 o),
+ *   dV = P^T dO,  dS = P * (dO V^T - D),
+ *   dQ = softmax_scale * dS K,  dK = softmax_scale * dS^T Q.
+ * The pages train this model with the same fused kernels as the forward
+ * (picx.dev summary of Mage-Flow, Methodology > Training Infrastructure);
+ * these are the chain-rule gradients of the forward above.  bf16 MFMA
+ * products with fp32 accumulation; P and dS are rounded to bf16 as MFMA
+ * operands; outputs rounded to bf16.  Deterministic (no atomics).
+ *
+ * q, k, v: the forward's bf16 [T][H][D] inputs, token stride ld_qkv.
+ * o, dout: bf16 [T][H][D], token stride ld_o (the forward's output and its
+ *   gradient).
+ * lse: fp32 [H][T], the forward's natural-log row sums.
+ * dq, dk, dv: bf16 [T][H][D], token stride ld_dqkv; fully written (every
+ *   row of every head); they must not overlap any input.
+ * cu_seqlens, n_seq, max_seqlen, softmax_scale: as for the forward.
+ * workspace: device memory of at least mf_varlen_attn_bwd_workspace_bytes
+ *   bytes, 256-byte aligned (it holds D and the work-unit tables; concurrent
+ *   calls need distinct workspaces).
+ * D in {64, 128}; strides multiples of 8 elements.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
+ * MF_ERR_WORKSPACE, MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+size_t mf_varlen_attn_bwd_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D);
+
+mf_status mf_varlen_attn_bwd(void* stream,
+                             const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             const int32_t* cu_seqlens, int32_t n_seq, int32_t max_seqlen,
+                             int64_t T, int32_t H, int32_t D, int64_t ld_qkv, int64_t ld_o,
+                             int64_t ld_dqkv, float softmax_scale, void* workspace,
+                             size_t workspace_bytes);
+
+/* ------------------------------------------------------------------------
  * Gated residual, optionally fused with the next sub-layer's adaLN.
  *
  *   y[t] = x[t] + gate[m(t)] * o[t]                        (fp32, then bf16)

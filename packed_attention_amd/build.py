@@ -34,7 +34,8 @@ HIP_FLAGS = [
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE]
 
-HIP_SOURCES = ["abi.cpp", "modulate_rope.hip", "gated_residual.hip", "varlen_attn_fwd.hip"]
+HIP_SOURCES = ["abi.cpp", "modulate_rope.hip", "gated_residual.hip", "varlen_attn_fwd.hip",
+               "varlen_attn_bwd.hip"]
 HOST_SOURCES = ["pack_tables.cpp"]
 
 

@@ -169,6 +169,63 @@ mf_status mf_varlen_attn_fwd(void* stream, const void* q, const void* k, const v
     return finish(mf::launch_varlen_attn_fwd(a, s), s);
 }
 
+size_t mf_varlen_attn_bwd_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D) {
+    return mf::attn_bwd_workspace_bytes(n_seq, T, H, D);
+}
+
+mf_status mf_varlen_attn_bwd(void* stream, const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             const int32_t* cu_seqlens, int32_t n_seq, int32_t max_seqlen, int64_t T,
+                             int32_t H, int32_t D, int64_t ld_qkv, int64_t ld_o, int64_t ld_dqkv,
+                             float softmax_scale, void* workspace, size_t workspace_bytes) {
+    if (T < 0 || T > INT32_MAX || H <= 0 || H > 4096) return MF_ERR_SHAPE;
+    if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
+    if (n_seq < 0 || (T > 0 && n_seq < 1) || n_seq > (1 << 24)) return MF_ERR_SHAPE;
+    if (max_seqlen < 0 || max_seqlen > T || (T > 0 && max_seqlen == 0)) return MF_ERR_SHAPE;
+    if (ld_qkv < int64_t(H) * D || ld_o < int64_t(H) * D || ld_dqkv < int64_t(H) * D) return MF_ERR_SHAPE;
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MF_ERR_SHAPE;
+    // 32-bit buffer offsets inside one sequence's rows (plus a ragged tile)
+    const int64_t ld_max = ld_qkv > ld_o ? ld_qkv : ld_o;
+    if ((int64_t(max_seqlen) + 256) * ld_max * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
+    // work units must fit a 1D grid
+    if (int64_t(H) * (T / 128 + 1 + n_seq) > (int64_t(1) << 30)) return MF_ERR_SHAPE;
+    if (T == 0) return MF_OK;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens) return MF_ERR_NULL;
+    if (ld_qkv % 8 || ld_o % 8 || ld_dqkv % 8) return MF_ERR_ALIGN;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) ||
+        !aligned(cu_seqlens, 4))
+        return MF_ERR_ALIGN;
+    const size_t need = mf::attn_bwd_workspace_bytes(n_seq, T, H, D);
+    if (workspace == nullptr || workspace_bytes < need) return MF_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MF_ERR_ALIGN;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        std::vector<int32_t> cu;
+        if (!fetch(cu_seqlens, size_t(n_seq) + 1, cu, s)) return MF_ERR_HIP;
+        if (cu[0] != 0 || cu[n_seq] != T) return MF_ERR_TABLE;
+        for (int32_t i = 0; i < n_seq; ++i) {
+            const int64_t L = int64_t(cu[i + 1]) - cu[i];
+            if (L < 0 || L > max_seqlen) return MF_ERR_TABLE;
+        }
+    }
+    mf::AttnBwdArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<const uint16_t*>(o);
+    a.dout = static_cast<const uint16_t*>(dout);
+    a.lse = lse;
+    a.dq = static_cast<uint16_t*>(dq);
+    a.dk = static_cast<uint16_t*>(dk);
+    a.dv = static_cast<uint16_t*>(dv);
+    a.cu_seqlens = cu_seqlens; a.n_seq = n_seq; a.max_seqlen = max_seqlen;
+    a.T = T; a.H = H; a.D = D; a.ld_qkv = ld_qkv; a.ld_o = ld_o; a.ld_d = ld_dqkv;
+    a.softmax_scale = softmax_scale; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return finish(mf::launch_varlen_attn_bwd(a, s), s);
+}
+
 mf_status mf_gated_residual(void* stream, const void* x, const void* o, void* y, const void* gate,
                             const int32_t* mod_row, const void* shift2, const void* scale2, void* z,
                             int64_t T, int32_t C, float eps) {

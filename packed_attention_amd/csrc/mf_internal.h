@@ -68,4 +68,26 @@ struct AttnArgs {
 size_t attn_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D);
 hipError_t launch_varlen_attn_fwd(const AttnArgs& a, hipStream_t stream);
 
+struct AttnBwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    const int32_t* cu_seqlens;
+    int32_t n_seq, max_seqlen;
+    int64_t T;
+    int32_t H, D;
+    int64_t ld_qkv, ld_o, ld_d;
+    float softmax_scale;
+    void* workspace;
+    size_t workspace_bytes;
+};
+size_t attn_bwd_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D);
+hipError_t launch_varlen_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
+
 }  // namespace mf

@@ -1,0 +1,581 @@
+// Block-diagonal (varlen) softmax attention backward for gfx950.
+//
+// What it computes: the gradients dQ, dK, dV of O = softmax(tau Q K^T) V,
+// per packed sequence and head, given dO and the forward's row log-sum-exp.
+// With P = softmax rows and D_i = sum_e dO[i,e] O[i,e]:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = tau dS K,
+//   dK = tau dS^T Q.
+// P is recomputed from the forward's LSE: P = exp(tau S - LSE) (exact, no
+// running max).  Sources: the method's attention is the block-diagonal joint
+// attention of the picx.dev summary of Mage-Flow, Methodology >
+// Native-Resolution MMDiT (variable-length kernels over packed samples with
+// per-sample cumulative offsets); the pages report training with these
+// kernels (Methodology > Training Infrastructure), whose backward is this
+// chain rule.
+//
+// Design (MI355X, CDNA4): three kernels, no atomics, deterministic.
+//  * bwd_tiles_kernel: per-sequence tile counts and their prefix sums (one
+//    workgroup), so work units map to (sequence, head, tile) by a binary
+//    search, with no empty workgroups for packs of many short sequences.
+//  * bwd_dot_kernel: D = rowsum(dO * O) in fp32, HBM-bound.
+//  * attn_bwd_dkdv_kernel: a work unit is 128 keys of one head (4
+//    wavefronts, one per SIMD, 32 keys each).  A wavefront keeps its K and V
+//    rows in registers as MFMA B operands and streams the sequence's queries
+//    in steps of 64 through LDS (Q and dO tiles plus LSE and D, by direct
+//    global->LDS loads, two steps ahead, three buffers).  Per 32-query block:
+//    S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16; every lane then
+//    holds one key and 16 queries), P and dS in fp32 VALU, then
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read transposed from
+//    LDS (ds_read_b64_tr_b16) and P / dS rounded to bf16 straight from the
+//    accumulator layout as the B operand.  The accumulators are transposed
+//    (d x keys), so the epilogue stores 4 consecutive dims per lane.
+//  * attn_bwd_dq_kernel: a work unit is 256 queries of one head (8
+//    wavefronts, 2 per SIMD, 32 queries each), the forward's structure: Q and
+//    dO rows in registers, K and V tiles of 64 keys through LDS,
+//    S^T = K Q^T and dP^T = V dO^T (every lane holds one query and 16 keys,
+//    so LSE and D are per-lane scalars), dS^T in VALU, dQ^T += K^T dS^T with
+//    K^T read transposed.
+//  * Rows that are read both row-wise (16-byte reads) and transposed are
+//    padded to 2D+48 bytes: the 16-byte reads are conflict-free, the
+//    transposed reads 2-way.  Rows read row-wise only are padded to 2D+16.
+//  * Ragged tiles: buffer resources end at the sequence's last row, so rows
+//    past it read as zeros.  Zero Q and dO rows contribute nothing to dK and
+//    dV; keys past the end of the last key tile of the dQ kernel get P = 0.
+#include <cmath>
+
+#include "mf_device.h"
+#include "mf_internal.h"
+
+namespace mf {
+namespace {
+
+constexpr int kKvWaves = 4;                // dK/dV kernel: one wavefront per SIMD
+constexpr int kKvKeys = 32 * kKvWaves;     // keys per dK/dV work unit
+constexpr int kKvQ = 64;                   // queries per dK/dV step
+constexpr int kQWaves = 8;                 // dQ kernel: two wavefronts per SIMD
+constexpr int kQRows = 32 * kQWaves;       // queries per dQ work unit
+constexpr int kQK = 64;                    // keys per dQ step
+constexpr int kStages = 3;                 // LDS buffers (loads two steps ahead)
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct BT {
+    static constexpr int KK = D / 16;              // MFMA k-steps along d
+    static constexpr int EB = D / 32;              // 32-wide blocks of d
+    static constexpr int KCH = D / 8;              // 16-byte chunks per row
+    static constexpr int X_UNITS = KCH + 3;        // row read both ways
+    static constexpr int X_ROW = 16 * X_UNITS;
+    static constexpr int R_UNITS = KCH + 1;        // row read row-wise only
+    static constexpr int R_ROW = 16 * R_UNITS;
+    // dK/dV step: Q tile, dO tile, then LSE[64] and D[64] (fp32)
+    static constexpr int QT_BYTES = kKvQ * X_ROW;
+    static constexpr int KV_STAGE = 2 * QT_BYTES + 2 * kKvQ * 4;
+    static constexpr int KV_LDS = kStages * KV_STAGE;
+    static constexpr int QT_DMA = kKvQ * X_UNITS / 64;   // wave instructions per tile
+    static constexpr int KV_DMA = 2 * QT_DMA;
+    static constexpr int KV_DMA_PER_WAVE = (KV_DMA + kKvWaves - 1) / kKvWaves;
+    // dQ step: K tile (read both ways), V tile (row-wise)
+    static constexpr int KT_BYTES = kQK * X_ROW;
+    static constexpr int VT_BYTES = kQK * R_ROW;
+    static constexpr int Q_STAGE = KT_BYTES + VT_BYTES;
+    static constexpr int Q_LDS = kStages * Q_STAGE;
+    static constexpr int KT_DMA = kQK * X_UNITS / 64;
+    static constexpr int VT_DMA = kQK * R_UNITS / 64;
+    static constexpr int Q_DMA = KT_DMA + VT_DMA;
+    static constexpr int Q_DMA_PER_WAVE = (Q_DMA + kQWaves - 1) / kQWaves;
+    static_assert(kKvQ * X_UNITS % 64 == 0 && kQK * R_UNITS % 64 == 0, "whole DMA instructions");
+};
+
+struct BwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;        // [H][T]
+    float* dsum;             // workspace: D = rowsum(dO * O), [H][T]
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    const int32_t* cu;
+    const int64_t* pre_kv;   // workspace: prefix sums of key tiles per sequence [n+1]
+    const int64_t* pre_q;    // workspace: prefix sums of query tiles per sequence [n+1]
+    int n_seq;
+    int H;
+    int64_t T;
+    int64_t ld_qkv, ld_o, ld_d;
+    float scale;             // tau
+    float c;                 // tau * log2(e)
+};
+
+// Workspace layout: D values, then the two prefix arrays, each 256-aligned.
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+__host__ __device__ constexpr size_t ws_dsum_bytes(int64_t T, int H) { return align256(size_t(T) * H * 4); }
+__host__ __device__ constexpr size_t ws_pre_bytes(int n) { return align256(size_t(n + 1) * 8); }
+
+// ---------------------------------------------------------------------------
+// Tile prefix sums (one workgroup of 256 threads, each a contiguous chunk).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_tiles_kernel(const int32_t* __restrict__ cu, int n,
+                                                        int64_t* __restrict__ pre_kv,
+                                                        int64_t* __restrict__ pre_q) {
+    __shared__ int64_t part_kv[256], part_q[256];
+    const int tid = threadIdx.x;
+    const int per = (n + 255) / 256;
+    const int s0 = min(n, tid * per), s1 = min(n, s0 + per);
+    int64_t akv = 0, aq = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int L = cu[s + 1] - cu[s];
+        akv += (L + kKvKeys - 1) / kKvKeys;
+        aq += (L + kQRows - 1) / kQRows;
+    }
+    part_kv[tid] = akv;
+    part_q[tid] = aq;
+    __syncthreads();
+    if (tid == 0) {
+        int64_t rk = 0, rq = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int64_t a = part_kv[i], b = part_q[i];
+            part_kv[i] = rk;
+            part_q[i] = rq;
+            rk += a;
+            rq += b;
+        }
+        pre_kv[n] = rk;
+        pre_q[n] = rq;
+    }
+    __syncthreads();
+    int64_t bkv = part_kv[tid], bq = part_q[tid];
+    for (int s = s0; s < s1; ++s) {
+        pre_kv[s] = bkv;
+        pre_q[s] = bq;
+        const int L = cu[s + 1] - cu[s];
+        bkv += (L + kKvKeys - 1) / kKvKeys;
+        bq += (L + kQRows - 1) / kQRows;
+    }
+}
+
+// Work unit -> (sequence, head, tile).  Units of sequence s are
+// [pre[s] * H, pre[s+1] * H), head-major.  False past the last unit.
+__device__ bool locate_unit(const int64_t* pre, int n, int H, int64_t unit, int& s, int& h, int& tile) {
+    if (unit >= pre[n] * H) return false;
+    int lo = 0, hi = n - 1;              // last s with pre[s] * H <= unit
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] * H <= unit) lo = mid; else hi = mid - 1;
+    }
+    const int64_t local = unit - pre[lo] * H;
+    const int64_t tiles = pre[lo + 1] - pre[lo];
+    s = lo;
+    h = int(local / tiles);
+    tile = int(local - int64_t(h) * tiles);
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// D[h][t] = sum_e dO[t,h,e] * O[t,h,e]  (fp32 from bf16)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict__ o,
+                                                      const uint16_t* __restrict__ dout, int64_t ld_o,
+                                                      float* __restrict__ dsum, int64_t T, int H) {
+    constexpr int TPR = D / 8;            // threads per (token, head) row, 16 bytes each
+    constexpr int RPB = 256 / TPR;
+    const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / TPR;   // t * H + h
+    const int part = threadIdx.x % TPR;
+    const bool live = row < T * H;
+    const int64_t t = live ? row / H : 0;
+    const int h = live ? int(row - t * H) : 0;
+    float acc = 0.f;
+    if (live) {
+        const u32x4_t a = ld16(o + t * ld_o + int64_t(h) * D + 8 * part);
+        const u32x4_t b = ld16(dout + t * ld_o + int64_t(h) * D + 8 * part);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc += bf_lo(a[i]) * bf_lo(b[i]) + bf_hi(a[i]) * bf_hi(b[i]);
+    }
+#pragma unroll
+    for (int m = TPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, TPR);
+    if (live && part == 0) dsum[int64_t(h) * T + t] = acc;
+}
+
+// Wait for this wavefront's direct global->LDS loads (vmcnt(0)).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposed 8-row x 4-dim fragment pair of a row-major tile: lanes receive
+// dim 32*blk + (lane & 31) of rows {4h..4h+3} and {8+4h..8+4h+3} of the
+// 16-row chunk `chunk` (h = lane / 32), as an MFMA A operand whose k index
+// follows the 32x32 accumulator's row pattern.
+template <int ROW>
+__device__ __forceinline__ bf16x8_t tr_frag(const unsigned char* tile, int tr_rd, int chunk, int blk) {
+    const unsigned char* a = tile + tr_rd + chunk * 16 * ROW + blk * 64;
+    const s16x4_t lo = lds_read_tr16_b64(a);
+    const s16x4_t hi = lds_read_tr16_b64(a + 8 * ROW);
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Lane's byte offset for tr_frag: row (4h + (lane&15)/4) of the chunk, dims
+// 16*((lane>>4)&1) + 4*(lane&3).
+template <int ROW>
+__device__ __forceinline__ int tr_offset(int lane) {
+    return (4 * (lane >> 5) + ((lane & 15) >> 2)) * ROW + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+}
+
+// bf16 B operand of chunk cc (16 rows of the accumulator's m index) from a
+// pair of 32x32 accumulators: registers 8*(cc&1) .. +7 of block cc>>1.
+__device__ __forceinline__ bf16x8_t pack_chunk(const f32x16_t& acc, int half) {
+    u32x4_t u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = pack_bf16x2(acc[8 * half + 2 * i], acc[8 * half + 2 * i + 1]);
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Store a transposed accumulator set (d x 32 rows; lane = row l32, dims
+// 32m + 8gq + 4h .. +3) as bf16 rows, times `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows_t(uint16_t* base, const f32x16_t (&acc)[D / 32], float mul, int hlf) {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            u32x2_t val;
+            val[0] = pack_bf16x2(acc[m][4 * gq] * mul, acc[m][4 * gq + 1] * mul);
+            val[1] = pack_bf16x2(acc[m][4 * gq + 2] * mul, acc[m][4 * gq + 3] * mul);
+            *reinterpret_cast<u32x2_t*>(base + 32 * m + 8 * gq + 4 * hlf) = val;
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(BwdParams p) {
+    using TL = BT<D>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    int seq, head, tile;
+    if (!locate_unit(p.pre_kv, p.n_seq, p.H, blockIdx.x, seq, head, tile)) return;
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    head = __builtin_amdgcn_readfirstlane(head);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hlf = lane >> 5;
+    const int64_t tok0 = __builtin_amdgcn_readfirstlane(p.cu[seq]);
+    const int L = __builtin_amdgcn_readfirstlane(p.cu[seq + 1]) - int(tok0);
+    const uint32_t qrow = uint32_t(p.ld_qkv) * 2u, orow = uint32_t(p.ld_o) * 2u;
+    const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(p.q + tok0 * p.ld_qkv + int64_t(head) * D, uint64_t(L) * qrow);
+    const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(p.k + tok0 * p.ld_qkv + int64_t(head) * D, uint64_t(L) * qrow);
+    const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(p.v + tok0 * p.ld_qkv + int64_t(head) * D, uint64_t(L) * qrow);
+    const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(p.dout + tok0 * p.ld_o + int64_t(head) * D, uint64_t(L) * orow);
+    const __amdgpu_buffer_rsrc_t l_rs = make_rsrc(p.lse + int64_t(head) * p.T + tok0, uint64_t(L) * 4u);
+    const __amdgpu_buffer_rsrc_t d_rs = make_rsrc(p.dsum + int64_t(head) * p.T + tok0, uint64_t(L) * 4u);
+
+    // K and V rows of this wavefront's 32 keys: MFMA B operands of
+    // S = Q K^T and dP = dO V^T (lane: key l32, dims 16kk + 8h .. +7).
+    const int key0 = tile * kKvKeys + wave * 32;
+    bf16x8_t kf[TL::KK], vf[TL::KK];
+    {
+        const uint32_t off = uint32_t(key0 + l32) * qrow + 16u * hlf;
+#pragma unroll
+        for (int kk = 0; kk < TL::KK; ++kk) {
+            kf[kk] = __builtin_bit_cast(bf16x8_t, bload16(k_rs, off, 32u * kk));
+            vf[kk] = __builtin_bit_cast(bf16x8_t, bload16(v_rs, off, 32u * kk));
+        }
+    }
+
+    // Direct loads: instruction n < KV_DMA fills units [64m, 64m+64) of the
+    // Q tile (n < QT_DMA, m = n) or the dO tile (m = n - QT_DMA); wavefront
+    // n % kKvWaves issues it.  Wavefront 0 also loads LSE and D (16 lanes).
+    uint32_t dma_off[TL::KV_DMA_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < TL::KV_DMA_PER_WAVE; ++j) {
+        const int nidx = wave + kKvWaves * j;
+        const int m = nidx < TL::QT_DMA ? nidx : nidx - TL::QT_DMA;
+        const int u = 64 * m + lane;
+        const int cc = u % TL::X_UNITS;
+        const uint32_t rb = nidx < TL::QT_DMA ? qrow : orow;
+        dma_off[j] = uint32_t(u / TL::X_UNITS) * rb + 16u * uint32_t(cc < TL::KCH ? cc : TL::KCH - 1);
+    }
+    auto issue = [&](int t, int stage) {
+        unsigned char* base = smem + stage * TL::KV_STAGE;
+#pragma unroll
+        for (int j = 0; j < TL::KV_DMA_PER_WAVE; ++j) {
+            const int nidx = wave + kKvWaves * j;
+            if (TL::KV_DMA % kKvWaves == 0 || nidx < TL::KV_DMA) {
+                if (nidx < TL::QT_DMA)
+                    dma16(q_rs, base + 1024 * nidx, dma_off[j], uint32_t(t) * kKvQ * qrow);
+                else
+                    dma16(do_rs, base + TL::QT_BYTES + 1024 * (nidx - TL::QT_DMA), dma_off[j],
+                          uint32_t(t) * kKvQ * orow);
+            }
+        }
+        if (wave == 0 && lane < 16) {
+            dma16(l_rs, base + 2 * TL::QT_BYTES, 16u * lane, uint32_t(t) * kKvQ * 4u);
+            dma16(d_rs, base + 2 * TL::QT_BYTES + 4 * kKvQ, 16u * lane, uint32_t(t) * kKvQ * 4u);
+        }
+    };
+
+    f32x16_t dva[TL::EB], dka[TL::EB];
+#pragma unroll
+    for (int m = 0; m < TL::EB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dva[m][r] = dka[m][r] = 0.f;
+
+    const int tr_rd = tr_offset<TL::X_ROW>(lane);
+    const float c = p.c;
+    const int nq = (L + kKvQ - 1) / kKvQ;
+    issue(0, 0);
+    if (nq > 1) issue(1, 1);
+    for (int t = 0; t < nq; ++t) {
+        wait_dma();
+        __syncthreads();
+        if (t + 2 < nq) issue(t + 2, (t + 2) % kStages);
+        const unsigned char* qt = smem + (t % kStages) * TL::KV_STAGE;
+        const unsigned char* ot = qt + TL::QT_BYTES;
+        const float* st = reinterpret_cast<const float*>(qt + 2 * TL::QT_BYTES);
+
+        // S = Q K^T and dP = dO V^T for the two 32-query blocks (lane: key
+        // l32; register r: query 8(r/4) + 4h + r%4 of the block).
+        f32x16_t s[2], dp[2];
+#pragma unroll
+        for (int kk = 0; kk < TL::KK; ++kk)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int off = (32 * b + l32) * TL::X_ROW + 32 * kk + 16 * hlf;
+                const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + off);
+                const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(ot + off);
+                s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], kk == 0 ? f32x16_t{} : s[b], 0, 0, 0);
+                dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], kk == 0 ? f32x16_t{} : dp[b], 0, 0, 0);
+            }
+
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            // P = exp(tau S - LSE), dS = P (dP - D), rows of this block
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + 32 * b + 8 * gq + 4 * hlf);
+                const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(st + kKvQ + 32 * b + 8 * gq + 4 * hlf);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][4 * gq + i], c, -l4[i] * kLog2e));
+                    s[b][4 * gq + i] = pr;
+                    dp[b][4 * gq + i] = pr * (dp[b][4 * gq + i] - d4[i]);
+                }
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS over the block's two 16-query chunks
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const bf16x8_t pb = pack_chunk(s[b], h2);
+                const bf16x8_t sb = pack_chunk(dp[b], h2);
+                const int chunk = 2 * b + h2;
+#pragma unroll
+                for (int m = 0; m < TL::EB; ++m) {
+                    const bf16x8_t oa = tr_frag<TL::X_ROW>(ot, tr_rd, chunk, m);
+                    dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb, dva[m], 0, 0, 0);
+                    const bf16x8_t qa = tr_frag<TL::X_ROW>(qt, tr_rd, chunk, m);
+                    dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb, dka[m], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // epilogue: lane l32 owns key key0 + l32
+    if (key0 + l32 < L) {
+        const int64_t row = (tok0 + key0 + l32) * p.ld_d + int64_t(head) * D;
+        store_rows_t<D>(p.dv + row, dva, 1.0f, hlf);
+        store_rows_t<D>(p.dk + row, dka, p.scale, hlf);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * kQWaves) void attn_bwd_dq_kernel(BwdParams p) {
+    using TL = BT<D>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    int seq, head, tile;
+    if (!locate_unit(p.pre_q, p.n_seq, p.H, blockIdx.x, seq, head, tile)) return;
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    head = __builtin_amdgcn_readfirstlane(head);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hlf = lane >> 5;
+    const int64_t tok0 = __builtin_amdgcn_readfirstlane(p.cu[seq]);
+    const int L = __builtin_amdgcn_readfirstlane(p.cu[seq + 1]) - int(tok0);
+    const uint32_t qrow = uint32_t(p.ld_qkv) * 2u, orow = uint32_t(p.ld_o) * 2u;
+    const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(p.q + tok0 * p.ld_qkv + int64_t(head) * D, uint64_t(L) * qrow);
+    const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(p.k + tok0 * p.ld_qkv + int64_t(head) * D, uint64_t(L) * qrow);
+    const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(p.v + tok0 * p.ld_qkv + int64_t(head) * D, uint64_t(L) * qrow);
+    const __amdgpu_buffer_rsrc_t do_rs = make_rsrc(p.dout + tok0 * p.ld_o + int64_t(head) * D, uint64_t(L) * orow);
+    const __amdgpu_buffer_rsrc_t l_rs = make_rsrc(p.lse + int64_t(head) * p.T + tok0, uint64_t(L) * 4u);
+    const __amdgpu_buffer_rsrc_t d_rs = make_rsrc(p.dsum + int64_t(head) * p.T + tok0, uint64_t(L) * 4u);
+
+    // Q and dO rows of this wavefront's 32 queries: B operands of
+    // S^T = K Q^T and dP^T = V dO^T; LSE and D of the lane's query.
+    const int q0 = tile * kQRows + wave * 32;
+    bf16x8_t qf[TL::KK], of[TL::KK];
+    {
+        const uint32_t qoff = uint32_t(q0 + l32) * qrow + 16u * hlf;
+        const uint32_t ooff = uint32_t(q0 + l32) * orow + 16u * hlf;
+#pragma unroll
+        for (int kk = 0; kk < TL::KK; ++kk) {
+            qf[kk] = __builtin_bit_cast(bf16x8_t, bload16(q_rs, qoff, 32u * kk));
+            of[kk] = __builtin_bit_cast(bf16x8_t, bload16(do_rs, ooff, 32u * kk));
+        }
+    }
+    const float nl = -__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(l_rs, uint32_t(q0 + l32) * 4u, 0, 0)) * kLog2e;
+    const float dq_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d_rs, uint32_t(q0 + l32) * 4u, 0, 0));
+
+    // Direct loads: instruction n < KT_DMA fills units [64n, 64n+64) of the
+    // K tile, the rest the V tile; wavefront n % kQWaves issues it.
+    uint32_t dma_off[TL::Q_DMA_PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < TL::Q_DMA_PER_WAVE; ++j) {
+        const int nidx = wave + kQWaves * j;
+        const bool kt = nidx < TL::KT_DMA;
+        const int units = kt ? TL::X_UNITS : TL::R_UNITS;
+        const int u = 64 * (kt ? nidx : nidx - TL::KT_DMA) + lane;
+        const int cc = u % units;
+        dma_off[j] = uint32_t(u / units) * qrow + 16u * uint32_t(cc < TL::KCH ? cc : TL::KCH - 1);
+    }
+    auto issue = [&](int t, int stage) {
+        unsigned char* base = smem + stage * TL::Q_STAGE;
+        const uint32_t soff = uint32_t(t) * kQK * qrow;
+#pragma unroll
+        for (int j = 0; j < TL::Q_DMA_PER_WAVE; ++j) {
+            const int nidx = wave + kQWaves * j;
+            if (TL::Q_DMA % kQWaves == 0 || nidx < TL::Q_DMA) {
+                if (nidx < TL::KT_DMA)
+                    dma16(k_rs, base + 1024 * nidx, dma_off[j], soff);
+                else
+                    dma16(v_rs, base + TL::KT_BYTES + 1024 * (nidx - TL::KT_DMA), dma_off[j], soff);
+            }
+        }
+    };
+
+    f32x16_t dqa[TL::EB];
+#pragma unroll
+    for (int m = 0; m < TL::EB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqa[m][r] = 0.f;
+
+    const int tr_rd = tr_offset<TL::X_ROW>(lane);
+    const float c = p.c;
+    const int nk = (L + kQK - 1) / kQK;
+    const int masked_tile = (L % kQK) != 0 ? nk - 1 : nk;
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    for (int t = 0; t < nk; ++t) {
+        wait_dma();
+        __syncthreads();
+        if (t + 2 < nk) issue(t + 2, (t + 2) % kStages);
+        const unsigned char* kt = smem + (t % kStages) * TL::Q_STAGE;
+        const unsigned char* vt = kt + TL::KT_BYTES;
+
+        // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks (lane:
+        // query l32; register r: key 8(r/4) + 4h + r%4 of the block).
+        f32x16_t s[2], dp[2];
+#pragma unroll
+        for (int kk = 0; kk < TL::KK; ++kk)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kt + (32 * b + l32) * TL::X_ROW + 32 * kk + 16 * hlf);
+                const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vt + (32 * b + l32) * TL::R_ROW + 32 * kk + 16 * hlf);
+                s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], kk == 0 ? f32x16_t{} : s[b], 0, 0, 0);
+                dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[kk], kk == 0 ? f32x16_t{} : dp[b], 0, 0, 0);
+            }
+        if (t == masked_tile) {
+            const int key0 = t * kQK;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = key0 + 32 * b + 8 * (r >> 2) + 4 * hlf + (r & 3);
+                    if (key >= L) s[b][r] = -INFINITY;
+                }
+        }
+        // dS^T = P^T (dP^T - D), P^T = exp(tau S^T - LSE)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl));
+                dp[b][r] = pr * (dp[b][r] - dq_d);
+            }
+        // dQ^T += K^T dS^T over the four 16-key chunks
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const bf16x8_t sb = pack_chunk(dp[cc >> 1], cc & 1);
+#pragma unroll
+            for (int m = 0; m < TL::EB; ++m) {
+                const bf16x8_t ka = tr_frag<TL::X_ROW>(kt, tr_rd, cc, m);
+                dqa[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sb, dqa[m], 0, 0, 0);
+            }
+        }
+    }
+
+    if (q0 + l32 < L) store_rows_t<D>(p.dq + (tok0 + q0 + l32) * p.ld_d + int64_t(head) * D, dqa, p.scale, hlf);
+}
+
+template <int D>
+hipError_t launch_bwd_d(const AttnBwdArgs& a, hipStream_t stream) {
+    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+    BwdParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.dout = a.dout; p.lse = a.lse;
+    p.dsum = reinterpret_cast<float*>(ws);
+    p.pre_kv = reinterpret_cast<const int64_t*>(ws + ws_dsum_bytes(a.T, a.H));
+    p.pre_q = reinterpret_cast<const int64_t*>(ws + ws_dsum_bytes(a.T, a.H) + ws_pre_bytes(a.n_seq));
+    p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.cu = a.cu_seqlens;
+    p.n_seq = a.n_seq; p.H = a.H; p.T = a.T;
+    p.ld_qkv = a.ld_qkv; p.ld_o = a.ld_o; p.ld_d = a.ld_d;
+    p.scale = a.softmax_scale;
+    p.c = a.softmax_scale * kLog2e;
+
+    hipLaunchKernelGGL(bwd_tiles_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.n_seq,
+                       const_cast<int64_t*>(p.pre_kv), const_cast<int64_t*>(p.pre_q));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t rows = a.T * a.H;
+    hipLaunchKernelGGL(bwd_dot_kernel<D>, dim3(unsigned((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                       a.o, a.dout, a.ld_o, p.dsum, a.T, a.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    static const hipError_t attr_kv = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        int(BT<D>::KV_LDS));
+    if (attr_kv != hipSuccess) return attr_kv;
+    static const hipError_t attr_q = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        int(BT<D>::Q_LDS));
+    if (attr_q != hipSuccess) return attr_q;
+    // Upper bounds of the unit counts: sum_s ceil(L_s / n) <= T / n + n_seq.
+    const int64_t units_kv = int64_t(a.H) * (a.T / kKvKeys + a.n_seq);
+    const int64_t units_q = int64_t(a.H) * (a.T / kQRows + a.n_seq);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(unsigned(units_kv)), dim3(64 * kKvWaves),
+                       BT<D>::KV_LDS, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(unsigned(units_q)), dim3(64 * kQWaves),
+                       BT<D>::Q_LDS, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t /*D*/) {
+    const int n = n_seq < 0 ? 0 : n_seq;
+    return ws_dsum_bytes(T, H) + 2 * ws_pre_bytes(n);
+}
+
+hipError_t launch_varlen_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
+    if (a.D == 128) return launch_bwd_d<128>(a, stream);
+    return launch_bwd_d<64>(a, stream);
+}
+
+}  // namespace mf

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "MF_OK", -1: "MF_ERR_NULL", -2: "MF_ERR_SHAPE", -3: "MF_ERR_A
 # Every symbol include/mf.h declares.
 EXPORTS = ("mf_status_string", "mf_abi_version", "mf_pack_count", "mf_pack_tables",
            "mf_modulate_rope", "mf_varlen_attn_workspace_bytes", "mf_varlen_attn_fwd",
-           "mf_gated_residual")
+           "mf_gated_residual", "mf_varlen_attn_bwd_workspace_bytes", "mf_varlen_attn_bwd")
 
 
 class MFError(RuntimeError):
@@ -71,6 +71,11 @@ def lib() -> ctypes.CDLL:
     L.mf_varlen_attn_fwd.restype = i32
     L.mf_gated_residual.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, f32]
     L.mf_gated_residual.restype = i32
+    L.mf_varlen_attn_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32]
+    L.mf_varlen_attn_bwd_workspace_bytes.restype = sz
+    L.mf_varlen_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32,
+                                     i32, i64, i64, i64, f32, vp, sz]
+    L.mf_varlen_attn_bwd.restype = i32
     _lib = L
     return L
 
@@ -207,3 +212,43 @@ def gated_residual(x, o, y, gate, mod_row, shift2=None, scale2=None, z=None, eps
     check(lib().mf_gated_residual(_stream(stream), _ptr(x), _ptr(o), _ptr(y), _ptr(gate),
                                   _ptr(mod_row), _ptr(shift2), _ptr(scale2), _ptr(z), T, C,
                                   float(eps)))
+
+
+def attn_bwd_workspace_bytes(n_seq: int, T: int, H: int, D: int) -> int:
+    return int(lib().mf_varlen_attn_bwd_workspace_bytes(n_seq, T, H, D))
+
+
+def varlen_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, max_seqlen, softmax_scale=None,
+                    workspace=None, stream=None):
+    """mf_varlen_attn_bwd: dq, dk, dv ([T][H][D] bf16, one token stride) from the forward's
+    q, k, v (one token stride), o and dout (one token stride) and lse (float32 [H][T])."""
+    import torch
+    T, H, D = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                 ("dv", dv)):
+        _check_bf16_rows(n, t, H * D)
+        if tuple(t.shape) != (T, H, D):
+            raise ValueError(f"{n}: shape {tuple(t.shape)} != {(T, H, D)}")
+    ld = _token_stride(q, H * D)
+    if _token_stride(k, H * D) != ld or _token_stride(v, H * D) != ld:
+        raise ValueError("q, k and v must share a token stride")
+    ld_o = _token_stride(o, H * D)
+    if _token_stride(dout, H * D) != ld_o:
+        raise ValueError("o and dout must share a token stride")
+    ld_d = _token_stride(dq, H * D)
+    if _token_stride(dk, H * D) != ld_d or _token_stride(dv, H * D) != ld_d:
+        raise ValueError("dq, dk and dv must share a token stride")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+        raise TypeError("cu_seqlens: expected an int32 CUDA tensor")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (H, T) or not lse.is_contiguous():
+        raise ValueError("lse: expected contiguous float32 [H][T]")
+    n_seq = cu_seqlens.numel() - 1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    need = attn_bwd_workspace_bytes(n_seq, T, H, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    check(lib().mf_varlen_attn_bwd(_stream(stream), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                   _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), n_seq,
+                                   int(max_seqlen), T, H, D, ld, ld_o, ld_d, float(softmax_scale),
+                                   _ptr(workspace), workspace.numel()))

@@ -103,6 +103,37 @@ def test_workspace_query():
     assert a > 0 and a % 256 == 0 and b % 256 == 0 and b >= (3 + 3 * 1000) * 4
 
 
+def attn_bwd(**kw):
+    a = dict(stream=None, q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, cu=P, n_seq=1,
+             max_seqlen=4, T=4, H=2, D=128, ld=256, ld_o=256, ld_d=256, scale=0.088, ws=P,
+             ws_bytes=1 << 31)
+    a.update(kw)
+    return native.lib().mf_varlen_attn_bwd(*a.values())
+
+
+def test_attention_bwd_validation():
+    assert attn_bwd(D=96) == UNSUP
+    assert attn_bwd(H=0) == SHAPE
+    assert attn_bwd(n_seq=0) == SHAPE
+    assert attn_bwd(max_seqlen=5) == SHAPE
+    assert attn_bwd(ld_d=128) == SHAPE
+    assert attn_bwd(scale=-1.0) == SHAPE
+    for name in ("q", "o", "dout", "lse", "dq", "dk", "dv", "cu"):
+        assert attn_bwd(**{name: None}) == NULL, name
+    assert attn_bwd(ld_d=260) == ALIGN
+    assert attn_bwd(dk=PODD) == ALIGN
+    assert attn_bwd(lse=P + 2) == ALIGN
+    assert attn_bwd(ws=None) == WS
+    assert attn_bwd(ws_bytes=64) == WS
+    assert attn_bwd(ws=P + 16) == ALIGN
+    assert attn_bwd(T=2_000_000, max_seqlen=2_000_000, ld=256, ld_o=4096) == UNSUP
+    assert attn_bwd(T=0, n_seq=0, max_seqlen=0, q=None, k=None, v=None, o=None, dout=None,
+                    lse=None, dq=None, dk=None, dv=None, cu=None) == 0
+    lib = native.lib()
+    a = lib.mf_varlen_attn_bwd_workspace_bytes(1, 4352, 24, 128)
+    assert a % 256 == 0 and a >= 4352 * 24 * 4
+
+
 def gres(**kw):
     a = dict(stream=None, x=P, o=P, y=P, gate=P, mod_row=P, shift2=None, scale2=None, z=None, T=4,
              C=256, eps=1e-6)
