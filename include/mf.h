@@ -211,6 +211,74 @@ mf_status mf_varlen_attn_bwd(void* stream,
                              size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
+ * Backward of the fused adaLN modulation + RoPE (training).
+ *
+ * Gradients of mf_modulate_rope for q and for k, given the gradients
+ * dq_out, dk_out of its outputs:
+ *   RoPE: each pair's gradient is turned back by -angle (the rotation's
+ *   transpose);
+ *   modulation (scale != NULL): with xh = (x - mu) / sigma of the input row
+ *   (fp32 statistics, population variance) and du the RoPE-back gradient,
+ *     gx = du * (1 + scale[m(t)]),
+ *     dx = (gx - mean(gx) - xh * mean(gx * xh)) / sigma,
+ *     dshift[r] = sum over tokens t with m(t) = r of (du_q[t] + du_k[t]),
+ *     dscale[r] = sum of (du_q[t] * xh_q[t] + du_k[t] * xh_k[t])
+ *   (the adaLN rows are shared by q and k); without modulation dx = du.
+ * Sources as for mf_modulate_rope; the pages train the model with these
+ * fused kernels (picx.dev summary, Methodology > Training Infrastructure).
+ *
+ * q_in, k_in: the forward's bf16 inputs [T][H][D], token stride ld_in.
+ * dq_out, dk_out: bf16 [T][H][D], token stride ld_gout.
+ * dq_in, dk_in: bf16 [T][H][D] outputs, token stride ld_gin; they may equal
+ *   dq_out / dk_out (in place), other overlaps are undefined.
+ * scale: bf16 [n_rows][H*D] or NULL (RoPE only; then mod_row, dshift and
+ *   dscale are ignored).  shift is not needed.
+ * dshift, dscale: fp32 [n_rows][H*D], overwritten (zeroed, then summed with
+ *   fp32 atomics: the order of the additions varies between calls, so the row
+ *   sums are not bitwise reproducible).
+ * mod_row, pos, rope dims, rope_base, eps: as for mf_modulate_rope;
+ *   0 <= mod_row[t] < n_rows.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
+ * MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+mf_status mf_modulate_rope_bwd(void* stream,
+                               const void* q_in, const void* k_in, int64_t ld_in,
+                               const void* dq_out, const void* dk_out, int64_t ld_gout,
+                               void* dq_in, void* dk_in, int64_t ld_gin,
+                               int64_t T, int32_t H, int32_t D,
+                               const void* scale, const int32_t* mod_row, int32_t n_rows,
+                               float* dshift, float* dscale, const int32_t* pos,
+                               int32_t rope_f, int32_t rope_r, int32_t rope_c,
+                               float rope_base, float eps);
+
+/* ------------------------------------------------------------------------
+ * Backward of the gated residual and its fused next adaLN (training).
+ *
+ * With y = x + gate[m(t)] * o and z = LN(y) (1 + scale2[m(t)]) + shift2[m(t)]
+ * (recomputed in fp32 from the bf16 inputs), given dy and dz:
+ *   dyt = dy + (LN backward of dz * (1 + scale2[m(t)])),
+ *   dx = dyt, dout = gate[m(t)] * dyt,
+ *   dgate[r] = sum over tokens with m(t) = r of dyt * o,
+ *   dshift2[r] = sum of dz, dscale2[r] = sum of dz * yh.
+ * Without the fused adaLN (scale2, dz, dshift2, dscale2 all NULL) dyt = dy.
+ *
+ * x, o: the forward's bf16 [T][C] inputs (o = attention output as [T][H*D]).
+ * gate, scale2: bf16 [n_rows][C]; mod_row: int32 [T], 0 <= m < n_rows.
+ * dy: bf16 [T][C] or NULL (zero); dz: bf16 [T][C] (fused) or NULL.
+ * dx, dout: bf16 [T][C] outputs; dx may equal dy; no other overlap.
+ * dgate, dshift2, dscale2: fp32 [n_rows][C], overwritten (row sums by fp32
+ *   atomics, as above).
+ * C a multiple of 64 and at most 8192; eps > 0 when fused.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_TABLE (MF_DEBUG
+ * only), MF_ERR_HIP. */
+mf_status mf_gated_residual_bwd(void* stream,
+                                const void* x, const void* o, const void* gate,
+                                const int32_t* mod_row, int32_t n_rows,
+                                const void* dy, const void* scale2, const void* dz,
+                                void* dx, void* dout,
+                                float* dgate, float* dshift2, float* dscale2,
+                                int64_t T, int32_t C, float eps);
+
+/* ------------------------------------------------------------------------
  * Gated residual, optionally fused with the next sub-layer's adaLN.
  *
  *   y[t] = x[t] + gate[m(t)] * o[t]                        (fp32, then bf16)

@@ -258,4 +258,105 @@ mf_status mf_gated_residual(void* stream, const void* x, const void* o, void* y,
     return finish(mf::launch_gated_residual(a, s), s);
 }
 
+mf_status mf_modulate_rope_bwd(void* stream, const void* q_in, const void* k_in, int64_t ld_in,
+                               const void* dq_out, const void* dk_out, int64_t ld_gout, void* dq_in,
+                               void* dk_in, int64_t ld_gin, int64_t T, int32_t H, int32_t D,
+                               const void* scale, const int32_t* mod_row, int32_t n_rows, float* dshift,
+                               float* dscale, const int32_t* pos, int32_t rope_f, int32_t rope_r,
+                               int32_t rope_c, float rope_base, float eps) {
+    if (T < 0 || T > INT32_MAX || H <= 0) return MF_ERR_SHAPE;
+    if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
+    if (int64_t(H) * D > 8192) return MF_ERR_UNSUPPORTED;
+    if (rope_f < 0 || rope_r < 0 || rope_c < 0 || rope_f % 8 || rope_r % 8 || rope_c % 8 ||
+        rope_f + rope_r + rope_c != D)
+        return MF_ERR_SHAPE;
+    if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return MF_ERR_SHAPE;
+    if (ld_in < int64_t(H) * D || ld_gout < int64_t(H) * D || ld_gin < int64_t(H) * D) return MF_ERR_SHAPE;
+    const bool modulate = scale != nullptr;
+    if (modulate && (!(eps > 0.f) || n_rows <= 0)) return MF_ERR_SHAPE;
+    if (modulate && int64_t(n_rows) * H * D > (int64_t(1) << 31)) return MF_ERR_SHAPE;
+    if (T == 0) {
+        // nothing to read; the row sums are still defined (zero)
+        if (!modulate) return MF_OK;
+        if (!dshift || !dscale) return MF_ERR_NULL;
+    } else {
+        if (!q_in || !k_in || !dq_out || !dk_out || !dq_in || !dk_in || !pos) return MF_ERR_NULL;
+        if (modulate && (!mod_row || !dshift || !dscale)) return MF_ERR_NULL;
+        if (ld_in % 8 || ld_gout % 8 || ld_gin % 8) return MF_ERR_ALIGN;
+        if (!aligned(q_in, 16) || !aligned(k_in, 16) || !aligned(dq_out, 16) || !aligned(dk_out, 16) ||
+            !aligned(dq_in, 16) || !aligned(dk_in, 16) || !aligned(pos, 4))
+            return MF_ERR_ALIGN;
+    }
+    if (modulate && (!aligned(scale, 16) || !aligned(dshift, 4) || !aligned(dscale, 4) ||
+                     (T > 0 && !aligned(mod_row, 4))))
+        return MF_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode() && T > 0) {
+        std::vector<int32_t> hp;
+        if (!fetch(pos, size_t(T) * 3, hp, s)) return MF_ERR_HIP;
+        for (int32_t v : hp)
+            if (v < 0) return MF_ERR_TABLE;
+        if (modulate) {
+            std::vector<int32_t> hm;
+            if (!fetch(mod_row, size_t(T), hm, s)) return MF_ERR_HIP;
+            for (int32_t m : hm)
+                if (m < 0 || m >= n_rows) return MF_ERR_TABLE;
+        }
+    }
+    mf::ModRopeBwdArgs a;
+    a.q_in = static_cast<const uint16_t*>(q_in);
+    a.k_in = static_cast<const uint16_t*>(k_in);
+    a.dq_out = static_cast<const uint16_t*>(dq_out);
+    a.dk_out = static_cast<const uint16_t*>(dk_out);
+    a.dq_in = static_cast<uint16_t*>(dq_in);
+    a.dk_in = static_cast<uint16_t*>(dk_in);
+    a.T = T; a.H = H; a.D = D; a.ld_in = ld_in; a.ld_gout = ld_gout; a.ld_gin = ld_gin;
+    a.scale = static_cast<const uint16_t*>(scale);
+    a.mod_row = mod_row; a.n_rows = n_rows; a.dshift = dshift; a.dscale = dscale; a.pos = pos;
+    a.rope_f = rope_f; a.rope_r = rope_r; a.rope_c = rope_c; a.rope_base = rope_base; a.eps = eps;
+    return finish(mf::launch_modulate_rope_bwd(a, s), s);
+}
+
+mf_status mf_gated_residual_bwd(void* stream, const void* x, const void* o, const void* gate,
+                                const int32_t* mod_row, int32_t n_rows, const void* dy, const void* scale2,
+                                const void* dz, void* dx, void* dout, float* dgate, float* dshift2,
+                                float* dscale2, int64_t T, int32_t C, float eps) {
+    if (T < 0 || T > INT32_MAX || C <= 0 || C % 64 || C > 8192) return MF_ERR_SHAPE;
+    if (n_rows <= 0 || int64_t(n_rows) * C > (int64_t(1) << 31)) return MF_ERR_SHAPE;
+    const int n_fused = (scale2 != nullptr) + (dz != nullptr) + (dshift2 != nullptr) + (dscale2 != nullptr);
+    if (n_fused != 0 && n_fused != 4) return MF_ERR_NULL;
+    const bool fused = n_fused == 4;
+    if (fused && !(eps > 0.f)) return MF_ERR_SHAPE;
+    if (!dgate) return MF_ERR_NULL;
+    if (T > 0 && (!x || !o || !gate || !mod_row || !dx || !dout)) return MF_ERR_NULL;
+    if (!aligned(dgate, 4) || (fused && (!aligned(dshift2, 4) || !aligned(dscale2, 4))))
+        return MF_ERR_ALIGN;
+    if (T > 0) {
+        if (!aligned(x, 16) || !aligned(o, 16) || !aligned(gate, 16) || !aligned(mod_row, 4) ||
+            !aligned(dx, 16) || !aligned(dout, 16) || (dy && !aligned(dy, 16)))
+            return MF_ERR_ALIGN;
+        if (fused && (!aligned(scale2, 16) || !aligned(dz, 16))) return MF_ERR_ALIGN;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode() && T > 0) {
+        std::vector<int32_t> hm;
+        if (!fetch(mod_row, size_t(T), hm, s)) return MF_ERR_HIP;
+        for (int32_t m : hm)
+            if (m < 0 || m >= n_rows) return MF_ERR_TABLE;
+    }
+    mf::GatedResBwdArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.o = static_cast<const uint16_t*>(o);
+    a.gate = static_cast<const uint16_t*>(gate);
+    a.mod_row = mod_row; a.n_rows = n_rows;
+    a.dy = static_cast<const uint16_t*>(dy);
+    a.scale2 = static_cast<const uint16_t*>(scale2);
+    a.dz = static_cast<const uint16_t*>(dz);
+    a.dx = static_cast<uint16_t*>(dx);
+    a.dout = static_cast<uint16_t*>(dout);
+    a.dgate = dgate; a.dshift2 = dshift2; a.dscale2 = dscale2;
+    a.T = T; a.C = C; a.eps = eps;
+    return finish(mf::launch_gated_residual_bwd(a, s), s);
+}
+
 }  // extern "C"

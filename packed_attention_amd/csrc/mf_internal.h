@@ -35,6 +35,48 @@ struct ModRopeArgs {
 };
 hipError_t launch_modulate_rope(const ModRopeArgs& a, hipStream_t stream);
 
+struct ModRopeBwdArgs {
+    const uint16_t* q_in;     // forward inputs
+    const uint16_t* k_in;
+    const uint16_t* dq_out;   // gradients of the forward outputs
+    const uint16_t* dk_out;
+    uint16_t* dq_in;          // gradients of the forward inputs (written)
+    uint16_t* dk_in;
+    int64_t T;
+    int32_t H, D;
+    int64_t ld_in, ld_gout, ld_gin;
+    const uint16_t* scale;    // nullptr: RoPE only
+    const int32_t* mod_row;
+    int32_t n_rows;
+    float* dshift;            // fp32 [n_rows][H*D] (written)
+    float* dscale;
+    const int32_t* pos;
+    int32_t rope_f, rope_r, rope_c;
+    float rope_base, eps;
+    double theta_turns[64];   // filled by the launcher, as for the forward
+};
+hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& a, hipStream_t stream);
+
+struct GatedResBwdArgs {
+    const uint16_t* x;
+    const uint16_t* o;
+    const uint16_t* gate;
+    const int32_t* mod_row;
+    int32_t n_rows;
+    const uint16_t* dy;       // nullptr: zero
+    const uint16_t* scale2;   // nullptr with dz: no fused adaLN
+    const uint16_t* dz;
+    uint16_t* dx;
+    uint16_t* dout;           // gradient of the attention output o
+    float* dgate;             // fp32 [n_rows][C] (written)
+    float* dshift2;
+    float* dscale2;
+    int64_t T;
+    int32_t C;
+    float eps;
+};
+hipError_t launch_gated_residual_bwd(const GatedResBwdArgs& a, hipStream_t stream);
+
 struct GatedResArgs {
     const uint16_t* x;
     const uint16_t* o;

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "MF_OK", -1: "MF_ERR_NULL", -2: "MF_ERR_SHAPE", -3: "MF_ERR_A
 # Every symbol include/mf.h declares.
 EXPORTS = ("mf_status_string", "mf_abi_version", "mf_pack_count", "mf_pack_tables",
            "mf_modulate_rope", "mf_varlen_attn_workspace_bytes", "mf_varlen_attn_fwd",
-           "mf_gated_residual", "mf_varlen_attn_bwd_workspace_bytes", "mf_varlen_attn_bwd")
+           "mf_gated_residual", "mf_varlen_attn_bwd_workspace_bytes", "mf_varlen_attn_bwd",
+           "mf_modulate_rope_bwd", "mf_gated_residual_bwd")
 
 
 class MFError(RuntimeError):
@@ -76,6 +77,12 @@ def lib() -> ctypes.CDLL:
     L.mf_varlen_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32,
                                      i32, i64, i64, i64, f32, vp, sz]
     L.mf_varlen_attn_bwd.restype = i32
+    L.mf_modulate_rope_bwd.argtypes = [vp, vp, vp, i64, vp, vp, i64, vp, vp, i64, i64, i32, i32, vp, vp,
+                                       i32, vp, vp, vp, i32, i32, i32, f32, f32]
+    L.mf_modulate_rope_bwd.restype = i32
+    L.mf_gated_residual_bwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                        i32, f32]
+    L.mf_gated_residual_bwd.restype = i32
     _lib = L
     return L
 
@@ -252,3 +259,53 @@ def varlen_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, max_seqlen, s
                                    _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), n_seq,
                                    int(max_seqlen), T, H, D, ld, ld_o, ld_d, float(softmax_scale),
                                    _ptr(workspace), workspace.numel()))
+
+
+def modulate_rope_bwd(q_in, k_in, dq_out, dk_out, dq_in, dk_in, pos, rope_dims, rope_base=10000.0,
+                      scale=None, mod_row=None, dshift=None, dscale=None, eps=1e-6, stream=None):
+    """mf_modulate_rope_bwd on [T][H][D] bf16 tensors; dshift/dscale float32 [n_rows][H*D]."""
+    import torch
+    T, H, D = q_in.shape
+    for n, t in (("q_in", q_in), ("k_in", k_in), ("dq_out", dq_out), ("dk_out", dk_out),
+                 ("dq_in", dq_in), ("dk_in", dk_in)):
+        _check_bf16_rows(n, t, H * D)
+        if tuple(t.shape) != (T, H, D):
+            raise ValueError(f"{n}: shape {tuple(t.shape)} != {(T, H, D)}")
+    ld_in = _token_stride(q_in, H * D)
+    ld_gout = _token_stride(dq_out, H * D)
+    ld_gin = _token_stride(dq_in, H * D)
+    if (_token_stride(k_in, H * D) != ld_in or _token_stride(dk_out, H * D) != ld_gout
+            or _token_stride(dk_in, H * D) != ld_gin):
+        raise ValueError("q and k tensors of each pair must share a token stride")
+    n_rows = 0
+    if scale is not None:
+        n_rows = scale.shape[0]
+        for n, t in (("dshift", dshift), ("dscale", dscale)):
+            if t is None or t.dtype != torch.float32 or tuple(t.shape) != (n_rows, H * D):
+                raise ValueError(f"{n}: expected float32 [n_rows][H*D]")
+    f, r, c = (int(x) for x in rope_dims)
+    check(lib().mf_modulate_rope_bwd(_stream(stream), _ptr(q_in), _ptr(k_in), ld_in, _ptr(dq_out),
+                                     _ptr(dk_out), ld_gout, _ptr(dq_in), _ptr(dk_in), ld_gin, T, H, D,
+                                     _ptr(scale), _ptr(mod_row), n_rows, _ptr(dshift), _ptr(dscale),
+                                     _ptr(pos), f, r, c, float(rope_base), float(eps)))
+
+
+def gated_residual_bwd(x, o, gate, mod_row, dy, dx, dout, dgate, scale2=None, dz=None, dshift2=None,
+                       dscale2=None, eps=1e-6, stream=None):
+    """mf_gated_residual_bwd on contiguous [T][C] bf16 rows; row sums float32 [n_rows][C]."""
+    import torch
+    T = x.shape[0]
+    C = x.shape[-1]
+    for n, t in (("x", x), ("o", o), ("dy", dy), ("dz", dz), ("dx", dx), ("dout", dout)):
+        if t is None:
+            continue
+        _check_bf16_rows(n, t, C)
+        if not t.is_contiguous() or t.numel() != T * C:
+            raise ValueError(f"{n}: expected a contiguous [T][C] tensor")
+    n_rows = gate.shape[0]
+    for n, t in (("dgate", dgate), ("dshift2", dshift2), ("dscale2", dscale2)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (n_rows, C)):
+            raise ValueError(f"{n}: expected float32 [n_rows][C]")
+    check(lib().mf_gated_residual_bwd(_stream(stream), _ptr(x), _ptr(o), _ptr(gate), _ptr(mod_row),
+                                      n_rows, _ptr(dy), _ptr(scale2), _ptr(dz), _ptr(dx), _ptr(dout),
+                                      _ptr(dgate), _ptr(dshift2), _ptr(dscale2), T, C, float(eps)))

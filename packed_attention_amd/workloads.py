@@ -212,13 +212,18 @@ def descs_edit(rng: np.random.Generator) -> List[Desc]:
 def upstream_grads(w: Workload) -> dict:
     """Seeded stand-ins for the gradients a training loss sends back into the
     hot path: dO [T][H][D] (attention output), dy and dz [T][C] (residual
-    stream and next adaLN output), all N(0, 1) bf16 bits.  Drawn from their
+    stream and next adaLN output), dq and dk [T][H][D] (q', k' of the
+    modulate+RoPE step), all N(0, 1) bf16 bits.  Drawn from their
     own generator (seed + 1000003), so the forward tensors of a workload do not
     change."""
     rng = np.random.default_rng(w.seed + 1000003)
     T, H, D = w.T, w.H, w.D
-    return dict(dO=_normal_bf16(rng, (T, H, D), 1.0), dy=_normal_bf16(rng, (T, H * D), 1.0),
-                dz=_normal_bf16(rng, (T, H * D), 1.0))
+    g = dict(dO=_normal_bf16(rng, (T, H, D), 1.0), dy=_normal_bf16(rng, (T, H * D), 1.0),
+             dz=_normal_bf16(rng, (T, H * D), 1.0))
+    # gradients of the modulate+RoPE outputs q', k' (for that kernel alone)
+    g["dq"] = _normal_bf16(rng, (T, H, D), 1.0)
+    g["dk"] = _normal_bf16(rng, (T, H, D), 1.0)
+    return g
 
 
 # ---------------------------------------------------------------------------

@@ -134,6 +134,52 @@ def test_attention_bwd_validation():
     assert a % 256 == 0 and a >= 4352 * 24 * 4
 
 
+def modrope_bwd(**kw):
+    a = dict(stream=None, q_in=P, k_in=P, ld_in=128, dq_out=P, dk_out=P, ld_gout=128, dq_in=P,
+             dk_in=P, ld_gin=128, T=4, H=2, D=64, scale=None, mod_row=None, n_rows=0, dshift=None,
+             dscale=None, pos=P, f=0, r=32, c=32, base=10000.0, eps=1e-6)
+    a.update(kw)
+    return native.lib().mf_modulate_rope_bwd(*a.values())
+
+
+def test_modulate_rope_bwd_validation():
+    mod = dict(scale=P, mod_row=P, n_rows=2, dshift=P, dscale=P)
+    assert modrope_bwd(D=96) == UNSUP
+    assert modrope_bwd(H=0) == SHAPE
+    assert modrope_bwd(r=20, c=44) == SHAPE
+    assert modrope_bwd(ld_gin=100) == SHAPE
+    assert modrope_bwd(**{**mod, "n_rows": 0}) == SHAPE
+    assert modrope_bwd(**{**mod, "eps": 0.0}) == SHAPE
+    for name in ("q_in", "dq_out", "dk_in", "pos"):
+        assert modrope_bwd(**{name: None}) == NULL, name
+    assert modrope_bwd(**{**mod, "dscale": None}) == NULL
+    assert modrope_bwd(**{**mod, "mod_row": None}) == NULL
+    assert modrope_bwd(ld_in=132) == ALIGN
+    assert modrope_bwd(dk_out=PODD) == ALIGN
+    assert modrope_bwd(**{**mod, "dshift": P + 2}) == ALIGN
+    assert modrope_bwd(T=0, q_in=None, k_in=None, dq_out=None, dk_out=None, dq_in=None, dk_in=None,
+                       pos=None) == 0
+
+
+def gres_bwd(**kw):
+    a = dict(stream=None, x=P, o=P, gate=P, mod_row=P, n_rows=2, dy=P, scale2=None, dz=None, dx=P,
+             dout=P, dgate=P, dshift2=None, dscale2=None, T=4, C=256, eps=1e-6)
+    a.update(kw)
+    return native.lib().mf_gated_residual_bwd(*a.values())
+
+
+def test_gated_residual_bwd_validation():
+    assert gres_bwd(C=100) == SHAPE
+    assert gres_bwd(n_rows=0) == SHAPE
+    assert gres_bwd(dz=P) == NULL                      # fused set incomplete
+    assert gres_bwd(scale2=P, dz=P, dshift2=P, dscale2=P, eps=0.0) == SHAPE
+    for name in ("x", "o", "gate", "mod_row", "dx", "dout", "dgate"):
+        assert gres_bwd(**{name: None}) == NULL, name
+    assert gres_bwd(o=PODD) == ALIGN
+    assert gres_bwd(dy=PODD) == ALIGN
+    assert gres_bwd(dgate=P + 2) == ALIGN
+
+
 def gres(**kw):
     a = dict(stream=None, x=P, o=P, y=P, gate=P, mod_row=P, shift2=None, scale2=None, z=None, T=4,
              C=256, eps=1e-6)

@@ -143,3 +143,139 @@ def test_bwd_single_1024_sampled():
     check_grad(G.f64(dq.cpu()[ti(rows), ti(heads)]), ref_q, "single_1024.dQ")
     check_grad(G.f64(dk.cpu()[ti(keys), ti(kheads)]), ref_k, "single_1024.dK")
     check_grad(G.f64(dv.cpu()[ti(keys), ti(kheads)]), ref_v, "single_1024.dV")
+
+
+# ---------------------------------------------------------------------------
+# Elementwise backward kernels and the whole backward chain
+# ---------------------------------------------------------------------------
+
+ROWSUM_REL_RMS = 1e-4    # fp32 sums of fp32 per-token terms from bf16 data
+CHAIN_REL_RMS = 2e-2     # three bf16-rounded stages, each near 2^-9 relative
+
+
+def check_rows(got, ref, name):
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert np.all(np.isfinite(got)) and rel <= ROWSUM_REL_RMS, f"{name}: relative RMS {rel:.3e}"
+
+
+def _f32(t):
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def modrope_bwd_check(w):
+    import torch
+    G.say(w.name, "modulate_rope_bwd", "T", w.T, "H", w.H, "D", w.D)
+    b = runner.to_device(w)
+    g = W.upstream_grads(w)
+    dq_out, dk_out = runner.bf16_tensor(g["dq"]), runner.bf16_tensor(g["dk"])
+    dq, dk = torch.empty_like(b.q), torch.empty_like(b.k)
+    n_rows = len(w.descs)
+    C = w.H * w.D
+    dsh = torch.empty((n_rows, C), dtype=torch.float32, device="cuda") if w.modulate else None
+    dsc = torch.empty((n_rows, C), dtype=torch.float32, device="cuda") if w.modulate else None
+    native.modulate_rope_bwd(b.q, b.k, dq_out, dk_out, dq, dk, b.pos, w.rope_dims, w.rope_base,
+                             b.scale, b.mod_row if w.modulate else None, dsh, dsc, w.eps)
+    torch.cuda.synchronize()
+    a = G.wl_f64(w)
+    ref = B.modulate_rope_bwd(a["q"], a["k"], b.pos_host, w.rope_dims, w.rope_base,
+                              G.f64(dq_out), G.f64(dk_out), a["shift"], a["scale"], b.mod_row_host,
+                              n_rows, w.eps)
+    check_grad(G.f64(dq), ref[0], w.name + ".dq")
+    check_grad(G.f64(dk), ref[1], w.name + ".dk")
+    if w.modulate:
+        check_rows(_f32(dsh), ref[2], w.name + ".dshift")
+        check_rows(_f32(dsc), ref[3], w.name + ".dscale")
+
+
+def gres_bwd_check(w, fused=True, with_dy=True):
+    import torch
+    G.say(w.name, "gated_residual_bwd", "fused", fused, "dy", with_dy)
+    b = runner.to_device(w)
+    runner.run_chain(b)
+    g = W.upstream_grads(w)
+    T, C = w.T, w.H * w.D
+    n_rows = len(w.descs)
+    dy = runner.bf16_tensor(g["dy"]) if with_dy else None
+    dz = runner.bf16_tensor(g["dz"]) if fused else None
+    dx = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
+    do = torch.empty_like(dx)
+    rows = lambda: torch.empty((n_rows, C), dtype=torch.float32, device="cuda")  # noqa: E731
+    dgate, dsh2, dsc2 = rows(), (rows() if fused else None), (rows() if fused else None)
+    o2 = b.o.view(T, C)
+    native.gated_residual_bwd(b.x, o2, b.gate, b.mod_row, dy, dx, do, dgate,
+                              b.scale2 if fused else None, dz, dsh2, dsc2, w.eps)
+    torch.cuda.synchronize()
+    a = G.wl_f64(w)
+    ref = B.gated_residual_bwd(a["x"], G.f64(o2), a["gate"], b.mod_row_host,
+                               G.f64(dy) if with_dy else None, G.f64(dz) if fused else None,
+                               a["shift2"], a["scale2"], n_rows, w.eps)
+    check_grad(G.f64(dx), ref[0], w.name + ".dx")
+    check_grad(G.f64(do), ref[1], w.name + ".do")
+    check_rows(_f32(dgate), ref[2], w.name + ".dgate")
+    if fused:
+        check_rows(_f32(dsh2), ref[3], w.name + ".dshift2")
+        check_rows(_f32(dsc2), ref[4], w.name + ".dscale2")
+
+
+def test_modulate_rope_bwd_tiny():
+    modrope_bwd_check(W.tiny())          # RoPE only
+    modrope_bwd_check(W.tiny_mod())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_modulate_rope_bwd_ragged(D):
+    descs = [(t, f, h, ww, s, s) for s, (t, f, h, ww) in enumerate(RAGGED)]
+    dims = (0, D // 2, D // 2) if D == 64 else (16, 56, 56)
+    modrope_bwd_check(W.custom(descs, H=3, D=D, rope_dims=dims, modulate=True, residual=True,
+                               seed=79, name=f"ragged_erbwd_d{D}"))
+
+
+def test_gated_residual_bwd_variants():
+    w = W.tiny_mod()
+    gres_bwd_check(w, fused=True, with_dy=True)
+    gres_bwd_check(w, fused=True, with_dy=False)
+    gres_bwd_check(w, fused=False, with_dy=True)
+
+
+def test_elementwise_bwd_single_1024():
+    """Full size: every token (these kernels are cheap for the oracle)."""
+    w = W.single_1024()
+    modrope_bwd_check(w)
+    gres_bwd_check(w)
+
+
+def test_backward_chain_end_to_end():
+    """GPU forward, then gated residual -> attention -> modulate+RoPE
+    backward, against the fp64 oracle chain from the same seeded inputs."""
+    import torch
+    w = W.tiny_mod()
+    G.say(w.name, "backward chain end to end")
+    b = runner.to_device(w)
+    runner.run_chain(b)
+    g = W.upstream_grads(w)
+    T, H, D = w.T, w.H, w.D
+    C = H * D
+    n_rows = len(w.descs)
+    dy, dz = runner.bf16_tensor(g["dy"]), runner.bf16_tensor(g["dz"])
+    rows = lambda: torch.empty((n_rows, C), dtype=torch.float32, device="cuda")  # noqa: E731
+    dx = torch.empty((T, C), dtype=torch.bfloat16, device="cuda")
+    do = torch.empty_like(dx)
+    dgate, dsh2, dsc2, dsh, dsc = rows(), rows(), rows(), rows(), rows()
+    native.gated_residual_bwd(b.x, b.o.view(T, C), b.gate, b.mod_row, dy, dx, do, dgate, b.scale2,
+                              dz, dsh2, dsc2, w.eps)
+    dqr, dkr, dv = (torch.empty_like(b.q) for _ in range(3))
+    native.varlen_attn_bwd(b.qr, b.kr, b.v, b.o, do.view(T, H, D), b.lse, dqr, dkr, dv, b.cu,
+                           b.max_seqlen)
+    dq, dk = torch.empty_like(b.q), torch.empty_like(b.k)
+    native.modulate_rope_bwd(b.q, b.k, dqr, dkr, dq, dk, b.pos, w.rope_dims, w.rope_base, b.scale,
+                             b.mod_row, dsh, dsc, w.eps)
+    torch.cuda.synchronize()
+    a = G.wl_f64(w)
+    ref = B.backward(w.descs, a["q"], a["k"], a["v"], w.rope_dims, w.rope_base, G.f64(dy), G.f64(dz),
+                     a["shift"], a["scale"], a["x"], a["gate"], a["shift2"], a["scale2"], w.eps)
+    for name, got in (("dq", G.f64(dq)), ("dk", G.f64(dk)), ("dv", G.f64(dv)), ("dx", G.f64(dx)),
+                      ("dshift", _f32(dsh)), ("dscale", _f32(dsc)), ("dgate", _f32(dgate)),
+                      ("dshift2", _f32(dsh2)), ("dscale2", _f32(dsc2))):
+        r = ref[name]
+        rel = float(np.linalg.norm(got - r) / max(np.linalg.norm(r), 1e-30))
+        assert rel <= CHAIN_REL_RMS, f"chain {name}: relative RMS {rel:.3e}"
