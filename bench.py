@@ -19,6 +19,11 @@ Prints one JSON line:
   kernels     per-kernel average durations, algorithmic bytes and GB/s
               against the HBM peak (the two elementwise kernels are
               HBM-bound);
+  backward    the training backward of the same step (gated residual ->
+              attention -> modulate+RoPE, eager calls), per-kernel HIP-event
+              durations; attention at 2.5x the forward's flops (five
+              products), the elementwise kernels in GB/s of their
+              algorithmic bytes;
   cpu_baseline the fp64 oracle's whole step over the same workload, repeated
               for about 10 s, timed on the host cores.
 """
@@ -49,6 +54,15 @@ def algorithmic_bytes(w):
     attn = 4 * T * C * 2 + 4 * w.H * T + 4 * (w.n_seq + 1)
     gres = (T * (4 * C * 2 + 4) + 3 * n_rows * C * 2) if w.x is not None else 0
     return dict(modulate_rope=mod, varlen_attn_fwd=attn, gated_residual=gres)
+
+
+def backward_bytes(w):
+    """Bytes each backward kernel must move at least once per launch."""
+    T, C, H, n_rows = w.T, w.C, w.H, w.n_seq
+    gres = T * (6 * C * 2 + 4) + n_rows * C * (2 * 2 + 3 * 4)
+    attn = 8 * T * C * 2 + 4 * H * T * 3 + 4 * (w.n_seq + 1)
+    mod = T * (6 * C * 2 + 16) + n_rows * C * (2 + 2 * 4)
+    return dict(gated_residual_bwd=gres, varlen_attn_bwd=attn, modulate_rope_bwd=mod)
 
 
 def source_hash():
@@ -180,6 +194,25 @@ def main():
     kern_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
                for j, n in enumerate(names)}
 
+    # Backward pass of the same step (training): gated residual -> attention
+    # -> modulate+RoPE, per-kernel HIP events, eager calls.
+    gsets = [runner.grads_to_device(b) for b in sets]
+    bnames = ("gated_residual_bwd", "varlen_attn_bwd", "modulate_rope_bwd")
+    bfns = (runner.run_gated_residual_bwd, runner.run_attention_bwd, runner.run_modulate_rope_bwd)
+    for i in range(args.warmup):
+        runner.run_backward_chain(sets[i % len(sets)], gsets[i % len(sets)])
+    bevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        b, gb = sets[i % len(sets)], gsets[i % len(sets)]
+        bevs[i][0].record(stream)
+        for j, fn in enumerate(bfns):
+            fn(b, gb)
+            bevs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    bkern_ms = {n: sum(bevs[i][j].elapsed_time(bevs[i][j + 1]) for i in range(args.steps)) / args.steps
+                for j, n in enumerate(bnames)}
+
     if args.copy_calib_mb:
         n = args.copy_calib_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -201,6 +234,22 @@ def main():
         kernels[n] = e
     kernels["varlen_attn_fwd"]["TFLOP/s"] = round(attn_tflops, 2)
     kernels["varlen_attn_fwd"]["frac_bf16_peak"] = round(attn_tflops / PEAK_BF16_TFLOPS, 4)
+
+    bbytes = backward_bytes(w)
+    bflops = 2.5 * flops      # dQ, dK, dV, dP, S: five products of 2*d*H*sum L^2 flops
+    backward = {"ms_per_step": round(sum(bkern_ms.values()), 5),
+                "attn_bwd_flops": bflops,
+                "kernels": {}}
+    for n in bnames:
+        ms = bkern_ms[n]
+        e = {"ms": round(ms, 5), "algorithmic_bytes": bbytes[n]}
+        gbs = bbytes[n] / (ms * 1e-3) / 1e9
+        e["GB/s"] = round(gbs, 1)
+        e["frac_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+        backward["kernels"][n] = e
+    bt = bflops / (bkern_ms["varlen_attn_bwd"] * 1e-3) / 1e12
+    backward["kernels"]["varlen_attn_bwd"]["TFLOP/s"] = round(bt, 2)
+    backward["kernels"]["varlen_attn_bwd"]["frac_bf16_peak"] = round(bt / PEAK_BF16_TFLOPS, 4)
 
     traffic = measured_traffic() if args.workload == "single_1024" else None
     out = {
@@ -227,6 +276,7 @@ def main():
                      "kernel": f"mf_varlen_attn_fwd call (attn_fwd_kernel<{w.D}> + attn_fixup_kernel<{w.D}>)",
                      "flops_per_launch": flops, "launch_ms": round(kern_ms["varlen_attn_fwd"], 5)},
         "kernels": kernels,
+        "backward": backward,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

@@ -233,13 +233,19 @@ mf_status mf_varlen_attn_bwd(void* stream,
  *   dq_out / dk_out (in place), other overlaps are undefined.
  * scale: bf16 [n_rows][H*D] or NULL (RoPE only; then mod_row, dshift and
  *   dscale are ignored).  shift is not needed.
- * dshift, dscale: fp32 [n_rows][H*D], overwritten (zeroed, then summed with
- *   fp32 atomics: the order of the additions varies between calls, so the row
- *   sums are not bitwise reproducible).
+ * dshift, dscale: fp32 [n_rows][H*D], overwritten (zeroed, then summed per
+ *   run of tokens and added with fp32 atomics: the order of the additions
+ *   varies between calls, so the row sums are not bitwise reproducible).
  * mod_row, pos, rope dims, rope_base, eps: as for mf_modulate_rope;
  *   0 <= mod_row[t] < n_rows.
+ * workspace: device memory of at least mf_modulate_rope_bwd_workspace_bytes
+ *   bytes, 256-byte aligned, when modulating (per-run partial row sums);
+ *   unused (may be NULL) for RoPE only.  Concurrent calls need distinct
+ *   workspaces.
  * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
- * MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+ * MF_ERR_WORKSPACE, MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+size_t mf_modulate_rope_bwd_workspace_bytes(int64_t T, int32_t H, int32_t D);
+
 mf_status mf_modulate_rope_bwd(void* stream,
                                const void* q_in, const void* k_in, int64_t ld_in,
                                const void* dq_out, const void* dk_out, int64_t ld_gout,
@@ -248,7 +254,8 @@ mf_status mf_modulate_rope_bwd(void* stream,
                                const void* scale, const int32_t* mod_row, int32_t n_rows,
                                float* dshift, float* dscale, const int32_t* pos,
                                int32_t rope_f, int32_t rope_r, int32_t rope_c,
-                               float rope_base, float eps);
+                               float rope_base, float eps, void* workspace,
+                               size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
  * Backward of the gated residual and its fused next adaLN (training).
@@ -265,18 +272,24 @@ mf_status mf_modulate_rope_bwd(void* stream,
  * gate, scale2: bf16 [n_rows][C]; mod_row: int32 [T], 0 <= m < n_rows.
  * dy: bf16 [T][C] or NULL (zero); dz: bf16 [T][C] (fused) or NULL.
  * dx, dout: bf16 [T][C] outputs; dx may equal dy; no other overlap.
- * dgate, dshift2, dscale2: fp32 [n_rows][C], overwritten (row sums by fp32
- *   atomics, as above).
+ * dgate, dshift2, dscale2: fp32 [n_rows][C], overwritten (row sums as
+ *   above).
  * C a multiple of 64 and at most 8192; eps > 0 when fused.
- * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_TABLE (MF_DEBUG
- * only), MF_ERR_HIP. */
+ * workspace: device memory of at least mf_gated_residual_bwd_workspace_bytes
+ *   bytes, 256-byte aligned (per-run partial row sums); concurrent calls
+ *   need distinct workspaces.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_WORKSPACE,
+ * MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+size_t mf_gated_residual_bwd_workspace_bytes(int64_t T, int32_t C);
+
 mf_status mf_gated_residual_bwd(void* stream,
                                 const void* x, const void* o, const void* gate,
                                 const int32_t* mod_row, int32_t n_rows,
                                 const void* dy, const void* scale2, const void* dz,
                                 void* dx, void* dout,
                                 float* dgate, float* dshift2, float* dscale2,
-                                int64_t T, int32_t C, float eps);
+                                int64_t T, int32_t C, float eps, void* workspace,
+                                size_t workspace_bytes);
 
 /* ------------------------------------------------------------------------
  * Gated residual, optionally fused with the next sub-layer's adaLN.

@@ -258,12 +258,21 @@ mf_status mf_gated_residual(void* stream, const void* x, const void* o, void* y,
     return finish(mf::launch_gated_residual(a, s), s);
 }
 
+size_t mf_modulate_rope_bwd_workspace_bytes(int64_t T, int32_t H, int32_t D) {
+    return mf::elementwise_bwd_workspace_bytes(T, H * D, 2);
+}
+
+size_t mf_gated_residual_bwd_workspace_bytes(int64_t T, int32_t C) {
+    return mf::elementwise_bwd_workspace_bytes(T, C, 3);
+}
+
 mf_status mf_modulate_rope_bwd(void* stream, const void* q_in, const void* k_in, int64_t ld_in,
                                const void* dq_out, const void* dk_out, int64_t ld_gout, void* dq_in,
                                void* dk_in, int64_t ld_gin, int64_t T, int32_t H, int32_t D,
                                const void* scale, const int32_t* mod_row, int32_t n_rows, float* dshift,
                                float* dscale, const int32_t* pos, int32_t rope_f, int32_t rope_r,
-                               int32_t rope_c, float rope_base, float eps) {
+                               int32_t rope_c, float rope_base, float eps, void* workspace,
+                               size_t workspace_bytes) {
     if (T < 0 || T > INT32_MAX || H <= 0) return MF_ERR_SHAPE;
     if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
     if (int64_t(H) * D > 8192) return MF_ERR_UNSUPPORTED;
@@ -290,6 +299,11 @@ mf_status mf_modulate_rope_bwd(void* stream, const void* q_in, const void* k_in,
     if (modulate && (!aligned(scale, 16) || !aligned(dshift, 4) || !aligned(dscale, 4) ||
                      (T > 0 && !aligned(mod_row, 4))))
         return MF_ERR_ALIGN;
+    if (modulate && T > 0) {
+        if (workspace == nullptr || workspace_bytes < mf::elementwise_bwd_workspace_bytes(T, H * D, 2))
+            return MF_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return MF_ERR_ALIGN;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (debug_mode() && T > 0) {
         std::vector<int32_t> hp;
@@ -314,13 +328,15 @@ mf_status mf_modulate_rope_bwd(void* stream, const void* q_in, const void* k_in,
     a.scale = static_cast<const uint16_t*>(scale);
     a.mod_row = mod_row; a.n_rows = n_rows; a.dshift = dshift; a.dscale = dscale; a.pos = pos;
     a.rope_f = rope_f; a.rope_r = rope_r; a.rope_c = rope_c; a.rope_base = rope_base; a.eps = eps;
+    a.workspace = workspace;
     return finish(mf::launch_modulate_rope_bwd(a, s), s);
 }
 
 mf_status mf_gated_residual_bwd(void* stream, const void* x, const void* o, const void* gate,
                                 const int32_t* mod_row, int32_t n_rows, const void* dy, const void* scale2,
                                 const void* dz, void* dx, void* dout, float* dgate, float* dshift2,
-                                float* dscale2, int64_t T, int32_t C, float eps) {
+                                float* dscale2, int64_t T, int32_t C, float eps, void* workspace,
+                                size_t workspace_bytes) {
     if (T < 0 || T > INT32_MAX || C <= 0 || C % 64 || C > 8192) return MF_ERR_SHAPE;
     if (n_rows <= 0 || int64_t(n_rows) * C > (int64_t(1) << 31)) return MF_ERR_SHAPE;
     const int n_fused = (scale2 != nullptr) + (dz != nullptr) + (dshift2 != nullptr) + (dscale2 != nullptr);
@@ -336,6 +352,9 @@ mf_status mf_gated_residual_bwd(void* stream, const void* x, const void* o, cons
             !aligned(dx, 16) || !aligned(dout, 16) || (dy && !aligned(dy, 16)))
             return MF_ERR_ALIGN;
         if (fused && (!aligned(scale2, 16) || !aligned(dz, 16))) return MF_ERR_ALIGN;
+        if (workspace == nullptr || workspace_bytes < mf::elementwise_bwd_workspace_bytes(T, C, fused ? 3 : 1))
+            return MF_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return MF_ERR_ALIGN;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (debug_mode() && T > 0) {
@@ -355,7 +374,7 @@ mf_status mf_gated_residual_bwd(void* stream, const void* x, const void* o, cons
     a.dx = static_cast<uint16_t*>(dx);
     a.dout = static_cast<uint16_t*>(dout);
     a.dgate = dgate; a.dshift2 = dshift2; a.dscale2 = dscale2;
-    a.T = T; a.C = C; a.eps = eps;
+    a.T = T; a.C = C; a.eps = eps; a.workspace = workspace;
     return finish(mf::launch_gated_residual_bwd(a, s), s);
 }
 

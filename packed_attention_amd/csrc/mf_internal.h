@@ -53,6 +53,7 @@ struct ModRopeBwdArgs {
     const int32_t* pos;
     int32_t rope_f, rope_r, rope_c;
     float rope_base, eps;
+    void* workspace;          // row-sum slots (modulated only)
     double theta_turns[64];   // filled by the launcher, as for the forward
 };
 hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& a, hipStream_t stream);
@@ -74,8 +75,12 @@ struct GatedResBwdArgs {
     int64_t T;
     int32_t C;
     float eps;
+    void* workspace;          // row-sum slots
 };
 hipError_t launch_gated_residual_bwd(const GatedResBwdArgs& a, hipStream_t stream);
+// Workspace of the two elementwise backward kernels: tagged row-sum slots of
+// n_arrays x C floats per run of tokens.
+size_t elementwise_bwd_workspace_bytes(int64_t T, int32_t C, int32_t n_arrays);
 
 struct GatedResArgs {
     const uint16_t* x;

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "MF_OK", -1: "MF_ERR_NULL", -2: "MF_ERR_SHAPE", -3: "MF_ERR_A
 EXPORTS = ("mf_status_string", "mf_abi_version", "mf_pack_count", "mf_pack_tables",
            "mf_modulate_rope", "mf_varlen_attn_workspace_bytes", "mf_varlen_attn_fwd",
            "mf_gated_residual", "mf_varlen_attn_bwd_workspace_bytes", "mf_varlen_attn_bwd",
-           "mf_modulate_rope_bwd", "mf_gated_residual_bwd")
+           "mf_modulate_rope_bwd", "mf_gated_residual_bwd", "mf_modulate_rope_bwd_workspace_bytes",
+           "mf_gated_residual_bwd_workspace_bytes")
 
 
 class MFError(RuntimeError):
@@ -78,10 +79,14 @@ def lib() -> ctypes.CDLL:
                                      i32, i64, i64, i64, f32, vp, sz]
     L.mf_varlen_attn_bwd.restype = i32
     L.mf_modulate_rope_bwd.argtypes = [vp, vp, vp, i64, vp, vp, i64, vp, vp, i64, i64, i32, i32, vp, vp,
-                                       i32, vp, vp, vp, i32, i32, i32, f32, f32]
+                                       i32, vp, vp, vp, i32, i32, i32, f32, f32, vp, sz]
+    L.mf_modulate_rope_bwd_workspace_bytes.argtypes = [i64, i32, i32]
+    L.mf_modulate_rope_bwd_workspace_bytes.restype = sz
+    L.mf_gated_residual_bwd_workspace_bytes.argtypes = [i64, i32]
+    L.mf_gated_residual_bwd_workspace_bytes.restype = sz
     L.mf_modulate_rope_bwd.restype = i32
     L.mf_gated_residual_bwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64,
-                                        i32, f32]
+                                        i32, f32, vp, sz]
     L.mf_gated_residual_bwd.restype = i32
     _lib = L
     return L
@@ -262,7 +267,8 @@ def varlen_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, max_seqlen, s
 
 
 def modulate_rope_bwd(q_in, k_in, dq_out, dk_out, dq_in, dk_in, pos, rope_dims, rope_base=10000.0,
-                      scale=None, mod_row=None, dshift=None, dscale=None, eps=1e-6, stream=None):
+                      scale=None, mod_row=None, dshift=None, dscale=None, eps=1e-6, workspace=None,
+                      stream=None):
     """mf_modulate_rope_bwd on [T][H][D] bf16 tensors; dshift/dscale float32 [n_rows][H*D]."""
     import torch
     T, H, D = q_in.shape
@@ -284,14 +290,18 @@ def modulate_rope_bwd(q_in, k_in, dq_out, dk_out, dq_in, dk_in, pos, rope_dims, 
             if t is None or t.dtype != torch.float32 or tuple(t.shape) != (n_rows, H * D):
                 raise ValueError(f"{n}: expected float32 [n_rows][H*D]")
     f, r, c = (int(x) for x in rope_dims)
+    if workspace is None and scale is not None:
+        workspace = torch.empty(int(lib().mf_modulate_rope_bwd_workspace_bytes(T, H, D)),
+                                dtype=torch.uint8, device=q_in.device)
     check(lib().mf_modulate_rope_bwd(_stream(stream), _ptr(q_in), _ptr(k_in), ld_in, _ptr(dq_out),
                                      _ptr(dk_out), ld_gout, _ptr(dq_in), _ptr(dk_in), ld_gin, T, H, D,
                                      _ptr(scale), _ptr(mod_row), n_rows, _ptr(dshift), _ptr(dscale),
-                                     _ptr(pos), f, r, c, float(rope_base), float(eps)))
+                                     _ptr(pos), f, r, c, float(rope_base), float(eps), _ptr(workspace),
+                                     0 if workspace is None else workspace.numel()))
 
 
 def gated_residual_bwd(x, o, gate, mod_row, dy, dx, dout, dgate, scale2=None, dz=None, dshift2=None,
-                       dscale2=None, eps=1e-6, stream=None):
+                       dscale2=None, eps=1e-6, workspace=None, stream=None):
     """mf_gated_residual_bwd on contiguous [T][C] bf16 rows; row sums float32 [n_rows][C]."""
     import torch
     T = x.shape[0]
@@ -306,6 +316,10 @@ def gated_residual_bwd(x, o, gate, mod_row, dy, dx, dout, dgate, scale2=None, dz
     for n, t in (("dgate", dgate), ("dshift2", dshift2), ("dscale2", dscale2)):
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (n_rows, C)):
             raise ValueError(f"{n}: expected float32 [n_rows][C]")
+    if workspace is None:
+        workspace = torch.empty(int(lib().mf_gated_residual_bwd_workspace_bytes(T, C)),
+                                dtype=torch.uint8, device=x.device)
     check(lib().mf_gated_residual_bwd(_stream(stream), _ptr(x), _ptr(o), _ptr(gate), _ptr(mod_row),
                                       n_rows, _ptr(dy), _ptr(scale2), _ptr(dz), _ptr(dx), _ptr(dout),
-                                      _ptr(dgate), _ptr(dshift2), _ptr(dscale2), T, C, float(eps)))
+                                      _ptr(dgate), _ptr(dshift2), _ptr(dscale2), T, C, float(eps),
+                                      _ptr(workspace), workspace.numel()))

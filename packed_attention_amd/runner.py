@@ -118,3 +118,80 @@ def capture_chain(b: DeviceBatch):
     with torch.cuda.graph(g):
         run_chain(b)
     return g
+
+
+@dataclasses.dataclass
+class GradBatch:
+    """Upstream gradients and backward outputs for one DeviceBatch."""
+    dy: object
+    dz: object
+    dx: object
+    do: object
+    dgate: object
+    dshift2: object
+    dscale2: object
+    dqr: object
+    dkr: object
+    dv: object
+    dq: object
+    dk: object
+    dshift: object
+    dscale: object
+    workspace: object
+    ws_mod: object
+    ws_gres: object
+
+
+def grads_to_device(b: DeviceBatch, device="cuda") -> GradBatch:
+    """Seeded upstream gradients dy, dz (bf16 [T][C]) and every backward
+    output, allocated once."""
+    import torch
+    from .workloads import upstream_grads
+    w = b.w
+    g = upstream_grads(w)
+    T, H, D = w.T, w.H, w.D
+    C = H * D
+    n_rows = len(w.descs)
+    rows = lambda: torch.empty((n_rows, C), dtype=torch.float32, device=device)  # noqa: E731
+    return GradBatch(
+        dy=bf16_tensor(g["dy"], device), dz=bf16_tensor(g["dz"], device),
+        dx=torch.empty((T, C), dtype=torch.bfloat16, device=device),
+        do=torch.empty((T, C), dtype=torch.bfloat16, device=device),
+        dgate=rows(), dshift2=rows(), dscale2=rows(),
+        dqr=torch.empty_like(b.q), dkr=torch.empty_like(b.k), dv=torch.empty_like(b.v),
+        dq=torch.empty_like(b.q), dk=torch.empty_like(b.k),
+        dshift=rows() if w.modulate else None, dscale=rows() if w.modulate else None,
+        workspace=torch.empty(native.attn_bwd_workspace_bytes(len(w.descs), T, H, D),
+                              dtype=torch.uint8, device=device),
+        ws_mod=torch.empty(int(native.lib().mf_modulate_rope_bwd_workspace_bytes(T, H, D)),
+                           dtype=torch.uint8, device=device),
+        ws_gres=torch.empty(int(native.lib().mf_gated_residual_bwd_workspace_bytes(T, C)),
+                            dtype=torch.uint8, device=device))
+
+
+def run_gated_residual_bwd(b: DeviceBatch, gb: GradBatch, stream=None):
+    T, C = b.w.T, b.w.H * b.w.D
+    native.gated_residual_bwd(b.x, b.o.view(T, C), b.gate, b.mod_row, gb.dy, gb.dx, gb.do, gb.dgate,
+                              b.scale2, gb.dz, gb.dshift2, gb.dscale2, b.w.eps, workspace=gb.ws_gres,
+                              stream=stream)
+
+
+def run_attention_bwd(b: DeviceBatch, gb: GradBatch, stream=None):
+    w = b.w
+    native.varlen_attn_bwd(b.qr, b.kr, b.v, b.o, gb.do.view(w.T, w.H, w.D), b.lse, gb.dqr, gb.dkr,
+                           gb.dv, b.cu, b.max_seqlen, workspace=gb.workspace, stream=stream)
+
+
+def run_modulate_rope_bwd(b: DeviceBatch, gb: GradBatch, stream=None):
+    w = b.w
+    native.modulate_rope_bwd(b.q, b.k, gb.dqr, gb.dkr, gb.dq, gb.dk, b.pos, w.rope_dims, w.rope_base,
+                             b.scale, b.mod_row if b.scale is not None else None, gb.dshift,
+                             gb.dscale, w.eps, workspace=gb.ws_mod, stream=stream)
+
+
+def run_backward_chain(b: DeviceBatch, gb: GradBatch, stream=None):
+    """One backward pass of the hot path (after run_chain on the same batch):
+    gated residual -> attention -> modulate+RoPE."""
+    run_gated_residual_bwd(b, gb, stream)
+    run_attention_bwd(b, gb, stream)
+    run_modulate_rope_bwd(b, gb, stream)

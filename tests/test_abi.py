@@ -137,7 +137,7 @@ def test_attention_bwd_validation():
 def modrope_bwd(**kw):
     a = dict(stream=None, q_in=P, k_in=P, ld_in=128, dq_out=P, dk_out=P, ld_gout=128, dq_in=P,
              dk_in=P, ld_gin=128, T=4, H=2, D=64, scale=None, mod_row=None, n_rows=0, dshift=None,
-             dscale=None, pos=P, f=0, r=32, c=32, base=10000.0, eps=1e-6)
+             dscale=None, pos=P, f=0, r=32, c=32, base=10000.0, eps=1e-6, ws=P, ws_bytes=1 << 31)
     a.update(kw)
     return native.lib().mf_modulate_rope_bwd(*a.values())
 
@@ -157,13 +157,17 @@ def test_modulate_rope_bwd_validation():
     assert modrope_bwd(ld_in=132) == ALIGN
     assert modrope_bwd(dk_out=PODD) == ALIGN
     assert modrope_bwd(**{**mod, "dshift": P + 2}) == ALIGN
+    assert modrope_bwd(**{**mod, "ws": None}) == WS
+    assert modrope_bwd(**{**mod, "ws_bytes": 64}) == WS
+    assert modrope_bwd(**{**mod, "ws": P + 16}) == ALIGN
     assert modrope_bwd(T=0, q_in=None, k_in=None, dq_out=None, dk_out=None, dq_in=None, dk_in=None,
                        pos=None) == 0
 
 
 def gres_bwd(**kw):
     a = dict(stream=None, x=P, o=P, gate=P, mod_row=P, n_rows=2, dy=P, scale2=None, dz=None, dx=P,
-             dout=P, dgate=P, dshift2=None, dscale2=None, T=4, C=256, eps=1e-6)
+             dout=P, dgate=P, dshift2=None, dscale2=None, T=4, C=256, eps=1e-6, ws=P,
+             ws_bytes=1 << 31)
     a.update(kw)
     return native.lib().mf_gated_residual_bwd(*a.values())
 
@@ -178,6 +182,12 @@ def test_gated_residual_bwd_validation():
     assert gres_bwd(o=PODD) == ALIGN
     assert gres_bwd(dy=PODD) == ALIGN
     assert gres_bwd(dgate=P + 2) == ALIGN
+    assert gres_bwd(ws=None) == WS
+    assert gres_bwd(ws_bytes=16) == WS
+    assert gres_bwd(ws=P + 32) == ALIGN
+    lib = native.lib()
+    assert lib.mf_gated_residual_bwd_workspace_bytes(4352, 3072) >= 3 * 4352 * 3072
+    assert lib.mf_modulate_rope_bwd_workspace_bytes(4352, 24, 128) >= 2 * 4352 * 3072
 
 
 def gres(**kw):
