@@ -19,16 +19,20 @@
 //    search, with no empty workgroups for packs of many short sequences.
 //  * bwd_dot_kernel: D = rowsum(dO * O) in fp32, HBM-bound.
 //  * attn_bwd_dkdv_kernel: a work unit is 128 keys of one head (4
-//    wavefronts, one per SIMD, 32 keys each).  A wavefront keeps its K and V
-//    rows in registers as MFMA B operands and streams the sequence's queries
-//    in steps of 64 through LDS (Q and dO tiles plus LSE and D, by direct
-//    global->LDS loads, two steps ahead, three buffers).  Per 32-query block:
-//    S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16; every lane then
-//    holds one key and 16 queries), P and dS in fp32 VALU, then
-//    dV^T += dO^T P and dK^T += Q^T dS with dO^T / Q^T read transposed from
-//    LDS (ds_read_b64_tr_b16) and P / dS rounded to bf16 straight from the
-//    accumulator layout as the B operand.  The accumulators are transposed
-//    (d x keys), so the epilogue stores 4 consecutive dims per lane.
+//    wavefronts, one per SIMD, 32 keys each, up to 512 registers).  A
+//    wavefront keeps its K and V rows in registers as MFMA B operands and
+//    streams the sequence's queries in steps of 64 through LDS (Q and dO
+//    tiles plus LSE and D, staged through registers one step ahead, two
+//    buffers).  Per 32-query block: S = Q K^T and dP = dO V^T
+//    (v_mfma_f32_32x32x16_bf16; every lane then holds one key and 16
+//    queries), P and dS in fp32 VALU, then dV^T += dO^T P and dK^T += Q^T dS
+//    with dO^T / Q^T read transposed from LDS (ds_read_b64_tr_b16) and P / dS
+//    rounded to bf16 straight from the accumulator layout as the B operand.
+//    A step is one compile-time sequence of 64 MFMAs with every LDS operand
+//    read six MFMAs ahead and each block's VALU work threaded through the
+//    other block's MFMAs (with one wavefront per SIMD nothing else hides LDS
+//    latency or VALU time).  The accumulators are transposed (d x keys), so
+//    the epilogue stores 4 consecutive dims per lane.
 //  * attn_bwd_dq_kernel: a work unit is 256 queries of one head (8
 //    wavefronts, 2 per SIMD, 32 queries each), the forward's structure: Q and
 //    dO rows in registers, K and V tiles of 64 keys through LDS,
@@ -42,6 +46,7 @@
 //    past it read as zeros.  Zero Q and dO rows contribute nothing to dK and
 //    dV; keys past the end of the last key tile of the dQ kernel get P = 0.
 #include <cmath>
+#include <utility>
 
 #include "mf_device.h"
 #include "mf_internal.h"
@@ -70,10 +75,7 @@ struct BT {
     // dK/dV step: Q tile, dO tile, then LSE[64] and D[64] (fp32)
     static constexpr int QT_BYTES = kKvQ * X_ROW;
     static constexpr int KV_STAGE = 2 * QT_BYTES + 2 * kKvQ * 4;
-    static constexpr int KV_LDS = kStages * KV_STAGE;
-    static constexpr int QT_DMA = kKvQ * X_UNITS / 64;   // wave instructions per tile
-    static constexpr int KV_DMA = 2 * QT_DMA;
-    static constexpr int KV_DMA_PER_WAVE = (KV_DMA + kKvWaves - 1) / kKvWaves;
+    static constexpr int KV_LDS = 2 * KV_STAGE;                 // double-buffered
     // dQ step: K tile (read both ways), V tile (row-wise)
     static constexpr int KT_BYTES = kQK * X_ROW;
     static constexpr int VT_BYTES = kQK * R_ROW;
@@ -83,7 +85,8 @@ struct BT {
     static constexpr int VT_DMA = kQK * R_UNITS / 64;
     static constexpr int Q_DMA = KT_DMA + VT_DMA;
     static constexpr int Q_DMA_PER_WAVE = (Q_DMA + kQWaves - 1) / kQWaves;
-    static_assert(kKvQ * X_UNITS % 64 == 0 && kQK * R_UNITS % 64 == 0, "whole DMA instructions");
+    static_assert(kQK * X_UNITS % 64 == 0 && kQK * R_UNITS % 64 == 0, "whole DMA instructions");
+    static_assert(kKvQ * KCH % (64 * kKvWaves) == 0, "whole staging chunks per thread");
 };
 
 struct BwdParams {
@@ -285,36 +288,35 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
         }
     }
 
-    // Direct loads: instruction n < KV_DMA fills units [64m, 64m+64) of the
-    // Q tile (n < QT_DMA, m = n) or the dO tile (m = n - QT_DMA); wavefront
-    // n % kKvWaves issues it.  Wavefront 0 also loads LSE and D (16 lanes).
-    uint32_t dma_off[TL::KV_DMA_PER_WAVE];
+    // Q/dO tiles are staged through registers (buffer loads of step t+1
+    // issued before step t's products, written to the other LDS buffer after
+    // them): unlike direct global->LDS loads, this leaves the transposed LDS
+    // reads free of waits on the loads in flight.  Thread `tid` owns the
+    // 16-byte chunks tid + 256j of each tile (row = chunk / KCH); threads 0..31
+    // also carry 16 bytes of LSE or D.
+    constexpr int kCh = kKvQ * TL::KCH / (64 * kKvWaves);    // chunks per thread per tile
+    u32x4_t sq[kCh], so[kCh], sst;
+    auto stage_load = [&](int t) {
 #pragma unroll
-    for (int j = 0; j < TL::KV_DMA_PER_WAVE; ++j) {
-        const int nidx = wave + kKvWaves * j;
-        const int m = nidx < TL::QT_DMA ? nidx : nidx - TL::QT_DMA;
-        const int u = 64 * m + lane;
-        const int cc = u % TL::X_UNITS;
-        const uint32_t rb = nidx < TL::QT_DMA ? qrow : orow;
-        dma_off[j] = uint32_t(u / TL::X_UNITS) * rb + 16u * uint32_t(cc < TL::KCH ? cc : TL::KCH - 1);
-    }
-    auto issue = [&](int t, int stage) {
+        for (int j = 0; j < kCh; ++j) {
+            const int ch = tid + 64 * kKvWaves * j;
+            const uint32_t row = uint32_t(t * kKvQ + ch / TL::KCH), col = 16u * uint32_t(ch % TL::KCH);
+            sq[j] = bload16(q_rs, row * qrow + col, 0);
+            so[j] = bload16(do_rs, row * orow + col, 0);
+        }
+        if (tid < 32)
+            sst = bload16(tid < 16 ? l_rs : d_rs, 16u * uint32_t(tid & 15), uint32_t(t) * kKvQ * 4u);
+    };
+    auto stage_store = [&](int stage) {
         unsigned char* base = smem + stage * TL::KV_STAGE;
 #pragma unroll
-        for (int j = 0; j < TL::KV_DMA_PER_WAVE; ++j) {
-            const int nidx = wave + kKvWaves * j;
-            if (TL::KV_DMA % kKvWaves == 0 || nidx < TL::KV_DMA) {
-                if (nidx < TL::QT_DMA)
-                    dma16(q_rs, base + 1024 * nidx, dma_off[j], uint32_t(t) * kKvQ * qrow);
-                else
-                    dma16(do_rs, base + TL::QT_BYTES + 1024 * (nidx - TL::QT_DMA), dma_off[j],
-                          uint32_t(t) * kKvQ * orow);
-            }
+        for (int j = 0; j < kCh; ++j) {
+            const int ch = tid + 64 * kKvWaves * j;
+            const int off = (ch / TL::KCH) * TL::X_ROW + 16 * (ch % TL::KCH);
+            *reinterpret_cast<u32x4_t*>(base + off) = sq[j];
+            *reinterpret_cast<u32x4_t*>(base + TL::QT_BYTES + off) = so[j];
         }
-        if (wave == 0 && lane < 16) {
-            dma16(l_rs, base + 2 * TL::QT_BYTES, 16u * lane, uint32_t(t) * kKvQ * 4u);
-            dma16(d_rs, base + 2 * TL::QT_BYTES + 4 * kKvQ, 16u * lane, uint32_t(t) * kKvQ * 4u);
-        }
+        if (tid < 32) *reinterpret_cast<u32x4_t*>(base + 2 * TL::QT_BYTES + 16 * tid) = sst;
     };
 
     f32x16_t dva[TL::EB], dka[TL::EB];
@@ -326,59 +328,118 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     const int tr_rd = tr_offset<TL::X_ROW>(lane);
     const float c = p.c;
     const int nq = (L + kKvQ - 1) / kKvQ;
-    issue(0, 0);
-    if (nq > 1) issue(1, 1);
+    stage_load(0);
+    stage_store(0);
+    __syncthreads();
     for (int t = 0; t < nq; ++t) {
-        wait_dma();
-        __syncthreads();
-        if (t + 2 < nq) issue(t + 2, (t + 2) % kStages);
-        const unsigned char* qt = smem + (t % kStages) * TL::KV_STAGE;
+        if (t + 1 < nq) stage_load(t + 1);
+        const unsigned char* qt = smem + (t & 1) * TL::KV_STAGE;
         const unsigned char* ot = qt + TL::QT_BYTES;
         const float* st = reinterpret_cast<const float*>(qt + 2 * TL::QT_BYTES);
 
-        // S = Q K^T and dP = dO V^T for the two 32-query blocks (lane: key
-        // l32; register r: query 8(r/4) + 4h + r%4 of the block).
+        // The step is one sequence of 64 MFMAs (32 for D = 64), with every LDS
+        // operand read kPre MFMAs ahead and the VALU work of one block threaded
+        // through the MFMAs of the other (a wavefront's VALU overlaps its own
+        // MFMAs; there is no second wavefront on the SIMD to hide latency):
+        //   ops [0, NA)      S, dP of block 0     (S = Q K^T, dP = dO V^T)
+        //   ops [NA, 2NA)    S, dP of block 1     + P, dS of block 0
+        //   ops [2NA, 2NA+NB)    dV, dK of block 0 + P, dS of block 1
+        //   ops [2NA+NB, 2NA+2NB) dV, dK of block 1
+        // After S and dP a lane holds one key (l32) and 16 queries of the block
+        // (register r: query 8(r/4) + 4h + r%4); dV^T += dO^T P and dK^T += Q^T dS
+        // take dO^T / Q^T from transposed LDS reads and P / dS as bf16 B operands.
+        constexpr int NA = 2 * TL::KK;          // S and dP MFMAs of one 32-query block
+        constexpr int NB = 4 * TL::EB;          // dV and dK MFMAs of one block
+        constexpr int NOPS = 2 * NA + 2 * NB;
+        constexpr int kPre = 6;
+        constexpr int kUnits = 16;              // VALU units of one block (one register each)
         f32x16_t s[2], dp[2];
-#pragma unroll
-        for (int kk = 0; kk < TL::KK; ++kk)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int off = (32 * b + l32) * TL::X_ROW + 32 * kk + 16 * hlf;
-                const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + off);
-                const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(ot + off);
-                s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], kk == 0 ? f32x16_t{} : s[b], 0, 0, 0);
-                dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], kk == 0 ? f32x16_t{} : dp[b], 0, 0, 0);
+        bf16x8_t pk[2][2][2];                   // [block][16-query half][P, dS]
+        f32x4_t l4[2][4], d4[2][4];
+        // Every index below is a compile-time constant (integral_constant
+        // arguments), so all register arrays stay in registers.
+        auto frag = [&](auto opc) -> bf16x8_t {
+            constexpr int op = decltype(opc)::value;
+            if constexpr (op < 2 * NA) {        // 16-byte row reads of Q (S) or dO (dP)
+                constexpr int b = op / NA, i = op % NA, kk = i >> 1;
+                const unsigned char* tile = (i & 1) ? ot : qt;
+                return *reinterpret_cast<const bf16x8_t*>(tile + (32 * b + l32) * TL::X_ROW + 32 * kk + 16 * hlf);
+            } else {                            // transposed reads of dO^T (dV) or Q^T (dK)
+                constexpr int b = (op - 2 * NA) / NB, j = (op - 2 * NA) % NB;
+                constexpr int h2 = j / (2 * TL::EB), m = (j >> 1) % TL::EB;
+                return tr_frag<TL::X_ROW>((j & 1) ? qt : ot, tr_rd, 2 * b + h2, m);
             }
-
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            // P = exp(tau S - LSE), dS = P (dP - D), rows of this block
+        };
+        auto mfma_op = [&](auto opc, const bf16x8_t& f) {
+            constexpr int op = decltype(opc)::value;
+            if constexpr (op < 2 * NA) {
+                constexpr int b = op / NA, i = op % NA, kk = i >> 1;
+                if constexpr (i & 1)
+                    dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, vf[kk], kk == 0 ? f32x16_t{} : dp[b], 0, 0, 0);
+                else
+                    s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, kf[kk], kk == 0 ? f32x16_t{} : s[b], 0, 0, 0);
+            } else {
+                constexpr int b = (op - 2 * NA) / NB, j = (op - 2 * NA) % NB;
+                constexpr int h2 = j / (2 * TL::EB), m = (j >> 1) % TL::EB;
+                if constexpr (j & 1)
+                    dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pk[b][h2][1], dka[m], 0, 0, 0);
+                else
+                    dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pk[b][h2][0], dva[m], 0, 0, 0);
+            }
+        };
+        auto load_stats = [&](int b) {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(st + 32 * b + 8 * gq + 4 * hlf);
-                const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(st + kKvQ + 32 * b + 8 * gq + 4 * hlf);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][4 * gq + i], c, -l4[i] * kLog2e));
-                    s[b][4 * gq + i] = pr;
-                    dp[b][4 * gq + i] = pr * (dp[b][4 * gq + i] - d4[i]);
-                }
+                l4[b][gq] = *reinterpret_cast<const f32x4_t*>(st + 32 * b + 8 * gq + 4 * hlf);
+                d4[b][gq] = *reinterpret_cast<const f32x4_t*>(st + kKvQ + 32 * b + 8 * gq + 4 * hlf);
             }
-            // dV^T += dO^T P, dK^T += Q^T dS over the block's two 16-query chunks
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const bf16x8_t pb = pack_chunk(s[b], h2);
-                const bf16x8_t sb = pack_chunk(dp[b], h2);
-                const int chunk = 2 * b + h2;
-#pragma unroll
-                for (int m = 0; m < TL::EB; ++m) {
-                    const bf16x8_t oa = tr_frag<TL::X_ROW>(ot, tr_rd, chunk, m);
-                    dva[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb, dva[m], 0, 0, 0);
-                    const bf16x8_t qa = tr_frag<TL::X_ROW>(qt, tr_rd, chunk, m);
-                    dka[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb, dka[m], 0, 0, 0);
-                }
+        };
+        // P = exp(tau S - LSE), dS = P (dP - D) for register u of block b;
+        // after registers 7 and 15 the half's bf16 B operands are packed.
+        auto v_unit = [&](auto bc, auto uc) {
+            constexpr int b = decltype(bc)::value, u = decltype(uc)::value;
+            constexpr int gq = u >> 2, i = u & 3;
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][u], c, -l4[b][gq][i] * kLog2e));
+            s[b][u] = pr;
+            dp[b][u] = pr * (dp[b][u] - d4[b][gq][i]);
+            if constexpr ((u & 7) == 7) {
+                pk[b][u >> 3][0] = pack_chunk(s[b], u >> 3);
+                pk[b][u >> 3][1] = pack_chunk(dp[b], u >> 3);
             }
-        }
+        };
+        load_stats(0);
+        load_stats(1);
+        bf16x8_t fr[kPre];
+        [&]<int... P>(std::integer_sequence<int, P...>) {
+            ((fr[P] = frag(std::integral_constant<int, P>{})), ...);
+        }(std::make_integer_sequence<int, kPre>{});
+        auto one_op = [&](auto opc) {
+            constexpr int op = decltype(opc)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_op(opc, fr[op % kPre]);
+            if constexpr (op + kPre < NOPS) fr[op % kPre] = frag(std::integral_constant<int, op + kPre>{});
+            // VALU of block 0 rides on the S/dP MFMAs of block 1, that of
+            // block 1 on the dV/dK MFMAs of block 0
+            if constexpr (op >= NA && op < 2 * NA) {
+                constexpr int per = kUnits / NA;
+                [&]<int... K>(std::integer_sequence<int, K...>) {
+                    (v_unit(std::integral_constant<int, 0>{}, std::integral_constant<int, (op - NA) * per + K>{}), ...);
+                }(std::make_integer_sequence<int, per>{});
+            } else if constexpr (op >= 2 * NA && op < 2 * NA + NB) {
+                constexpr int per = kUnits / NB;
+                [&]<int... K>(std::integer_sequence<int, K...>) {
+                    (v_unit(std::integral_constant<int, 1>{}, std::integral_constant<int, (op - 2 * NA) * per + K>{}), ...);
+                }(std::make_integer_sequence<int, per>{});
+            }
+        };
+        [&]<int... OPS>(std::integer_sequence<int, OPS...>) {
+            (one_op(std::integral_constant<int, OPS>{}), ...);
+        }(std::make_integer_sequence<int, NOPS>{});
+        __builtin_amdgcn_sched_barrier(0);
+        // the other buffer was last read in step t-1, which every wavefront
+        // finished before the barrier that opened step t
+        if (t + 1 < nq) stage_store((t + 1) & 1);
+        __syncthreads();
     }
 
     // epilogue: lane l32 owns key key0 + l32
