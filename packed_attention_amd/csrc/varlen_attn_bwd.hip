@@ -46,6 +46,7 @@
 //    past it read as zeros.  Zero Q and dO rows contribute nothing to dK and
 //    dV; keys past the end of the last key tile of the dQ kernel get P = 0.
 #include <cmath>
+#include <mutex>
 #include <utility>
 
 #include "mf_device.h"
@@ -60,7 +61,6 @@ constexpr int kKvQ = 64;                   // queries per dK/dV step
 constexpr int kQWaves = 8;                 // dQ kernel: two wavefronts per SIMD
 constexpr int kQRows = 32 * kQWaves;       // queries per dQ work unit
 constexpr int kQK = 64;                    // keys per dQ step
-constexpr int kStages = 3;                 // LDS buffers (loads two steps ahead)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -80,13 +80,9 @@ struct BT {
     static constexpr int KT_BYTES = kQK * X_ROW;
     static constexpr int VT_BYTES = kQK * R_ROW;
     static constexpr int Q_STAGE = KT_BYTES + VT_BYTES;
-    static constexpr int Q_LDS = kStages * Q_STAGE;
-    static constexpr int KT_DMA = kQK * X_UNITS / 64;
-    static constexpr int VT_DMA = kQK * R_UNITS / 64;
-    static constexpr int Q_DMA = KT_DMA + VT_DMA;
-    static constexpr int Q_DMA_PER_WAVE = (Q_DMA + kQWaves - 1) / kQWaves;
-    static_assert(kQK * X_UNITS % 64 == 0 && kQK * R_UNITS % 64 == 0, "whole DMA instructions");
+    static constexpr int Q_LDS = 2 * Q_STAGE;                   // double-buffered
     static_assert(kKvQ * KCH % (64 * kKvWaves) == 0, "whole staging chunks per thread");
+    static_assert(kQK * KCH % (64 * kQWaves) == 0, "whole staging chunks per thread");
 };
 
 struct BwdParams {
@@ -200,9 +196,6 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict
     for (int m = TPR / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, TPR);
     if (live && part == 0) dsum[int64_t(h) * T + t] = acc;
 }
-
-// Wait for this wavefront's direct global->LDS loads (vmcnt(0)).
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Transposed 8-row x 4-dim fragment pair of a row-major tile: lanes receive
 // dim 32*blk + (lane & 31) of rows {4h..4h+3} and {8+4h..8+4h+3} of the
@@ -454,7 +447,8 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
 // dQ
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(64 * kQWaves) void attn_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(BwdParams p) {
     using TL = BT<D>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     int seq, head, tile;
@@ -493,30 +487,26 @@ __global__ __launch_bounds__(64 * kQWaves) void attn_bwd_dq_kernel(BwdParams p) 
     const float nl = -__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(l_rs, uint32_t(q0 + l32) * 4u, 0, 0)) * kLog2e;
     const float dq_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d_rs, uint32_t(q0 + l32) * 4u, 0, 0));
 
-    // Direct loads: instruction n < KT_DMA fills units [64n, 64n+64) of the
-    // K tile, the rest the V tile; wavefront n % kQWaves issues it.
-    uint32_t dma_off[TL::Q_DMA_PER_WAVE];
+    // K/V tiles staged through registers one step ahead into two LDS
+    // buffers (see the dK/dV kernel): thread `tid` owns chunks tid + 512j.
+    constexpr int kCh = kQK * TL::KCH / (64 * kQWaves);
+    u32x4_t sk[kCh], sv[kCh];
+    auto stage_load = [&](int t) {
 #pragma unroll
-    for (int j = 0; j < TL::Q_DMA_PER_WAVE; ++j) {
-        const int nidx = wave + kQWaves * j;
-        const bool kt = nidx < TL::KT_DMA;
-        const int units = kt ? TL::X_UNITS : TL::R_UNITS;
-        const int u = 64 * (kt ? nidx : nidx - TL::KT_DMA) + lane;
-        const int cc = u % units;
-        dma_off[j] = uint32_t(u / units) * qrow + 16u * uint32_t(cc < TL::KCH ? cc : TL::KCH - 1);
-    }
-    auto issue = [&](int t, int stage) {
+        for (int j = 0; j < kCh; ++j) {
+            const int ch = tid + 64 * kQWaves * j;
+            const uint32_t off = uint32_t(t * kQK + ch / TL::KCH) * qrow + 16u * uint32_t(ch % TL::KCH);
+            sk[j] = bload16(k_rs, off, 0);
+            sv[j] = bload16(v_rs, off, 0);
+        }
+    };
+    auto stage_store = [&](int stage) {
         unsigned char* base = smem + stage * TL::Q_STAGE;
-        const uint32_t soff = uint32_t(t) * kQK * qrow;
 #pragma unroll
-        for (int j = 0; j < TL::Q_DMA_PER_WAVE; ++j) {
-            const int nidx = wave + kQWaves * j;
-            if (TL::Q_DMA % kQWaves == 0 || nidx < TL::Q_DMA) {
-                if (nidx < TL::KT_DMA)
-                    dma16(k_rs, base + 1024 * nidx, dma_off[j], soff);
-                else
-                    dma16(v_rs, base + TL::KT_BYTES + 1024 * (nidx - TL::KT_DMA), dma_off[j], soff);
-            }
+        for (int j = 0; j < kCh; ++j) {
+            const int ch = tid + 64 * kQWaves * j;
+            *reinterpret_cast<u32x4_t*>(base + (ch / TL::KCH) * TL::X_ROW + 16 * (ch % TL::KCH)) = sk[j];
+            *reinterpret_cast<u32x4_t*>(base + TL::KT_BYTES + (ch / TL::KCH) * TL::R_ROW + 16 * (ch % TL::KCH)) = sv[j];
         }
     };
 
@@ -530,58 +520,137 @@ __global__ __launch_bounds__(64 * kQWaves) void attn_bwd_dq_kernel(BwdParams p) 
     const float c = p.c;
     const int nk = (L + kQK - 1) / kQK;
     const int masked_tile = (L % kQK) != 0 ? nk - 1 : nk;
-    issue(0, 0);
-    if (nk > 1) issue(1, 1);
+    stage_load(0);
+    stage_store(0);
+    __syncthreads();
     for (int t = 0; t < nk; ++t) {
-        wait_dma();
-        __syncthreads();
-        if (t + 2 < nk) issue(t + 2, (t + 2) % kStages);
-        const unsigned char* kt = smem + (t % kStages) * TL::Q_STAGE;
+        if (t + 1 < nk) stage_load(t + 1);
+        const unsigned char* kt = smem + (t & 1) * TL::Q_STAGE;
         const unsigned char* vt = kt + TL::KT_BYTES;
 
-        // S^T = K Q^T and dP^T = V dO^T for the two 32-key blocks (lane:
-        // query l32; register r: key 8(r/4) + 4h + r%4 of the block).
+        // One compile-time sequence per step (48 MFMAs for D = 128):
+        //   ops [0, NA)           S^T, dP^T of key block 0
+        //   ops [NA, 2NA)         S^T, dP^T of key block 1 + dS^T of block 0
+        //   ops [2NA, 2NA+NB)     dQ^T += K^T dS^T for block 0 + dS^T of block 1
+        //   ops [2NA+NB, 2NA+2NB) dQ^T for block 1
+        // (lane: query l32; register r of a block: key 8(r/4) + 4h + r%4).
+        constexpr int NA = 2 * TL::KK;
+        constexpr int NB = 2 * TL::EB;
+        constexpr int NOPS = 2 * NA + 2 * NB;
+        constexpr int kPre = 4;
+        constexpr int kUnits = 16;
         f32x16_t s[2], dp[2];
-#pragma unroll
-        for (int kk = 0; kk < TL::KK; ++kk)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kt + (32 * b + l32) * TL::X_ROW + 32 * kk + 16 * hlf);
-                const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vt + (32 * b + l32) * TL::R_ROW + 32 * kk + 16 * hlf);
-                s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], kk == 0 ? f32x16_t{} : s[b], 0, 0, 0);
-                dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[kk], kk == 0 ? f32x16_t{} : dp[b], 0, 0, 0);
+        bf16x8_t pk[2][2];                  // [key block][16-key half] dS^T as bf16 B operand
+        auto frag = [&](auto opc) -> bf16x8_t {
+            constexpr int op = decltype(opc)::value;
+            if constexpr (op < 2 * NA) {    // 16-byte row reads of K (S^T) or V (dP^T)
+                constexpr int b = op / NA, i = op % NA, kk = i >> 1;
+                if constexpr (i & 1)
+                    return *reinterpret_cast<const bf16x8_t*>(vt + (32 * b + l32) * TL::R_ROW + 32 * kk + 16 * hlf);
+                else
+                    return *reinterpret_cast<const bf16x8_t*>(kt + (32 * b + l32) * TL::X_ROW + 32 * kk + 16 * hlf);
+            } else {                        // transposed reads of K^T
+                constexpr int b = (op - 2 * NA) / NB, j = (op - 2 * NA) % NB;
+                return tr_frag<TL::X_ROW>(kt, tr_rd, 2 * b + j / TL::EB, j % TL::EB);
             }
-        if (t == masked_tile) {
-            const int key0 = t * kQK;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
+        };
+        auto mfma_op = [&](auto opc, const bf16x8_t& f) {
+            constexpr int op = decltype(opc)::value;
+            if constexpr (op < 2 * NA) {
+                constexpr int b = op / NA, i = op % NA, kk = i >> 1;
+                if constexpr (i & 1)
+                    dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, of[kk], kk == 0 ? f32x16_t{} : dp[b], 0, 0, 0);
+                else
+                    s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], kk == 0 ? f32x16_t{} : s[b], 0, 0, 0);
+            } else {
+                constexpr int b = (op - 2 * NA) / NB, j = (op - 2 * NA) % NB;
+                constexpr int m = j % TL::EB;
+                dqa[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pk[b][j / TL::EB], dqa[m], 0, 0, 0);
+            }
+        };
+        // keys past the end of the sequence (last tile only) get P = 0
+        auto mask_block = [&](int b) {
+            if (t == masked_tile) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + 32 * b + 8 * (r >> 2) + 4 * hlf + (r & 3);
+                    const int key = t * kQK + 32 * b + 8 * (r >> 2) + 4 * hlf + (r & 3);
                     if (key >= L) s[b][r] = -INFINITY;
                 }
-        }
-        // dS^T = P^T (dP^T - D), P^T = exp(tau S^T - LSE)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl));
-                dp[b][r] = pr * (dp[b][r] - dq_d);
             }
-        // dQ^T += K^T dS^T over the four 16-key chunks
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            const bf16x8_t sb = pack_chunk(dp[cc >> 1], cc & 1);
-#pragma unroll
-            for (int m = 0; m < TL::EB; ++m) {
-                const bf16x8_t ka = tr_frag<TL::X_ROW>(kt, tr_rd, cc, m);
-                dqa[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sb, dqa[m], 0, 0, 0);
+        };
+        // dS^T = P^T (dP^T - D), P^T = exp(tau S^T - LSE), register u of block b
+        auto v_unit = [&](auto bc, auto uc) {
+            constexpr int b = decltype(bc)::value, u = decltype(uc)::value;
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][u], c, nl));
+            dp[b][u] = pr * (dp[b][u] - dq_d);
+            if constexpr ((u & 7) == 7) pk[b][u >> 3] = pack_chunk(dp[b], u >> 3);
+        };
+        bf16x8_t fr[kPre];
+        [&]<int... P>(std::integer_sequence<int, P...>) {
+            ((fr[P] = frag(std::integral_constant<int, P>{})), ...);
+        }(std::make_integer_sequence<int, kPre>{});
+        auto one_op = [&](auto opc) {
+            constexpr int op = decltype(opc)::value;
+            if constexpr (op == NA) mask_block(0);
+            if constexpr (op == 2 * NA) mask_block(1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_op(opc, fr[op % kPre]);
+            if constexpr (op + kPre < NOPS) fr[op % kPre] = frag(std::integral_constant<int, op + kPre>{});
+            if constexpr (op >= NA && op < 2 * NA) {
+                constexpr int per = kUnits / NA;
+                [&]<int... K>(std::integer_sequence<int, K...>) {
+                    (v_unit(std::integral_constant<int, 0>{}, std::integral_constant<int, (op - NA) * per + K>{}), ...);
+                }(std::make_integer_sequence<int, per>{});
+            } else if constexpr (op >= 2 * NA && op < 2 * NA + NB) {
+                constexpr int per = kUnits / NB;
+                [&]<int... K>(std::integer_sequence<int, K...>) {
+                    (v_unit(std::integral_constant<int, 1>{}, std::integral_constant<int, (op - 2 * NA) * per + K>{}), ...);
+                }(std::make_integer_sequence<int, per>{});
             }
-        }
+        };
+        [&]<int... OPS>(std::integer_sequence<int, OPS...>) {
+            (one_op(std::integral_constant<int, OPS>{}), ...);
+        }(std::make_integer_sequence<int, NOPS>{});
+        __builtin_amdgcn_sched_barrier(0);
+        // the other buffer was last read in step t-1, finished by everyone
+        // before the barrier that opened step t
+        if (t + 1 < nk) stage_store((t + 1) & 1);
+        __syncthreads();
     }
 
     if (q0 + l32 < L) store_rows_t<D>(p.dq + (tok0 + q0 + l32) * p.ld_d + int64_t(head) * D, dqa, p.scale, hlf);
+}
+
+// One non-blocking side stream and a fork/join event pair per device,
+// created on the first call that is not under stream capture (creating a
+// stream is not allowed during capture); until then, and if creation fails,
+// both kernels run on the caller's stream.  The mutex keeps one call's
+// record/wait pairs together when several host threads launch at once (a
+// wait binds to the event's latest record).
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+bool g_side_tried[kMaxDevices];
+std::mutex g_side_mu;
+
+// Caller holds g_side_mu.
+SideStream* side_stream(hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    if (!g_side_tried[dev]) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+        g_side_tried[dev] = true;
+        SideStream s;
+        if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&s.join, hipEventDisableTiming) == hipSuccess)
+            g_side[dev] = s;
+    }
+    return g_side[dev].join ? &g_side[dev] : nullptr;
 }
 
 template <int D>
@@ -619,12 +688,27 @@ hipError_t launch_bwd_d(const AttnBwdArgs& a, hipStream_t stream) {
     // Upper bounds of the unit counts: sum_s ceil(L_s / n) <= T / n + n_seq.
     const int64_t units_kv = int64_t(a.H) * (a.T / kKvKeys + a.n_seq);
     const int64_t units_q = int64_t(a.H) * (a.T / kQRows + a.n_seq);
+    // The dQ kernel runs beside the dK/dV kernel on a second stream: both
+    // only read what the dot kernel wrote, and each alone leaves the last of
+    // its ~3 rounds of work units on part of the chip.
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* side = side_stream(stream);
+    hipStream_t qs = side ? side->stream : stream;
+    if (side) {
+        if ((e = hipEventRecord(side->fork, stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(qs, side->fork, 0)) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(unsigned(units_q)), dim3(64 * kQWaves),
+                       BT<D>::Q_LDS, qs, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<D>, dim3(unsigned(units_kv)), dim3(64 * kKvWaves),
                        BT<D>::KV_LDS, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<D>, dim3(unsigned(units_q)), dim3(64 * kQWaves),
-                       BT<D>::Q_LDS, stream, p);
-    return hipGetLastError();
+    if (side) {
+        if ((e = hipEventRecord(side->join, qs)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(stream, side->join, 0)) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace

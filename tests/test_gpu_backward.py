@@ -124,6 +124,31 @@ def test_bwd_packed_equals_alone_and_determinism():
             assert torch.equal(x[sl], y), s
 
 
+def test_bwd_orders_with_caller_stream():
+    """The dQ kernel runs on a second stream forked from and joined to the
+    caller's: on a non-default caller stream, inputs written just before the
+    call and copies of the outputs taken just after it, with no host
+    synchronisation between, match a run on the default stream bitwise."""
+    import torch
+    descs = [(30, 1, 16, 16, 0, 0), (2, 1, 9, 7, 1, 1)]
+    w = W.custom(descs, H=4, D=128, seed=21, name="bwd_stream_order")
+    G.say(w.name, "side caller stream")
+    b, dO, dq, dk, dv = forward_and_grads(w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    copies = []
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            dO2 = dO * 2.0 * 0.5
+            outs = [torch.full_like(b.q, float("nan")) for _ in range(3)]
+            native.varlen_attn_bwd(b.qr, b.kr, b.v, b.o, dO2, b.lse, *outs, b.cu, b.max_seqlen)
+            copies.append([o.clone() for o in outs])
+    torch.cuda.synchronize()
+    for rep in copies:
+        for x, y in zip((dq, dk, dv), rep):
+            assert torch.equal(x, y)
+
+
 def test_bwd_single_1024_sampled():
     """Full size (256 + 64x64 tokens, H=24, d=128), sampled rows and keys."""
     import torch
