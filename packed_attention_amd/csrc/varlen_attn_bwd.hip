@@ -523,7 +523,11 @@ void attn_bwd_dq_kernel(BwdParams p) {
     stage_load(0);
     stage_store(0);
     __syncthreads();
-    for (int t = 0; t < nk; ++t) {
+    // Only the last key tile can need masking.  The steady steps are built
+    // without the masking branch: a branch inside the sequence lets the
+    // compiler gather the VALU work threaded before it into one block.
+    auto step = [&](auto maskc, const int t) {
+        constexpr bool kMask = decltype(maskc)::value;
         if (t + 1 < nk) stage_load(t + 1);
         const unsigned char* kt = smem + (t & 1) * TL::Q_STAGE;
         const unsigned char* vt = kt + TL::KT_BYTES;
@@ -570,11 +574,13 @@ void attn_bwd_dq_kernel(BwdParams p) {
         };
         // keys past the end of the sequence (last tile only) get P = 0
         auto mask_block = [&](int b) {
-            if (t == masked_tile) {
+            if constexpr (kMask) {
+                if (t == masked_tile) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = t * kQK + 32 * b + 8 * (r >> 2) + 4 * hlf + (r & 3);
-                    if (key >= L) s[b][r] = -INFINITY;
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = t * kQK + 32 * b + 8 * (r >> 2) + 4 * hlf + (r & 3);
+                        if (key >= L) s[b][r] = -INFINITY;
+                    }
                 }
             }
         };
@@ -616,7 +622,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
         // before the barrier that opened step t
         if (t + 1 < nk) stage_store((t + 1) & 1);
         __syncthreads();
-    }
+    };
+    for (int t = 0; t + 1 < nk; ++t) step(std::false_type{}, t);
+    step(std::true_type{}, nk - 1);
 
     if (q0 + l32 < L) store_rows_t<D>(p.dq + (tok0 + q0 + l32) * p.ld_d + int64_t(head) * D, dqa, p.scale, hlf);
 }
