@@ -1,10 +1,11 @@
 """Oracle for the packed varlen RoPE joint-attention forward.
 
 TEST INFRASTRUCTURE ONLY: the fp64 numpy definition (``reference``), a
-pure-Python loop version for tiny packs (``brute``) and the exact gradients of
+pure-Python loop version for tiny packs (``brute``), the block projections
+around the attention (``block``) and the exact gradients of
 the forward steps for the backward pass (``backward``).  Only the tests, the
 smoke check and the benchmark's CPU-baseline leg may import this package; the
 HIP library and its binding never do, and this package imports nothing from
 them.
 """
-from . import backward, brute, reference  # noqa: F401
+from . import backward, block, brute, reference  # noqa: F401

@@ -226,6 +226,19 @@ def upstream_grads(w: Workload) -> dict:
     return g
 
 
+def block_inputs(w: Workload) -> dict:
+    """Seeded stand-ins for the block around the attention: the residual
+    stream x [T][C] (the workload's own x when it has one, else N(0, 1)), the
+    projection weights W_qkv [3C][C] and W_o [C][C] (output x input, as a
+    random initialisation: N(0, 1/C) entries) -- there are no trained weights
+    here.  bf16 bits from their own generator (seed + 2000003)."""
+    rng = np.random.default_rng(w.seed + 2000003)
+    T, C = w.T, w.H * w.D
+    x = w.x if w.x is not None else _normal_bf16(rng, (T, C), 1.0)
+    sig = 1.0 / np.sqrt(C)
+    return dict(x=x, w_qkv=_normal_bf16(rng, (3 * C, C), sig), w_o=_normal_bf16(rng, (C, C), sig))
+
+
 # ---------------------------------------------------------------------------
 # Named workloads
 # ---------------------------------------------------------------------------
