@@ -309,6 +309,59 @@ mf_status mf_gated_residual(void* stream,
                             const void* shift2, const void* scale2, void* z,
                             int64_t T, int32_t C, float eps);
 
+/* ------------------------------------------------------------------------
+ * Block projections around the attention (the pages fuse the adaptive
+ * normalisation, rotary embedding and gating / residual chains with the
+ * operators around them: picx.dev summary of Mage-Flow, Methodology >
+ * Training Infrastructure; gist.science "Resumo Tecnico: Mage-Flow",
+ * Metodologia > 3. Otimizacao de Nivel de Sistema > Kernels Fundidos; in an
+ * NR-MMDiT block, picx.dev Methodology > Native-Resolution MMDiT, those
+ * operators are the projections into and out of the joint attention).
+ *
+ * mf_block_qkv: QKV projection of the adaLN-modulated residual stream with
+ * the rotary embedding of q and k:
+ *   u[t]   = LN(x[t]) * (1 + scale[m(t)]) + shift[m(t)]   (fp32, then bf16)
+ *   qkv[t] = u[t] W_qkv^T   (fp32 accumulation of bf16 products)
+ *   q' = RoPE(qkv[t][0:C]), k' = RoPE(qkv[t][C:2C]), v = qkv[t][2C:3C]
+ * with RoPE as in mf_modulate_rope (pairs of adjacent dims of each head,
+ * axes frame / row / col in contiguous blocks).
+ * x: bf16 [T][C] (C = H*D), token stride ld_x >= C, a multiple of 8.
+ * w_qkv: bf16 [3C][C] contiguous (output x input, no bias).
+ * qkv: bf16 [T][3C] output (q', k', v side by side), token stride
+ *   ld_qkv >= 3C, a multiple of 8; must not overlap x or w_qkv.
+ * shift, scale: bf16 [n_rows][C], both NULL (no modulation: u = x) or both
+ *   set with mod_row int32 [T]; pos: int32 [T][3]; rope dims as for
+ *   mf_modulate_rope; eps > 0 when modulating.
+ * workspace: device memory of at least mf_block_qkv_workspace_bytes(T, H,
+ *   D) bytes, 16-byte aligned (the modulated rows; may be NULL without
+ *   modulation); owned by the caller, used between calls on one stream only.
+ * Limits: D in {64, 128}, C <= 8192, T * ld_x * 2 and 3C * C * 2 below 2^32.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
+ * MF_ERR_WORKSPACE, MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+size_t mf_block_qkv_workspace_bytes(int64_t T, int32_t H, int32_t D);
+
+mf_status mf_block_qkv(void* stream,
+                       const void* x, int64_t ld_x, const void* w_qkv,
+                       void* qkv, int64_t ld_qkv,
+                       const void* shift, const void* scale, const int32_t* mod_row,
+                       const int32_t* pos, int64_t T, int32_t H, int32_t D,
+                       int32_t rope_f, int32_t rope_r, int32_t rope_c,
+                       float rope_base, float eps, void* workspace, size_t workspace_bytes);
+
+/* mf_block_out: out projection with the gated residual:
+ *   y[t] = x[t] + gate[m(t)] * (o[t] W_o^T)        (fp32, then bf16)
+ * o: bf16 [T][C] (the attention output viewed as [T][H*D]), token stride
+ *   ld_o >= C, a multiple of 8.  w_o: bf16 [C][C] contiguous (output x
+ *   input, no bias).  x, y: bf16 [T][C] contiguous; y must not overlap o,
+ *   w_o or x.  gate: bf16 [n_rows][C]; mod_row: int32 [T].
+ * Limits: C a multiple of 64, at most 8192; T * ld_o * 2 below 2^32.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
+ * MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+mf_status mf_block_out(void* stream,
+                       const void* o, int64_t ld_o, const void* w_o,
+                       const void* x, const void* gate, const int32_t* mod_row,
+                       void* y, int64_t T, int32_t C);
+
 #ifdef __cplusplus
 }
 #endif

@@ -378,4 +378,92 @@ mf_status mf_gated_residual_bwd(void* stream, const void* x, const void* o, cons
     return finish(mf::launch_gated_residual_bwd(a, s), s);
 }
 
+size_t mf_block_qkv_workspace_bytes(int64_t T, int32_t H, int32_t D) {
+    return mf::block_qkv_workspace_bytes(T, H * D);
+}
+
+mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_qkv, void* qkv,
+                       int64_t ld_qkv, const void* shift, const void* scale, const int32_t* mod_row,
+                       const int32_t* pos, int64_t T, int32_t H, int32_t D, int32_t rope_f, int32_t rope_r,
+                       int32_t rope_c, float rope_base, float eps, void* workspace, size_t workspace_bytes) {
+    if (T < 0 || T > INT32_MAX || H <= 0) return MF_ERR_SHAPE;
+    if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
+    const int64_t C = int64_t(H) * D;
+    if (C > 8192) return MF_ERR_UNSUPPORTED;
+    if (rope_f < 0 || rope_r < 0 || rope_c < 0 || rope_f % 8 || rope_r % 8 || rope_c % 8 ||
+        rope_f + rope_r + rope_c != D)
+        return MF_ERR_SHAPE;
+    if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return MF_ERR_SHAPE;
+    if (ld_x < C || ld_qkv < 3 * C) return MF_ERR_SHAPE;
+    // 32-bit buffer offsets over the activations and the weights
+    if (T * ld_x * 2 >= (int64_t(1) << 32) || 3 * C * C * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
+    if ((shift == nullptr) != (scale == nullptr)) return MF_ERR_NULL;
+    const bool modulate = shift != nullptr;
+    if (modulate && !(eps > 0.f)) return MF_ERR_SHAPE;
+    if (T == 0) return MF_OK;
+    if (!x || !w_qkv || !qkv || !pos) return MF_ERR_NULL;
+    if (modulate && !mod_row) return MF_ERR_NULL;
+    if (ld_x % 8 || ld_qkv % 8) return MF_ERR_ALIGN;
+    if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(qkv, 16) || !aligned(pos, 4)) return MF_ERR_ALIGN;
+    if (modulate) {
+        if (!aligned(shift, 16) || !aligned(scale, 16) || !aligned(mod_row, 4)) return MF_ERR_ALIGN;
+        if (workspace == nullptr || workspace_bytes < mf::block_qkv_workspace_bytes(T, int32_t(C)))
+            return MF_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return MF_ERR_ALIGN;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        std::vector<int32_t> hp;
+        if (!fetch(pos, size_t(T) * 3, hp, s)) return MF_ERR_HIP;
+        for (int32_t v : hp)
+            if (v < 0) return MF_ERR_TABLE;
+        if (modulate) {
+            mf_status st = check_rows(mod_row, T, s);
+            if (st != MF_OK) return st;
+        }
+    }
+    mf::BlockQkvArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.ld_x = ld_x;
+    a.w = static_cast<const uint16_t*>(w_qkv);
+    a.qkv = static_cast<uint16_t*>(qkv);
+    a.ld_qkv = ld_qkv;
+    a.shift = static_cast<const uint16_t*>(shift);
+    a.scale = static_cast<const uint16_t*>(scale);
+    a.mod_row = mod_row; a.pos = pos;
+    a.T = T; a.H = H; a.D = D;
+    a.rope_f = rope_f; a.rope_r = rope_r; a.rope_c = rope_c;
+    a.rope_base = rope_base; a.eps = eps;
+    a.workspace = workspace;
+    return finish(mf::launch_block_qkv(a, s), s);
+}
+
+mf_status mf_block_out(void* stream, const void* o, int64_t ld_o, const void* w_o, const void* x,
+                       const void* gate, const int32_t* mod_row, void* y, int64_t T, int32_t C) {
+    if (T < 0 || T > INT32_MAX || C <= 0 || C % 64 || C > 8192) return MF_ERR_SHAPE;
+    if (ld_o < C) return MF_ERR_SHAPE;
+    if (T * ld_o * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
+    if (T == 0) return MF_OK;
+    if (!o || !w_o || !x || !gate || !mod_row || !y) return MF_ERR_NULL;
+    if (ld_o % 8) return MF_ERR_ALIGN;
+    if (!aligned(o, 16) || !aligned(w_o, 16) || !aligned(x, 16) || !aligned(gate, 16) || !aligned(y, 16) ||
+        !aligned(mod_row, 4))
+        return MF_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        mf_status st = check_rows(mod_row, T, s);
+        if (st != MF_OK) return st;
+    }
+    mf::BlockOutArgs a;
+    a.o = static_cast<const uint16_t*>(o);
+    a.ld_o = ld_o;
+    a.w = static_cast<const uint16_t*>(w_o);
+    a.x = static_cast<const uint16_t*>(x);
+    a.gate = static_cast<const uint16_t*>(gate);
+    a.mod_row = mod_row;
+    a.y = static_cast<uint16_t*>(y);
+    a.T = T; a.C = C;
+    return finish(mf::launch_block_out(a, s), s);
+}
+
 }  // extern "C"

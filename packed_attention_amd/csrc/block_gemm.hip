@@ -1,0 +1,385 @@
+// Block projections around the attention (gfx950): the QKV projection of the
+// adaLN-modulated residual stream with the rotary embedding of q and k as its
+// epilogue, and the out projection with the gated residual as its epilogue.
+//
+// The pages fuse the adaptive normalisation, rotary embedding and gating /
+// residual chains with the operators around them (picx.dev summary of
+// Mage-Flow, Methodology > Training Infrastructure; gist.science "Resumo
+// Tecnico: Mage-Flow", Metodologia > 3. Otimizacao de Nivel de Sistema >
+// Kernels Fundidos); in an NR-MMDiT block (picx.dev, Methodology >
+// Native-Resolution MMDiT) those operators are these two projections.
+//
+//   u   = LN(x) * (1 + scale[m(t)]) + shift[m(t)]        (x: [T][C])
+//   qkv = u W_qkv^T,  q' = RoPE(q), k' = RoPE(k), v       (W_qkv: [3C][C])
+//   y   = x + gate[m(t)] * (o W_o^T)                      (W_o: [C][C])
+//
+// Design (MI355X, CDNA4):
+//  * adaln_kernel: one wavefront per token row, LayerNorm statistics in fp32
+//    (two passes over registers), the modulated row rounded to bf16 into the
+//    caller's workspace.  The modulation is not recomputed inside the GEMM:
+//    each activation element meets every 256-feature tile of the weight
+//    (36 of them for the QKV projection at C = 3072), so a K-loop prologue
+//    would cost ~4.5 VALU instructions per element per tile, about half of
+//    the MFMA time, against 2*T*C*2 bytes of HBM traffic for writing the
+//    modulated rows once and reading them back.
+//  * gemm_kernel<MODE>: out^T = W act^T with v_mfma_f32_32x32x16_bf16, both
+//    operands K-contiguous (weights [N][K] as stored, activations [T][K]), so
+//    every MFMA fragment is one 16-byte LDS read.  A workgroup computes 256
+//    features x 256 tokens with 8 wavefronts (2 per SIMD, 64 features x 128
+//    tokens each, 128 accumulator registers).  K advances in steps of 32
+//    through a ring of three LDS stages filled by direct global->LDS loads
+//    two steps ahead (no staging registers); LDS rows are 64 data bytes
+//    padded to 80, so the 16-byte fragment reads are conflict-free.
+//    Transposed output: each lane holds one token and 16 features, so the
+//    RoPE pairs (adjacent features) sit in one lane and each lane stores 4
+//    consecutive features (8 bytes) per register group.
+//  * Tiles are numbered so that the tiles one XCD runs are consecutive and
+//    share their weight tile (its L2 serves the re-reads).
+//  * Ragged edges: buffer resources end at the last token / feature, so rows
+//    past them read as zeros; the epilogue stores only rows inside.
+#include <cmath>
+
+#include "mf_device.h"
+#include "mf_internal.h"
+
+namespace mf {
+namespace {
+
+constexpr int kGW = 8;                     // wavefronts per workgroup
+constexpr int kGT = 64 * kGW;
+constexpr int kBF = 256;                   // features per tile
+constexpr int kBT = 256;                   // tokens per tile
+constexpr int kBK = 32;                    // K per step
+constexpr int kUnits = kBK / 8 + 1;        // 16-byte units per LDS row: 4 data + 1 pad
+constexpr int kRowB = 16 * kUnits;         // 80 bytes
+constexpr int kStageRows = kBF + kBT;
+constexpr int kStageB = kStageRows * kRowB;
+constexpr int kStages = 3;
+constexpr int kLdsB = kStages * kStageB;   // 120 KiB
+constexpr int kDma = kStageRows * kUnits / 64;   // direct-load instructions per stage
+constexpr int kDmaW = kBF * kUnits / 64;         // of which fill the weight rows
+constexpr int kDmaPerWave = kDma / kGW;
+constexpr int kXcds = 8;
+static_assert(kDma % kGW == 0 && kBF * kUnits % 64 == 0, "whole direct-load instructions");
+
+enum { kModeQkv = 0, kModeOut = 1 };
+
+struct GemmParams {
+    const uint16_t* w;       // [N][K]
+    const uint16_t* act;     // [T][K], token stride ld_act
+    int64_t ld_act;
+    int64_t T;
+    int N, K;
+    uint16_t* out;           // [T][N], token stride ld_out
+    int64_t ld_out;
+    // QKV: RoPE on the features below rope_limit (q and k)
+    int rope_limit, D, rope_f, rope_r;
+    const int32_t* pos;
+    // out projection: y = resid + gate[m] * acc
+    const uint16_t* resid;
+    const uint16_t* gate;
+    const int32_t* mod_row;
+    int tiles_t;
+    double theta_turns[64];
+};
+
+// Wait until at most N of this wavefront's direct global->LDS loads are in
+// flight (they complete in order); expcnt and lgkmcnt unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int nb = gridDim.x;
+    const int b = blockIdx.x;
+    // consecutive logical tiles on one XCD (blockIdx round-robins over XCDs)
+    const int lt = nb % kXcds == 0 ? (b % kXcds) * (nb / kXcds) + b / kXcds : b;
+    const int ft = lt / p.tiles_t, tt = lt - ft * p.tiles_t;
+    const int f0 = ft * kBF;
+    const int64_t t0 = int64_t(tt) * kBT;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hlf = lane >> 5;
+    const int wf = wave & 3;      // 64-feature quarter of the tile
+    const int wt = wave >> 2;     // 128-token half of the tile
+
+    const uint32_t kbytes = uint32_t(p.K) * 2u;
+    const uint32_t abytes = uint32_t(p.ld_act) * 2u;
+    const __amdgpu_buffer_rsrc_t w_rs =
+        make_rsrc(p.w + int64_t(f0) * p.K, uint64_t(p.N - f0) * kbytes);
+    const __amdgpu_buffer_rsrc_t a_rs =
+        make_rsrc(p.act + t0 * p.ld_act, uint64_t(p.T - t0) * abytes);
+
+    // Direct loads: instruction n of a stage fills units [64n, 64n+64) of the
+    // stage image, unit u = (row u / kUnits, column u % kUnits); rows below
+    // kBF are weight rows, the rest activation rows.  The pad column fetches
+    // a duplicate of the row's last chunk (never read).  Wavefront w issues
+    // instructions w, w + kGW, ...
+    uint32_t voff[kDmaPerWave];
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+        const int n = wave + kGW * j;
+        const int u = 64 * n + lane;
+        const int row = u / kUnits, col = u % kUnits;
+        const uint32_t c16 = 16u * uint32_t(col < kUnits - 1 ? col : kUnits - 2);
+        voff[j] = row < kBF ? uint32_t(row) * kbytes + c16 : uint32_t(row - kBF) * abytes + c16;
+    }
+    auto issue = [&](int s) {
+        unsigned char* base = smem + (s % kStages) * kStageB;
+        const uint32_t soff = uint32_t(s) * kBK * 2u;
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j) {
+            const int n = wave + kGW * j;
+            if (n < kDmaW)
+                dma16(w_rs, base + 1024 * n, voff[j], soff);
+            else
+                dma16(a_rs, base + 1024 * n, voff[j], soff);
+        }
+    };
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[fb][tb][r] = 0.f;
+
+    const int a_rd = (64 * wf + l32) * kRowB + 16 * hlf;
+    const int b_rd = (kBF + 128 * wt + l32) * kRowB + 16 * hlf;
+    const int nks = (p.K + kBK - 1) / kBK;
+    issue(0);
+    if (nks > 1) issue(1);
+    for (int s = 0; s < nks; ++s) {
+        if (s + 1 < nks)
+            wait_vm<kDmaPerWave>();
+        else
+            wait_vm<0>();
+        // stage s landed for every wavefront; stage (s+2)%3 was last read in
+        // step s-1, which every wavefront has finished
+        __syncthreads();
+        if (s + 2 < nks) issue(s + 2);
+        const unsigned char* st = smem + (s % kStages) * kStageB;
+        bf16x8_t af[2][2], bf[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb)
+                af[kk][fb] = *reinterpret_cast<const bf16x8_t*>(st + a_rd + 32 * fb * kRowB + 32 * kk);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                bf[kk][tb] = *reinterpret_cast<const bf16x8_t*>(st + b_rd + 32 * tb * kRowB + 32 * kk);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][fb], bf[kk][tb], acc[fb][tb], 0, 0, 0);
+    }
+
+    // ---- epilogue: lane = token, register r of block fb = feature
+    //      8(r/4) + 4h + r%4 of the block
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const int64_t t = t0 + 128 * wt + 32 * tb + l32;
+        if (t >= p.T) continue;
+        int64_t m = 0;
+        if constexpr (MODE == kModeOut) m = p.mod_row[t];
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) {
+            const int nblk = f0 + 64 * wf + 32 * fb;   // first feature of the block
+            if (nblk >= p.N) continue;
+            f32x16_t& a = acc[fb][tb];
+            if constexpr (MODE == kModeQkv) {
+                if (nblk < p.rope_limit) {
+                    // q or k: turn each adjacent pair (r, r+1) by pos_axis *
+                    // theta; the angle is formed in fp64 in turns and reduced
+                    // to [-1/2, 1/2] before the hardware sine and cosine
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        const int e = (nblk + 8 * (r >> 2) + 4 * hlf + (r & 3)) % p.D;
+                        const int axis = e < p.rope_f ? 0 : (e < p.rope_f + p.rope_r ? 1 : 2);
+                        const double turns = double(p.pos[3 * t + axis]) * p.theta_turns[e >> 1];
+                        const float f = float(turns - rint(turns));
+                        const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+                        const float x0 = a[r], x1 = a[r + 1];
+                        a[r] = x0 * cs - x1 * sn;
+                        a[r + 1] = x0 * sn + x1 * cs;
+                    }
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n0 = nblk + 8 * g + 4 * hlf;
+                uint16_t* op = p.out + t * p.ld_out + n0;
+                float v0 = a[4 * g], v1 = a[4 * g + 1], v2 = a[4 * g + 2], v3 = a[4 * g + 3];
+                if constexpr (MODE == kModeOut) {
+                    const u32x2_t xr = *reinterpret_cast<const u32x2_t*>(p.resid + t * int64_t(p.N) + n0);
+                    const u32x2_t gr = *reinterpret_cast<const u32x2_t*>(p.gate + m * int64_t(p.N) + n0);
+                    v0 = bf_lo(xr[0]) + bf_lo(gr[0]) * v0;
+                    v1 = bf_hi(xr[0]) + bf_hi(gr[0]) * v1;
+                    v2 = bf_lo(xr[1]) + bf_lo(gr[1]) * v2;
+                    v3 = bf_hi(xr[1]) + bf_hi(gr[1]) * v3;
+                }
+                u32x2_t val;
+                val[0] = pack_bf16x2(v0, v1);
+                val[1] = pack_bf16x2(v2, v3);
+                *reinterpret_cast<u32x2_t*>(op) = val;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// adaLN of the residual stream: u = LN(x) * (1 + scale[m]) + shift[m], bf16
+// ---------------------------------------------------------------------------
+constexpr int kLnTokensPerBlock = 4;
+
+template <int NCH>
+__global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
+                                                    const uint16_t* __restrict__ shift,
+                                                    const uint16_t* __restrict__ scale,
+                                                    const int32_t* __restrict__ mod_row,
+                                                    uint16_t* __restrict__ u, int64_t T, int C, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = int64_t(blockIdx.x) * kLnTokensPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (t >= T) return;
+    const int nch = C >> 3;
+    const uint32_t row_bytes = uint32_t(C) * 2u;
+    const __amdgpu_buffer_rsrc_t x_rs = make_rsrc(x + t * ld_x, row_bytes);
+    u32x4_t px[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) px[i] = bload16(x_rs, 16u * uint32_t(lane + kWave * i), 0);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) s += bf_lo(px[i][w]) + bf_hi(px[i][w]);
+    const float invC = 1.0f / float(C);
+    const float mean = wave_sum(s) * invC;
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const bool in = lane + kWave * i < nch;   // zero-filled chunks are not row data
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float a0 = bf_lo(px[i][w]) - mean, a1 = bf_hi(px[i][w]) - mean;
+            v += in ? a0 * a0 + a1 * a1 : 0.f;
+        }
+    }
+    const float rstd = rsqrtf(wave_sum(v) * invC + eps);
+    const int64_t m = __builtin_amdgcn_readfirstlane(mod_row[t]);
+    const __amdgpu_buffer_rsrc_t sh_rs = make_rsrc(shift + m * C, row_bytes);
+    const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(scale + m * C, row_bytes);
+    const __amdgpu_buffer_rsrc_t u_rs = make_rsrc(u + t * C, row_bytes);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const uint32_t off = 16u * uint32_t(lane + kWave * i);
+        float fx[8], fs[8], fc[8], r[8];
+        unpack8(px[i], fx);
+        unpack8(bload16(sh_rs, off, 0), fs);
+        unpack8(bload16(sc_rs, off, 0), fc);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = (fx[j] - mean) * rstd * (1.0f + fc[j]) + fs[j];
+        bstore16(u_rs, off, 0, pack8(r));
+    }
+}
+
+template <int NCH>
+hipError_t launch_adaln_nch(const BlockQkvArgs& a, uint16_t* u, hipStream_t stream) {
+    const int64_t blocks = (a.T + kLnTokensPerBlock - 1) / kLnTokensPerBlock;
+    hipLaunchKernelGGL(adaln_kernel<NCH>, dim3(unsigned(blocks)), dim3(256), 0, stream, a.x, a.ld_x, a.shift,
+                       a.scale, a.mod_row, u, a.T, a.H * a.D, a.eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_adaln(const BlockQkvArgs& a, uint16_t* u, hipStream_t stream) {
+    const int per_lane = (a.H * a.D / 8 + kWave - 1) / kWave;
+    if (per_lane <= 1) return launch_adaln_nch<1>(a, u, stream);
+    if (per_lane <= 2) return launch_adaln_nch<2>(a, u, stream);
+    if (per_lane <= 4) return launch_adaln_nch<4>(a, u, stream);
+    if (per_lane <= 6) return launch_adaln_nch<6>(a, u, stream);
+    if (per_lane <= 8) return launch_adaln_nch<8>(a, u, stream);
+    if (per_lane <= 12) return launch_adaln_nch<12>(a, u, stream);
+    return launch_adaln_nch<16>(a, u, stream);
+}
+
+template <int MODE>
+hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsB);
+    if (attr != hipSuccess) return attr;
+    const int tiles_f = (p.N + kBF - 1) / kBF;
+    p.tiles_t = int((p.T + kBT - 1) / kBT);
+    hipLaunchKernelGGL(gemm_kernel<MODE>, dim3(unsigned(tiles_f * p.tiles_t)), dim3(kGT), kLdsB, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t block_qkv_workspace_bytes(int64_t T, int32_t C) {
+    return size_t(T < 0 ? 0 : T) * size_t(C < 0 ? 0 : C) * 2;
+}
+
+hipError_t launch_block_qkv(const BlockQkvArgs& args, hipStream_t stream) {
+    if (args.T == 0) return hipSuccess;
+    const int C = args.H * args.D;
+    const uint16_t* act = args.x;
+    int64_t ld_act = args.ld_x;
+    if (args.shift != nullptr) {
+        uint16_t* u = static_cast<uint16_t*>(args.workspace);
+        const hipError_t e = launch_adaln(args, u, stream);
+        if (e != hipSuccess) return e;
+        act = u;
+        ld_act = C;
+    }
+    GemmParams p = {};
+    p.w = args.w;
+    p.act = act;
+    p.ld_act = ld_act;
+    p.T = args.T;
+    p.N = 3 * C;
+    p.K = C;
+    p.out = args.qkv;
+    p.ld_out = args.ld_qkv;
+    p.rope_limit = 2 * C;
+    p.D = args.D;
+    p.rope_f = args.rope_f;
+    p.rope_r = args.rope_r;
+    p.pos = args.pos;
+    const int dims[3] = {args.rope_f, args.rope_r, args.rope_c};
+    int pair = 0;
+    for (int ax = 0; ax < 3; ++ax)
+        for (int j = 0; j < dims[ax] / 2; ++j)
+            p.theta_turns[pair++] = std::pow(double(args.rope_base), -2.0 * j / double(dims[ax])) *
+                                    0.15915494309189535;   // radians -> turns (1 / 2 pi)
+    return launch_gemm<kModeQkv>(p, stream);
+}
+
+hipError_t launch_block_out(const BlockOutArgs& a, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    GemmParams p = {};
+    p.w = a.w;
+    p.act = a.o;
+    p.ld_act = a.ld_o;
+    p.T = a.T;
+    p.N = a.C;
+    p.K = a.C;
+    p.out = a.y;
+    p.ld_out = a.C;
+    p.resid = a.x;
+    p.gate = a.gate;
+    p.mod_row = a.mod_row;
+    return launch_gemm<kModeOut>(p, stream);
+}
+
+}  // namespace mf

@@ -137,4 +137,40 @@ struct AttnBwdArgs {
 size_t attn_bwd_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D);
 hipError_t launch_varlen_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
 
+// Block projections around the attention: the QKV projection of the
+// adaLN-modulated residual stream with RoPE on q and k, and the out
+// projection with the gated residual.
+struct BlockQkvArgs {
+    const uint16_t* x;        // [T][C], token stride ld_x
+    int64_t ld_x;
+    const uint16_t* w;        // [3C][C]
+    uint16_t* qkv;            // [T][3C], token stride ld_qkv
+    int64_t ld_qkv;
+    const uint16_t* shift;    // nullptr: no modulation
+    const uint16_t* scale;
+    const int32_t* mod_row;
+    const int32_t* pos;
+    int64_t T;
+    int32_t H, D;
+    int32_t rope_f, rope_r, rope_c;
+    float rope_base, eps;
+    void* workspace;          // the modulated rows, bf16 [T][C]
+    double theta_turns[64];   // filled by the launcher, as for the forward
+};
+size_t block_qkv_workspace_bytes(int64_t T, int32_t C);
+hipError_t launch_block_qkv(const BlockQkvArgs& a, hipStream_t stream);
+
+struct BlockOutArgs {
+    const uint16_t* o;        // [T][C], token stride ld_o
+    int64_t ld_o;
+    const uint16_t* w;        // [C][C]
+    const uint16_t* x;        // [T][C] residual
+    const uint16_t* gate;     // [n_rows][C]
+    const int32_t* mod_row;
+    uint16_t* y;              // [T][C]
+    int64_t T;
+    int32_t C;
+};
+hipError_t launch_block_out(const BlockOutArgs& a, hipStream_t stream);
+
 }  // namespace mf

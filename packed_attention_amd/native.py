@@ -26,7 +26,8 @@ EXPORTS = ("mf_status_string", "mf_abi_version", "mf_pack_count", "mf_pack_table
            "mf_modulate_rope", "mf_varlen_attn_workspace_bytes", "mf_varlen_attn_fwd",
            "mf_gated_residual", "mf_varlen_attn_bwd_workspace_bytes", "mf_varlen_attn_bwd",
            "mf_modulate_rope_bwd", "mf_gated_residual_bwd", "mf_modulate_rope_bwd_workspace_bytes",
-           "mf_gated_residual_bwd_workspace_bytes")
+           "mf_gated_residual_bwd_workspace_bytes", "mf_block_qkv_workspace_bytes", "mf_block_qkv",
+           "mf_block_out")
 
 
 class MFError(RuntimeError):
@@ -88,6 +89,13 @@ def lib() -> ctypes.CDLL:
     L.mf_gated_residual_bwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i64,
                                         i32, f32, vp, sz]
     L.mf_gated_residual_bwd.restype = i32
+    L.mf_block_qkv_workspace_bytes.argtypes = [i64, i32, i32]
+    L.mf_block_qkv_workspace_bytes.restype = sz
+    L.mf_block_qkv.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
+                               f32, f32, vp, sz]
+    L.mf_block_qkv.restype = i32
+    L.mf_block_out.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, i32]
+    L.mf_block_out.restype = i32
     _lib = L
     return L
 
@@ -323,3 +331,44 @@ def gated_residual_bwd(x, o, gate, mod_row, dy, dx, dout, dgate, scale2=None, dz
                                       n_rows, _ptr(dy), _ptr(scale2), _ptr(dz), _ptr(dx), _ptr(dout),
                                       _ptr(dgate), _ptr(dshift2), _ptr(dscale2), T, C, float(eps),
                                       _ptr(workspace), workspace.numel()))
+
+
+def block_qkv_workspace_bytes(T: int, H: int, D: int) -> int:
+    return int(lib().mf_block_qkv_workspace_bytes(T, H, D))
+
+
+def block_qkv(x, w_qkv, qkv, pos, H, rope_dims, rope_base=10000.0, shift=None, scale=None, mod_row=None,
+              eps=1e-6, workspace=None, stream=None):
+    """mf_block_qkv: qkv [T][3C] bf16 (q', k', v) from the residual stream x [T][C] bf16 and
+    W_qkv [3C][C] bf16 (modulated by shift/scale rows when given)."""
+    import torch
+    T, C = x.shape
+    D = C // H
+    _check_bf16_rows("x", x, C)
+    _check_bf16_rows("qkv", qkv, 3 * C)
+    _check_bf16_rows("w_qkv", w_qkv, C)
+    if tuple(w_qkv.shape) != (3 * C, C) or not w_qkv.is_contiguous():
+        raise ValueError("w_qkv: expected a contiguous [3C][C] tensor")
+    if qkv.dim() != 2 or qkv.shape[0] != T or qkv.shape[1] != 3 * C:
+        raise ValueError("qkv: expected [T][3C]")
+    if workspace is None and shift is not None:
+        workspace = torch.empty(block_qkv_workspace_bytes(T, H, D), dtype=torch.uint8, device=x.device)
+    f, r, c = (int(v) for v in rope_dims)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().mf_block_qkv(_stream(stream), _ptr(x), _token_stride(x, C), _ptr(w_qkv), _ptr(qkv),
+                             _token_stride(qkv, 3 * C), _ptr(shift), _ptr(scale), _ptr(mod_row), _ptr(pos),
+                             T, H, D, f, r, c, float(rope_base), float(eps), _ptr(workspace), nbytes))
+
+
+def block_out(o, w_o, x, gate, mod_row, y, stream=None):
+    """mf_block_out: y = x + gate[m] * (o W_o^T) on [T][C] bf16 rows (o may be [T][H][D])."""
+    T, C = x.shape
+    _check_bf16_rows("o", o, C)
+    for n, t in (("x", x), ("y", y), ("w_o", w_o)):
+        _check_bf16_rows(n, t, C)
+        if not t.is_contiguous():
+            raise ValueError(f"{n}: expected a contiguous tensor")
+    if tuple(w_o.shape) != (C, C):
+        raise ValueError("w_o: expected [C][C]")
+    check(lib().mf_block_out(_stream(stream), _ptr(o), _token_stride(o, C), _ptr(w_o), _ptr(x), _ptr(gate),
+                             _ptr(mod_row), _ptr(y), T, C))

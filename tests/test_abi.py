@@ -210,6 +210,48 @@ def test_gated_residual_validation():
     assert gres(T=0, x=None, o=None, y=None, gate=None, mod_row=None) == 0
 
 
+def bqkv(**kw):
+    a = dict(stream=None, x=P, ld_x=128, w=P, qkv=P, ld_qkv=384, shift=None, scale=None, mod_row=None,
+             pos=P, T=4, H=2, D=64, f=0, r=32, c=32, base=10000.0, eps=1e-6, ws=None, ws_bytes=0)
+    a.update(kw)
+    return native.lib().mf_block_qkv(*a.values())
+
+
+def bout(**kw):
+    a = dict(stream=None, o=P, ld_o=256, w=P, x=P, gate=P, mod_row=P, y=P, T=4, C=256)
+    a.update(kw)
+    return native.lib().mf_block_out(*a.values())
+
+
+def test_block_projection_validation():
+    assert bqkv(D=96) == UNSUP
+    assert bqkv(H=72, D=128, ld_x=9216, ld_qkv=27648) == UNSUP          # C > 8192
+    assert bqkv(r=20, c=44) == SHAPE
+    assert bqkv(ld_x=64) == SHAPE
+    assert bqkv(ld_qkv=256) == SHAPE
+    assert bqkv(shift=P) == NULL
+    assert bqkv(shift=P, scale=P, mod_row=P, eps=0.0) == SHAPE
+    assert bqkv(x=None) == NULL
+    assert bqkv(pos=None) == NULL
+    assert bqkv(shift=P, scale=P, mod_row=None) == NULL
+    assert bqkv(ld_x=132) == ALIGN
+    assert bqkv(w=PODD) == ALIGN
+    assert bqkv(shift=P, scale=P, mod_row=P) == WS
+    assert bqkv(shift=P, scale=P, mod_row=P, ws=P, ws_bytes=16) == WS
+    assert bqkv(shift=P, scale=P, mod_row=P, ws=PODD, ws_bytes=1 << 20) == ALIGN
+    assert bqkv(T=1 << 20, ld_x=4096) == UNSUP                           # 32-bit offsets
+    assert bqkv(T=0, x=None, w=None, qkv=None, pos=None) == 0
+    assert bout(C=100) == SHAPE
+    assert bout(ld_o=128) == SHAPE
+    assert bout(ld_o=260) == ALIGN
+    assert bout(o=None) == NULL
+    assert bout(gate=None) == NULL
+    assert bout(y=PODD) == ALIGN
+    assert bout(T=1 << 22, C=1024, ld_o=1024) == UNSUP
+    assert bout(T=0, o=None, w=None, x=None, gate=None, mod_row=None, y=None) == 0
+    assert native.lib().mf_block_qkv_workspace_bytes(4352, 24, 128) == 4352 * 3072 * 2
+
+
 def test_library_has_no_oracle_dependency():
     """The product path never touches the oracle: no module of the package
     imports it, and the native sources do not mention it."""
