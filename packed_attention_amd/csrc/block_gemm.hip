@@ -26,10 +26,11 @@
 //    operands K-contiguous (weights [N][K] as stored, activations [T][K]), so
 //    every MFMA fragment is one 16-byte LDS read.  A workgroup computes 256
 //    features x 256 tokens with 8 wavefronts (2 per SIMD, 64 features x 128
-//    tokens each, 128 accumulator registers).  K advances in steps of 32
-//    through a ring of three LDS stages filled by direct global->LDS loads
-//    two steps ahead (no staging registers); LDS rows are 64 data bytes
-//    padded to 80, so the 16-byte fragment reads are conflict-free.
+//    tokens each, 128 accumulator registers).  K advances in steps of 64
+//    through two LDS stages filled by direct global->LDS loads one step
+//    ahead (no staging registers); LDS rows are 128 bytes with their 16-byte
+//    chunks swizzled, so the fragment reads are conflict-free without
+//    padding.
 //    Transposed output: each lane holds one token and 16 features, so the
 //    RoPE pairs (adjacent features) sit in one lane and each lane stores 4
 //    consecutive features (8 bytes) per register group.
@@ -49,18 +50,30 @@ constexpr int kGW = 8;                     // wavefronts per workgroup
 constexpr int kGT = 64 * kGW;
 constexpr int kBF = 256;                   // features per tile
 constexpr int kBT = 256;                   // tokens per tile
-constexpr int kBK = 32;                    // K per step
-constexpr int kUnits = kBK / 8 + 1;        // 16-byte units per LDS row: 4 data + 1 pad
-constexpr int kRowB = 16 * kUnits;         // 80 bytes
+constexpr int kBK = 64;                    // K per step
+constexpr int kChunks = kBK / 8;           // 16-byte chunks per LDS row (128 bytes, no padding)
+constexpr int kRowB = 16 * kChunks;
 constexpr int kStageRows = kBF + kBT;
 constexpr int kStageB = kStageRows * kRowB;
-constexpr int kStages = 3;
-constexpr int kLdsB = kStages * kStageB;   // 120 KiB
-constexpr int kDma = kStageRows * kUnits / 64;   // direct-load instructions per stage
-constexpr int kDmaW = kBF * kUnits / 64;         // of which fill the weight rows
+constexpr int kStages = 2;
+constexpr int kLdsB = kStages * kStageB;   // 128 KiB
+static_assert(kStages >= 2 && kStages <= 4, "waits below cover up to two later groups");
+constexpr int kRowsPerDma = 64 / kChunks;  // LDS rows one direct-load instruction fills
+constexpr int kDma = kStageRows / kRowsPerDma;   // direct-load instructions per stage
+constexpr int kDmaW = kBF / kRowsPerDma;         // of which fill the weight rows
 constexpr int kDmaPerWave = kDma / kGW;
 constexpr int kXcds = 8;
-static_assert(kDma % kGW == 0 && kBF * kUnits % 64 == 0, "whole direct-load instructions");
+constexpr int kGroupF = 4;                 // feature tiles per group of the tile order
+static_assert(kDma % kGW == 0, "whole direct-load instructions");
+// The epilogue stages the bf16 output tile [kBT tokens][kBF features]
+// through the (then free) LDS stages.
+static_assert(kBT * kBF * 2 <= kLdsB, "output tile fits the LDS stages");
+
+// LDS rows are stored swizzled: chunk c of row r sits in slot c ^ sw(r),
+// sw(r) = (r / 2) % 8.  The 16 lanes one LDS cycle serves read 16-byte
+// chunks of 16 consecutive rows (two per 256-byte bank line), and the swizzle
+// gives each of them its own 4 banks without padding.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 enum { kModeQkv = 0, kModeOut = 1 };
 
@@ -79,7 +92,7 @@ struct GemmParams {
     const uint16_t* resid;
     const uint16_t* gate;
     const int32_t* mod_row;
-    int tiles_t;
+    int tiles_t, tiles_f;
     double theta_turns[64];
 };
 
@@ -98,7 +111,13 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
     const int b = blockIdx.x;
     // consecutive logical tiles on one XCD (blockIdx round-robins over XCDs)
     const int lt = nb % kXcds == 0 ? (b % kXcds) * (nb / kXcds) + b / kXcds : b;
-    const int ft = lt / p.tiles_t, tt = lt - ft * p.tiles_t;
+    // groups of kGroupF feature tiles: consecutive tiles walk the group's
+    // feature tiles for one token tile, then the next token tile, so the
+    // tiles running together on an XCD share both operands' K slabs
+    const int gsz = kGroupF * p.tiles_t;
+    const int grp = lt / gsz, rem = lt - grp * gsz;
+    const int gf = min(kGroupF, p.tiles_f - grp * kGroupF);
+    const int ft = grp * kGroupF + rem % gf, tt = rem / gf;
     const int f0 = ft * kBF;
     const int64_t t0 = int64_t(tt) * kBT;
 
@@ -117,18 +136,18 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
     const __amdgpu_buffer_rsrc_t a_rs =
         make_rsrc(p.act + t0 * p.ld_act, uint64_t(p.T - t0) * abytes);
 
-    // Direct loads: instruction n of a stage fills units [64n, 64n+64) of the
-    // stage image, unit u = (row u / kUnits, column u % kUnits); rows below
-    // kBF are weight rows, the rest activation rows.  The pad column fetches
-    // a duplicate of the row's last chunk (never read).  Wavefront w issues
-    // instructions w, w + kGW, ...
+    // Direct loads: instruction n of a stage fills LDS rows
+    // [kRowsPerDma n, kRowsPerDma (n+1)); lane i lands in row
+    // kRowsPerDma n + i / kChunks, slot i % kChunks, and so fetches the
+    // global chunk (slot ^ sw(row)) of that row.  Rows below kBF are weight
+    // rows, the rest activation rows.  Wavefront w issues instructions
+    // w, w + kGW, ...
     uint32_t voff[kDmaPerWave];
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
         const int n = wave + kGW * j;
-        const int u = 64 * n + lane;
-        const int row = u / kUnits, col = u % kUnits;
-        const uint32_t c16 = 16u * uint32_t(col < kUnits - 1 ? col : kUnits - 2);
+        const int row = kRowsPerDma * n + lane / kChunks;
+        const uint32_t c16 = 16u * uint32_t((lane % kChunks) ^ swz(row));
         voff[j] = row < kBF ? uint32_t(row) * kbytes + c16 : uint32_t(row - kBF) * abytes + c16;
     }
     auto issue = [&](int s) {
@@ -152,55 +171,81 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fb][tb][r] = 0.f;
 
-    const int a_rd = (64 * wf + l32) * kRowB + 16 * hlf;
-    const int b_rd = (kBF + 128 * wt + l32) * kRowB + 16 * hlf;
-    const int nks = (p.K + kBK - 1) / kBK;
-    issue(0);
-    if (nks > 1) issue(1);
-    for (int s = 0; s < nks; ++s) {
-        if (s + 1 < nks)
-            wait_vm<kDmaPerWave>();
-        else
-            wait_vm<0>();
-        // stage s landed for every wavefront; stage (s+2)%3 was last read in
-        // step s-1, which every wavefront has finished
-        __syncthreads();
-        if (s + 2 < nks) issue(s + 2);
-        const unsigned char* st = smem + (s % kStages) * kStageB;
-        bf16x8_t af[2][2], bf[2][4];
+    // Fragment rows: weight rows 64 wf + 32 fb + l32, activation rows
+    // kBF + 128 wt + 32 tb + l32; their swizzle is sw(l32) for all of them
+    // (the row offsets are multiples of 16).  K sub-step kk reads chunk
+    // 2 kk + h.
+    const int sw = swz(l32);
+    const int a_rd = (64 * wf + l32) * kRowB;
+    const int b_rd = (kBF + 128 * wt + l32) * kRowB;
+    int cofs[kBK / 16];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kBK / 16; ++kk) cofs[kk] = 16 * ((2 * kk + hlf) ^ sw);
+    const int nks = (p.K + kBK - 1) / kBK;
+    constexpr int kAhead = kStages - 1;        // steps loaded ahead
+    for (int s = 0; s < kAhead; ++s)
+        if (s < nks) issue(s);
+    for (int s = 0; s < nks; ++s) {
+        // this wavefront's loads of stage s have landed once at most the
+        // later groups (up to kAhead - 1 of them) are still in flight
+        const int later = min(kAhead - 1, nks - 1 - s);
+        if constexpr (kAhead >= 3) {
+            if (later >= 2) wait_vm<2 * kDmaPerWave>();
+        }
+        if constexpr (kAhead >= 2) {
+            if (later == 1) wait_vm<kDmaPerWave>();
+        }
+        if (later == 0) wait_vm<0>();
+        // stage s landed for every wavefront; the stage refilled next was
+        // last read in step s-1, which every wavefront has finished
+        __syncthreads();
+        if (s + kAhead < nks) issue(s + kAhead);
+        const unsigned char* st = smem + (s % kStages) * kStageB;
+        // K sub-steps: the six fragments of sub-step kk+1 are read while
+        // the eight MFMAs of sub-step kk run
+        bf16x8_t af[2][2], bf[2][4];
+        auto rd = [&](int buf, int kk) {
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb)
-                af[kk][fb] = *reinterpret_cast<const bf16x8_t*>(st + a_rd + 32 * fb * kRowB + 32 * kk);
+                af[buf][fb] = *reinterpret_cast<const bf16x8_t*>(st + a_rd + 32 * fb * kRowB + cofs[kk]);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
-                bf[kk][tb] = *reinterpret_cast<const bf16x8_t*>(st + b_rd + 32 * tb * kRowB + 32 * kk);
-        }
+                bf[buf][tb] = *reinterpret_cast<const bf16x8_t*>(st + b_rd + 32 * tb * kRowB + cofs[kk]);
+        };
+        rd(0, 0);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            if (kk + 1 < kBK / 16) rd((kk + 1) & 1, kk + 1);
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
-                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][fb], bf[kk][tb], acc[fb][tb], 0, 0, 0);
+                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][fb], bf[kk & 1][tb],
+                                                                          acc[fb][tb], 0, 0, 0);
+        }
     }
 
     // ---- epilogue: lane = token, register r of block fb = feature
-    //      8(r/4) + 4h + r%4 of the block
+    //      8(r/4) + 4h + r%4 of the block.  The finished bf16 values go to an
+    //      LDS image of the output tile (rows = tokens, 512 bytes; 16-byte
+    //      chunk c of row t in slot c ^ (t % 32), so the 8-byte writes of 32
+    //      consecutive rows and the 16-byte reads along a row are both
+    //      conflict-free), then out to global memory one 512-byte row segment
+    //      per 32 lanes.
+    __syncthreads();                       // every wavefront is done with the stages
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-        const int64_t t = t0 + 128 * wt + 32 * tb + l32;
-        if (t >= p.T) continue;
+        const int tl = 128 * wt + 32 * tb + l32;   // token row inside the tile
+        const int64_t t = t0 + tl;
         int64_t m = 0;
-        if constexpr (MODE == kModeOut) m = p.mod_row[t];
+        if constexpr (MODE == kModeOut) m = t < p.T ? p.mod_row[t] : 0;
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) {
-            const int nblk = f0 + 64 * wf + 32 * fb;   // first feature of the block
-            if (nblk >= p.N) continue;
+            const int fl = 64 * wf + 32 * fb;      // first feature of the block inside the tile
+            const int nblk = f0 + fl;
             f32x16_t& a = acc[fb][tb];
             if constexpr (MODE == kModeQkv) {
-                if (nblk < p.rope_limit) {
+                if (nblk < p.rope_limit && t < p.T) {
                     // q or k: turn each adjacent pair (r, r+1) by pos_axis *
                     // theta; the angle is formed in fp64 in turns and reduced
                     // to [-1/2, 1/2] before the hardware sine and cosine
@@ -219,23 +264,36 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
             }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n0 = nblk + 8 * g + 4 * hlf;
-                uint16_t* op = p.out + t * p.ld_out + n0;
+                const int f = fl + 8 * g + 4 * hlf;        // feature inside the tile
                 float v0 = a[4 * g], v1 = a[4 * g + 1], v2 = a[4 * g + 2], v3 = a[4 * g + 3];
                 if constexpr (MODE == kModeOut) {
-                    const u32x2_t xr = *reinterpret_cast<const u32x2_t*>(p.resid + t * int64_t(p.N) + n0);
-                    const u32x2_t gr = *reinterpret_cast<const u32x2_t*>(p.gate + m * int64_t(p.N) + n0);
-                    v0 = bf_lo(xr[0]) + bf_lo(gr[0]) * v0;
-                    v1 = bf_hi(xr[0]) + bf_hi(gr[0]) * v1;
-                    v2 = bf_lo(xr[1]) + bf_lo(gr[1]) * v2;
-                    v3 = bf_hi(xr[1]) + bf_hi(gr[1]) * v3;
+                    if (t < p.T && f0 + f < p.N) {
+                        const int64_t n0 = f0 + f;
+                        const u32x2_t xr = *reinterpret_cast<const u32x2_t*>(p.resid + t * int64_t(p.N) + n0);
+                        const u32x2_t gr = *reinterpret_cast<const u32x2_t*>(p.gate + m * int64_t(p.N) + n0);
+                        v0 = bf_lo(xr[0]) + bf_lo(gr[0]) * v0;
+                        v1 = bf_hi(xr[0]) + bf_hi(gr[0]) * v1;
+                        v2 = bf_lo(xr[1]) + bf_lo(gr[1]) * v2;
+                        v3 = bf_hi(xr[1]) + bf_hi(gr[1]) * v3;
+                    }
                 }
                 u32x2_t val;
                 val[0] = pack_bf16x2(v0, v1);
                 val[1] = pack_bf16x2(v2, v3);
-                *reinterpret_cast<u32x2_t*>(op) = val;
+                const int slot = (f >> 3) ^ (tl & 31);
+                *reinterpret_cast<u32x2_t*>(smem + tl * 512 + 16 * slot + 8 * ((f >> 2) & 1)) = val;
             }
         }
+    }
+    __syncthreads();
+    // rows 2 (i kGW + wave) + h, chunk l32: 32 lanes per 512-byte row segment
+#pragma unroll 4
+    for (int i = 0; i < kBT / (2 * kGW); ++i) {
+        const int tl = 2 * (i * kGW + wave) + hlf;
+        const int64_t t = t0 + tl;
+        const int n = f0 + 8 * l32;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + tl * 512 + 16 * (l32 ^ (tl & 31)));
+        if (t < p.T && n < p.N) st16(p.out + t * p.ld_out + n, v);
     }
 }
 
@@ -318,9 +376,9 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsB);
     if (attr != hipSuccess) return attr;
-    const int tiles_f = (p.N + kBF - 1) / kBF;
+    p.tiles_f = (p.N + kBF - 1) / kBF;
     p.tiles_t = int((p.T + kBT - 1) / kBT);
-    hipLaunchKernelGGL(gemm_kernel<MODE>, dim3(unsigned(tiles_f * p.tiles_t)), dim3(kGT), kLdsB, stream, p);
+    hipLaunchKernelGGL(gemm_kernel<MODE>, dim3(unsigned(p.tiles_f * p.tiles_t)), dim3(kGT), kLdsB, stream, p);
     return hipGetLastError();
 }
 
