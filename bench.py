@@ -24,6 +24,12 @@ Prints one JSON line:
               durations; attention at 2.5x the forward's flops (five
               products), the elementwise kernels in GB/s of their
               algorithmic bytes;
+  block       the block projections around the attention: the QKV projection
+              of the adaLN-modulated residual stream with RoPE on q and k
+              (mf_block_qkv, modulation pass included) and the out projection
+              with the gated residual (mf_block_out), per-call HIP-event
+              durations against the bf16 MFMA peak at 2*T*N*K flops, with
+              seeded random-init weights;
   cpu_baseline the fp64 oracle's whole step over the same workload, repeated
               for about 10 s, timed on the host cores.
 """
@@ -213,6 +219,26 @@ def main():
     bkern_ms = {n: sum(bevs[i][j].elapsed_time(bevs[i][j + 1]) for i in range(args.steps)) / args.steps
                 for j, n in enumerate(bnames)}
 
+    # Block projections around the attention (QKV with adaLN-modulate and
+    # RoPE, out projection with the gated residual), per-call HIP events.
+    bsets = [runner.block_to_device(b) for b in sets]
+    knames = ("block_qkv", "block_out")
+    kfns = (runner.run_block_qkv, runner.run_block_out)
+    for i in range(args.warmup):
+        for fn in kfns:
+            fn(sets[i % len(sets)], bsets[i % len(sets)])
+    kevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        b, bb = sets[i % len(sets)], bsets[i % len(sets)]
+        kevs[i][0].record(stream)
+        for j, fn in enumerate(kfns):
+            fn(b, bb)
+            kevs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    blk_ms = {n: sum(kevs[i][j].elapsed_time(kevs[i][j + 1]) for i in range(args.steps)) / args.steps
+              for j, n in enumerate(knames)}
+
     if args.copy_calib_mb:
         n = args.copy_calib_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -251,6 +277,14 @@ def main():
     backward["kernels"]["varlen_attn_bwd"]["TFLOP/s"] = round(bt, 2)
     backward["kernels"]["varlen_attn_bwd"]["frac_bf16_peak"] = round(bt / PEAK_BF16_TFLOPS, 4)
 
+    C = w.H * w.D
+    bflop = {"block_qkv": 2.0 * w.T * 3 * C * C, "block_out": 2.0 * w.T * C * C}
+    block = {"kernels": {}}
+    for n in knames:
+        tf = bflop[n] / (blk_ms[n] * 1e-3) / 1e12
+        block["kernels"][n] = {"ms": round(blk_ms[n], 5), "gemm_flops": bflop[n], "TFLOP/s": round(tf, 2),
+                               "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
     traffic = measured_traffic() if args.workload == "single_1024" else None
     out = {
         "metric": METRIC,
@@ -277,6 +311,7 @@ def main():
                      "flops_per_launch": flops, "launch_ms": round(kern_ms["varlen_attn_fwd"], 5)},
         "kernels": kernels,
         "backward": backward,
+        "block": block,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

@@ -12,7 +12,7 @@ from typing import Optional
 
 import numpy as np
 
-from . import native
+from . import native, workloads
 from .workloads import Workload
 
 
@@ -195,3 +195,43 @@ def run_backward_chain(b: DeviceBatch, gb: GradBatch, stream=None):
     run_gated_residual_bwd(b, gb, stream)
     run_attention_bwd(b, gb, stream)
     run_modulate_rope_bwd(b, gb, stream)
+
+
+# ---------------------------------------------------------------------------
+# Block projections around the attention
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class BlockBatch:
+    x: object          # residual stream [T][C]
+    w_qkv: object      # [3C][C]
+    w_o: object        # [C][C]
+    gate: object       # [n_rows][C]
+    qkv: object        # [T][3C] output
+    y: object          # [T][C] output
+    workspace: object
+
+
+def block_to_device(b: DeviceBatch, device="cuda") -> BlockBatch:
+    """Seeded residual stream and random-init projection weights for b's workload."""
+    import torch
+    w = b.w
+    T, C = w.T, w.H * w.D
+    bi = workloads.block_inputs(w)
+    gate = b.gate if b.gate is not None else torch.zeros((len(w.descs), C), dtype=torch.bfloat16, device=device)
+    return BlockBatch(x=bf16_tensor(bi["x"], device), w_qkv=bf16_tensor(bi["w_qkv"], device),
+                      w_o=bf16_tensor(bi["w_o"], device), gate=gate,
+                      qkv=torch.empty((T, 3 * C), dtype=torch.bfloat16, device=device),
+                      y=torch.empty((T, C), dtype=torch.bfloat16, device=device),
+                      workspace=torch.empty(native.block_qkv_workspace_bytes(T, w.H, w.D), dtype=torch.uint8,
+                                            device=device))
+
+
+def run_block_qkv(b: DeviceBatch, bb: BlockBatch, stream=None):
+    w = b.w
+    native.block_qkv(bb.x, bb.w_qkv, bb.qkv, b.pos, w.H, w.rope_dims, w.rope_base, b.shift, b.scale,
+                     b.mod_row if b.shift is not None else None, w.eps, workspace=bb.workspace, stream=stream)
+
+
+def run_block_out(b: DeviceBatch, bb: BlockBatch, stream=None):
+    native.block_out(b.o.view(b.w.T, -1), bb.w_o, bb.x, bb.gate, b.mod_row, bb.y, stream=stream)
