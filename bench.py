@@ -30,6 +30,9 @@ Prints one JSON line:
               with the gated residual (mf_block_out), per-call HIP-event
               durations against the bf16 MFMA peak at 2*T*N*K flops, with
               seeded random-init weights;
+  sampler     the packed-CFG guidance + Euler step after the last block
+              (mf_cfg_euler_step) on the packed CFG pack's tables, GB/s of its
+              algorithmic bytes against the HBM peak;
   cpu_baseline the fp64 oracle's whole step over the same workload, repeated
               for about 10 s, timed on the host cores.
 """
@@ -239,6 +242,36 @@ def main():
     blk_ms = {n: sum(kevs[i][j].elapsed_time(kevs[i][j + 1]) for i in range(args.steps)) / args.steps
               for j, n in enumerate(knames)}
 
+    # Packed-CFG guidance + Euler step after the last block, on the packed
+    # CFG pack (4 prompts of 1024^2, conditional and unconditional copies):
+    # per-call HIP events over enough rotated input sets to leave the cache.
+    import numpy as np
+    cdescs = W.descs_cfg(np.random.default_rng(W.CFG_SEED))
+    crows_h = native.cfg_pair_rows(cdescs, list(range(0, len(cdescs), 2)), list(range(1, len(cdescs), 2)))
+    cT = sum(W.sample_len(d) for d in cdescs)
+    cN, Cl = crows_h.shape[0], W.LATENT_CHANNELS
+    crows = torch.from_numpy(crows_h).cuda()
+    csets = [dict(v=torch.randn((cT, Cl), device="cuda").to(torch.bfloat16),
+                  z=torch.randn((cN, Cl), device="cuda"), zo=torch.empty((cN, Cl), device="cuda"),
+                  x=torch.empty((cT, Cl), dtype=torch.bfloat16, device="cuda")) for _ in range(10)]
+    def cfg_step(c):
+        native.cfg_euler_step(c["v"], crows, c["z"], c["zo"], 4.5, 0.75, 0.5, x_next=c["x"])
+    for i in range(args.warmup):
+        cfg_step(csets[i % len(csets)])
+    cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        cevs[i][0].record(stream)
+        cfg_step(csets[i % len(csets)])
+        cevs[i][1].record(stream)
+    torch.cuda.synchronize()
+    cfg_ms = sum(e0.elapsed_time(e1) for e0, e1 in cevs) / args.steps
+    cfg_bytes = cN * (16 * Cl + 8)      # v_c, v_u, z read, z' and both input rows written, rows
+    sampler = {"call": "mf_cfg_euler_step", "workload": f"cfg_pack descriptors (4 prompts, T={cT}, "
+               f"{cN} evolving latent tokens x {Cl} channels)", "ms": round(cfg_ms, 5),
+               "algorithmic_bytes": cfg_bytes, "GB/s": round(cfg_bytes / (cfg_ms * 1e-3) / 1e9, 1),
+               "frac_hbm_peak": round(cfg_bytes / (cfg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
     if args.copy_calib_mb:
         n = args.copy_calib_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -312,6 +345,7 @@ def main():
         "kernels": kernels,
         "backward": backward,
         "block": block,
+        "sampler": sampler,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

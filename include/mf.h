@@ -362,6 +362,50 @@ mf_status mf_block_out(void* stream,
                        const void* x, const void* gate, const int32_t* mod_row,
                        void* y, int64_t T, int32_t C);
 
+/* ------------------------------------------------------------------------
+ * Packed classifier-free guidance + Euler sampler step after the last block.
+ *
+ * The backbone predicts a velocity for the straight interpolation
+ * z_t = (1 - t) z + t eps between data and noise (gist.science "Resumo
+ * Tecnico: Mage-Flow", Metodologia; picx.dev summary, Introduction and
+ * Theoretical Foundation); the conditional and unconditional branches of
+ * classifier-free guidance run packed in one forward (picx.dev, Methodology
+ * > Native-Resolution MMDiT), and the Turbo variants sample in 4 steps.
+ *
+ * Host (no device): prompt p owns the conditional sample cond[p] and the
+ * unconditional sample uncond[p] of the pack described by descs (same
+ * latent grid h x w, n_frames >= 1).  Its evolving latents are the last
+ * frame's h*w tokens (generation: the only frame; editing: the target
+ * frame), in raster order.  mf_cfg_pair_count returns N = sum of h*w;
+ * mf_cfg_pair_rows fills the caller-allocated host array rows[N][2] with
+ * the packed rows (as in mf_pack_tables) of the conditional and the
+ * unconditional copy of each such token, prompts in order.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE (bad sample index, cond == uncond,
+ * differing grids, no frame, or any mf_pack_count error). */
+mf_status mf_cfg_pair_count(const mf_sample_desc* descs, int32_t n, const int32_t* cond,
+                            const int32_t* uncond, int32_t n_prompts, int64_t* n_tokens);
+mf_status mf_cfg_pair_rows(const mf_sample_desc* descs, int32_t n, const int32_t* cond,
+                           const int32_t* uncond, int32_t n_prompts, int32_t* rows);
+
+/* Device: for every evolving token k (rows[k] = (rc, ru), device int32
+ * [N][2]) and latent channel c:
+ *   g          = v[ru][c] + guidance * (v[rc][c] - v[ru][c])   (fp32)
+ *   z_out[k][c] = z[k][c] + (t - t_next) * g                     (fp32)
+ *   x_next[rc][c] = x_next[ru][c] = bf16(z_out[k][c])   (when x_next != NULL)
+ * i.e. one Euler step from t to t_next along the guided velocity.
+ * v: bf16 velocities of the packed batch [T][Cl], token stride ld_v >= Cl.
+ * z, z_out: fp32 [N][Cl] contiguous (z_out may equal z).
+ * x_next: NULL or bf16 [T][Cl] with token stride ld_x >= Cl (the next
+ *   forward's input rows; rows not in the table are left untouched); must
+ *   not overlap v.
+ * Cl a multiple of 8, at most 4096; strides multiples of 8; guidance, t and
+ * t_next finite.  N = 0 is a no-op.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_TABLE (MF_DEBUG
+ * only), MF_ERR_HIP. */
+mf_status mf_cfg_euler_step(void* stream, const void* v, int64_t ld_v, const int32_t* rows,
+                            const float* z, float* z_out, void* x_next, int64_t ld_x,
+                            int64_t n_tokens, int32_t Cl, float guidance, float t, float t_next);
+
 #ifdef __cplusplus
 }
 #endif

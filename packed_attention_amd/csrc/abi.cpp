@@ -466,4 +466,37 @@ mf_status mf_block_out(void* stream, const void* o, int64_t ld_o, const void* w_
     return finish(mf::launch_block_out(a, s), s);
 }
 
+mf_status mf_cfg_euler_step(void* stream, const void* v, int64_t ld_v, const int32_t* rows, const float* z,
+                            float* z_out, void* x_next, int64_t ld_x, int64_t n_tokens, int32_t Cl,
+                            float guidance, float t, float t_next) {
+    if (n_tokens < 0 || n_tokens > INT32_MAX || Cl <= 0 || Cl % 8 || Cl > 4096) return MF_ERR_SHAPE;
+    if (ld_v < Cl || (x_next != nullptr && ld_x < Cl)) return MF_ERR_SHAPE;
+    if (!std::isfinite(guidance) || !std::isfinite(t) || !std::isfinite(t_next)) return MF_ERR_SHAPE;
+    if (n_tokens == 0) return MF_OK;
+    if (!v || !rows || !z || !z_out) return MF_ERR_NULL;
+    if (ld_v % 8 || (x_next != nullptr && ld_x % 8)) return MF_ERR_ALIGN;
+    if (!aligned(v, 16) || !aligned(rows, 8) || !aligned(z, 16) || !aligned(z_out, 16) ||
+        (x_next != nullptr && !aligned(x_next, 16)))
+        return MF_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        std::vector<int32_t> hr;
+        if (!fetch(rows, size_t(n_tokens) * 2, hr, s)) return MF_ERR_HIP;
+        for (int32_t r : hr)
+            if (r < 0) return MF_ERR_TABLE;
+    }
+    mf::CfgEulerArgs a;
+    a.v = static_cast<const uint16_t*>(v);
+    a.ld_v = ld_v;
+    a.rows = rows;
+    a.z = z;
+    a.z_out = z_out;
+    a.x_next = static_cast<uint16_t*>(x_next);
+    a.ld_x = ld_x;
+    a.N = n_tokens;
+    a.Cl = Cl;
+    a.w = guidance; a.t = t; a.t_next = t_next;
+    return finish(mf::launch_cfg_euler(a, s), s);
+}
+
 }  // extern "C"

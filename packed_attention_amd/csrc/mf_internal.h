@@ -173,4 +173,19 @@ struct BlockOutArgs {
 };
 hipError_t launch_block_out(const BlockOutArgs& a, hipStream_t stream);
 
+// Packed classifier-free guidance + Euler step over the evolving latents.
+struct CfgEulerArgs {
+    const uint16_t* v;        // bf16 velocities of the packed batch, [T][Cl] with token stride ld_v
+    int64_t ld_v;
+    const int32_t* rows;      // [N][2] packed rows of the conditional and unconditional copy
+    const float* z;           // fp32 state [N][Cl]
+    float* z_out;             // fp32 [N][Cl] (may equal z)
+    uint16_t* x_next;         // nullptr, or bf16 rows [T][Cl] with token stride ld_x
+    int64_t ld_x;
+    int64_t N;
+    int32_t Cl;
+    float w, t, t_next;
+};
+hipError_t launch_cfg_euler(const CfgEulerArgs& a, hipStream_t stream);
+
 }  // namespace mf

@@ -72,3 +72,67 @@ extern "C" mf_status mf_pack_tables(const mf_sample_desc* descs, int32_t n, int3
     }
     return MF_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Packed classifier-free guidance: the conditional and unconditional copies
+// of a prompt run as two samples of one pack (picx.dev summary,
+// Methodology > Native-Resolution MMDiT).  The latents that the sampler step
+// moves are the last frame's (generation: the only frame; editing: the
+// target frame, after the source frame), h*w tokens in raster order after
+// the sample's text and earlier frames.
+// ---------------------------------------------------------------------------
+namespace {
+
+mf_status cfg_count(const mf_sample_desc* d, int32_t n, const int32_t* cond, const int32_t* uncond,
+                    int32_t P, int64_t* total) {
+    int64_t T = 0;
+    mf_status st = count_tokens(d, n, &T);
+    if (st != MF_OK) return st;
+    if (P < 0) return MF_ERR_SHAPE;
+    if (P > 0 && (cond == nullptr || uncond == nullptr)) return MF_ERR_NULL;
+    int64_t N = 0;
+    for (int32_t p = 0; p < P; ++p) {
+        const int32_t c = cond[p], u = uncond[p];
+        if (c < 0 || c >= n || u < 0 || u >= n || c == u) return MF_ERR_SHAPE;
+        if (d[c].n_frames < 1 || d[u].n_frames < 1) return MF_ERR_SHAPE;
+        if (d[c].grid_h != d[u].grid_h || d[c].grid_w != d[u].grid_w) return MF_ERR_SHAPE;
+        N += int64_t(d[c].grid_h) * d[c].grid_w;
+    }
+    *total = N;
+    return MF_OK;
+}
+
+}  // namespace
+
+extern "C" mf_status mf_cfg_pair_count(const mf_sample_desc* descs, int32_t n, const int32_t* cond,
+                                       const int32_t* uncond, int32_t n_prompts, int64_t* n_tokens) {
+    if (n_tokens == nullptr) return MF_ERR_NULL;
+    return cfg_count(descs, n, cond, uncond, n_prompts, n_tokens);
+}
+
+extern "C" mf_status mf_cfg_pair_rows(const mf_sample_desc* descs, int32_t n, const int32_t* cond,
+                                      const int32_t* uncond, int32_t n_prompts, int32_t* rows) {
+    int64_t N = 0;
+    mf_status st = cfg_count(descs, n, cond, uncond, n_prompts, &N);
+    if (st != MF_OK) return st;
+    if (N > 0 && rows == nullptr) return MF_ERR_NULL;
+    // sample starts (cumulative offsets)
+    int64_t k = 0;
+    for (int32_t p = 0; p < n_prompts; ++p) {
+        const int32_t c = cond[p], u = uncond[p];
+        int64_t bc = 0, bu = 0, off = 0;
+        for (int32_t s = 0; s < n; ++s) {
+            if (s == c) bc = off;
+            if (s == u) bu = off;
+            off += int64_t(descs[s].text_len) + int64_t(descs[s].n_frames) * descs[s].grid_h * descs[s].grid_w;
+        }
+        const int64_t hw = int64_t(descs[c].grid_h) * descs[c].grid_w;
+        bc += descs[c].text_len + int64_t(descs[c].n_frames - 1) * hw;
+        bu += descs[u].text_len + int64_t(descs[u].n_frames - 1) * hw;
+        for (int64_t j = 0; j < hw; ++j, ++k) {
+            rows[2 * k] = int32_t(bc + j);
+            rows[2 * k + 1] = int32_t(bu + j);
+        }
+    }
+    return MF_OK;
+}

@@ -27,7 +27,7 @@ EXPORTS = ("mf_status_string", "mf_abi_version", "mf_pack_count", "mf_pack_table
            "mf_gated_residual", "mf_varlen_attn_bwd_workspace_bytes", "mf_varlen_attn_bwd",
            "mf_modulate_rope_bwd", "mf_gated_residual_bwd", "mf_modulate_rope_bwd_workspace_bytes",
            "mf_gated_residual_bwd_workspace_bytes", "mf_block_qkv_workspace_bytes", "mf_block_qkv",
-           "mf_block_out")
+           "mf_block_out", "mf_cfg_pair_count", "mf_cfg_pair_rows", "mf_cfg_euler_step")
 
 
 class MFError(RuntimeError):
@@ -96,6 +96,12 @@ def lib() -> ctypes.CDLL:
     L.mf_block_qkv.restype = i32
     L.mf_block_out.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, i32]
     L.mf_block_out.restype = i32
+    L.mf_cfg_pair_count.argtypes = [vp, i32, vp, vp, i32, ctypes.POINTER(i64)]
+    L.mf_cfg_pair_count.restype = i32
+    L.mf_cfg_pair_rows.argtypes = [vp, i32, vp, vp, i32, vp]
+    L.mf_cfg_pair_rows.restype = i32
+    L.mf_cfg_euler_step.argtypes = [vp, vp, i64, vp, vp, vp, vp, i64, i64, i32, f32, f32, f32]
+    L.mf_cfg_euler_step.restype = i32
     _lib = L
     return L
 
@@ -372,3 +378,36 @@ def block_out(o, w_o, x, gate, mod_row, y, stream=None):
         raise ValueError("w_o: expected [C][C]")
     check(lib().mf_block_out(_stream(stream), _ptr(o), _token_stride(o, C), _ptr(w_o), _ptr(x), _ptr(gate),
                              _ptr(mod_row), _ptr(y), T, C))
+
+
+def cfg_pair_rows(descs, cond, uncond) -> np.ndarray:
+    """mf_cfg_pair_count + mf_cfg_pair_rows: int32 [N][2] packed rows of the
+    conditional and unconditional copy of every evolving latent token."""
+    arr = _desc_array(descs)
+    P = len(cond)
+    ca = np.ascontiguousarray(cond, dtype=np.int32)
+    ua = np.ascontiguousarray(uncond, dtype=np.int32)
+    n = ctypes.c_int64(0)
+    check(lib().mf_cfg_pair_count(arr, len(descs), ca.ctypes.data, ua.ctypes.data, P, ctypes.byref(n)))
+    rows = np.zeros((max(n.value, 1), 2), dtype=np.int32)
+    check(lib().mf_cfg_pair_rows(arr, len(descs), ca.ctypes.data, ua.ctypes.data, P, rows.ctypes.data))
+    return rows[:n.value]
+
+
+def cfg_euler_step(v, rows, z, z_out, guidance, t, t_next, x_next=None, stream=None):
+    """mf_cfg_euler_step: v bf16 [T][Cl] rows, rows int32 [N][2] (device), z/z_out fp32 [N][Cl]."""
+    import torch
+    T, Cl = v.shape
+    _check_bf16_rows("v", v, Cl)
+    if rows.dtype != torch.int32 or not rows.is_contiguous() or rows.dim() != 2 or rows.shape[1] != 2:
+        raise ValueError("rows: expected a contiguous int32 [N][2] tensor")
+    N = rows.shape[0]
+    for n_, t_ in (("z", z), ("z_out", z_out)):
+        if t_.dtype != torch.float32 or not t_.is_contiguous() or tuple(t_.shape) != (N, Cl):
+            raise ValueError(f"{n_}: expected a contiguous float32 [N][Cl] tensor")
+    ld_x = 0
+    if x_next is not None:
+        _check_bf16_rows("x_next", x_next, Cl)
+        ld_x = _token_stride(x_next, Cl)
+    check(lib().mf_cfg_euler_step(_stream(stream), _ptr(v), _token_stride(v, Cl), _ptr(rows), _ptr(z), _ptr(z_out),
+                                  _ptr(x_next), ld_x, N, Cl, float(guidance), float(t), float(t_next)))

@@ -239,6 +239,27 @@ def block_inputs(w: Workload) -> dict:
     return dict(x=x, w_qkv=_normal_bf16(rng, (3 * C, C), sig), w_o=_normal_bf16(rng, (C, C), sig))
 
 
+LATENT_CHANNELS = 128   # Mage-VAE latents: 16x downsampling, 128 channels per token
+
+
+def cfg_prompts(w: Workload) -> Tuple[List[int], List[int]]:
+    """(cond, uncond) sample indices of a packed-CFG workload: the packs here
+    place each prompt's conditional sample right before its unconditional one."""
+    n = len(w.descs)
+    return list(range(0, n - 1, 2)), list(range(1, n, 2))
+
+
+def sampler_inputs(w: Workload, n_tokens: int, Cl: int = LATENT_CHANNELS) -> dict:
+    """Seeded stand-ins for one sampler step: the model's velocity output for
+    every packed token v [T][Cl] (N(0, 1), bf16 bits) and the fp32 latent
+    state of the n_tokens evolving tokens z [N][Cl] (N(0, 1)); own generator
+    (seed + 3000003)."""
+    rng = np.random.default_rng(w.seed + 3000003)
+    v = _normal_bf16(rng, (w.T, Cl), 1.0)
+    z = rng.standard_normal((n_tokens, Cl)).astype(np.float32)
+    return dict(v=v, z=z)
+
+
 # ---------------------------------------------------------------------------
 # Named workloads
 # ---------------------------------------------------------------------------
@@ -271,7 +292,10 @@ def native_pack(seed: int = 2000, budget: int = 16384) -> Workload:
     return _draw_tensors(f"native_pack_{seed}", seed, rng, descs, 24, 128, (0, 64, 64), True, True)
 
 
-def cfg_pack(seed: int = 1003) -> Workload:
+CFG_SEED = 1003
+
+
+def cfg_pack(seed: int = CFG_SEED) -> Workload:
     """Packed CFG inference at 1024^2: 8 sequences, H=24, d=128."""
     rng = np.random.default_rng(seed)
     descs = descs_cfg(rng)

@@ -252,6 +252,31 @@ def test_block_projection_validation():
     assert native.lib().mf_block_qkv_workspace_bytes(4352, 24, 128) == 4352 * 3072 * 2
 
 
+def cfg_step(**kw):
+    a = dict(stream=None, v=P, ld_v=128, rows=P, z=P, z_out=P, x=None, ld_x=0, N=16, Cl=128, w=4.5, t=0.75,
+             tn=0.5)
+    a.update(kw)
+    return native.lib().mf_cfg_euler_step(*a.values())
+
+
+def test_cfg_euler_validation():
+    assert cfg_step(Cl=100) == SHAPE
+    assert cfg_step(Cl=8192) == SHAPE
+    assert cfg_step(N=-1) == SHAPE
+    assert cfg_step(ld_v=64) == SHAPE
+    assert cfg_step(x=P, ld_x=64) == SHAPE
+    assert cfg_step(w=float("nan")) == SHAPE
+    assert cfg_step(t=float("inf")) == SHAPE
+    assert cfg_step(v=None) == NULL
+    assert cfg_step(rows=None) == NULL
+    assert cfg_step(z_out=None) == NULL
+    assert cfg_step(ld_v=132) == ALIGN
+    assert cfg_step(rows=P + 4) == ALIGN
+    assert cfg_step(z=PODD) == ALIGN
+    assert cfg_step(x=PODD, ld_x=128) == ALIGN
+    assert cfg_step(N=0, v=None, rows=None, z=None, z_out=None) == 0
+
+
 def test_library_has_no_oracle_dependency():
     """The product path never touches the oracle: no module of the package
     imports it, and the native sources do not mention it."""
