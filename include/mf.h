@@ -406,6 +406,60 @@ mf_status mf_cfg_euler_step(void* stream, const void* v, int64_t ld_v, const int
                             const float* z, float* z_out, void* x_next, int64_t ld_x,
                             int64_t n_tokens, int32_t Cl, float guidance, float t, float t_next);
 
+/* ------------------------------------------------------------------------
+ * Text-encoder variant: the pages fuse the normalisation and rotary
+ * embedding chains inside the frozen Qwen3-VL text encoder's blocks as in the
+ * backbone (picx.dev summary of Mage-Flow, Methodology > Training
+ * Infrastructure; gist.science "Resumo Tecnico: Mage-Flow", Metodologia > 3
+ * > Kernels Fundidos); its prompts are packed like the backbone's samples.
+ *
+ * mf_qk_norm_rope: per-head RMS normalisation + 1D rotary embedding:
+ *   q'[t][h] = RoPE_pos[t](q[t][h] / sqrt(mean_e q[t][h][e]^2 + eps) * wq)
+ *   k'[t][h] = RoPE_pos[t](k[t][h] / sqrt(mean_e k[t][h][e]^2 + eps) * wk)
+ * RoPE turns pair (2j, 2j+1) of every head counter-clockwise by
+ * pos[t] * rope_base^(-2j/D); pos[t] is the token's index inside its prompt.
+ * q_in / q_out: bf16 [T][Hq][D] (token strides ld_q / ld_qo); k_in / k_out:
+ *   bf16 [T][Hkv][D] (ld_k / ld_ko); strides multiples of 8, outputs may
+ *   equal inputs.  wq, wk: bf16 [D]; pos: int32 [T] >= 0.
+ * D in {64, 128}; Hq * D and Hkv * D at most 8192; rope_base, eps > 0.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
+ * MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+mf_status mf_qk_norm_rope(void* stream,
+                          const void* q_in, int64_t ld_q, const void* k_in, int64_t ld_k,
+                          void* q_out, int64_t ld_qo, void* k_out, int64_t ld_ko,
+                          const void* wq, const void* wk, const int32_t* pos,
+                          int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                          float rope_base, float eps);
+
+/* Host (no device): cumulative offsets cu_seqlens[n+1] and per-token
+ * positions pos[T] (index inside its prompt) of n packed prompts of lengths
+ * lens[n] (caller-allocated host arrays, T = sum of lens).
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE (n < 0, a negative length, T > INT32_MAX). */
+mf_status mf_prompt_tables(const int32_t* lens, int32_t n, int32_t* cu_seqlens, int32_t* pos);
+
+/* mf_varlen_attn_causal_fwd: causal attention inside each packed prompt,
+ * query head h reading key/value head h / (Hq / Hkv):
+ *   O[i][h] = sum_{j<=i} softmax_j(softmax_scale * q[i][h] . k[j][h']) v[j][h']
+ *   lse[h][i] = natural-log sum-exp of the scaled scores (when lse != NULL)
+ * with i, j inside one prompt (cu_seqlens as for mf_varlen_attn_fwd).
+ * q, o: bf16 [T][Hq][D] (token strides ld_q, ld_o); k, v: bf16
+ *   [T][Hkv][D] sharing token stride ld_kv; strides multiples of 8; o must
+ *   not overlap q, k or v.  lse: NULL or fp32 [Hq][T].
+ * workspace: >= mf_varlen_attn_causal_workspace_bytes(n_seq) bytes, 8-byte
+ *   aligned, caller-owned, one call at a time per workspace.
+ * Hq a multiple of Hkv; D in {64, 128}; T * ld_q * 2 and T * ld_kv * 2
+ * below 2^32.  T = 0 or n_seq = 0 is a no-op.
+ * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
+ * MF_ERR_WORKSPACE, MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
+size_t mf_varlen_attn_causal_workspace_bytes(int32_t n_seq);
+
+mf_status mf_varlen_attn_causal_fwd(void* stream,
+                                    const void* q, int64_t ld_q, const void* k, const void* v,
+                                    int64_t ld_kv, void* o, int64_t ld_o, float* lse,
+                                    const int32_t* cu_seqlens, int32_t n_seq, int64_t T,
+                                    int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                    void* workspace, size_t workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif

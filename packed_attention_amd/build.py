@@ -36,7 +36,7 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE]
 
 HIP_SOURCES = ["abi.cpp", "modulate_rope.hip", "gated_residual.hip", "varlen_attn_fwd.hip",
                "varlen_attn_bwd.hip", "elementwise_bwd.hip",
-               "block_gemm.hip", "cfg_sampler.hip"]
+               "block_gemm.hip", "cfg_sampler.hip", "text_encoder.hip"]
 HOST_SOURCES = ["pack_tables.cpp"]
 
 

@@ -499,4 +499,81 @@ mf_status mf_cfg_euler_step(void* stream, const void* v, int64_t ld_v, const int
     return finish(mf::launch_cfg_euler(a, s), s);
 }
 
+mf_status mf_qk_norm_rope(void* stream, const void* q_in, int64_t ld_q, const void* k_in, int64_t ld_k,
+                          void* q_out, int64_t ld_qo, void* k_out, int64_t ld_ko, const void* wq, const void* wk,
+                          const int32_t* pos, int64_t T, int32_t Hq, int32_t Hkv, int32_t D, float rope_base,
+                          float eps) {
+    if (T < 0 || T > INT32_MAX || Hq <= 0 || Hkv <= 0) return MF_ERR_SHAPE;
+    if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
+    if (int64_t(Hq) * D > 8192 || int64_t(Hkv) * D > 8192) return MF_ERR_UNSUPPORTED;
+    if (ld_q < int64_t(Hq) * D || ld_qo < int64_t(Hq) * D || ld_k < int64_t(Hkv) * D || ld_ko < int64_t(Hkv) * D)
+        return MF_ERR_SHAPE;
+    if (!(rope_base > 0.f) || !std::isfinite(rope_base) || !(eps > 0.f)) return MF_ERR_SHAPE;
+    if (T == 0) return MF_OK;
+    if (!q_in || !k_in || !q_out || !k_out || !wq || !wk || !pos) return MF_ERR_NULL;
+    if (ld_q % 8 || ld_k % 8 || ld_qo % 8 || ld_ko % 8) return MF_ERR_ALIGN;
+    if (!aligned(q_in, 16) || !aligned(k_in, 16) || !aligned(q_out, 16) || !aligned(k_out, 16) ||
+        !aligned(wq, 16) || !aligned(wk, 16) || !aligned(pos, 4))
+        return MF_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        std::vector<int32_t> hp;
+        if (!fetch(pos, size_t(T), hp, s)) return MF_ERR_HIP;
+        for (int32_t v : hp)
+            if (v < 0) return MF_ERR_TABLE;
+    }
+    mf::QkNormRopeArgs a;
+    a.q_in = static_cast<const uint16_t*>(q_in);
+    a.k_in = static_cast<const uint16_t*>(k_in);
+    a.q_out = static_cast<uint16_t*>(q_out);
+    a.k_out = static_cast<uint16_t*>(k_out);
+    a.ld_q = ld_q; a.ld_k = ld_k; a.ld_qo = ld_qo; a.ld_ko = ld_ko;
+    a.wq = static_cast<const uint16_t*>(wq);
+    a.wk = static_cast<const uint16_t*>(wk);
+    a.pos = pos;
+    a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+    a.rope_base = rope_base; a.eps = eps;
+    return finish(mf::launch_qk_norm_rope(a, s), s);
+}
+
+size_t mf_varlen_attn_causal_workspace_bytes(int32_t n_seq) { return mf::causal_attn_workspace_bytes(n_seq); }
+
+mf_status mf_varlen_attn_causal_fwd(void* stream, const void* q, int64_t ld_q, const void* k, const void* v,
+                                    int64_t ld_kv, void* o, int64_t ld_o, float* lse, const int32_t* cu_seqlens,
+                                    int32_t n_seq, int64_t T, int32_t Hq, int32_t Hkv, int32_t D,
+                                    float softmax_scale, void* workspace, size_t workspace_bytes) {
+    if (T < 0 || T > INT32_MAX || n_seq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return MF_ERR_SHAPE;
+    if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
+    if (ld_q < int64_t(Hq) * D || ld_o < int64_t(Hq) * D || ld_kv < int64_t(Hkv) * D) return MF_ERR_SHAPE;
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MF_ERR_SHAPE;
+    if (T * ld_q * 2 >= (int64_t(1) << 32) || T * ld_kv * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
+    if (T == 0 || n_seq == 0) return MF_OK;
+    if (!q || !k || !v || !o || !cu_seqlens) return MF_ERR_NULL;
+    if (ld_q % 8 || ld_kv % 8 || ld_o % 8) return MF_ERR_ALIGN;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(cu_seqlens, 4) ||
+        (lse && !aligned(lse, 4)))
+        return MF_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < mf::causal_attn_workspace_bytes(n_seq)) return MF_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return MF_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        std::vector<int32_t> hc;
+        if (!fetch(cu_seqlens, size_t(n_seq) + 1, hc, s)) return MF_ERR_HIP;
+        if (hc[0] != 0 || hc[n_seq] != T) return MF_ERR_TABLE;
+        for (int32_t i = 0; i < n_seq; ++i)
+            if (hc[i + 1] < hc[i]) return MF_ERR_TABLE;
+    }
+    mf::CausalAttnArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse; a.cu_seqlens = cu_seqlens; a.n_seq = n_seq;
+    a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
+    a.ld_q = ld_q; a.ld_kv = ld_kv; a.ld_o = ld_o;
+    a.softmax_scale = softmax_scale;
+    a.workspace = workspace;
+    return finish(mf::launch_varlen_attn_causal(a, s), s);
+}
+
 }  // extern "C"

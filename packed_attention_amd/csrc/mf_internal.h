@@ -188,4 +188,39 @@ struct CfgEulerArgs {
 };
 hipError_t launch_cfg_euler(const CfgEulerArgs& a, hipStream_t stream);
 
+// Text-encoder variant: per-head RMS norm + 1D RoPE of q and k, and causal
+// attention with grouped key/value heads over packed prompts.
+struct QkNormRopeArgs {
+    const uint16_t* q_in;     // [T][Hq][D], token stride ld_q
+    const uint16_t* k_in;     // [T][Hkv][D], token stride ld_k
+    uint16_t* q_out;          // token stride ld_qo
+    uint16_t* k_out;          // token stride ld_ko
+    int64_t ld_q, ld_k, ld_qo, ld_ko;
+    const uint16_t* wq;       // [D]
+    const uint16_t* wk;       // [D]
+    const int32_t* pos;       // [T] index inside the prompt
+    int64_t T;
+    int32_t Hq, Hkv, D;
+    float rope_base, eps;
+    double theta_turns[64];   // filled by the launcher: base^(-2j/D) / (2 pi)
+};
+hipError_t launch_qk_norm_rope(const QkNormRopeArgs& a, hipStream_t stream);
+
+struct CausalAttnArgs {
+    const uint16_t* q;        // [T][Hq][D], token stride ld_q
+    const uint16_t* k;        // [T][Hkv][D], token stride ld_kv
+    const uint16_t* v;
+    uint16_t* o;              // [T][Hq][D], token stride ld_o
+    float* lse;               // nullable, [Hq][T]
+    const int32_t* cu_seqlens;
+    int32_t n_seq;
+    int64_t T;
+    int32_t Hq, Hkv, D;
+    int64_t ld_q, ld_kv, ld_o;
+    float softmax_scale;
+    void* workspace;          // int64 [n_seq + 1]
+};
+size_t causal_attn_workspace_bytes(int32_t n_seq);
+hipError_t launch_varlen_attn_causal(const CausalAttnArgs& a, hipStream_t stream);
+
 }  // namespace mf

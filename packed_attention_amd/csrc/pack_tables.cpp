@@ -136,3 +136,26 @@ extern "C" mf_status mf_cfg_pair_rows(const mf_sample_desc* descs, int32_t n, co
     }
     return MF_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Packed prompts of the text encoder: cumulative offsets and every token's
+// index inside its prompt (the rotary position of the causal encoder).
+// ---------------------------------------------------------------------------
+extern "C" mf_status mf_prompt_tables(const int32_t* lens, int32_t n, int32_t* cu_seqlens, int32_t* pos) {
+    if (n < 0) return MF_ERR_SHAPE;
+    if (cu_seqlens == nullptr || (n > 0 && lens == nullptr)) return MF_ERR_NULL;
+    int64_t T = 0;
+    for (int32_t s = 0; s < n; ++s) {
+        if (lens[s] < 0) return MF_ERR_SHAPE;
+        T += lens[s];
+        if (T > INT32_MAX) return MF_ERR_SHAPE;
+    }
+    if (T > 0 && pos == nullptr) return MF_ERR_NULL;
+    int32_t t = 0;
+    cu_seqlens[0] = 0;
+    for (int32_t s = 0; s < n; ++s) {
+        for (int32_t j = 0; j < lens[s]; ++j) pos[t++] = j;
+        cu_seqlens[s + 1] = t;
+    }
+    return MF_OK;
+}

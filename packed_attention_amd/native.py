@@ -27,7 +27,8 @@ EXPORTS = ("mf_status_string", "mf_abi_version", "mf_pack_count", "mf_pack_table
            "mf_gated_residual", "mf_varlen_attn_bwd_workspace_bytes", "mf_varlen_attn_bwd",
            "mf_modulate_rope_bwd", "mf_gated_residual_bwd", "mf_modulate_rope_bwd_workspace_bytes",
            "mf_gated_residual_bwd_workspace_bytes", "mf_block_qkv_workspace_bytes", "mf_block_qkv",
-           "mf_block_out", "mf_cfg_pair_count", "mf_cfg_pair_rows", "mf_cfg_euler_step")
+           "mf_block_out", "mf_cfg_pair_count", "mf_cfg_pair_rows", "mf_cfg_euler_step", "mf_qk_norm_rope",
+           "mf_varlen_attn_causal_workspace_bytes", "mf_varlen_attn_causal_fwd", "mf_prompt_tables")
 
 
 class MFError(RuntimeError):
@@ -102,6 +103,15 @@ def lib() -> ctypes.CDLL:
     L.mf_cfg_pair_rows.restype = i32
     L.mf_cfg_euler_step.argtypes = [vp, vp, i64, vp, vp, vp, vp, i64, i64, i32, f32, f32, f32]
     L.mf_cfg_euler_step.restype = i32
+    L.mf_qk_norm_rope.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, vp, i64, i32, i32, i32, f32, f32]
+    L.mf_qk_norm_rope.restype = i32
+    L.mf_varlen_attn_causal_workspace_bytes.argtypes = [i32]
+    L.mf_varlen_attn_causal_workspace_bytes.restype = sz
+    L.mf_varlen_attn_causal_fwd.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, i32, i64, i32, i32, i32, f32,
+                                            vp, sz]
+    L.mf_varlen_attn_causal_fwd.restype = i32
+    L.mf_prompt_tables.argtypes = [vp, i32, vp, vp]
+    L.mf_prompt_tables.restype = i32
     _lib = L
     return L
 
@@ -411,3 +421,53 @@ def cfg_euler_step(v, rows, z, z_out, guidance, t, t_next, x_next=None, stream=N
         ld_x = _token_stride(x_next, Cl)
     check(lib().mf_cfg_euler_step(_stream(stream), _ptr(v), _token_stride(v, Cl), _ptr(rows), _ptr(z), _ptr(z_out),
                                   _ptr(x_next), ld_x, N, Cl, float(guidance), float(t), float(t_next)))
+
+
+def qk_norm_rope(q_in, k_in, q_out, k_out, wq, wk, pos, rope_base=10000.0, eps=1e-6, stream=None):
+    """mf_qk_norm_rope on q [T][Hq][D] and k [T][Hkv][D] bf16 (outputs may alias inputs)."""
+    T, Hq, D = q_in.shape
+    Hkv = k_in.shape[1]
+    for n, t, H in (("q_in", q_in, Hq), ("q_out", q_out, Hq), ("k_in", k_in, Hkv), ("k_out", k_out, Hkv)):
+        _check_bf16_rows(n, t, H * D)
+        if tuple(t.shape) != (T, H, D):
+            raise ValueError(f"{n}: shape {tuple(t.shape)} != {(T, H, D)}")
+    check(lib().mf_qk_norm_rope(_stream(stream), _ptr(q_in), _token_stride(q_in, Hq * D), _ptr(k_in),
+                                _token_stride(k_in, Hkv * D), _ptr(q_out), _token_stride(q_out, Hq * D),
+                                _ptr(k_out), _token_stride(k_out, Hkv * D), _ptr(wq), _ptr(wk), _ptr(pos), T, Hq,
+                                Hkv, D, float(rope_base), float(eps)))
+
+
+def varlen_attn_causal_fwd(q, k, v, o, cu_seqlens, lse=None, softmax_scale=None, workspace=None, stream=None):
+    """mf_varlen_attn_causal_fwd: q, o [T][Hq][D], k, v [T][Hkv][D] bf16 (k, v sharing a token stride)."""
+    import torch
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    for n, t, H in (("q", q, Hq), ("o", o, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        _check_bf16_rows(n, t, H * D)
+        if tuple(t.shape) != (T, H, D):
+            raise ValueError(f"{n}: shape {tuple(t.shape)} != {(T, H, D)}")
+    ld_kv = _token_stride(k, Hkv * D)
+    if _token_stride(v, Hkv * D) != ld_kv:
+        raise ValueError("k and v must share a token stride")
+    n_seq = cu_seqlens.numel() - 1
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    need = int(lib().mf_varlen_attn_causal_workspace_bytes(n_seq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=q.device)
+    check(lib().mf_varlen_attn_causal_fwd(_stream(stream), _ptr(q), _token_stride(q, Hq * D), _ptr(k), _ptr(v),
+                                          ld_kv, _ptr(o), _token_stride(o, Hq * D), _ptr(lse), _ptr(cu_seqlens),
+                                          n_seq, T, Hq, Hkv, D, float(softmax_scale), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size()))
+
+
+def prompt_tables(lens):
+    """mf_prompt_tables: (cu_seqlens[n+1], pos[T]) int32 numpy for packed prompts of the given lengths."""
+    la = np.ascontiguousarray(lens, dtype=np.int32)
+    n = len(la)
+    T = int(la.astype(np.int64).sum()) if n else 0
+    cu = np.zeros(n + 1, dtype=np.int32)
+    # the library rejects T > INT32_MAX before writing: no buffer that large
+    pos = np.zeros(max(T, 1) if T <= 2 ** 31 - 1 else 1, dtype=np.int32)
+    check(lib().mf_prompt_tables(la.ctypes.data if n else None, n, cu.ctypes.data, pos.ctypes.data))
+    return cu, pos[:T]

@@ -260,6 +260,49 @@ def sampler_inputs(w: Workload, n_tokens: int, Cl: int = LATENT_CHANNELS) -> dic
     return dict(v=v, z=z)
 
 
+@dataclasses.dataclass
+class TextPack:
+    """Packed prompts for the text-encoder variant (bf16 bit patterns)."""
+    name: str
+    seed: int
+    lens: List[int]
+    Hq: int
+    Hkv: int
+    D: int
+    q: np.ndarray       # [T][Hq][D]
+    k: np.ndarray       # [T][Hkv][D]
+    v: np.ndarray       # [T][Hkv][D]
+    wq: np.ndarray      # [D] per-head norm weights
+    wk: np.ndarray
+    rope_base: float = ROPE_BASE
+    eps: float = LN_EPS
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.lens))
+
+    def causal_flops(self) -> float:
+        """QK^T and PV over the unmasked pairs: 4 * D * Hq * sum L (L + 1) / 2."""
+        return 4.0 * self.D * self.Hq * sum(L * (L + 1) / 2 for L in self.lens)
+
+
+def text_pack(seed: int = 1005, n_prompts: int = 16, Hq: int = 32, Hkv: int = 8, D: int = 128,
+              lens: Optional[Sequence[int]] = None, name: str = "text_pack") -> TextPack:
+    """Packed prompts: lengths U{64..512} (the prompt lengths of the packed
+    CFG workload), q, k, v ~ N(0, 1), norm weights 1 + N(0, 0.1); default
+    heads 32 query / 8 key-value of 128 dims."""
+    rng = np.random.default_rng(seed)
+    if lens is None:
+        lens = [int(x) for x in rng.integers(64, 513, size=n_prompts)]
+    T = int(sum(lens))
+    q = _normal_bf16(rng, (T, Hq, D), 1.0)
+    k = _normal_bf16(rng, (T, Hkv, D), 1.0)
+    v = _normal_bf16(rng, (T, Hkv, D), 1.0)
+    wq = f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32))
+    wk = f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32))
+    return TextPack(name, seed, list(lens), Hq, Hkv, D, q, k, v, wq, wk)
+
+
 # ---------------------------------------------------------------------------
 # Named workloads
 # ---------------------------------------------------------------------------

@@ -277,6 +277,48 @@ def test_cfg_euler_validation():
     assert cfg_step(N=0, v=None, rows=None, z=None, z_out=None) == 0
 
 
+def qknr(**kw):
+    a = dict(stream=None, q=P, ld_q=256, k=P, ld_k=128, qo=P, ld_qo=256, ko=P, ld_ko=128, wq=P, wk=P, pos=P,
+             T=4, Hq=4, Hkv=2, D=64, base=10000.0, eps=1e-6)
+    a.update(kw)
+    return native.lib().mf_qk_norm_rope(*a.values())
+
+
+def causal(**kw):
+    a = dict(stream=None, q=P, ld_q=256, k=P, v=P, ld_kv=128, o=P, ld_o=256, lse=None, cu=P, n=2, T=4, Hq=4,
+             Hkv=2, D=64, scale=0.125, ws=None, ws_bytes=0)
+    a.update(kw)
+    return native.lib().mf_varlen_attn_causal_fwd(*a.values())
+
+
+def test_text_encoder_validation():
+    assert qknr(D=96) == UNSUP
+    assert qknr(Hq=160, ld_q=10240, ld_qo=10240) == UNSUP
+    assert qknr(ld_q=128) == SHAPE
+    assert qknr(ld_ko=64) == SHAPE
+    assert qknr(eps=0.0) == SHAPE
+    assert qknr(base=-1.0) == SHAPE
+    assert qknr(wq=None) == NULL
+    assert qknr(pos=None) == NULL
+    assert qknr(ld_k=132) == ALIGN
+    assert qknr(ko=PODD) == ALIGN
+    assert qknr(T=0, q=None, k=None, qo=None, ko=None, wq=None, wk=None, pos=None) == 0
+    assert causal(Hq=3) == SHAPE                 # Hq not a multiple of Hkv
+    assert causal(D=80) == UNSUP
+    assert causal(ld_kv=64) == SHAPE
+    assert causal(scale=0.0) == SHAPE
+    assert causal(T=1 << 24, ld_q=256) == UNSUP
+    assert causal(q=None) == NULL
+    assert causal(cu=None) == NULL
+    assert causal(ld_o=260) == ALIGN
+    assert causal(lse=P + 2) == ALIGN
+    assert causal() == WS
+    assert causal(ws=P, ws_bytes=8) == WS
+    assert causal(ws=P + 4, ws_bytes=64) == ALIGN
+    assert causal(n=0, q=None) == 0
+    assert native.lib().mf_varlen_attn_causal_workspace_bytes(16) == 17 * 8
+
+
 def test_library_has_no_oracle_dependency():
     """The product path never touches the oracle: no module of the package
     imports it, and the native sources do not mention it."""
