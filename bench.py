@@ -33,6 +33,10 @@ Prints one JSON line:
   sampler     the packed-CFG guidance + Euler step after the last block
               (mf_cfg_euler_step) on the packed CFG pack's tables, GB/s of its
               algorithmic bytes against the HBM peak;
+  text_encoder the text-encoder variant on 64 packed prompts: per-head RMS
+              norm + 1D RoPE of q and k (mf_qk_norm_rope, GB/s of its
+              algorithmic bytes) and causal grouped-head attention
+              (mf_varlen_attn_causal_fwd, TFLOP/s at 4*D*Hq*sum L(L+1)/2);
   cpu_baseline the fp64 oracle's whole step over the same workload, repeated
               for about 10 s, timed on the host cores.
 """
@@ -272,6 +276,52 @@ def main():
                "algorithmic_bytes": cfg_bytes, "GB/s": round(cfg_bytes / (cfg_ms * 1e-3) / 1e9, 1),
                "frac_hbm_peak": round(cfg_bytes / (cfg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
+    # Text-encoder variant: per-head RMS norm + 1D RoPE of q and k, then
+    # causal grouped-head attention inside each packed prompt; per-call HIP
+    # events over rotated input sets.
+    tp = W.text_pack(seed=W.TEXT_BENCH_SEED, n_prompts=W.TEXT_BENCH_PROMPTS, name="text_pack_64")
+    tcu_h, tpos_h = native.prompt_tables(tp.lens)
+    tcu, tpos = torch.from_numpy(tcu_h).cuda(), torch.from_numpy(tpos_h).cuda()
+    twq, twk = runner.bf16_tensor(tp.wq), runner.bf16_tensor(tp.wk)
+    tq0, tk0, tv0 = runner.bf16_tensor(tp.q), runner.bf16_tensor(tp.k), runner.bf16_tensor(tp.v)
+    tws = torch.empty(max(16, native.lib().mf_varlen_attn_causal_workspace_bytes(len(tp.lens), tp.T)),
+                      dtype=torch.uint8, device="cuda")
+    tsets = [dict(q=tq0.clone(), k=tk0.clone(), v=tv0.clone(), qo=torch.empty_like(tq0), ko=torch.empty_like(tk0),
+                  o=torch.empty_like(tq0), lse=torch.empty((tp.Hq, tp.T), dtype=torch.float32, device="cuda"))
+             for _ in range(max(1, args.sets))]
+    del tq0, tk0, tv0
+    tfns = (lambda c: native.qk_norm_rope(c["q"], c["k"], c["qo"], c["ko"], twq, twk, tpos, tp.rope_base, tp.eps),
+            lambda c: native.varlen_attn_causal_fwd(c["qo"], c["ko"], c["v"], c["o"], tcu, lse=c["lse"],
+                                                    workspace=tws))
+    for i in range(args.warmup):
+        for fn in tfns:
+            fn(tsets[i % len(tsets)])
+    tevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        c = tsets[i % len(tsets)]
+        tevs[i][0].record(stream)
+        for j, fn in enumerate(tfns):
+            fn(c)
+            tevs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    tnames = ("qk_norm_rope", "varlen_attn_causal_fwd")
+    te_ms = {n: sum(tevs[i][j].elapsed_time(tevs[i][j + 1]) for i in range(args.steps)) / args.steps
+             for j, n in enumerate(tnames)}
+    qn_bytes = 2 * 2 * tp.T * (tp.Hq + tp.Hkv) * tp.D + 4 * tp.T + 2 * 2 * tp.D
+    cflops = tp.causal_flops()
+    ct = cflops / (te_ms["varlen_attn_causal_fwd"] * 1e-3) / 1e12
+    qg = qn_bytes / (te_ms["qk_norm_rope"] * 1e-3) / 1e9
+    text_encoder = {
+        "workload": f"{tp.name}: {len(tp.lens)} prompts U{{64..512}}, T={tp.T}, Hq={tp.Hq}, Hkv={tp.Hkv}, "
+                    f"D={tp.D}", "input_sets": len(tsets),
+        "kernels": {
+            "qk_norm_rope": {"ms": round(te_ms["qk_norm_rope"], 5), "algorithmic_bytes": qn_bytes,
+                             "GB/s": round(qg, 1), "frac_hbm_peak": round(qg / PEAK_HBM_GBS, 4)},
+            "varlen_attn_causal_fwd": {"ms": round(te_ms["varlen_attn_causal_fwd"], 5), "causal_flops": cflops,
+                                       "TFLOP/s": round(ct, 2), "frac_bf16_peak": round(ct / PEAK_BF16_TFLOPS, 4)}}}
+    del tsets
+
     if args.copy_calib_mb:
         n = args.copy_calib_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -346,6 +396,7 @@ def main():
         "backward": backward,
         "block": block,
         "sampler": sampler,
+        "text_encoder": text_encoder,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

@@ -445,13 +445,14 @@ mf_status mf_prompt_tables(const int32_t* lens, int32_t n, int32_t* cu_seqlens, 
  * q, o: bf16 [T][Hq][D] (token strides ld_q, ld_o); k, v: bf16
  *   [T][Hkv][D] sharing token stride ld_kv; strides multiples of 8; o must
  *   not overlap q, k or v.  lse: NULL or fp32 [Hq][T].
- * workspace: >= mf_varlen_attn_causal_workspace_bytes(n_seq) bytes, 8-byte
- *   aligned, caller-owned, one call at a time per workspace.
+ * workspace: >= mf_varlen_attn_causal_workspace_bytes(n_seq, T) bytes
+ *   (16 * (T / 32 + n_seq + 1): one work descriptor per slab of queries),
+ *   16-byte aligned, caller-owned, one call at a time per workspace.
  * Hq a multiple of Hkv; D in {64, 128}; T * ld_q * 2 and T * ld_kv * 2
  * below 2^32.  T = 0 or n_seq = 0 is a no-op.
  * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
  * MF_ERR_WORKSPACE, MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
-size_t mf_varlen_attn_causal_workspace_bytes(int32_t n_seq);
+size_t mf_varlen_attn_causal_workspace_bytes(int32_t n_seq, int64_t T);
 
 mf_status mf_varlen_attn_causal_fwd(void* stream,
                                     const void* q, int64_t ld_q, const void* k, const void* v,

@@ -536,7 +536,9 @@ mf_status mf_qk_norm_rope(void* stream, const void* q_in, int64_t ld_q, const vo
     return finish(mf::launch_qk_norm_rope(a, s), s);
 }
 
-size_t mf_varlen_attn_causal_workspace_bytes(int32_t n_seq) { return mf::causal_attn_workspace_bytes(n_seq); }
+size_t mf_varlen_attn_causal_workspace_bytes(int32_t n_seq, int64_t T) {
+    return mf::causal_attn_workspace_bytes(n_seq, T);
+}
 
 mf_status mf_varlen_attn_causal_fwd(void* stream, const void* q, int64_t ld_q, const void* k, const void* v,
                                     int64_t ld_kv, void* o, int64_t ld_o, float* lse, const int32_t* cu_seqlens,
@@ -553,8 +555,8 @@ mf_status mf_varlen_attn_causal_fwd(void* stream, const void* q, int64_t ld_q, c
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(cu_seqlens, 4) ||
         (lse && !aligned(lse, 4)))
         return MF_ERR_ALIGN;
-    if (workspace == nullptr || workspace_bytes < mf::causal_attn_workspace_bytes(n_seq)) return MF_ERR_WORKSPACE;
-    if (!aligned(workspace, 8)) return MF_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < mf::causal_attn_workspace_bytes(n_seq, T)) return MF_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return MF_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (debug_mode()) {
         std::vector<int32_t> hc;

@@ -218,9 +218,9 @@ struct CausalAttnArgs {
     int32_t Hq, Hkv, D;
     int64_t ld_q, ld_kv, ld_o;
     float softmax_scale;
-    void* workspace;          // int64 [n_seq + 1]
+    void* workspace;          // slab descriptors, causal_attn_workspace_bytes
 };
-size_t causal_attn_workspace_bytes(int32_t n_seq);
+size_t causal_attn_workspace_bytes(int32_t n_seq, int64_t T);
 hipError_t launch_varlen_attn_causal(const CausalAttnArgs& a, hipStream_t stream);
 
 }  // namespace mf

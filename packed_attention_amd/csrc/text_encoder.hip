@@ -20,16 +20,22 @@
 //    e0 = 8 (l mod D/8), so the four rotation angles of a lane are computed
 //    once per token and a head's sum of squares is a reduction over the D/8
 //    lanes that hold it (DPP inside a 16-lane row).
-//  * attn_causal_kernel<D>: a work unit is 128 queries of one query head of
-//    one prompt (4 wavefronts, 32 queries each; two workgroups per CU), a
-//    one-workgroup prologue numbers the units.  The unit walks the key tiles
-//    of 64 up to its diagonal only; K and V tiles of the grouped key/value
-//    head are staged through registers one tile ahead into two LDS buffers.
-//    Per tile a wavefront computes S^T = K Q^T (each lane: one query, 16 keys
-//    per 32-key block), masks keys past the query or past the prompt on the
-//    tiles that reach them, runs the online softmax with a lazily raised
-//    reference max, and accumulates O^T += V^T P^T with V^T read transposed
-//    from LDS (ds_read_b64_tr_b16) and P^T rounded to bf16 in registers.
+//  * attn_causal_kernel<D>: a workgroup of 4 wavefronts covers gb query
+//    heads of one key/value group (gb = 4 when the group size allows it) and
+//    a slab of 128 / gb queries of one prompt, so the heads that share K and V
+//    share its tiles and, with gb = 4, all four wavefronts stop at the same
+//    diagonal.  A one-workgroup prologue writes one descriptor per (prompt,
+//    slab), the slabs of a prompt from the last to the first; the workgroups
+//    of one XCD take contiguous descriptors (all heads of a slab, then the
+//    next slab of the prompt), so a prompt's K and V meet in one L2.  The
+//    unit walks the key tiles of 64 up to its diagonal only; K and V tiles are
+//    staged through registers one tile ahead into two LDS buffers.  Per tile
+//    a wavefront computes S^T = K Q^T (each lane: one query, 16 keys per
+//    32-key block), masks keys past the query or past the prompt on the tiles
+//    that reach them, runs the online softmax with a lazily raised reference
+//    max, and accumulates O^T += V^T P^T with V^T read transposed from LDS
+//    (ds_read_b64_tr_b16) and P^T rounded to bf16 in registers.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -125,68 +131,91 @@ hipError_t launch_qknorm_d(const QkNormRopeArgs& a, hipStream_t stream) {
 // Causal attention with grouped key/value heads
 // ---------------------------------------------------------------------------
 constexpr int kCW = 4;                 // wavefronts per workgroup
-constexpr int kCM = 32 * kCW;          // queries per work unit
 constexpr int kCN = 64;                // keys per tile
+constexpr int kSlabMin = 32;           // smallest query slab (four grouped heads)
+constexpr int kWgPerCu = 2;            // resident workgroups per CU (LDS and VGPR bound)
+constexpr int kClasses = 1024;         // work classes (key-tile counts) of the longest-first order
+static_assert(kClasses % 256 == 0, "whole classes per prologue thread");
 constexpr float kRescale = 8.0f;       // lazy-rescale threshold (log2 units)
 
 template <int D>
 struct CT {
     static constexpr int KK = D / 16;
     static constexpr int EB = D / 32;
-    static constexpr int KCH = D / 8;
-    static constexpr int K_ROW = 16 * (KCH + 1);     // conflict-free 16-byte row reads
-    static constexpr int V_ROW = 16 * (KCH + 4);     // conflict-free transposed reads
+    static constexpr int KCH = D / 8;                // 16-byte chunks per row
+    static constexpr int K_UNITS = KCH + 1;          // K row: chunks + 1 pad (conflict-free row reads)
+    static constexpr int V_UNITS = KCH + 4;          // V row: chunks + 4 pad (conflict-free transposed reads)
+    static constexpr int K_ROW = 16 * K_UNITS;
+    static constexpr int V_ROW = 16 * V_UNITS;
     static constexpr int K_BYTES = kCN * K_ROW;
     static constexpr int V_BYTES = kCN * V_ROW;
     static constexpr int STAGE = K_BYTES + V_BYTES;
     static constexpr int LDS = 2 * STAGE;
-    static constexpr int STAGE_CH = kCN * KCH / (64 * kCW);   // 16-byte chunks per thread per tile
-    static_assert(kCN * KCH % (64 * kCW) == 0, "whole staging chunks");
+    // direct loads per tile (64 lanes x 16 bytes each) and per wavefront
+    static constexpr int K_DMA = kCN * K_UNITS / 64;
+    static constexpr int V_DMA = kCN * V_UNITS / 64;
+    static constexpr int K_DMA_W = (K_DMA + kCW - 1) / kCW;
+    static constexpr int V_DMA_W = (V_DMA + kCW - 1) / kCW;
+    static_assert(kCN * K_UNITS % 64 == 0 && kCN * V_UNITS % 64 == 0, "whole direct loads");
+    static_assert(kWgPerCu * LDS <= 160 * 1024, "resident workgroups fit the LDS");
 };
 
-// Per-prompt query-tile counts and their prefix sums (one workgroup).
-__global__ __launch_bounds__(256) void causal_tiles_kernel(const int32_t* __restrict__ cu, int n,
-                                                           int64_t* __restrict__ pre) {
-    __shared__ int64_t part[256];
+// Heads of one key/value group that share a workgroup: the largest of 4, 2, 1
+// dividing the group size.  The workgroup's four wavefronts cover those heads
+// times 128 / gb queries (a slab) of one prompt.
+__host__ __device__ constexpr int heads_per_wg(int group) { return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1; }
+
+// Key tiles that slab j (sq queries) of a prompt of length L walks.
+__device__ __forceinline__ int slab_tiles(int L, int j, int sq) { return (min(L, j * sq + sq) - 1) / kCN + 1; }
+
+// Slab descriptors {first token, prompt length, slab index, 0}, one per
+// (prompt, slab), sorted by key-tile count, longest first (a counting sort;
+// the order inside a class is arbitrary and does not affect any result);
+// entry max_slabs holds the slab count.  One workgroup.
+__global__ __launch_bounds__(256) void causal_slabs_kernel(const int32_t* __restrict__ cu, int n, int sq,
+                                                           int max_slabs, int4* __restrict__ desc) {
+    __shared__ int cls[kClasses];
     const int tid = threadIdx.x;
+    for (int c = tid; c < kClasses; c += 256) cls[c] = 0;
+    __syncthreads();
     const int per = (n + 255) / 256;
     const int s0 = min(n, tid * per), s1 = min(n, s0 + per);
-    int64_t acc = 0;
-    for (int s = s0; s < s1; ++s) acc += (cu[s + 1] - cu[s] + kCM - 1) / kCM;
-    part[tid] = acc;
-    __syncthreads();
-    if (tid == 0) {
-        int64_t r = 0;
-        for (int i = 0; i < 256; ++i) {
-            const int64_t v = part[i];
-            part[i] = r;
-            r += v;
-        }
-        pre[n] = r;
-    }
-    __syncthreads();
-    int64_t b = part[tid];
     for (int s = s0; s < s1; ++s) {
-        pre[s] = b;
-        b += (cu[s + 1] - cu[s] + kCM - 1) / kCM;
+        const int L = cu[s + 1] - cu[s];
+        for (int j = 0, ns = (L + sq - 1) / sq; j < ns; ++j) atomicAdd(&cls[min(slab_tiles(L, j, sq), kClasses - 1)], 1);
     }
-}
-
-// Work unit -> (prompt, query head, tile); units of prompt s are
-// [pre[s] H, pre[s+1] H), head-major.  False past the last unit.
-__device__ bool causal_unit(const int64_t* pre, int n, int H, int64_t unit, int& s, int& h, int& tile) {
-    if (unit >= pre[n] * H) return false;
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] * H <= unit) lo = mid; else hi = mid - 1;
+    __syncthreads();
+    // exclusive offsets of the classes, longest first: thread k owns classes
+    // kClasses-1-4k .. kClasses-4-4k; a scan of the 256 partial sums
+    constexpr int kPer = kClasses / 256;
+    __shared__ int part[256];
+    int own[kPer], sum = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        own[e] = cls[kClasses - 1 - (kPer * tid + e)];
+        sum += own[e];
     }
-    const int64_t local = unit - pre[lo] * H;
-    const int64_t tiles = pre[lo + 1] - pre[lo];
-    s = lo;
-    h = int(local / tiles);
-    tile = int(local - int64_t(h) * tiles);
-    return true;
+    part[tid] = sum;
+    __syncthreads();
+    for (int d = 1; d < 256; d *= 2) {
+        const int v = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int r = part[tid] - sum;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        cls[kClasses - 1 - (kPer * tid + e)] = r;
+        r += own[e];
+    }
+    if (tid == 255) desc[max_slabs] = int4{r, 0, 0, 0};
+    __syncthreads();
+    for (int s = s0; s < s1; ++s) {
+        const int a = cu[s], L = cu[s + 1] - a;
+        for (int j = 0, ns = (L + sq - 1) / sq; j < ns; ++j)
+            desc[atomicAdd(&cls[min(slab_tiles(L, j, sq), kClasses - 1)], 1)] = int4{a, L, j, 0};
+    }
 }
 
 __device__ __forceinline__ float half_max32(float x) {
@@ -204,192 +233,291 @@ struct CausalParams {
     const uint16_t* v;
     uint16_t* o;
     float* lse;
-    const int32_t* cu;
-    const int64_t* pre;
-    int n_seq, Hq, Hkv;
+    const int4* desc;
+    int max_slabs;
+    int Hq, Hkv;
+    int gb;             // heads per workgroup
+    int hg;             // workgroups per slab: Hkv * (Hq / Hkv) / gb
     int64_t T, ld_q, ld_kv, ld_o;
     float c;            // softmax scale * log2(e)
+};
+
+// One unit of work as the workgroup sees it (all wavefront-uniform).
+struct CUnit {
+    int tok0, L, j, hgi;
 };
 
 template <int D>
 __global__ __launch_bounds__(64 * kCW) void attn_causal_kernel(CausalParams p) {
     using TL = CT<D>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    int seq, head, tile;
-    if (!causal_unit(p.pre, p.n_seq, p.Hq, blockIdx.x, seq, head, tile)) return;
-    seq = __builtin_amdgcn_readfirstlane(seq);
-    head = __builtin_amdgcn_readfirstlane(head);
-    tile = __builtin_amdgcn_readfirstlane(tile);
-    const int kvh = head / (p.Hq / p.Hkv);
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hlf = lane >> 5;
-    const int64_t tok0 = __builtin_amdgcn_readfirstlane(p.cu[seq]);
-    const int L = __builtin_amdgcn_readfirstlane(p.cu[seq + 1]) - int(tok0);
+    const int group = p.Hq / p.Hkv;
+    const int ns = group / p.gb;                 // head groups per key/value head
+    const int sq = 128 / p.gb;                   // queries per slab
+    const int G = gridDim.x, b = blockIdx.x;
     const uint32_t qrow = uint32_t(p.ld_q) * 2u, kvrow = uint32_t(p.ld_kv) * 2u;
-    const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(p.q + tok0 * p.ld_q + int64_t(head) * D, uint64_t(L) * qrow);
-    const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(p.k + tok0 * p.ld_kv + int64_t(kvh) * D, uint64_t(L) * kvrow);
-    const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(p.v + tok0 * p.ld_kv + int64_t(kvh) * D, uint64_t(L) * kvrow);
+    const __amdgpu_buffer_rsrc_t desc_rs = make_rsrc(p.desc, uint64_t(p.max_slabs + 1) * 16u);
+    const int W = __builtin_amdgcn_readfirstlane(int(bload16(desc_rs, 0, uint32_t(p.max_slabs) * 16u)[0])) * p.hg;
 
-    // the wavefront's 32 queries (B operand of S^T = K Q^T)
-    const int q0 = tile * kCM + wave * 32;
-    const int qi = q0 + l32;                     // this lane's query, inside the prompt
-    bf16x8_t qf[TL::KK];
-    {
-        const uint32_t off = uint32_t(qi) * qrow + 16u * hlf;
+    // unit i of this workgroup: snake order over the longest-first list
+    auto unit_of = [&](int i) { return i * G + ((i & 1) ? G - 1 - b : b); };
+    // descriptor of unit i as a vector load (zeros, length 0, past the end)
+    auto load_desc = [&](int i) -> u32x4_t {
+        const int w = unit_of(i);
+        u32x4_t d = bload16(desc_rs, 0, uint32_t(w < W ? w / p.hg : p.max_slabs + 1) * 16u);
+        return d;
+    };
+    auto decode = [&](u32x4_t d, int i) {
+        CUnit u;
+        u.tok0 = __builtin_amdgcn_readfirstlane(int(d[0]));
+        u.L = __builtin_amdgcn_readfirstlane(int(d[1]));
+        u.j = __builtin_amdgcn_readfirstlane(int(d[2]));
+        u.hgi = unit_of(i) % p.hg;
+        if (unit_of(i) >= W) u.L = 0;
+        return u;
+    };
+    auto kvh_of = [&](const CUnit& u) { return u.hgi / ns; };
+    auto head_of = [&](const CUnit& u) { return kvh_of(u) * group + (u.hgi % ns) * p.gb + wave % p.gb; };
+    auto q0_of = [&](const CUnit& u) { return u.j * sq + (wave / p.gb) * 32; };
+    auto tiles_of = [&](const CUnit& u) { return (min(u.L, u.j * sq + sq) - 1) / kCN + 1; };
+
+    // Q fragments of a unit: lane holds query q0 + l32 (B operand of S^T = K Q^T)
+    auto q_load = [&](const CUnit& u, bf16x8_t* dst) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.q + int64_t(u.tok0) * p.ld_q + int64_t(head_of(u)) * D,
+                                                    uint64_t(u.L) * qrow);
+        const uint32_t off = uint32_t(q0_of(u) + l32) * qrow + 16u * hlf;
 #pragma unroll
-        for (int kk = 0; kk < TL::KK; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, bload16(q_rs, off, 32u * kk));
+        for (int kk = 0; kk < TL::KK; ++kk) dst[kk] = __builtin_bit_cast(bf16x8_t, bload16(rs, off, 32u * kk));
+    };
+
+    // Direct global->LDS loads of a key tile.  Instruction n of a tile fills
+    // LDS units [64n, 64n+64) of the padded K (or V) image: lane l fetches
+    // unit 64n+l = (row, chunk); pad units fetch the row's last chunk again
+    // (never read back).  Instruction n is issued by wavefront n % 4.  The
+    // resource starts at the tile's first row, so rows past the prompt read
+    // as zeros.
+    uint32_t k_off[TL::K_DMA_W], v_off[TL::V_DMA_W];
+#pragma unroll
+    for (int m = 0; m < TL::K_DMA_W; ++m) {
+        const int u = 64 * (wave + kCW * m) + lane;
+        k_off[m] = uint32_t(u / TL::K_UNITS) * kvrow + 16u * uint32_t(min(u % TL::K_UNITS, TL::KCH - 1));
     }
-    // key tiles up to the unit's last query (and the prompt's end)
-    const int last_q = min(L - 1, tile * kCM + kCM - 1);
-    const int nt = last_q / kCN + 1;
-
-    u32x4_t sk[TL::STAGE_CH], sv[TL::STAGE_CH];
-    auto st_row = [&](int j) { return (tid + 64 * kCW * j) / TL::KCH; };
-    auto st_col = [&](int j) { return (tid + 64 * kCW * j) % TL::KCH; };
-    auto stage_load = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < TL::STAGE_CH; ++j) {
-            const uint32_t off = uint32_t(t * kCN + st_row(j)) * kvrow + 16u * st_col(j);
-            sk[j] = bload16(k_rs, off, 0);
-            sv[j] = bload16(v_rs, off, 0);
-        }
-    };
-    auto stage_store = [&](int b) {
-        unsigned char* base = smem + b * TL::STAGE;
+    for (int m = 0; m < TL::V_DMA_W; ++m) {
+        const int u = 64 * (wave + kCW * m) + lane;
+        v_off[m] = uint32_t(u / TL::V_UNITS) * kvrow + 16u * uint32_t(min(u % TL::V_UNITS, TL::KCH - 1));
+    }
+    auto stage = [&](const CUnit& u, int t, unsigned char* kb) {
+        const int64_t base = int64_t(u.tok0) * p.ld_kv + int64_t(kvh_of(u)) * D;
+        const uint64_t bytes = uint64_t(u.L) * kvrow;
+        const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(p.k + base, bytes);
+        const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(p.v + base, bytes);
+        const uint32_t tile_off = uint32_t(t) * kCN * kvrow;   // range-checked like the lane offset
 #pragma unroll
-        for (int j = 0; j < TL::STAGE_CH; ++j) {
-            *reinterpret_cast<u32x4_t*>(base + st_row(j) * TL::K_ROW + 16 * st_col(j)) = sk[j];
-            *reinterpret_cast<u32x4_t*>(base + TL::K_BYTES + st_row(j) * TL::V_ROW + 16 * st_col(j)) = sv[j];
-        }
+        for (int m = 0; m < TL::K_DMA_W; ++m)
+            if (TL::K_DMA % kCW == 0 || wave + kCW * m < TL::K_DMA)
+                dma16(k_rs, kb + 1024 * (wave + kCW * m), k_off[m], tile_off);
+#pragma unroll
+        for (int m = 0; m < TL::V_DMA_W; ++m)
+            if (TL::V_DMA % kCW == 0 || wave + kCW * m < TL::V_DMA)
+                dma16(v_rs, kb + TL::K_BYTES + 1024 * (wave + kCW * m), v_off[m], tile_off);
     };
 
-    f32x16_t oacc[TL::EB];
-#pragma unroll
-    for (int m = 0; m < TL::EB; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[m][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    if (b >= W) return;
+    CUnit cur = decode(load_desc(0), 0);
+    bf16x8_t qf[TL::KK];
+    q_load(cur, qf);
+    stage(cur, 0, smem);
+    CUnit nxt = decode(load_desc(1), 1);
+    u32x4_t d2 = load_desc(2);
+    __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): first tile, Q and descriptors in
+    __syncthreads();
+
     const float c = p.c;
     const int k_rd = l32 * TL::K_ROW + hlf * 16;
     const int v_rd = (4 * hlf + ((lane & 15) >> 2)) * TL::V_ROW + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    f32x16_t oacc[TL::EB];          // set on each unit's first tile
+    float m_run = -INFINITY, l_run = 0.f;
+    int buf = 0;
 
-    stage_load(0);
-    stage_store(0);
-    __syncthreads();
-    for (int t = 0; t < nt; ++t) {
-        if (t + 1 < nt) stage_load(t + 1);
-        const unsigned char* kt = smem + (t & 1) * TL::STAGE;
-        const unsigned char* vt = kt + TL::K_BYTES;
-        // S^T = K Q^T: two 32-key blocks (lane: query qi, register r: key
-        // 32 b + 8 (r/4) + 4 h + r%4 of the tile)
-        f32x16_t s[2];
+    // One key tile t of the current unit on LDS buffer `buf`, with the next
+    // tile (this unit's t+1 or, on the last tile, the next unit's first)
+    // fetched into the other buffer.  First: the accumulators start at zero.
+    // Last: the next unit's Q is loaded into qf once the scores are formed,
+    // and the unit's output is written.
+    // The buffer read (kt) and the one filled (nb) are restrict pointers: the
+    // compiler then knows that the direct loads into nb do not feed this
+    // step's LDS reads and does not wait for them before the first read.
+    auto step = [&](auto first_c, auto last_c, const int t, const bool more, const unsigned char* __restrict__ kt,
+                    unsigned char* __restrict__ nb) {
+        constexpr bool kFirst = decltype(first_c)::value, kLast = decltype(last_c)::value;
+        const unsigned char* const vt = kt + TL::K_BYTES;
+        // nb was last read in the previous step, finished by everyone before
+        // the barrier that opened this one
+        if (more) {
+            if constexpr (kLast) stage(nxt, 0, nb);
+            else stage(cur, t + 1, nb);
+        }
+        const int q0 = q0_of(cur);
+        // S^T = K Q^T: two 32-key blocks (lane: query q0 + l32, register r:
+        // key 32 b + 8 (r/4) + 4 h + r%4 of the tile)
+        f32x16_t sc[2];
 #pragma unroll
         for (int kk = 0; kk < TL::KK; ++kk)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + k_rd + b * 32 * TL::K_ROW + kk * 32);
-                s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], kk == 0 ? f32x16_t{} : s[b], 0, 0, 0);
+            for (int bb = 0; bb < 2; ++bb) {
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + k_rd + bb * 32 * TL::K_ROW + kk * 32);
+                sc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], kk == 0 ? f32x16_t{} : sc[bb], 0, 0, 0);
             }
-        // keys past the query (causal) or past the prompt: only tiles that
-        // reach the wavefront's first query or the prompt's end
-        if ((t + 1) * kCN - 1 > q0 || (t + 1) * kCN > L) {
+        if constexpr (kLast) q_load(nxt, qf);     // length 0 past the end: zeros, no access
+        // keys past the query (causal) or past the prompt: only on the tiles
+        // that reach the wavefront's first query or the prompt's end
+        if ((t + 1) * kCN - 1 > q0 || (t + 1) * kCN > cur.L) {
+            const int lim = min(q0 + l32, cur.L - 1) - 4 * hlf - t * kCN;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = t * kCN + 32 * b + 8 * (r >> 2) + 4 * hlf + (r & 3);
-                    if (key > qi || key >= L) s[b][r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (32 * bb + 8 * (r >> 2) + (r & 3) > lim) sc[bb][r] = -INFINITY;
         }
         // online softmax, reference max raised lazily (numerator and
-        // denominator share it, so the result is the same softmax)
-        float mx = fmaxf(s[0][0], s[0][1]);
+        // denominator share it, so the result is the same softmax); on a
+        // unit's first tile the max is taken as it is
+        float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-            for (int r = (b == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+            for (int r = (bb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, sc[bb][r]);
         mx = half_max32(mx) * c;
-        const bool raise = mx > m_run + kRescale;
-        if (__any(raise)) {
-            const float m_new = raise ? mx : m_run;
-            const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+        if constexpr (kFirst) {
+            m_run = mx;
+        } else {
+            const bool raise = mx > m_run + kRescale;
+            if (__any(raise)) {
+                const float m_new = raise ? mx : m_run;
+                const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
 #pragma unroll
-            for (int m = 0; m < TL::EB; ++m)
+                for (int m = 0; m < TL::EB; ++m)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
+            }
         }
         float lsum = 0.f;
         bf16x8_t pf[4];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            const int b = cc >> 1, r0 = 8 * (cc & 1);
+            const int bb = cc >> 1, r0 = 8 * (cc & 1);
             float e[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r0 + i], c, -m_run));
-                lsum += e[i];
+            for (int ii = 0; ii < 8; ++ii) {
+                e[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[bb][r0 + ii], c, -m_run));
+                lsum += e[ii];
             }
             u32x4_t u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) u[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
+            for (int ii = 0; ii < 4; ++ii) u[ii] = pack_bf16x2(e[2 * ii], e[2 * ii + 1]);
             pf[cc] = __builtin_bit_cast(bf16x8_t, u);
         }
-        l_run += lsum;
+        l_run = kFirst ? lsum : l_run + lsum;
         // O^T += V^T P^T over the four 16-key chunks
 #pragma unroll
-        for (int j = 0; j < 4 * TL::EB; ++j) {
-            const unsigned char* ad = vt + v_rd + (j / TL::EB) * 16 * TL::V_ROW + (j % TL::EB) * 64;
+        for (int jj = 0; jj < 4 * TL::EB; ++jj) {
+            const unsigned char* ad = vt + v_rd + (jj / TL::EB) * 16 * TL::V_ROW + (jj % TL::EB) * 64;
             const s16x4_t lo = lds_read_tr16_b64(ad);
             const s16x4_t hi = lds_read_tr16_b64(ad + 8 * TL::V_ROW);
             const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[j % TL::EB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j / TL::EB], oacc[j % TL::EB], 0, 0, 0);
+            oacc[jj % TL::EB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                vf, pf[jj / TL::EB], (kFirst && jj < TL::EB) ? f32x16_t{} : oacc[jj % TL::EB], 0, 0, 0);
         }
-        // the other buffer was last read in step t-1, finished by everyone
-        // before the barrier that opened step t
-        if (t + 1 < nt) stage_store((t + 1) & 1);
-        __syncthreads();
-    }
-
-    const float l_tot = half_sum32(l_run);
-    if (qi < L) {
-        const float inv = 1.0f / l_tot;
-        uint16_t* op = p.o + (tok0 + qi) * p.ld_o + int64_t(head) * D + 4 * hlf;
+        if constexpr (kLast) {
+            // the unit's output rows (queries inside the prompt) and LSE
+            const int qi = q0 + l32;
+            const float l_tot = half_sum32(l_run);
+            if (qi < cur.L) {
+                const int head = head_of(cur);
+                const float inv = 1.0f / l_tot;
+                uint16_t* op = p.o + (int64_t(cur.tok0) + qi) * p.ld_o + int64_t(head) * D + 4 * hlf;
 #pragma unroll
-        for (int m = 0; m < TL::EB; ++m)
+                for (int m = 0; m < TL::EB; ++m)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2_t val;
-                val[0] = pack_bf16x2(oacc[m][4 * g] * inv, oacc[m][4 * g + 1] * inv);
-                val[1] = pack_bf16x2(oacc[m][4 * g + 2] * inv, oacc[m][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2_t*>(op + 32 * m + 8 * g) = val;
+                    for (int g = 0; g < 4; ++g) {
+                        u32x2_t val;
+                        val[0] = pack_bf16x2(oacc[m][4 * g] * inv, oacc[m][4 * g + 1] * inv);
+                        val[1] = pack_bf16x2(oacc[m][4 * g + 2] * inv, oacc[m][4 * g + 3] * inv);
+                        *reinterpret_cast<u32x2_t*>(op + 32 * m + 8 * g) = val;
+                    }
+                if (p.lse != nullptr && hlf == 0)
+                    p.lse[int64_t(head) * p.T + cur.tok0 + qi] = m_run * 0.69314718055994531f + logf(l_tot);
             }
-        if (p.lse != nullptr && hlf == 0) p.lse[int64_t(head) * p.T + tok0 + qi] = m_run * 0.69314718055994531f + logf(l_tot);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): the next tile (and Q) landed
+        __syncthreads();
+    };
+    auto run = [&](auto first_c, auto last_c, const int t, const bool more) {
+        step(first_c, last_c, t, more, smem + buf * TL::STAGE, smem + (buf ^ 1) * TL::STAGE);
+        buf ^= 1;
+    };
+
+    for (int i = 0;;) {
+        const int nt = tiles_of(cur);
+        const bool more = nxt.L > 0;
+        if (nt == 1) {
+            run(std::true_type{}, std::true_type{}, 0, more);
+        } else {
+            run(std::true_type{}, std::false_type{}, 0, true);
+            for (int t = 1; t + 1 < nt; ++t) run(std::false_type{}, std::false_type{}, t, true);
+            run(std::false_type{}, std::true_type{}, nt - 1, more);
+        }
+        if (!more) break;
+        // next unit: its first tile is in LDS and its Q in registers; fetch
+        // the descriptor of the one after the next
+        ++i;
+        cur = nxt;
+        nxt = decode(d2, i + 1);
+        d2 = load_desc(i + 2);
     }
+}
+
+int causal_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
 }
 
 template <int D>
 hipError_t launch_causal_d(const CausalAttnArgs& a, hipStream_t stream) {
     CausalParams p;
-    p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse; p.cu = a.cu_seqlens;
-    p.pre = static_cast<const int64_t*>(a.workspace);
-    p.n_seq = a.n_seq; p.Hq = a.Hq; p.Hkv = a.Hkv;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o; p.lse = a.lse;
+    p.desc = static_cast<const int4*>(a.workspace);
+    p.Hq = a.Hq; p.Hkv = a.Hkv;
+    p.gb = heads_per_wg(a.Hq / a.Hkv);
+    p.hg = a.Hkv * (a.Hq / a.Hkv / p.gb);
     p.T = a.T; p.ld_q = a.ld_q; p.ld_kv = a.ld_kv; p.ld_o = a.ld_o;
     p.c = a.softmax_scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(causal_tiles_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.n_seq,
-                       static_cast<int64_t*>(a.workspace));
+    const int sq = 128 / p.gb;
+    // upper bound of the slab count: sum_s ceil(L_s / sq) <= T / sq + n_seq
+    const int64_t max_slabs = a.T / sq + a.n_seq;
+    if (max_slabs * p.hg > INT32_MAX / 2) return hipErrorInvalidValue;
+    p.max_slabs = int(max_slabs);
+    const int cus = causal_cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    hipLaunchKernelGGL(causal_slabs_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.n_seq, sq,
+                       int(max_slabs), static_cast<int4*>(a.workspace));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_causal_kernel<D>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, CT<D>::LDS);
     if (attr != hipSuccess) return attr;
-    // upper bound of the unit count: sum_s ceil(L_s / kCM) <= T / kCM + n_seq
-    const int64_t units = int64_t(a.Hq) * (a.T / kCM + a.n_seq);
-    hipLaunchKernelGGL(attn_causal_kernel<D>, dim3(unsigned(units)), dim3(64 * kCW), CT<D>::LDS, stream, p);
+    const int64_t grid = std::min<int64_t>(int64_t(kWgPerCu) * cus, max_slabs * p.hg);
+    hipLaunchKernelGGL(attn_causal_kernel<D>, dim3(unsigned(grid)), dim3(64 * kCW), CT<D>::LDS, stream, p);
     return hipGetLastError();
 }
 
@@ -403,8 +531,10 @@ hipError_t launch_qk_norm_rope(const QkNormRopeArgs& args, hipStream_t stream) {
     return a.D == 128 ? launch_qknorm_d<128>(a, stream) : launch_qknorm_d<64>(a, stream);
 }
 
-size_t causal_attn_workspace_bytes(int32_t n_seq) {
-    return size_t(n_seq < 0 ? 0 : n_seq + 1) * sizeof(int64_t);
+size_t causal_attn_workspace_bytes(int32_t n_seq, int64_t T) {
+    if (n_seq < 0 || T < 0) return 0;
+    // one descriptor per slab of the smallest size, then the slab count
+    return size_t(T / kSlabMin + n_seq + 1) * sizeof(int4);
 }
 
 hipError_t launch_varlen_attn_causal(const CausalAttnArgs& a, hipStream_t stream) {

@@ -105,7 +105,7 @@ def lib() -> ctypes.CDLL:
     L.mf_cfg_euler_step.restype = i32
     L.mf_qk_norm_rope.argtypes = [vp, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, vp, i64, i32, i32, i32, f32, f32]
     L.mf_qk_norm_rope.restype = i32
-    L.mf_varlen_attn_causal_workspace_bytes.argtypes = [i32]
+    L.mf_varlen_attn_causal_workspace_bytes.argtypes = [i32, i64]
     L.mf_varlen_attn_causal_workspace_bytes.restype = sz
     L.mf_varlen_attn_causal_fwd.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, i32, i64, i32, i32, i32, f32,
                                             vp, sz]
@@ -452,9 +452,9 @@ def varlen_attn_causal_fwd(q, k, v, o, cu_seqlens, lse=None, softmax_scale=None,
     n_seq = cu_seqlens.numel() - 1
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
-    need = int(lib().mf_varlen_attn_causal_workspace_bytes(n_seq))
+    need = int(lib().mf_varlen_attn_causal_workspace_bytes(n_seq, T))
     if workspace is None:
-        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     check(lib().mf_varlen_attn_causal_fwd(_stream(stream), _ptr(q), _token_stride(q, Hq * D), _ptr(k), _ptr(v),
                                           ld_kv, _ptr(o), _token_stride(o, Hq * D), _ptr(lse), _ptr(cu_seqlens),
                                           n_seq, T, Hq, Hkv, D, float(softmax_scale), _ptr(workspace),

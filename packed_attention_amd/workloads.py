@@ -286,6 +286,10 @@ class TextPack:
         return 4.0 * self.D * self.Hq * sum(L * (L + 1) / 2 for L in self.lens)
 
 
+TEXT_BENCH_SEED = 1006
+TEXT_BENCH_PROMPTS = 64
+
+
 def text_pack(seed: int = 1005, n_prompts: int = 16, Hq: int = 32, Hkv: int = 8, D: int = 128,
               lens: Optional[Sequence[int]] = None, name: str = "text_pack") -> TextPack:
     """Packed prompts: lengths U{64..512} (the prompt lengths of the packed

@@ -313,10 +313,11 @@ def test_text_encoder_validation():
     assert causal(ld_o=260) == ALIGN
     assert causal(lse=P + 2) == ALIGN
     assert causal() == WS
-    assert causal(ws=P, ws_bytes=8) == WS
-    assert causal(ws=P + 4, ws_bytes=64) == ALIGN
+    assert causal(ws=P, ws_bytes=32) == WS       # T=4, n=2: (0 + 2 + 1) descriptors of 16 bytes
+    assert causal(ws=P + 8, ws_bytes=64) == ALIGN
     assert causal(n=0, q=None) == 0
-    assert native.lib().mf_varlen_attn_causal_workspace_bytes(16) == 17 * 8
+    assert native.lib().mf_varlen_attn_causal_workspace_bytes(16, 4096) == (128 + 16 + 1) * 16
+    assert native.lib().mf_varlen_attn_causal_workspace_bytes(-1, 4) == 0
 
 
 def test_library_has_no_oracle_dependency():

@@ -84,6 +84,11 @@ def test_text_pack_full():
     check_pack(W.text_pack())
 
 
+def test_text_pack_bench_size():
+    """The 64-prompt pack the benchmark times, every element."""
+    check_pack(W.text_pack(seed=W.TEXT_BENCH_SEED, n_prompts=W.TEXT_BENCH_PROMPTS, name="text_pack_64"))
+
+
 def test_first_token_attends_to_itself():
     """Closed form on the GPU: every prompt's first token outputs its own v."""
     import torch
