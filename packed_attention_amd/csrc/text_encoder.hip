@@ -20,21 +20,24 @@
 //    e0 = 8 (l mod D/8), so the four rotation angles of a lane are computed
 //    once per token and a head's sum of squares is a reduction over the D/8
 //    lanes that hold it (DPP inside a 16-lane row).
-//  * attn_causal_kernel<D>: a workgroup of 4 wavefronts covers gb query
-//    heads of one key/value group (gb = 4 when the group size allows it) and
-//    a slab of 128 / gb queries of one prompt, so the heads that share K and V
-//    share its tiles and, with gb = 4, all four wavefronts stop at the same
-//    diagonal.  A one-workgroup prologue writes one descriptor per (prompt,
-//    slab), the slabs of a prompt from the last to the first; the workgroups
-//    of one XCD take contiguous descriptors (all heads of a slab, then the
-//    next slab of the prompt), so a prompt's K and V meet in one L2.  The
-//    unit walks the key tiles of 64 up to its diagonal only; K and V tiles are
-//    staged through registers one tile ahead into two LDS buffers.  Per tile
-//    a wavefront computes S^T = K Q^T (each lane: one query, 16 keys per
-//    32-key block), masks keys past the query or past the prompt on the tiles
-//    that reach them, runs the online softmax with a lazily raised reference
-//    max, and accumulates O^T += V^T P^T with V^T read transposed from LDS
-//    (ds_read_b64_tr_b16) and P^T rounded to bf16 in registers.
+//  * attn_causal_kernel<D>: a unit of work is gb query heads of one
+//    key/value group (gb = 4 when the group size allows it) times a slab of
+//    128 / gb queries of one prompt, one wavefront per 32 queries of a head,
+//    so the heads that share K and V share its tiles and, with gb = 4, all
+//    four wavefronts stop at the same diagonal.  A one-workgroup prologue
+//    writes one descriptor per (prompt, slab), sorted by key-tile count,
+//    longest first.  Two persistent workgroups per CU walk that list in
+//    snake order; each step is one key tile of 64, and the next step's tile
+//    (this unit's next or the next unit's first) is fetched by direct
+//    global->LDS loads into the other of two padded buffers while the
+//    current one is used, so the pipeline does not drain between units.  The
+//    next unit's Q is loaded into registers once the last tile's scores are
+//    formed.  Per tile a wavefront computes S^T = K Q^T (each lane: one query,
+//    16 keys per 32-key block), masks keys past the query or past the prompt
+//    on the tiles that reach them, runs the online softmax with a lazily
+//    raised reference max, and accumulates O^T += V^T P^T with V^T read
+//    transposed from LDS (ds_read_b64_tr_b16) and P^T rounded to bf16 in
+//    registers.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
