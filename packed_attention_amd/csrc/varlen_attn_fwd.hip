@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
 
         // S^T = K Q^T for one key tile held in K buffer kb.
         f32x16_t s[2];
-        auto qk = [&](const unsigned char* kb) {
+        auto qk = [&](const unsigned char* __restrict__ kb) {
             bf16x8_t fr[kPrefetch];
 #pragma unroll
             for (int i = 0; i < kPrefetch; ++i) fr[i] = kfrag(i, kb);
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
         // 2^kRescaleLog2); numerator and denominator share m_run, so the
         // result is the same softmax, and the output accumulator is rescaled
         // only on those (rare, wave-uniform) occasions.
-        auto softmax_pv = [&](int t, const unsigned char* vb) {
+        auto softmax_pv = [&](int t, const unsigned char* __restrict__ vb) {
             if (t == masked_tile) {
                 const int key0 = t * kBN;
 #pragma unroll
@@ -604,46 +604,49 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     const int L = p.cu[seq + 1] - int(tok0);
     const unsigned char* partials = p.ws + sched_bytes(p.n_seq);
     const int ns = n_slots;
-    constexpr int kDims = D / 4;                 // dims per thread
-    const int row = threadIdx.x >> 2;
-    const int d0 = (threadIdx.x & 3) * kDims;
-    const int qrow = qtile * kBM + row;
-    if (qrow >= L) return;
+    auto slot_at = [&](int i) { return partials + size_t(slots[i]) * TL::SLOT_BYTES; };
+    auto ml_at = [&](int i) { return reinterpret_cast<const float*>(slot_at(i) + size_t(kBM) * D * 4); };
 
-    float M = -INFINITY;
-    for (int i = 0; i < ns; ++i) {
-        const float* ml = reinterpret_cast<const float*>(partials + size_t(slots[i]) * TL::SLOT_BYTES +
-                                                         size_t(kBM) * D * 4);
-        M = fmaxf(M, ml[row]);
+    // per row: the reference max M over the pieces and 1 / total weight
+    __shared__ float row_m[kBM], row_inv[kBM];
+    const int tid = threadIdx.x;
+    if (tid < kBM) {
+        float M = -INFINITY;
+        for (int i = 0; i < ns; ++i) M = fmaxf(M, ml_at(i)[tid]);
+        float lt = 0.f;
+        for (int i = 0; i < ns; ++i) lt += exp2f(ml_at(i)[tid] - M) * ml_at(i)[kBM + tid];
+        row_m[tid] = M;
+        row_inv[tid] = 1.0f / lt;
+        const int qrow = qtile * kBM + tid;
+        if (p.lse != nullptr && qrow < L) p.lse[int64_t(head) * p.T + tok0 + qrow] = M * 0.69314718055994531f + logf(lt);
     }
-    float lt = 0.f;
-    float o[kDims];
+    __syncthreads();
+
+    // weighted sum of the pieces over the tile's 16-byte fp32 chunks in
+    // memory order (consecutive lanes read consecutive chunks)
+    constexpr int kRowChunks = D / 4;
+    constexpr int kChunks = kBM * kRowChunks;
+    static_assert(kChunks % kFixThreads == 0, "whole chunks per thread");
 #pragma unroll
-    for (int d = 0; d < kDims; ++d) o[d] = 0.f;
-    for (int i = 0; i < ns; ++i) {
-        const unsigned char* slot = partials + size_t(slots[i]) * TL::SLOT_BYTES;
-        const float* ml = reinterpret_cast<const float*>(slot + size_t(kBM) * D * 4);
-        const float w = exp2f(ml[row] - M);
-        lt += w * ml[kBM + row];
-        const f32x4_t* acc = reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(slot) + row * D + d0);
+    for (int j = 0; j < kChunks / kFixThreads; ++j) {
+        const int cidx = tid + kFixThreads * j;
+        const int row = cidx / kRowChunks;
+        const int qrow = qtile * kBM + row;
+        if (qrow >= L) continue;
+        const float M = row_m[row];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < ns; ++i) {
+            const float w = exp2f(ml_at(i)[row] - M);
+            const f32x4_t a4 = reinterpret_cast<const f32x4_t*>(slot_at(i))[cidx];
 #pragma unroll
-        for (int d = 0; d < kDims / 4; ++d) {
-            const f32x4_t a4 = acc[d];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[4 * d + j] += w * a4[j];
+            for (int e = 0; e < 4; ++e) acc[e] += w * a4[e];
         }
+        const float inv = row_inv[row];
+        u32x2_t v;
+        v[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+        v[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+        *reinterpret_cast<u32x2_t*>(p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 4 * (cidx % kRowChunks)) = v;
     }
-    const float inv = 1.0f / lt;
-    uint16_t* op = p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + d0;
-#pragma unroll
-    for (int d = 0; d < kDims / 8; ++d) {
-        u32x4_t v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(o[8 * d + 2 * j] * inv, o[8 * d + 2 * j + 1] * inv);
-        st16(op + 8 * d, v);
-    }
-    if (p.lse != nullptr && (threadIdx.x & 3) == 0)
-        p.lse[int64_t(head) * p.T + tok0 + qrow] = M * 0.69314718055994531f + logf(lt);
 }
 
 int cu_count() {
