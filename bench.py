@@ -4,32 +4,34 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 mf_modulate_rope -> mf_varlen_attn_fwd -> mf_gated_residual, with the inputs
-already resident in HBM.  The timed steps replay one captured HIP graph per
-input set (the same kernels as the eager calls, submitted at once; --eager
-times the three Python calls instead, and the eager step time is reported
-beside it).  Steps rotate over several copies of the batch so
-that each step starts from inputs that are not in the 256 MB Infinity Cache.
-Prints one JSON line:
+already resident in HBM.  The timed steps are the three library calls made
+back to back from Python (the kernels queue on the stream with no gap between
+them); the same step replayed as one captured HIP graph per input set is timed
+too and reported beside it (ms_per_step_graph: each replay leaves a gap of
+several microseconds on this platform).  Steps rotate over several copies of
+the batch so that each step starts from inputs that are not in the 256 MB
+Infinity Cache.
+Every per-call figure below is K calls of one kind back to back between two
+HIP events on the stream they run on (queued behind a spin long enough to
+cover their submission), divided by K.  Prints one JSON line:
   value       attention FLOPs (4 * d * H * sum L^2) per step / step time,
               i.e. the whole hot path's throughput in attention TFLOP/s;
   roofline    one attention call (main kernel + fix-up kernel) against the
-              bf16 dense MFMA peak, timed with HIP events on the stream it
-              runs on; traffic = HBM bytes per call from the committed
-              FETCH_SIZE/WRITE_SIZE summary when it matches the kernel source;
-  kernels     per-kernel average durations, algorithmic bytes and GB/s
-              against the HBM peak (the two elementwise kernels are
-              HBM-bound);
+              bf16 dense MFMA peak; traffic = HBM bytes per call from the
+              committed FETCH_SIZE/WRITE_SIZE summary when it matches the
+              kernel source;
+  kernels     per-call durations, algorithmic bytes and GB/s against the HBM
+              peak (the two elementwise kernels are HBM-bound);
   backward    the training backward of the same step (gated residual ->
-              attention -> modulate+RoPE, eager calls), per-kernel HIP-event
-              durations; attention at 2.5x the forward's flops (five
-              products), the elementwise kernels in GB/s of their
-              algorithmic bytes;
+              attention -> modulate+RoPE), per-call durations; attention at
+              2.5x the forward's flops (five products), the elementwise
+              kernels in GB/s of their algorithmic bytes;
   block       the block projections around the attention: the QKV projection
               of the adaLN-modulated residual stream with RoPE on q and k
               (mf_block_qkv, modulation pass included) and the out projection
-              with the gated residual (mf_block_out), per-call HIP-event
-              durations against the bf16 MFMA peak at 2*T*N*K flops, with
-              seeded random-init weights;
+              with the gated residual (mf_block_out), per-call durations
+              against the bf16 MFMA peak at 2*T*N*K flops, with seeded
+              random-init weights;
   sampler     the packed-CFG guidance + Euler step after the last block
               (mf_cfg_euler_step) on the packed CFG pack's tables, GB/s of its
               algorithmic bytes against the HBM peak;
@@ -136,8 +138,8 @@ def main():
     ap.add_argument("--workload", default="single_1024")
     ap.add_argument("--sets", type=int, default=4, help="input copies rotated over (defeats MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true",
-                    help="time the step as three eager calls instead of a captured HIP graph")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing of the step")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -166,11 +168,27 @@ def main():
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
 
+    # torch's spin kernel keeps the stream busy while the host queues a timed
+    # loop, so that the timed calls run back to back on the GPU even when one
+    # call is shorter than its submission from Python.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(1 << 22)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    spin_cycles_per_ms = (1 << 22) / max(e0.elapsed_time(e1), 1e-3)
+
     def timed(fn):
-        """K calls of fn(i) bracketed by device synchronisation and events on
-        the current stream; returns (ms per call, wall seconds)."""
+        """K calls of fn(i) queued behind a spin long enough to cover their
+        submission, bracketed by events on the stream they run on and by
+        device synchronisation; returns (ms per call, wall seconds)."""
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        fn(0)
+        host_ms = (time.perf_counter() - h0) * 1e3       # one call's submission cost
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        torch.cuda._sleep(int((2.0 * host_ms * args.steps + 1.0) * spin_cycles_per_ms))
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
@@ -180,75 +198,46 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / args.steps, time.perf_counter() - t0
 
-    # Whole step, eager: three library calls per step from Python.
-    ms_step_eager, _ = timed(lambda i: step(sets[i % len(sets)]))
-    # Whole step as one HIP graph per input set (the same kernels, submitted
-    # at once): the reported value.
-    graphs = None
-    if not args.eager:
+    # Whole step: three library calls per step from Python, the reported value.
+    ms_step, wall = timed(lambda i: step(sets[i % len(sets)]))
+    # The same step as one HIP graph per input set (the same kernels).
+    ms_step_graph = None
+    if not args.no_graph:
         graphs = [runner.capture_chain(b) for b in sets]
         for i in range(args.warmup):
             graphs[i % len(graphs)].replay()
-        ms_step, wall = timed(lambda i: graphs[i % len(graphs)].replay())
-    else:
-        ms_step, wall = timed(lambda i: step(sets[i % len(sets)]))
+        ms_step_graph, _ = timed(lambda i: graphs[i % len(graphs)].replay())
 
-    # Per-kernel durations: HIP events on the stream the kernels run on.
+    # Per-call durations: K calls of one kind back to back between two HIP
+    # events on the stream the kernels run on.
     names = ("modulate_rope", "varlen_attn_fwd", "gated_residual")
     fns = (runner.run_modulate_rope, runner.run_attention, runner.run_gated_residual)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        b = sets[i % len(sets)]
-        evs[i][0].record(stream)
-        for j, fn in enumerate(fns):
-            fn(b)
-            evs[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    kern_ms = {n: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)) / args.steps
-               for j, n in enumerate(names)}
+    kern_ms = {n: timed(lambda i, fn=fn: fn(sets[i % len(sets)]))[0] for n, fn in zip(names, fns)}
 
     # Backward pass of the same step (training): gated residual -> attention
-    # -> modulate+RoPE, per-kernel HIP events, eager calls.
+    # -> modulate+RoPE, each call kind timed back to back.
     gsets = [runner.grads_to_device(b) for b in sets]
     bnames = ("gated_residual_bwd", "varlen_attn_bwd", "modulate_rope_bwd")
     bfns = (runner.run_gated_residual_bwd, runner.run_attention_bwd, runner.run_modulate_rope_bwd)
     for i in range(args.warmup):
         runner.run_backward_chain(sets[i % len(sets)], gsets[i % len(sets)])
-    bevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        b, gb = sets[i % len(sets)], gsets[i % len(sets)]
-        bevs[i][0].record(stream)
-        for j, fn in enumerate(bfns):
-            fn(b, gb)
-            bevs[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    bkern_ms = {n: sum(bevs[i][j].elapsed_time(bevs[i][j + 1]) for i in range(args.steps)) / args.steps
-                for j, n in enumerate(bnames)}
+    bkern_ms = {n: timed(lambda i, fn=fn: fn(sets[i % len(sets)], gsets[i % len(sets)]))[0]
+                for n, fn in zip(bnames, bfns)}
 
     # Block projections around the attention (QKV with adaLN-modulate and
-    # RoPE, out projection with the gated residual), per-call HIP events.
+    # RoPE, out projection with the gated residual), each timed back to back.
     bsets = [runner.block_to_device(b) for b in sets]
     knames = ("block_qkv", "block_out")
     kfns = (runner.run_block_qkv, runner.run_block_out)
     for i in range(args.warmup):
         for fn in kfns:
             fn(sets[i % len(sets)], bsets[i % len(sets)])
-    kevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        b, bb = sets[i % len(sets)], bsets[i % len(sets)]
-        kevs[i][0].record(stream)
-        for j, fn in enumerate(kfns):
-            fn(b, bb)
-            kevs[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    blk_ms = {n: sum(kevs[i][j].elapsed_time(kevs[i][j + 1]) for i in range(args.steps)) / args.steps
-              for j, n in enumerate(knames)}
+    blk_ms = {n: timed(lambda i, fn=fn: fn(sets[i % len(sets)], bsets[i % len(sets)]))[0]
+              for n, fn in zip(knames, kfns)}
 
     # Packed-CFG guidance + Euler step after the last block, on the packed
     # CFG pack (4 prompts of 1024^2, conditional and unconditional copies):
-    # per-call HIP events over enough rotated input sets to leave the cache.
+    # back-to-back calls over enough rotated input sets to leave the cache.
     import numpy as np
     cdescs = W.descs_cfg(np.random.default_rng(W.CFG_SEED))
     crows_h = native.cfg_pair_rows(cdescs, list(range(0, len(cdescs), 2)), list(range(1, len(cdescs), 2)))
@@ -262,14 +251,7 @@ def main():
         native.cfg_euler_step(c["v"], crows, c["z"], c["zo"], 4.5, 0.75, 0.5, x_next=c["x"])
     for i in range(args.warmup):
         cfg_step(csets[i % len(csets)])
-    cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        cevs[i][0].record(stream)
-        cfg_step(csets[i % len(csets)])
-        cevs[i][1].record(stream)
-    torch.cuda.synchronize()
-    cfg_ms = sum(e0.elapsed_time(e1) for e0, e1 in cevs) / args.steps
+    cfg_ms = timed(lambda i: cfg_step(csets[i % len(csets)]))[0]
     cfg_bytes = cN * (16 * Cl + 8)      # v_c, v_u, z read, z' and both input rows written, rows
     sampler = {"call": "mf_cfg_euler_step", "workload": f"cfg_pack descriptors (4 prompts, T={cT}, "
                f"{cN} evolving latent tokens x {Cl} channels)", "ms": round(cfg_ms, 5),
@@ -296,18 +278,8 @@ def main():
     for i in range(args.warmup):
         for fn in tfns:
             fn(tsets[i % len(tsets)])
-    tevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        c = tsets[i % len(tsets)]
-        tevs[i][0].record(stream)
-        for j, fn in enumerate(tfns):
-            fn(c)
-            tevs[i][j + 1].record(stream)
-    torch.cuda.synchronize()
     tnames = ("qk_norm_rope", "varlen_attn_causal_fwd")
-    te_ms = {n: sum(tevs[i][j].elapsed_time(tevs[i][j + 1]) for i in range(args.steps)) / args.steps
-             for j, n in enumerate(tnames)}
+    te_ms = {n: timed(lambda i, fn=fn: fn(tsets[i % len(tsets)]))[0] for n, fn in zip(tnames, tfns)}
     qn_bytes = 2 * 2 * tp.T * (tp.Hq + tp.Hkv) * tp.D + 4 * tp.T + 2 * 2 * tp.D
     cflops = tp.causal_flops()
     ct = cflops / (te_ms["varlen_attn_causal_fwd"] * 1e-3) / 1e12
@@ -377,8 +349,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
-        "ms_per_step_eager": round(ms_step_eager, 5),
-        "step_submission": "eager" if args.eager else "hip_graph",
+        "ms_per_step_graph": None if ms_step_graph is None else round(ms_step_graph, 5),
+        "step_submission": "eager library calls",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
