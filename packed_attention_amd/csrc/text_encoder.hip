@@ -140,6 +140,7 @@ constexpr int kWgPerCu = 2;            // resident workgroups per CU (LDS and VG
 constexpr int kClasses = 1024;         // work classes (key-tile counts) of the longest-first order
 static_assert(kClasses % 256 == 0, "whole classes per prologue thread");
 constexpr float kRescale = 8.0f;       // lazy-rescale threshold (log2 units)
+constexpr int kPrefetch = 4;           // MFMA operand fragments read ahead from LDS
 
 template <int D>
 struct CT {
@@ -369,14 +370,25 @@ __global__ __launch_bounds__(64 * kCW) void attn_causal_kernel(CausalParams p) {
         const int q0 = q0_of(cur);
         // S^T = K Q^T: two 32-key blocks (lane: query q0 + l32, register r:
         // key 32 b + 8 (r/4) + 4 h + r%4 of the tile)
+        // fragment i: key block i % 2, 16-dim slice i / 2; kPrefetch of them
+        // are read ahead of the MFMA that uses them
+        auto kfrag = [&](int i) {
+            return *reinterpret_cast<const bf16x8_t*>(kt + k_rd + (i & 1) * 32 * TL::K_ROW + (i >> 1) * 32);
+        };
         f32x16_t sc[2];
+        {
+            bf16x8_t fr[kPrefetch];
 #pragma unroll
-        for (int kk = 0; kk < TL::KK; ++kk)
+            for (int i = 0; i < kPrefetch; ++i) fr[i] = kfrag(i);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + k_rd + bb * 32 * TL::K_ROW + kk * 32);
-                sc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], kk == 0 ? f32x16_t{} : sc[bb], 0, 0, 0);
+            for (int i = 0; i < 2 * TL::KK; ++i) {
+                const bf16x8_t f = fr[i % kPrefetch];
+                sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[i >> 1], i < 2 ? f32x16_t{} : sc[i & 1], 0, 0, 0);
+                if (i + kPrefetch < 2 * TL::KK) fr[i % kPrefetch] = kfrag(i + kPrefetch);
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
         if constexpr (kLast) q_load(nxt, qf);     // length 0 past the end: zeros, no access
         // keys past the query (causal) or past the prompt: only on the tiles
         // that reach the wavefront's first query or the prompt's end
@@ -429,15 +441,26 @@ __global__ __launch_bounds__(64 * kCW) void attn_causal_kernel(CausalParams p) {
             pf[cc] = __builtin_bit_cast(bf16x8_t, u);
         }
         l_run = kFirst ? lsum : l_run + lsum;
-        // O^T += V^T P^T over the four 16-key chunks
-#pragma unroll
-        for (int jj = 0; jj < 4 * TL::EB; ++jj) {
+        // O^T += V^T P^T over the four 16-key chunks (fragment jj: chunk
+        // jj / EB, 32-dim block jj % EB), kPrefetch fragments read ahead
+        auto vfrag = [&](int jj) {
             const unsigned char* ad = vt + v_rd + (jj / TL::EB) * 16 * TL::V_ROW + (jj % TL::EB) * 64;
             const s16x4_t lo = lds_read_tr16_b64(ad);
             const s16x4_t hi = lds_read_tr16_b64(ad + 8 * TL::V_ROW);
-            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[jj % TL::EB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                vf, pf[jj / TL::EB], (kFirst && jj < TL::EB) ? f32x16_t{} : oacc[jj % TL::EB], 0, 0, 0);
+            return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        {
+            bf16x8_t fr[kPrefetch];
+#pragma unroll
+            for (int jj = 0; jj < kPrefetch; ++jj) fr[jj] = vfrag(jj);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jj = 0; jj < 4 * TL::EB; ++jj) {
+                oacc[jj % TL::EB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    fr[jj % kPrefetch], pf[jj / TL::EB], (kFirst && jj < TL::EB) ? f32x16_t{} : oacc[jj % TL::EB], 0, 0, 0);
+                if (jj + kPrefetch < 4 * TL::EB) fr[jj % kPrefetch] = vfrag(jj + kPrefetch);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if constexpr (kLast) {
             // the unit's output rows (queries inside the prompt) and LSE
