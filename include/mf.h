@@ -333,8 +333,12 @@ mf_status mf_gated_residual(void* stream,
  *   set with mod_row int32 [T]; pos: int32 [T][3]; rope dims as for
  *   mf_modulate_rope; eps > 0 when modulating.
  * workspace: device memory of at least mf_block_qkv_workspace_bytes(T, H,
- *   D) bytes, 16-byte aligned (the modulated rows; may be NULL without
- *   modulation); owned by the caller, used between calls on one stream only.
+ *   D) bytes, 256-byte aligned: the modulated rows, then fp32 partial tiles
+ *   of the split last round (when the last round of 256 x 256 output tiles
+ *   fills under half of the device's CUs, its tiles are cut into K ranges
+ *   that run side by side and are summed by a second kernel; the size
+ *   depends on the current device's CU count).  Owned by the caller, used
+ *   between calls on one stream only.
  * Limits: D in {64, 128}, C <= 8192, T * ld_x * 2 and 3C * C * 2 below 2^32.
  * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
  * MF_ERR_WORKSPACE, MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */

@@ -13,6 +13,17 @@
 #include "mf.h"
 #include "mf_internal.h"
 
+namespace mf {
+
+int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
+}  // namespace mf
+
 namespace {
 
 bool debug_mode() {
@@ -405,12 +416,10 @@ mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_
     if (modulate && !mod_row) return MF_ERR_NULL;
     if (ld_x % 8 || ld_qkv % 8) return MF_ERR_ALIGN;
     if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(qkv, 16) || !aligned(pos, 4)) return MF_ERR_ALIGN;
-    if (modulate) {
-        if (!aligned(shift, 16) || !aligned(scale, 16) || !aligned(mod_row, 4)) return MF_ERR_ALIGN;
-        if (workspace == nullptr || workspace_bytes < mf::block_qkv_workspace_bytes(T, int32_t(C)))
-            return MF_ERR_WORKSPACE;
-        if (!aligned(workspace, 16)) return MF_ERR_ALIGN;
-    }
+    if (modulate && (!aligned(shift, 16) || !aligned(scale, 16) || !aligned(mod_row, 4))) return MF_ERR_ALIGN;
+    if (workspace == nullptr || workspace_bytes < mf::block_qkv_workspace_bytes(T, int32_t(C)))
+        return MF_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MF_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (debug_mode()) {
         std::vector<int32_t> hp;

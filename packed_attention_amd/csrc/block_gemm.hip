@@ -36,8 +36,15 @@
 //    consecutive features (8 bytes) per register group.
 //  * Tiles are numbered so that the tiles one XCD runs are consecutive and
 //    share their weight tile (its L2 serves the re-reads).
+//  * Split tail (QKV projection): one workgroup per CU, so the tiles run in
+//    rounds of #CUs; when the last round is less than half full, each of its
+//    tiles is cut into s K-ranges (s = #CUs / tail tiles) that run side by
+//    side and write fp32 partial tiles to the workspace, and
+//    gemm_fixup_kernel adds the pieces in a fixed order and runs the same
+//    epilogue.
 //  * Ragged edges: buffer resources end at the last token / feature, so rows
 //    past them read as zeros; the epilogue stores only rows inside.
+#include <algorithm>
 #include <cmath>
 
 #include "mf_device.h"
@@ -93,8 +100,32 @@ struct GemmParams {
     const uint16_t* gate;
     const int32_t* mod_row;
     int tiles_t, tiles_f;
+    // split tail: tiles [n_full, tiles) run as `split` K-ranges each, fp32
+    // partial tiles in `partial` (kTileAcc floats per piece)
+    int n_full, split;
+    float* partial;
     double theta_turns[64];
 };
+
+constexpr int kTileAcc = kBF * kBT;        // fp32 accumulators of one tile
+
+// Logical tile -> (feature tile, token tile): groups of kGroupF feature
+// tiles; consecutive tiles walk the group's feature tiles for one token tile,
+// then the next token tile, so the tiles running together on an XCD share
+// both operands' K slabs.
+__device__ __forceinline__ void tile_of(const GemmParams& p, int lt, int& ft, int& tt) {
+    const int gsz = kGroupF * p.tiles_t;
+    const int grp = lt / gsz, rem = lt - grp * gsz;
+    const int gf = min(kGroupF, p.tiles_f - grp * kGroupF);
+    ft = grp * kGroupF + rem % gf;
+    tt = rem / gf;
+}
+
+// Item b of n in an order where the items one XCD runs are consecutive
+// (blockIdx round-robins over the XCDs).
+__device__ __forceinline__ int xcd_order(int b, int n) {
+    return n % kXcds == 0 ? (b % kXcds) * (n / kXcds) + b / kXcds : b;
+}
 
 // Wait until at most N of this wavefront's direct global->LDS loads are in
 // flight (they complete in order); expcnt and lgkmcnt unconstrained.
@@ -104,134 +135,23 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// Epilogue of one tile from its fp32 accumulators (lane = token, register r
+// of block fb = feature 8(r/4) + 4h + r%4 of the block).  The finished bf16
+// values go to an LDS image of the output tile (rows = tokens, 512 bytes;
+// 16-byte chunk c of row t in slot c ^ (t % 32), so the 8-byte writes of 32
+// consecutive rows and the 16-byte reads along a row are both
+// conflict-free), then out to global memory one 512-byte row segment per 32
+// lanes.
 template <int MODE>
-__global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int nb = gridDim.x;
-    const int b = blockIdx.x;
-    // consecutive logical tiles on one XCD (blockIdx round-robins over XCDs)
-    const int lt = nb % kXcds == 0 ? (b % kXcds) * (nb / kXcds) + b / kXcds : b;
-    // groups of kGroupF feature tiles: consecutive tiles walk the group's
-    // feature tiles for one token tile, then the next token tile, so the
-    // tiles running together on an XCD share both operands' K slabs
-    const int gsz = kGroupF * p.tiles_t;
-    const int grp = lt / gsz, rem = lt - grp * gsz;
-    const int gf = min(kGroupF, p.tiles_f - grp * kGroupF);
-    const int ft = grp * kGroupF + rem % gf, tt = rem / gf;
-    const int f0 = ft * kBF;
-    const int64_t t0 = int64_t(tt) * kBT;
-
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&acc)[2][4], const int f0,
+                                              const int64_t t0, unsigned char* smem) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hlf = lane >> 5;
-    const int wf = wave & 3;      // 64-feature quarter of the tile
-    const int wt = wave >> 2;     // 128-token half of the tile
-
-    const uint32_t kbytes = uint32_t(p.K) * 2u;
-    const uint32_t abytes = uint32_t(p.ld_act) * 2u;
-    const __amdgpu_buffer_rsrc_t w_rs =
-        make_rsrc(p.w + int64_t(f0) * p.K, uint64_t(p.N - f0) * kbytes);
-    const __amdgpu_buffer_rsrc_t a_rs =
-        make_rsrc(p.act + t0 * p.ld_act, uint64_t(p.T - t0) * abytes);
-
-    // Direct loads: instruction n of a stage fills LDS rows
-    // [kRowsPerDma n, kRowsPerDma (n+1)); lane i lands in row
-    // kRowsPerDma n + i / kChunks, slot i % kChunks, and so fetches the
-    // global chunk (slot ^ sw(row)) of that row.  Rows below kBF are weight
-    // rows, the rest activation rows.  Wavefront w issues instructions
-    // w, w + kGW, ...
-    uint32_t voff[kDmaPerWave];
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-        const int n = wave + kGW * j;
-        const int row = kRowsPerDma * n + lane / kChunks;
-        const uint32_t c16 = 16u * uint32_t((lane % kChunks) ^ swz(row));
-        voff[j] = row < kBF ? uint32_t(row) * kbytes + c16 : uint32_t(row - kBF) * abytes + c16;
-    }
-    auto issue = [&](int s) {
-        unsigned char* base = smem + (s % kStages) * kStageB;
-        const uint32_t soff = uint32_t(s) * kBK * 2u;
-#pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j) {
-            const int n = wave + kGW * j;
-            if (n < kDmaW)
-                dma16(w_rs, base + 1024 * n, voff[j], soff);
-            else
-                dma16(a_rs, base + 1024 * n, voff[j], soff);
-        }
-    };
-
-    f32x16_t acc[2][4];
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[fb][tb][r] = 0.f;
-
-    // Fragment rows: weight rows 64 wf + 32 fb + l32, activation rows
-    // kBF + 128 wt + 32 tb + l32; their swizzle is sw(l32) for all of them
-    // (the row offsets are multiples of 16).  K sub-step kk reads chunk
-    // 2 kk + h.
-    const int sw = swz(l32);
-    const int a_rd = (64 * wf + l32) * kRowB;
-    const int b_rd = (kBF + 128 * wt + l32) * kRowB;
-    int cofs[kBK / 16];
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) cofs[kk] = 16 * ((2 * kk + hlf) ^ sw);
-    const int nks = (p.K + kBK - 1) / kBK;
-    constexpr int kAhead = kStages - 1;        // steps loaded ahead
-    for (int s = 0; s < kAhead; ++s)
-        if (s < nks) issue(s);
-    for (int s = 0; s < nks; ++s) {
-        // this wavefront's loads of stage s have landed once at most the
-        // later groups (up to kAhead - 1 of them) are still in flight
-        const int later = min(kAhead - 1, nks - 1 - s);
-        if constexpr (kAhead >= 3) {
-            if (later >= 2) wait_vm<2 * kDmaPerWave>();
-        }
-        if constexpr (kAhead >= 2) {
-            if (later == 1) wait_vm<kDmaPerWave>();
-        }
-        if (later == 0) wait_vm<0>();
-        // stage s landed for every wavefront; the stage refilled next was
-        // last read in step s-1, which every wavefront has finished
-        __syncthreads();
-        if (s + kAhead < nks) issue(s + kAhead);
-        const unsigned char* st = smem + (s % kStages) * kStageB;
-        // K sub-steps: the six fragments of sub-step kk+1 are read while
-        // the eight MFMAs of sub-step kk run
-        bf16x8_t af[2][2], bf[2][4];
-        auto rd = [&](int buf, int kk) {
-#pragma unroll
-            for (int fb = 0; fb < 2; ++fb)
-                af[buf][fb] = *reinterpret_cast<const bf16x8_t*>(st + a_rd + 32 * fb * kRowB + cofs[kk]);
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                bf[buf][tb] = *reinterpret_cast<const bf16x8_t*>(st + b_rd + 32 * tb * kRowB + cofs[kk]);
-        };
-        rd(0, 0);
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            if (kk + 1 < kBK / 16) rd((kk + 1) & 1, kk + 1);
-#pragma unroll
-            for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][fb], bf[kk & 1][tb],
-                                                                          acc[fb][tb], 0, 0, 0);
-        }
-    }
-
-    // ---- epilogue: lane = token, register r of block fb = feature
-    //      8(r/4) + 4h + r%4 of the block.  The finished bf16 values go to an
-    //      LDS image of the output tile (rows = tokens, 512 bytes; 16-byte
-    //      chunk c of row t in slot c ^ (t % 32), so the 8-byte writes of 32
-    //      consecutive rows and the 16-byte reads along a row are both
-    //      conflict-free), then out to global memory one 512-byte row segment
-    //      per 32 lanes.
+    const int wf = wave & 3;
+    const int wt = wave >> 2;
     __syncthreads();                       // every wavefront is done with the stages
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -295,6 +215,182 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + tl * 512 + 16 * (l32 ^ (tl & 31)));
         if (t < p.T && n < p.N) st16(p.out + t * p.ld_out + n, v);
     }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int b = blockIdx.x;
+    // whole tiles first (blockIdx < n_full), then the pieces of the split
+    // tail tiles, which the dispatcher starts last
+    const bool piece = b >= p.n_full;
+    int lt, part = 0;
+    if (!piece) {
+        lt = xcd_order(b, p.n_full);
+    } else {
+        const int li = xcd_order(b - p.n_full, int(gridDim.x) - p.n_full);
+        lt = p.n_full + li / p.split;
+        part = li - (li / p.split) * p.split;
+    }
+    int ft, tt;
+    tile_of(p, lt, ft, tt);
+    const int f0 = ft * kBF;
+    const int64_t t0 = int64_t(tt) * kBT;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hlf = lane >> 5;
+    const int wf = wave & 3;      // 64-feature quarter of the tile
+    const int wt = wave >> 2;     // 128-token half of the tile
+
+    const uint32_t kbytes = uint32_t(p.K) * 2u;
+    const uint32_t abytes = uint32_t(p.ld_act) * 2u;
+    const __amdgpu_buffer_rsrc_t w_rs =
+        make_rsrc(p.w + int64_t(f0) * p.K, uint64_t(p.N - f0) * kbytes);
+    const __amdgpu_buffer_rsrc_t a_rs =
+        make_rsrc(p.act + t0 * p.ld_act, uint64_t(p.T - t0) * abytes);
+
+    // Direct loads: instruction n of a stage fills LDS rows
+    // [kRowsPerDma n, kRowsPerDma (n+1)); lane i lands in row
+    // kRowsPerDma n + i / kChunks, slot i % kChunks, and so fetches the
+    // global chunk (slot ^ sw(row)) of that row.  Rows below kBF are weight
+    // rows, the rest activation rows.  Wavefront w issues instructions
+    // w, w + kGW, ...
+    uint32_t voff[kDmaPerWave];
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+        const int n = wave + kGW * j;
+        const int row = kRowsPerDma * n + lane / kChunks;
+        const uint32_t c16 = 16u * uint32_t((lane % kChunks) ^ swz(row));
+        voff[j] = row < kBF ? uint32_t(row) * kbytes + c16 : uint32_t(row - kBF) * abytes + c16;
+    }
+    auto issue = [&](int s, int buf) {
+        unsigned char* base = smem + buf * kStageB;
+        const uint32_t soff = uint32_t(s) * kBK * 2u;
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j) {
+            const int n = wave + kGW * j;
+            if (n < kDmaW)
+                dma16(w_rs, base + 1024 * n, voff[j], soff);
+            else
+                dma16(a_rs, base + 1024 * n, voff[j], soff);
+        }
+    };
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[fb][tb][r] = 0.f;
+
+    // Fragment rows: weight rows 64 wf + 32 fb + l32, activation rows
+    // kBF + 128 wt + 32 tb + l32; their swizzle is sw(l32) for all of them
+    // (the row offsets are multiples of 16).  K sub-step kk reads chunk
+    // 2 kk + h.
+    const int sw = swz(l32);
+    const int a_rd = (64 * wf + l32) * kRowB;
+    const int b_rd = (kBF + 128 * wt + l32) * kRowB;
+    int cofs[kBK / 16];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) cofs[kk] = 16 * ((2 * kk + hlf) ^ sw);
+    // K steps [ks0, ks1): all of them, or this piece's share
+    const int nks_all = (p.K + kBK - 1) / kBK;
+    const int ks0 = piece ? part * nks_all / p.split : 0;
+    const int ks1 = piece ? (part + 1) * nks_all / p.split : nks_all;
+    const int nks = ks1 - ks0;
+    constexpr int kAhead = kStages - 1;        // steps loaded ahead
+    for (int s = 0; s < kAhead; ++s)
+        if (s < nks) issue(ks0 + s, s % kStages);
+    for (int s = 0; s < nks; ++s) {
+        // this wavefront's loads of stage s have landed once at most the
+        // later groups (up to kAhead - 1 of them) are still in flight
+        const int later = min(kAhead - 1, nks - 1 - s);
+        if constexpr (kAhead >= 3) {
+            if (later >= 2) wait_vm<2 * kDmaPerWave>();
+        }
+        if constexpr (kAhead >= 2) {
+            if (later == 1) wait_vm<kDmaPerWave>();
+        }
+        if (later == 0) wait_vm<0>();
+        // stage s landed for every wavefront; the stage refilled next was
+        // last read in step s-1, which every wavefront has finished
+        __syncthreads();
+        if (s + kAhead < nks) issue(ks0 + s + kAhead, (s + kAhead) % kStages);
+        const unsigned char* st = smem + (s % kStages) * kStageB;
+        // K sub-steps: the six fragments of sub-step kk+1 are read while
+        // the eight MFMAs of sub-step kk run
+        bf16x8_t af[2][2], bf[2][4];
+        auto rd = [&](int buf, int kk) {
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb)
+                af[buf][fb] = *reinterpret_cast<const bf16x8_t*>(st + a_rd + 32 * fb * kRowB + cofs[kk]);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                bf[buf][tb] = *reinterpret_cast<const bf16x8_t*>(st + b_rd + 32 * tb * kRowB + cofs[kk]);
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            if (kk + 1 < kBK / 16) rd((kk + 1) & 1, kk + 1);
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][fb], bf[kk & 1][tb],
+                                                                          acc[fb][tb], 0, 0, 0);
+        }
+    }
+
+    if (piece) {
+        // fp32 partial tile in fragment order: 16-byte groups of four
+        // registers, 64 lanes side by side (1 KiB per store instruction)
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(p.partial + size_t((lt - p.n_full) * p.split + part) * kTileAcc);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4_t v = {acc[fb][tb][4 * g], acc[fb][tb][4 * g + 1], acc[fb][tb][4 * g + 2],
+                                       acc[fb][tb][4 * g + 3]};
+                    dst[(((wave * 2 + fb) * 4 + tb) * 4 + g) * 64 + lane] = v;
+                }
+        return;
+    }
+    gemm_epilogue<MODE>(p, acc, f0, t0, smem);
+}
+
+// Sum of the pieces of split tail tile n_full + blockIdx.x (in piece order),
+// then the same epilogue as a whole tile.
+template <int MODE>
+__global__ __launch_bounds__(kGT) void gemm_fixup_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int lt = p.n_full + int(blockIdx.x);
+    int ft, tt;
+    tile_of(p, lt, ft, tt);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    f32x16_t acc[2][4];
+    for (int part = 0; part < p.split; ++part) {
+        const f32x4_t* src =
+            reinterpret_cast<const f32x4_t*>(p.partial + size_t((lt - p.n_full) * p.split + part) * kTileAcc);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4_t v = src[(((wave * 2 + fb) * 4 + tb) * 4 + g) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[fb][tb][4 * g + e] = part == 0 ? v[e] : acc[fb][tb][4 * g + e] + v[e];
+                }
+    }
+    gemm_epilogue<MODE>(p, acc, ft * kBF, int64_t(tt) * kBT, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -371,6 +467,33 @@ hipError_t launch_adaln(const BlockQkvArgs& a, uint16_t* u, hipStream_t stream) 
     return launch_adaln_nch<16>(a, u, stream);
 }
 
+// Whole tiles run in rounds of `cus` (one workgroup per CU); a last round
+// under half full is cut into K-ranges of at least four steps.
+struct SplitPlan {
+    int n_full, split;
+};
+SplitPlan split_plan(int n_tiles, int nks, int cus) {
+    SplitPlan sp{n_tiles, 1};
+    if (cus <= 0) return sp;
+    const int tail = n_tiles % cus;
+    if (tail == 0) return sp;
+    const int s = std::min(cus / tail, nks / 4);
+    if (s < 2) return sp;
+    sp.n_full = n_tiles - tail;
+    sp.split = s;
+    return sp;
+}
+
+int qkv_tiles(int64_t T, int C) { return ((3 * C + kBF - 1) / kBF) * int((T + kBT - 1) / kBT); }
+
+// Bytes of the modulated rows (256-byte aligned) and of the partial tiles.
+size_t qkv_rows_bytes(int64_t T, int C) { return (size_t(T) * size_t(C) * 2 + 255) & ~size_t(255); }
+size_t qkv_partial_bytes(int64_t T, int C, int cus) {
+    const int tiles = qkv_tiles(T, C);
+    const SplitPlan sp = split_plan(tiles, (C + kBK - 1) / kBK, cus);
+    return sp.split > 1 ? size_t(tiles - sp.n_full) * sp.split * kTileAcc * sizeof(float) : 0;
+}
+
 template <int MODE>
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE>),
@@ -378,14 +501,32 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
     if (attr != hipSuccess) return attr;
     p.tiles_f = (p.N + kBF - 1) / kBF;
     p.tiles_t = int((p.T + kBT - 1) / kBT);
-    hipLaunchKernelGGL(gemm_kernel<MODE>, dim3(unsigned(p.tiles_f * p.tiles_t)), dim3(kGT), kLdsB, stream, p);
+    const int n_tiles = p.tiles_f * p.tiles_t;
+    p.n_full = n_tiles;
+    p.split = 1;
+    if (p.partial != nullptr) {
+        const SplitPlan sp = split_plan(n_tiles, (p.K + kBK - 1) / kBK, device_cu_count());
+        p.n_full = sp.n_full;
+        p.split = sp.split;
+    }
+    const int grid = p.n_full + (n_tiles - p.n_full) * p.split;
+    hipLaunchKernelGGL(gemm_kernel<MODE>, dim3(unsigned(grid)), dim3(kGT), kLdsB, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.split == 1) return e;
+    static const hipError_t attr_fix = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_fixup_kernel<MODE>), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsB);
+    if (attr_fix != hipSuccess) return attr_fix;
+    hipLaunchKernelGGL(gemm_fixup_kernel<MODE>, dim3(unsigned(n_tiles - p.n_full)), dim3(kGT), kLdsB, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 size_t block_qkv_workspace_bytes(int64_t T, int32_t C) {
-    return size_t(T < 0 ? 0 : T) * size_t(C < 0 ? 0 : C) * 2;
+    if (T <= 0 || C <= 0) return 0;
+    int cus = device_cu_count();
+    if (cus <= 0) cus = 256;   // no device visible: size for an MI355X
+    return qkv_rows_bytes(T, C) + qkv_partial_bytes(T, C, cus);
 }
 
 hipError_t launch_block_qkv(const BlockQkvArgs& args, hipStream_t stream) {
@@ -394,7 +535,7 @@ hipError_t launch_block_qkv(const BlockQkvArgs& args, hipStream_t stream) {
     const uint16_t* act = args.x;
     int64_t ld_act = args.ld_x;
     if (args.shift != nullptr) {
-        uint16_t* u = static_cast<uint16_t*>(args.workspace);
+        uint16_t* u = static_cast<uint16_t*>(args.workspace);   // the modulated rows
         const hipError_t e = launch_adaln(args, u, stream);
         if (e != hipSuccess) return e;
         act = u;
@@ -414,6 +555,8 @@ hipError_t launch_block_qkv(const BlockQkvArgs& args, hipStream_t stream) {
     p.rope_f = args.rope_f;
     p.rope_r = args.rope_r;
     p.pos = args.pos;
+    // the split tail's partial tiles follow the modulated rows
+    p.partial = reinterpret_cast<float*>(static_cast<unsigned char*>(args.workspace) + qkv_rows_bytes(args.T, C));
     const int dims[3] = {args.rope_f, args.rope_r, args.rope_c};
     int pair = 0;
     for (int ax = 0; ax < 3; ++ax)

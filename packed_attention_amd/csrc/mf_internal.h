@@ -9,6 +9,9 @@
 
 namespace mf {
 
+// Compute units of the current device (0 when none is visible).
+int device_cu_count();
+
 // ---------------------------------------------------------------------------
 // Launchers (one per kernel family).  Arguments are already validated by the
 // C-ABI layer; each returns the hipError_t of its launches.

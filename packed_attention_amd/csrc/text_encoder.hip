@@ -511,13 +511,6 @@ __global__ __launch_bounds__(64 * kCW) void attn_causal_kernel(CausalParams p) {
     }
 }
 
-int causal_cu_count() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    return n;
-}
-
 template <int D>
 hipError_t launch_causal_d(const CausalAttnArgs& a, hipStream_t stream) {
     CausalParams p;
@@ -533,7 +526,7 @@ hipError_t launch_causal_d(const CausalAttnArgs& a, hipStream_t stream) {
     const int64_t max_slabs = a.T / sq + a.n_seq;
     if (max_slabs * p.hg > INT32_MAX / 2) return hipErrorInvalidValue;
     p.max_slabs = int(max_slabs);
-    const int cus = causal_cu_count();
+    const int cus = device_cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
     hipLaunchKernelGGL(causal_slabs_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.n_seq, sq,
                        int(max_slabs), static_cast<int4*>(a.workspace));

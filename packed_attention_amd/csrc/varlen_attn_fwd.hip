@@ -649,16 +649,9 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     }
 }
 
-int cu_count() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    return n;
-}
-
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
-    const int G = cu_count();
+    const int G = device_cu_count();
     if (G <= 0) return hipErrorInvalidDevice;
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     if (a.n_seq > kInlineSeqs) {
@@ -691,7 +684,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
 
 size_t attn_workspace_bytes(int32_t n_seq, int64_t /*T*/, int32_t /*H*/, int32_t D) {
     const int n = n_seq < 0 ? 0 : n_seq;
-    int G = cu_count();
+    int G = device_cu_count();
     if (G <= 0) G = 256;   // no device visible: size for an MI355X
     const size_t slot = D == 64 ? Tile<64>::SLOT_BYTES : Tile<128>::SLOT_BYTES;
     return sched_bytes(n) + size_t(2) * G * slot;

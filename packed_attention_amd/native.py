@@ -367,7 +367,7 @@ def block_qkv(x, w_qkv, qkv, pos, H, rope_dims, rope_base=10000.0, shift=None, s
         raise ValueError("w_qkv: expected a contiguous [3C][C] tensor")
     if qkv.dim() != 2 or qkv.shape[0] != T or qkv.shape[1] != 3 * C:
         raise ValueError("qkv: expected [T][3C]")
-    if workspace is None and shift is not None:
+    if workspace is None:
         workspace = torch.empty(block_qkv_workspace_bytes(T, H, D), dtype=torch.uint8, device=x.device)
     f, r, c = (int(v) for v in rope_dims)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -237,8 +237,9 @@ def test_block_projection_validation():
     assert bqkv(ld_x=132) == ALIGN
     assert bqkv(w=PODD) == ALIGN
     assert bqkv(shift=P, scale=P, mod_row=P) == WS
+    assert bqkv() == WS                                                  # required without modulation too
     assert bqkv(shift=P, scale=P, mod_row=P, ws=P, ws_bytes=16) == WS
-    assert bqkv(shift=P, scale=P, mod_row=P, ws=PODD, ws_bytes=1 << 20) == ALIGN
+    assert bqkv(shift=P, scale=P, mod_row=P, ws=P + 16, ws_bytes=1 << 20) == ALIGN
     assert bqkv(T=1 << 20, ld_x=4096) == UNSUP                           # 32-bit offsets
     assert bqkv(T=0, x=None, w=None, qkv=None, pos=None) == 0
     assert bout(C=100) == SHAPE
@@ -249,7 +250,13 @@ def test_block_projection_validation():
     assert bout(y=PODD) == ALIGN
     assert bout(T=1 << 22, C=1024, ld_o=1024) == UNSUP
     assert bout(T=0, o=None, w=None, x=None, gate=None, mod_row=None, y=None) == 0
-    assert native.lib().mf_block_qkv_workspace_bytes(4352, 24, 128) == 4352 * 3072 * 2
+    # no device here: sized for 256 CUs; 612 tiles of 256 x 256 leave a last
+    # round of 100 tiles, each cut in two K ranges (256 KiB fp32 per piece)
+    assert native.lib().mf_block_qkv_workspace_bytes(4352, 24, 128) == 4352 * 3072 * 2 + 200 * 256 * 1024
+    # 576 tiles: a tail of 64, cut in four
+    assert native.lib().mf_block_qkv_workspace_bytes(4096, 24, 128) == 4096 * 3072 * 2 + 256 * 256 * 1024
+    # 2304 tiles fill whole rounds: no split
+    assert native.lib().mf_block_qkv_workspace_bytes(16384, 24, 128) == 16384 * 3072 * 2
 
 
 def cfg_step(**kw):

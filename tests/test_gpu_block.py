@@ -124,6 +124,17 @@ def test_block_qkv_ragged(D):
     check_qkv(w)
 
 
+# Small grids on a 256-CU device: every tile is cut into K ranges that run
+# side by side and are summed by the fix-up kernel (C = 512: 18 tiles, two
+# ranges of 4 steps; C = 1024: 24 tiles, four ranges of 4 steps).
+@pytest.mark.parametrize("H,descs", [(4, [(88, 1, 16, 32, 0, 0)]), (8, [(27, 1, 13, 21, 0, 0), (0, 1, 1, 1, 1, 1)])],
+                         ids=["C512", "C1024"])
+def test_block_qkv_split_tail(H, descs):
+    w = W.custom(descs, H=H, D=128, rope_dims=(0, 64, 64), modulate=True, residual=True, seed=41,
+                 name=f"block_split_c{H * 128}")
+    check_qkv(w)
+
+
 def test_block_qkv_edit_3d_rope():
     """Frame positions > 0 (edit source and target) with the 3D split."""
     descs = [(12, 2, 8, 9, 0, 0), (4, 1, 6, 7, 1, 1)]
