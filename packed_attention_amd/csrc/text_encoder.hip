@@ -32,7 +32,10 @@
 //    global->LDS loads into the other of two padded buffers while the
 //    current one is used, so the pipeline does not drain between units.  The
 //    next unit's Q is loaded into registers once the last tile's scores are
-//    formed.  Per tile a wavefront computes S^T = K Q^T (each lane: one query,
+//    formed.  A unit's output waits in registers until the next unit's
+//    first step, which stages it through the buffer that step is about to
+//    fill and stores whole rows (one 16-byte chunk per lane, four rows per
+//    instruction) before issuing its tile loads.  Per tile a wavefront computes S^T = K Q^T (each lane: one query,
 //    16 keys per 32-key block), masks keys past the query or past the prompt
 //    on the tiles that reach them, runs the online softmax with a lazily
 //    raised reference max, and accumulates O^T += V^T P^T with V^T read
@@ -349,6 +352,41 @@ __global__ __launch_bounds__(64 * kCW) void attn_causal_kernel(CausalParams p) {
     float m_run = -INFINITY, l_run = 0.f;
     int buf = 0;
 
+    // A unit's output (bf16 rows and LSE) is held in registers and stored at
+    // the start of the next unit's first step (or after the last step).  The
+    // wavefront's 32 x D tile goes through its own slice of the LDS buffer
+    // that the step's tile loads are about to fill (free since the previous
+    // barrier; rows of 2D bytes, 16-byte chunk c of row r in slot
+    // c ^ (r % (D/8))), and is read back along rows, so each store instruction
+    // writes whole rows (64 lanes x 16 bytes) instead of 16 bytes of 32
+    // rows.  A barrier then hands the buffer to the loads.
+    static_assert(kCW * 32 * 2 * D <= TL::STAGE, "output tiles fit a stage");
+    constexpr int kRowCh = D / 8;                   // 16-byte chunks per output row
+    u32x4_t out_v[TL::EB][2];
+    float out_lse = 0.f;
+    int out_q0 = 0, out_L = 0, out_tok0 = 0, out_head = 0;
+    bool out_pending = false;
+    auto flush_out = [&](unsigned char* stg) {
+        unsigned char* const wb = stg + wave * (32 * 2 * D);
+#pragma unroll
+        for (int m = 0; m < TL::EB; ++m)
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+                const int cidx = 4 * m + 2 * gp + hlf;
+                *reinterpret_cast<u32x4_t*>(wb + l32 * (2 * D) + 16 * (cidx ^ (l32 & (kRowCh - 1)))) = out_v[m][gp];
+            }
+        constexpr int kRowsPer = 64 / kRowCh;       // rows one store instruction covers
+#pragma unroll 1
+        for (int k = 0; k < 32 / kRowsPer; ++k) {
+            const int row = kRowsPer * k + lane / kRowCh, cidx = lane % kRowCh;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wb + row * (2 * D) + 16 * (cidx ^ (row & (kRowCh - 1))));
+            if (out_q0 + row < out_L)
+                st16(p.o + (int64_t(out_tok0) + out_q0 + row) * p.ld_o + int64_t(out_head) * D + 8 * cidx, v);
+        }
+        if (p.lse != nullptr && hlf == 0 && out_q0 + l32 < out_L)
+            p.lse[int64_t(out_head) * p.T + out_tok0 + out_q0 + l32] = out_lse;
+    };
+
     // One key tile t of the current unit on LDS buffer `buf`, with the next
     // tile (this unit's t+1 or, on the last tile, the next unit's first)
     // fetched into the other buffer.  First: the accumulators start at zero.
@@ -361,6 +399,12 @@ __global__ __launch_bounds__(64 * kCW) void attn_causal_kernel(CausalParams p) {
                     unsigned char* __restrict__ nb) {
         constexpr bool kFirst = decltype(first_c)::value, kLast = decltype(last_c)::value;
         const unsigned char* const vt = kt + TL::K_BYTES;
+        if constexpr (kFirst) {
+            if (out_pending) {
+                flush_out(nb);
+                __syncthreads();
+            }
+        }
         // nb was last read in the previous step, finished by everyone before
         // the barrier that opened this one
         if (more) {
@@ -463,25 +507,35 @@ __global__ __launch_bounds__(64 * kCW) void attn_causal_kernel(CausalParams p) {
             }
         }
         if constexpr (kLast) {
-            // the unit's output rows (queries inside the prompt) and LSE
-            const int qi = q0 + l32;
+            // the unit's output rows (queries inside the prompt) and LSE,
+            // stored by the next unit's first step (or after the loop)
             const float l_tot = half_sum32(l_run);
-            if (qi < cur.L) {
-                const int head = head_of(cur);
-                const float inv = 1.0f / l_tot;
-                uint16_t* op = p.o + (int64_t(cur.tok0) + qi) * p.ld_o + int64_t(head) * D + 4 * hlf;
+            const float inv = 1.0f / l_tot;
+            // lane (q, h) holds dims 8g + 4h + 0..3 of block m; swapping the
+            // g = 2gp + 1 values of lanes q with the g = 2gp values of lanes
+            // q + 32 (v_permlane32_swap) leaves lane (q, h) with dims
+            // 16gp + 8h + 0..7, so each store writes 32 contiguous bytes per row
 #pragma unroll
-                for (int m = 0; m < TL::EB; ++m)
+            for (int m = 0; m < TL::EB; ++m)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        u32x2_t val;
-                        val[0] = pack_bf16x2(oacc[m][4 * g] * inv, oacc[m][4 * g + 1] * inv);
-                        val[1] = pack_bf16x2(oacc[m][4 * g + 2] * inv, oacc[m][4 * g + 3] * inv);
-                        *reinterpret_cast<u32x2_t*>(op + 32 * m + 8 * g) = val;
+                for (int gp = 0; gp < 2; ++gp) {
+                    uint32_t x[2], y[2];
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        x[w] = pack_bf16x2(oacc[m][8 * gp + 2 * w] * inv, oacc[m][8 * gp + 2 * w + 1] * inv);
+                        y[w] = pack_bf16x2(oacc[m][8 * gp + 4 + 2 * w] * inv, oacc[m][8 * gp + 4 + 2 * w + 1] * inv);
+                        const auto r = __builtin_amdgcn_permlane32_swap(x[w], y[w], false, false);
+                        x[w] = r[0];
+                        y[w] = r[1];
                     }
-                if (p.lse != nullptr && hlf == 0)
-                    p.lse[int64_t(head) * p.T + cur.tok0 + qi] = m_run * 0.69314718055994531f + logf(l_tot);
-            }
+                    out_v[m][gp] = u32x4_t{x[0], x[1], y[0], y[1]};
+                }
+            out_lse = m_run * 0.69314718055994531f + logf(l_tot);
+            out_q0 = q0;
+            out_L = cur.L;
+            out_tok0 = cur.tok0;
+            out_head = head_of(cur);
+            out_pending = true;
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): the next tile (and Q) landed
         __syncthreads();
@@ -501,7 +555,10 @@ __global__ __launch_bounds__(64 * kCW) void attn_causal_kernel(CausalParams p) {
             for (int t = 1; t + 1 < nt; ++t) run(std::false_type{}, std::false_type{}, t, true);
             run(std::false_type{}, std::true_type{}, nt - 1, more);
         }
-        if (!more) break;
+        if (!more) {
+            flush_out(smem);        // both buffers are free after the last barrier
+            break;
+        }
         // next unit: its first tile is in LDS and its Q in registers; fetch
         // the descriptor of the one after the next
         ++i;
