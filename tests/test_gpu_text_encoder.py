@@ -75,6 +75,14 @@ def test_ragged(D):
     check_pack(W.text_pack(seed=52 + D, Hq=8, Hkv=2, D=D, lens=lens, name=f"text_ragged_d{D}"))
 
 
+# group sizes 8 (four heads per workgroup, two workgroups per key/value head
+# and slab) and 3 (one head per workgroup, 128-query slabs)
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 2, 128), (6, 2, 64), (8, 1, 64)])
+def test_group_sizes(Hq, Hkv, D):
+    check_pack(W.text_pack(seed=60 + Hq, Hq=Hq, Hkv=Hkv, D=D, lens=[33, 129, 1, 200, 64],
+                           name=f"text_g{Hq // Hkv}_d{D}"))
+
+
 def test_no_grouping():
     check_pack(W.text_pack(seed=57, Hq=4, Hkv=4, D=128, lens=[70, 200, 3], name="text_mha"))
 
