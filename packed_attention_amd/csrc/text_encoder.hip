@@ -306,8 +306,9 @@ __global__ __launch_bounds__(64 * kCW) void attn_causal_kernel(CausalParams p) {
     // LDS units [64n, 64n+64) of the padded K (or V) image: lane l fetches
     // unit 64n+l = (row, chunk); pad units fetch the row's last chunk again
     // (never read back).  Instruction n is issued by wavefront n % 4.  The
-    // resource starts at the tile's first row, so rows past the prompt read
-    // as zeros.
+    // resource covers the prompt's rows of the key/value head and the tile
+    // offset is the instruction's scalar offset, which the range check
+    // includes, so rows past the prompt read as zeros.
     uint32_t k_off[TL::K_DMA_W], v_off[TL::V_DMA_W];
 #pragma unroll
     for (int m = 0; m < TL::K_DMA_W; ++m) {
