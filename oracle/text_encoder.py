@@ -104,3 +104,30 @@ def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu: np.ndarray
                 out[r0:r1, h, :] = (P / l) @ V
                 lse[h, r0:r1] = (m + np.log(l))[:, 0]
     return out, lse
+
+
+def causal_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu: np.ndarray, rows,
+                          scale: Optional[float] = None):
+    """O [len(rows)][H_q][d] and LSE [H_q][len(rows)] of causal attention at the
+    given packed rows only, one query row at a time: row i of a prompt
+    starting at a attends to keys a..i (for spot checks of long prompts)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, Hq, d = q.shape
+    g = Hq // k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.asarray(rows, dtype=np.int64)
+    first = np.asarray(cu, dtype=np.int64)[np.searchsorted(cu, rows, side="right") - 1]
+    out = np.zeros((len(rows), Hq, d))
+    lse = np.zeros((Hq, len(rows)))
+    for n, (i, a) in enumerate(zip(rows, first)):
+        for h in range(Hq):
+            s = scale * (k[a:i + 1, h // g, :] @ q[i, h, :])
+            m = s.max()
+            p = np.exp(s - m)
+            out[n, h] = (p @ v[a:i + 1, h // g, :]) / p.sum()
+            lse[h, n] = m + np.log(p.sum())
+    return out, lse
+

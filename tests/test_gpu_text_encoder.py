@@ -97,6 +97,29 @@ def test_text_pack_bench_size():
     check_pack(W.text_pack(seed=W.TEXT_BENCH_SEED, n_prompts=W.TEXT_BENCH_PROMPTS, name="text_pack_64"))
 
 
+def test_long_prompt_sampled():
+    """A 66 000-token prompt (units of more than 1023 key tiles, past the
+    prologue's largest work class) beside a short one: q', k' element by
+    element, O and LSE on sampled rows against the row-at-a-time oracle."""
+    import torch
+    tp = W.text_pack(seed=71, Hq=2, Hkv=1, D=64, lens=[66000, 300], name="text_long")
+    cu, qo, ko = run_norm_rope(tp)
+    G.say(tp.name, "causal attention, sampled rows")
+    o = torch.full_like(qo, float("nan"))
+    lse = torch.empty((tp.Hq, tp.T), dtype=torch.float32, device="cuda")
+    native.varlen_attn_causal_fwd(qo, ko, runner.bf16_tensor(tp.v), o, torch.from_numpy(cu).cuda(), lse=lse)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65471, 65472, 65535, 65999, 66000, 66001, 66299],
+                                     np.random.default_rng(72).choice(tp.T, 24, replace=False)]))
+    ref, rl = TE.causal_attention_rows(G.f64(qo), G.f64(ko), W.bf16_bits_to_f64(tp.v), cu, rows)
+    g = G.f64(o)[rows]
+    assert np.all(np.isfinite(g))
+    rel = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
+    assert rel <= 1e-2, rel
+    assert np.abs(g - ref).max() <= 2e-2 * np.abs(ref).max()
+    assert np.abs(lse.cpu().numpy()[:, rows] - rl).max() <= 1e-3
+
+
 def test_first_token_attends_to_itself():
     """Closed form on the GPU: every prompt's first token outputs its own v."""
     import torch

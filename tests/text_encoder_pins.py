@@ -114,4 +114,15 @@ def pin_norm_rope_torch(e):
     _close(q0, 2.0 * q / rms)
 
 
-ALL_PINS = [pin_torch_sdpa, pin_first_token, pin_brute, pin_packed_alone, pin_norm_rope_torch]
+def pin_rows(e):
+    """The row-at-a-time evaluation equals the full one (first, middle and
+    last rows of every prompt)."""
+    cu, q, k, v = _case(26, lens=(5, 1, 9, 3, 12))
+    O, L = e.causal_attention(q, k, v, cu)
+    rows = [0, 2, 4, 5, 6, 10, 14, 15, 17, 18, 25, 29]
+    Or, Lr = e.causal_attention_rows(q, k, v, cu, rows)
+    _close(Or, O[rows])
+    _close(Lr, L[:, rows])
+
+
+ALL_PINS = [pin_torch_sdpa, pin_first_token, pin_brute, pin_packed_alone, pin_norm_rope_torch, pin_rows]
