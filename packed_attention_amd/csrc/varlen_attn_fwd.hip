@@ -17,7 +17,7 @@
 //    the contiguous range [g*W/G, (g+1)*W/G) of the W (tile, key-step)
 //    iterations, so mixed lengths and tile counts that are not a multiple of
 //    the CU count leave no CU idle.  A tile cut by a range boundary leaves
-//    fp32 partial results (unnormalised O, reference max, sum) of each piece
+//    partial results (unnormalised O in bf16, reference max and sum in fp32)
 //    in the workspace; a fix-up kernel merges them with the log-sum-exp rule.
 //    The partition is fixed by (W, G), so results are deterministic.
 //    Logical workgroups map to blockIdx so that consecutive ranges (same
@@ -99,9 +99,10 @@ struct Tile {
     static constexpr int V_DMA = V_UNITS;
     static constexpr int K_DMA_PER_WAVE = (K_DMA + kLoaders - 1) / kLoaders;
     static constexpr int V_DMA_PER_WAVE = (V_DMA + kLoaders - 1) / kLoaders;
-    // One partial-result slot of the workspace: unnormalised O (fp32,
-    // kBM x D), then the reference max (log2 units) and sum of each row.
-    static constexpr size_t SLOT_BYTES = size_t(kBM) * D * 4 + size_t(kBM) * 8;
+    // One partial-result slot of the workspace: unnormalised O (rounded to
+    // bf16, kBM x D), then the reference max (log2 units) and sum of each
+    // row in fp32.
+    static constexpr size_t SLOT_BYTES = size_t(kBM) * D * 2 + size_t(kBM) * 8;
 };
 
 // ---------------------------------------------------------------------------
@@ -538,18 +539,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
                     p.lse[int64_t(head) * p.T + tok0 + qrow] = m_run * 0.69314718055994531f + logf(l_tot);
             }
         } else {
-            // piece of a tile shared with other workgroups: fp32 partial in
-            // slot 2g (this workgroup's first segment) or 2g+1 (its last)
+            // piece of a tile shared with other workgroups: partial in slot
+            // 2g (this workgroup's first segment) or 2g+1 (its last)
             unsigned char* slot = partials + size_t(2 * g + (first_segment ? 0 : 1)) * TL::SLOT_BYTES;
-            float* acc = reinterpret_cast<float*>(slot);
-            float* ml = reinterpret_cast<float*>(slot + size_t(kBM) * D * 4);
+            uint16_t* acc = reinterpret_cast<uint16_t*>(slot);
+            float* ml = reinterpret_cast<float*>(slot + size_t(kBM) * D * 2);
             const int row = wave * 32 + l32;
 #pragma unroll
             for (int m = 0; m < TL::EB; ++m)
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    f32x4_t val = {oacc[m][4 * gq], oacc[m][4 * gq + 1], oacc[m][4 * gq + 2], oacc[m][4 * gq + 3]};
-                    *reinterpret_cast<f32x4_t*>(acc + row * D + 32 * m + 8 * gq + 4 * hlf) = val;
+                    u32x2_t val;
+                    val[0] = pack_bf16x2(oacc[m][4 * gq], oacc[m][4 * gq + 1]);
+                    val[1] = pack_bf16x2(oacc[m][4 * gq + 2], oacc[m][4 * gq + 3]);
+                    *reinterpret_cast<u32x2_t*>(acc + row * D + 32 * m + 8 * gq + 4 * hlf) = val;
                 }
             if (hlf == 0) {
                 ml[row] = m_run;
@@ -605,7 +608,7 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     const unsigned char* partials = p.ws + sched_bytes(p.n_seq);
     const int ns = n_slots;
     auto slot_at = [&](int i) { return partials + size_t(slots[i]) * TL::SLOT_BYTES; };
-    auto ml_at = [&](int i) { return reinterpret_cast<const float*>(slot_at(i) + size_t(kBM) * D * 4); };
+    auto ml_at = [&](int i) { return reinterpret_cast<const float*>(slot_at(i) + size_t(kBM) * D * 2); };
 
     // per row: the reference max M over the pieces and 1 / total weight
     __shared__ float row_m[kBM], row_inv[kBM];
@@ -622,9 +625,9 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     }
     __syncthreads();
 
-    // weighted sum of the pieces over the tile's 16-byte fp32 chunks in
+    // weighted sum of the pieces over the tile's 16-byte chunks (8 bf16) in
     // memory order (consecutive lanes read consecutive chunks)
-    constexpr int kRowChunks = D / 4;
+    constexpr int kRowChunks = D / 8;
     constexpr int kChunks = kBM * kRowChunks;
     static_assert(kChunks % kFixThreads == 0, "whole chunks per thread");
 #pragma unroll
@@ -634,18 +637,18 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
         const int qrow = qtile * kBM + row;
         if (qrow >= L) continue;
         const float M = row_m[row];
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < ns; ++i) {
             const float w = exp2f(ml_at(i)[row] - M);
-            const f32x4_t a4 = reinterpret_cast<const f32x4_t*>(slot_at(i))[cidx];
+            float a8[8];
+            unpack8(reinterpret_cast<const u32x4_t*>(slot_at(i))[cidx], a8);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += w * a4[e];
+            for (int e = 0; e < 8; ++e) acc[e] += w * a8[e];
         }
         const float inv = row_inv[row];
-        u32x2_t v;
-        v[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-        v[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-        *reinterpret_cast<u32x2_t*>(p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 4 * (cidx % kRowChunks)) = v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= inv;
+        st16(p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 8 * (cidx % kRowChunks), pack8(acc));
     }
 }
 
