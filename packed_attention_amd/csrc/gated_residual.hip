@@ -85,12 +85,19 @@ gated_residual_kernel(GatedResArgs a) {
         const __amdgpu_buffer_rsrc_t sh_rs = make_rsrc(a.shift2 + m * C, row_bytes);
         const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(a.scale2 + m * C, row_bytes);
         const __amdgpu_buffer_rsrc_t z_rs = make_rsrc(a.z + t * C, row_bytes);
+        // adaLN chunks loaded one chunk ahead of the stores (a load written
+        // after a store would wait for it)
+        u32x4_t nsh = bload16(sh_rs, 16u * uint32_t(lane), 0), nsc = bload16(sc_rs, 16u * uint32_t(lane), 0);
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const uint32_t off = 16u * uint32_t(lane + kWave * i);
             float fs[8], fc[8], r[8];
-            unpack8(bload16(sh_rs, off, 0), fs);
-            unpack8(bload16(sc_rs, off, 0), fc);
+            unpack8(nsh, fs);
+            unpack8(nsc, fc);
+            if (i + 1 < NCH) {
+                nsh = bload16(sh_rs, off + 16u * kWave, 0);
+                nsc = bload16(sc_rs, off + 16u * kWave, 0);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) r[j] = (y[i][j] - mean) * rstd * (1.0f + fc[j]) + fs[j];
             bstore16(z_rs, off, 0, pack8(r));

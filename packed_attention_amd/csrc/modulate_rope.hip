@@ -63,6 +63,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH <= 6 ? 
         pq[i] = bload16(q_rs, 16u * uint32_t(lane + kWave * i), 0);
         pk[i] = bload16(k_rs, 16u * uint32_t(lane + kWave * i), 0);
     }
+    const bool mod = a.shift != nullptr;
 
     // Rotation angles of this lane's four pairs (the same in every head),
     // computed while the rows are in flight.  The angle pos * theta is formed
@@ -82,7 +83,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH <= 6 ? 
     }
 
     float mq = 0.f, mk = 0.f, rq = 1.f, rk = 1.f;
-    const bool mod = a.shift != nullptr;
     __amdgpu_buffer_rsrc_t sh_rs = make_rsrc(nullptr, 0), sc_rs = make_rsrc(nullptr, 0);
     if (mod) {
         // LayerNorm statistics (population variance) in fp32, two passes.
@@ -120,6 +120,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH <= 6 ? 
 
     const __amdgpu_buffer_rsrc_t qo_rs = make_rsrc(a.q_out + t * a.ld_out, row_bytes);
     const __amdgpu_buffer_rsrc_t ko_rs = make_rsrc(a.k_out + t * a.ld_out, row_bytes);
+    // The adaLN chunks are loaded one chunk ahead of the stores: a load
+    // written after a store waits for it (the compiler cannot tell the
+    // buffers apart), so each chunk would otherwise pay a full round trip.
+    u32x4_t nsh = {0u, 0u, 0u, 0u}, nsc = {0u, 0u, 0u, 0u};
+    if (mod) {
+        nsh = bload16(sh_rs, 16u * uint32_t(lane), 0);
+        nsc = bload16(sc_rs, 16u * uint32_t(lane), 0);
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const uint32_t off = 16u * uint32_t(lane + kWave * i);
@@ -128,8 +136,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH <= 6 ? 
         unpack8(pk[i], xk);
         if (mod) {
             float fs[8], fc[8];
-            unpack8(bload16(sh_rs, off, 0), fs);
-            unpack8(bload16(sc_rs, off, 0), fc);
+            unpack8(nsh, fs);
+            unpack8(nsc, fc);
+            if (i + 1 < NCH) {
+                nsh = bload16(sh_rs, off + 16u * kWave, 0);
+                nsc = bload16(sc_rs, off + 16u * kWave, 0);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float g = 1.0f + fc[j];
