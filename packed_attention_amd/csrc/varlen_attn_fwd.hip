@@ -10,9 +10,10 @@
 //
 // Design (MI355X, CDNA4):
 //  * Work = (sequence, head, 256-query tile, 64-key step).  Sequences are
-//    ordered longest first (in-kernel for packs of up to 64 sequences,
-//    otherwise by a one-workgroup prologue kernel writing into the caller's
-//    workspace); within a sequence the order is head-major, then q-tile.
+//    ordered by descending octave of their key-step count, ties by index
+//    (in-kernel for packs of up to 64 sequences, otherwise by a one-workgroup
+//    O(n) prologue kernel writing into the caller's workspace); within a
+//    sequence the order is head-major, then q-tile.
 //  * Stream-K: a persistent grid of one workgroup per CU; workgroup g takes
 //    the contiguous range [g*W/G, (g+1)*W/G) of the W (tile, key-step)
 //    iterations, so mixed lengths and tile counts that are not a multiple of
@@ -22,9 +23,9 @@
 //    The partition is fixed by (W, G), so results are deterministic.
 //    Logical workgroups map to blockIdx so that consecutive ranges (same
 //    sequence and head, hence the same K/V) run on one XCD and share its L2.
-//  * 8 wavefronts (2 per SIMD, <= 256 VGPRs each) share every K/V tile; each
-//    wavefront owns 32 query rows, held in VGPRs as MFMA B operands.
-//  * Scores are computed transposed, S^T = K Q^T, with
+//  * One wavefront per SIMD (4 per workgroup), each owning 64 query rows as
+//    two 32-row blocks, so every K or V fragment read from LDS feeds two
+//    MFMAs.  Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: every lane holds 16 keys of one query row, so
 //    the online-softmax max/sum need one v_permlane32_swap and the rescale of
 //    the output accumulator is a per-lane scalar.  The fp32 probabilities are
@@ -33,26 +34,39 @@
 //    {4h..4h+3, 8+4h..8+4h+3} of every 16-key chunk, which is exactly what
 //    two transposed LDS reads (ds_read_b64_tr_b16) of the row-major V tile
 //    deliver as the V^T operand.
-//  * Per 64-key tile a wavefront runs S^T = K Q^T (2*D/16 MFMAs), the online
-//    softmax (VALU), then O^T += V^T P^T (D/8 MFMAs).  The two wavefronts of
-//    a SIMD are half a tile apart: waves 0..3 run S, softmax, PV of tile i
-//    between two barriers while waves 4..7 run softmax, PV of tile i and S
-//    of tile i+1, so one wave's softmax overlaps the other's MFMAs.  Operand
-//    fragments are read from LDS four MFMAs ahead, pinned with
-//    sched_barrier so the scheduler does not sink them next to their use.
-//  * K and V arrive by direct global->LDS buffer loads (no staging
-//    registers, no LDS stores) issued by waves 0..3, two K tiles and one V
-//    tile ahead of use (3 K buffers, 2 V buffers), one barrier per tile.
-//    Rows are padded (K: 2D -> 2D+16 bytes, V: 2D -> 2D+64) so every LDS
-//    read cycle hits distinct banks of the 64, with affine addresses.
+//  * The 128 output accumulators of a wavefront live in AGPRs: the PV MFMA is
+//    issued from inline assembly with its accumulator bound to AGPRs, which
+//    leaves the 256 VGPRs to the score tiles (VALU reads them), the
+//    probabilities and the Q fragments.  The accumulators are read or
+//    written by VALU only in the rare rescale and the epilogue, each behind
+//    explicit wait states.
+//  * Per 64-key step t a wavefront runs two phases of 32 MFMAs each, with the
+//    softmax VALU work threaded between the MFMAs of the same wavefront:
+//      phase 1: S(t+1) = K(t+1) Q^T   ||  p = exp2(x(t)), bf16 rounding, row sums
+//      phase 2: O += V(t)^T P(t)^T     ||  max of S(t+1), reference-max update,
+//                                          x(t+1) = S(t+1) * scale*log2e - max
+//    Operand fragments are read from LDS three MFMAs ahead.
+//  * K and V arrive by direct global->LDS buffer loads (no staging registers,
+//    no LDS stores), issued by all four wavefronts from inline assembly (the
+//    compiler would otherwise order every transposed LDS read behind all
+//    outstanding direct loads); completion is tracked with explicit vmcnt
+//    waits.  K of tiles t+1..t+4 and V of tiles t..t+2 are resident (4 + 3
+//    stages of 16 KB), loads run two steps ahead, and one barrier per step
+//    publishes them.  Every step issues the same number of loads (a tile past
+//    the segment is addressed out of range, which returns zeros without
+//    memory traffic), so the wait count is a constant.  LDS rows are not
+//    padded: the 16-byte units of each row are XOR-swizzled so that every
+//    LDS read cycle of the K reads and of the transposed V reads touches 64
+//    distinct banks.
 //  * Q/K/V are read through raw buffer resources that end at the sequence's
 //    last row, so ragged tiles read zeros without branches; only the last
 //    key tile of a sequence masks its scores.
 //  * exp2 with the softmax scale folded into one FMA (scale * log2 e); the
 //    reference max is raised lazily (only when a row max grows by more than
 //    2^8), so the output accumulator is rarely rescaled; all softmax state
-//    in fp32.
+//    in fp32, row sums of the fp32 probabilities.
 #include <cmath>
+#include <utility>
 
 #include "mf_device.h"
 #include "mf_internal.h"
@@ -60,56 +74,71 @@
 namespace mf {
 namespace {
 
-constexpr int kWaves = 8;        // wavefronts per workgroup: 2 per SIMD
-constexpr int kBM = 32 * kWaves; // query rows per tile (32 per wavefront)
-constexpr int kBN = 64;          // keys per K/V step
+constexpr int kWaves = 4;            // wavefronts per workgroup: one per SIMD
+constexpr int kRows = 64;            // query rows per wavefront (two 32-row blocks)
+constexpr int kBM = kWaves * kRows;  // query rows per tile
+constexpr int kBN = 32;              // keys per K/V step (one 32-key MFMA block)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kXcds = 8;         // XCDs of an MI355X; blockIdx round-robins over them
-constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold (log2 units)
-constexpr int kInlineSeqs = 64;  // packs up to this many sequences schedule in-kernel
-constexpr int kPrefetch = 4;     // MFMA operand fragments read ahead from LDS
-constexpr int kLoaders = kWaves / 2;  // leading wavefronts, which issue the K/V loads
+constexpr int kXcds = 8;             // XCDs of an MI355X; blockIdx round-robins over them
+constexpr float kRescaleLog2 = 8.0f; // lazy-rescale threshold (log2 units)
+constexpr int kInlineSeqs = 64;      // packs up to this many sequences schedule in-kernel
+constexpr int kSlack = 2;            // steps a direct load may stay in flight
+constexpr int kKStages = 3 + kSlack; // K of tiles t+1 .. t+kKStages
+constexpr int kVStages = 2 + kSlack; // V of tiles t .. t+kVStages-1
+constexpr int kPfK = 3;              // K fragments read ahead of their MFMA
+constexpr int kPfV = 3;              // V fragments read ahead of their MFMA
+constexpr uint32_t kOutOfRange = 0x80000000u;  // scalar offset past any sequence's rows
 
 template <int D>
 struct Tile {
-    static constexpr int KK = D / 16;            // QK^T MFMA steps along d
-    static constexpr int EB = D / 32;            // 32-wide blocks of the output dim
-    static constexpr int KCH = D / 8;            // 16-byte chunks per K or V row
-    static constexpr int NQK = 2 * KK;           // MFMAs of one S tile
-    static constexpr int NPV = 4 * EB;           // MFMAs of one PV tile
-    // K rows padded by one 16-byte unit: the 16 lanes one LDS cycle serves
-    // (rows r..r+15, same chunk) start 17 units apart, i.e. on 16 distinct
-    // 4-bank groups of the 64 banks, with affine addresses.
-    static constexpr int K_UNITS = KCH + 1;
-    static constexpr int K_ROW_BYTES = 16 * K_UNITS;
-    static constexpr int K_BYTES = kBN * K_ROW_BYTES;
-    // V rows stay row-major (keys x dims) and are read transposed; rows are
-    // padded to 80 dwords (D=128) / 48 dwords (D=64) so that the 4 rows x 2
-    // column blocks one 32-lane transposed read touches map to all 64 banks.
-    static constexpr int V_UNITS = KCH + 4;
-    static constexpr int V_ROW_BYTES = 16 * V_UNITS;
-    static constexpr int V_BYTES = kBN * V_ROW_BYTES;
-    static constexpr int K_STAGES = 3;           // K of tiles i, i+1, i+2
-    static constexpr int V_STAGES = 2;           // V of tiles i, i+1
-    static constexpr int LDS_BYTES = K_STAGES * K_BYTES + V_STAGES * V_BYTES;
-    // Direct global->LDS loads: one wave instruction fills 64 consecutive
-    // 16-byte units, so a tile takes K_UNITS (V_UNITS) instructions, dealt
-    // round-robin to the leading wavefronts.
-    static constexpr int K_DMA = K_UNITS;
-    static constexpr int V_DMA = V_UNITS;
-    static constexpr int K_DMA_PER_WAVE = (K_DMA + kLoaders - 1) / kLoaders;
-    static constexpr int V_DMA_PER_WAVE = (V_DMA + kLoaders - 1) / kLoaders;
+    static constexpr int KK = D / 16;              // QK^T MFMA steps along d
+    static constexpr int EB = D / 32;              // 32-wide blocks of the output dim
+    static constexpr int U = D / 8;                // 16-byte units per K or V row
+    static constexpr int R = 16 / U;               // rows per 256-byte line of the 64 banks
+    static constexpr int ROW_BYTES = 2 * D;        // K/V rows are stored unpadded
+    static constexpr int TILE_BYTES = kBN * ROW_BYTES;
+    static constexpr int NI = TILE_BYTES / 1024;   // direct-load instructions per tile
+    static constexpr int NI_W = NI / kWaves;       // ... issued by each wavefront
+    static constexpr int NS = 2 * KK;              // S MFMAs per step (KK d-steps x 2 row blocks)
+    static constexpr int NP = 4 * EB;              // PV MFMAs per step (2 chunks x EB x 2 row blocks)
+    static constexpr int NV_FR = 2 * EB;           // V fragments per step
+    static constexpr int LDS_BYTES = (kKStages + kVStages) * TILE_BYTES;
     // One partial-result slot of the workspace: unnormalised O (rounded to
     // bf16, kBM x D), then the reference max (log2 units) and sum of each
     // row in fp32.
     static constexpr size_t SLOT_BYTES = size_t(kBM) * D * 2 + size_t(kBM) * 8;
+    static_assert(NI % kWaves == 0, "whole direct-load instructions per wavefront");
 };
 
+// XOR swizzles of the 16-byte units of LDS row `row` (unit u is stored at
+// u ^ swz(row)).  K: the 16 rows that one ds_read_b128 cycle serves fall on
+// 16 distinct units of the 64 banks.  V: the 4 rows x 4 units that 32 lanes
+// of one transposed read touch fall on 16 distinct units.
+template <int D>
+__device__ __forceinline__ constexpr int swz_k(int row) {
+    return (row / Tile<D>::R) % Tile<D>::U;
+}
+template <int D>
+__device__ __forceinline__ constexpr int swz_v(int row) {
+    return 4 * ((row / Tile<D>::R) % (Tile<D>::U / 4));
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // ---------------------------------------------------------------------------
-// Schedule.  Per rank r (sequences sorted longest first, ties by index):
-// seq[r], tiles[r] = ceil(L/kBM), nkv[r] = ceil(L/kBN) and the exclusive
-// prefix it_start[r] of tiles*H*nkv (it_start[n] = W, the total number of
-// (tile, key-step) iterations).  Workspace header (bytes): [0,8) W,
+// Schedule.  Per rank r: seq[r], tiles[r] = ceil(L/kBM), nkv[r] = ceil(L/kBN)
+// and the exclusive prefix it_start[r] of tiles*H*nkv (it_start[n] = W, the
+// total number of (tile, key-step) iterations).  Sequences are ranked by
+// descending octave floor(log2(nkv)) of their key-step count, ties by
+// sequence index (empty sequences last).  Workspace header (bytes): [0,8) W,
 // [8,12) n, then int32 seq[n], tiles[n], nkv[n], then (8-aligned) int64
 // it_start[n+1]; partial slots start at the next 256-byte boundary.
 // ---------------------------------------------------------------------------
@@ -122,22 +151,32 @@ struct Sched {
     int64_t W;
 };
 
+constexpr int kOctaves = 32;   // octave classes of the key-step count (class 0: empty)
+
 __host__ __device__ constexpr size_t sched_ints_end(int n) { return size_t(12) + size_t(12) * n; }
 __host__ __device__ constexpr size_t sched_prefix_off(int n) { return (sched_ints_end(n) + 7) / 8 * 8; }
 __host__ __device__ constexpr size_t sched_bytes(int n) {
     return (sched_prefix_off(n) + size_t(8) * (n + 1) + 255) / 256 * 256;
 }
 
-// Build the schedule into the given arrays (LDS or global); every thread of
-// the block calls it.
-__device__ void build_schedule(const int32_t* __restrict__ cu, int n, int H, int32_t* seq,
-                               int32_t* tiles, int32_t* nkv, int64_t* it_start) {
+// Octave class of a sequence of L tokens: 1 + floor(log2(ceil(L / kBN))),
+// 0 for an empty sequence.
+__device__ __forceinline__ int octave_class(int L) {
+    const int nk = (L + kBN - 1) / kBN;
+    return nk == 0 ? 0 : 32 - __clz(nk);
+}
+
+// In-kernel schedule of a small pack (n <= kInlineSeqs), built in LDS by
+// every thread of the block.
+__device__ void build_schedule_small(const int32_t* __restrict__ cu, int n, int H, int32_t* seq,
+                                     int32_t* tiles, int32_t* nkv, int64_t* it_start) {
     for (int s = threadIdx.x; s < n; s += blockDim.x) {
         const int Ls = cu[s + 1] - cu[s];
+        const int cs = octave_class(Ls);
         int rank = 0;
         for (int i = 0; i < n; ++i) {
-            const int Li = cu[i + 1] - cu[i];
-            rank += (Li > Ls) || (Li == Ls && i < s);
+            const int ci = octave_class(cu[i + 1] - cu[i]);
+            rank += (ci > cs) || (ci == cs && i < s);
         }
         seq[rank] = s;
         tiles[rank] = (Ls + kBM - 1) / kBM;
@@ -155,14 +194,78 @@ __device__ void build_schedule(const int32_t* __restrict__ cu, int n, int H, int
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void attn_schedule_kernel(const int32_t* __restrict__ cu, int n,
-                                                            int H, unsigned char* __restrict__ ws) {
+// Schedule of a pack of any size in O(n / 256 + 256) per thread: a stable
+// counting sort on the octave class.  Thread t owns the contiguous index
+// range [t*per, (t+1)*per); its per-class counts, prefix-summed over the
+// threads, give every sequence its rank in (descending class, index) order.
+constexpr int kSchedThreads = 256;
+__global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(const int32_t* __restrict__ cu, int n,
+                                                                      int H, unsigned char* __restrict__ ws) {
+    __shared__ int cnt[kSchedThreads][kOctaves];
+    __shared__ int start[kOctaves];
+    __shared__ int64_t part[kSchedThreads];
     int32_t* ints = reinterpret_cast<int32_t*>(ws + 8);
+    int32_t* seq = ints + 1;
+    int32_t* tiles = ints + 1 + n;
+    int32_t* nkv = ints + 1 + 2 * n;
     int64_t* pre = reinterpret_cast<int64_t*>(ws + sched_prefix_off(n));
-    build_schedule(cu, n, H, ints + 1, ints + 1 + n, ints + 1 + 2 * n, pre);
-    if (threadIdx.x == 0) {
-        *reinterpret_cast<int64_t*>(ws) = pre[n];
+    const int tid = threadIdx.x;
+    const int per = (n + kSchedThreads - 1) / kSchedThreads;
+    const int s0 = min(n, tid * per), s1 = min(n, s0 + per);
+#pragma unroll
+    for (int c = 0; c < kOctaves; ++c) cnt[tid][c] = 0;
+    for (int s = s0; s < s1; ++s) ++cnt[tid][octave_class(cu[s + 1] - cu[s])];
+    __syncthreads();
+    if (tid < kOctaves) {                 // exclusive prefix over the threads, per class
+        int acc = 0;
+        for (int t = 0; t < kSchedThreads; ++t) {
+            const int v = cnt[t][tid];
+            cnt[t][tid] = acc;
+            acc += v;
+        }
+        start[tid] = acc;                 // class total for now
+    }
+    __syncthreads();
+    if (tid == 0) {                       // class starts, highest class first
+        int acc = 0;
+        for (int c = kOctaves - 1; c >= 0; --c) {
+            const int v = start[c];
+            start[c] = acc;
+            acc += v;
+        }
+    }
+    __syncthreads();
+    for (int s = s0; s < s1; ++s) {
+        const int L = cu[s + 1] - cu[s];
+        const int c = octave_class(L);
+        const int r = start[c] + cnt[tid][c]++;
+        seq[r] = s;
+        tiles[r] = (L + kBM - 1) / kBM;
+        nkv[r] = (L + kBN - 1) / kBN;
+    }
+    __threadfence_block();
+    __syncthreads();
+    // exclusive prefix of tiles*H*nkv over the ranks
+    int64_t sum = 0;
+    for (int r = s0; r < s1; ++r) sum += int64_t(tiles[r]) * H * nkv[r];
+    part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int64_t acc = 0;
+        for (int t = 0; t < kSchedThreads; ++t) {
+            const int64_t v = part[t];
+            part[t] = acc;
+            acc += v;
+        }
+        pre[n] = acc;
+        *reinterpret_cast<int64_t*>(ws) = acc;
         ints[0] = n;
+    }
+    __syncthreads();
+    int64_t acc = part[tid];
+    for (int r = s0; r < s1; ++r) {
+        pre[r] = acc;
+        acc += int64_t(tiles[r]) * H * nkv[r];
     }
 }
 
@@ -176,7 +279,7 @@ __device__ Sched get_schedule(const int32_t* cu, int n, int H, const unsigned ch
     Sched s;
     s.n = n;
     if (n <= kInlineSeqs) {
-        build_schedule(cu, n, H, lds.seq, lds.tiles, lds.nkv, lds.it_start);
+        build_schedule_small(cu, n, H, lds.seq, lds.tiles, lds.nkv, lds.it_start);
         s.seq = lds.seq;
         s.tiles = lds.tiles;
         s.nkv = lds.nkv;
@@ -238,9 +341,36 @@ struct KParams {
     float scale_log2;    // softmax_scale * log2(e)
 };
 
-// Wait until this wavefront's direct global->LDS loads have landed
-// (vmcnt(0); expcnt and lgkmcnt left unconstrained).
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// LDS byte address of a pointer into LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) unsigned char*)(p)));
+}
+
+// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at LDS
+// address lds + 16*i; offsets past the resource's range deposit zeros.
+// Written in assembly so that the compiler does not treat it as an LDS write
+// (it would then wait for all outstanding loads before every transposed LDS
+// read); its completion is awaited explicitly with vmcnt.  lds and soff are
+// wavefront-uniform.  The load gets the five wait states a VMEM read of an
+// SGPR needs after a VALU (readfirstlane) wrote it, which the compiler cannot
+// provide for an instruction inside assembly; they also cover the one a
+// direct load needs after M0 is written.
+__device__ __forceinline__ void dma16_asm(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r),
+                   "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory");
+}
+
+// vmcnt waits (expcnt and lgkmcnt unconstrained); vmcnt is 6 bits, split
+// over bits [3:0] and [15:14] of the immediate.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // Lanes l and l+32 hold the two halves of one query row's keys: combine them
 // with one v_permlane32_swap (each lane ends with {own, partner} in some order).
@@ -253,14 +383,21 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Score tile of one 32-key step for the lane's query row: 16 keys per lane,
+// for both 32-row blocks of the wavefront.
+typedef f32x16_t Scores[2];
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
     using TL = Tile<D>;
+    constexpr int KK = TL::KK, EB = TL::EB, NI_W = TL::NI_W, NS = TL::NS, NP = TL::NP;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ SchedLds sched_lds;
+    __shared__ int redo_flag[kWaves];
 
     const Sched sch = get_schedule(p.cu, p.n_seq, p.H, p.ws, sched_lds);
     const int g = logical_wg(blockIdx.x, p.G);
+    const int64_t it_begin = range_begin(sch.W, g, p.G);
     const int64_t it_end = range_begin(sch.W, g + 1, p.G);
     unsigned char* const partials = p.ws + sched_bytes(p.n_seq);
 
@@ -269,45 +406,56 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hlf = lane >> 5;
-    // Waves 0..3 (one per SIMD) lead and issue the direct loads; waves 4..7
-    // trail them by one softmax phase (see the step loop below).
-    const bool lead = wave < kLoaders;
-    const int lw = wave & (kLoaders - 1);
     const int64_t ld = p.ld_qkv;
     const uint32_t row_bytes = uint32_t(ld) * 2u;
     const float c = p.scale_log2;
 
-    // ---- direct-load offsets and LDS read addresses (same for every tile) --
-    // DMA instruction n of a tile covers units [64n, 64n+64); lane i fetches
-    // unit 64n+i = (row, chunk) of the padded LDS image.  Pad units fetch a
-    // duplicate of the row's last chunk (never read back).  Instruction n is
-    // issued by leading wave n % kLoaders.
-    uint32_t k_dma_off[TL::K_DMA_PER_WAVE], v_dma_off[TL::V_DMA_PER_WAVE];
+    // LDS: K stages 0 .. kKStages-1, then V stages 0 .. kVStages-1.
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+    auto kstage = [&](int s) -> const unsigned char* { return smem + s * TL::TILE_BYTES; };
+    auto vstage = [&](int s) -> const unsigned char* { return smem + (kKStages + s) * TL::TILE_BYTES; };
+
+    // ---- direct-load source offsets (same for every tile) ------------------
+    // Instruction n of a tile fills LDS units [64n, 64n+64) of the stage;
+    // lane i fills unit 64n+i = (row, stored unit) and so fetches the row's
+    // unit (stored unit ^ swizzle).  Wavefront w issues instructions
+    // w, w+4, ...
+    uint32_t k_voff[NI_W], v_voff[NI_W];
 #pragma unroll
-    for (int j = 0; j < TL::K_DMA_PER_WAVE; ++j) {
-        const int u = 64 * (lw + kLoaders * j) + lane;
-        const int cc = u % TL::K_UNITS;
-        k_dma_off[j] = uint32_t(u / TL::K_UNITS) * row_bytes + 16u * uint32_t(cc < TL::KCH ? cc : TL::KCH - 1);
+    for (int j = 0; j < NI_W; ++j) {
+        const int u = 64 * (wave + kWaves * j) + lane;
+        const int row = u / TL::U, su = u % TL::U;
+        k_voff[j] = uint32_t(row) * row_bytes + 16u * uint32_t(su ^ swz_k<D>(row));
+        v_voff[j] = uint32_t(row) * row_bytes + 16u * uint32_t(su ^ swz_v<D>(row));
     }
-#pragma unroll
-    for (int j = 0; j < TL::V_DMA_PER_WAVE; ++j) {
-        const int u = 64 * (lw + kLoaders * j) + lane;
-        const int cc = u % TL::V_UNITS;
-        v_dma_off[j] = uint32_t(u / TL::V_UNITS) * row_bytes + 16u * uint32_t(cc < TL::KCH ? cc : TL::KCH - 1);
-    }
-    // K fragment of lane: row l32 (+32 per key block), bytes 16*hlf (+32 per kk).
-    const int k_rd = l32 * TL::K_ROW_BYTES + hlf * 16;
-    // V^T fragment via two transposed reads: in each 16-lane group lane j
-    // addresses row (4h + j/4) of the 16-key chunk (+8 rows for the second
-    // read) at dims 32m + 16*(group&1) + 4*(j&3); lane i then receives dim
-    // 32m + (lane&31) for 4 consecutive keys.
-    const int v_rd = (4 * hlf + ((lane & 15) >> 2)) * TL::V_ROW_BYTES +
-                     2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-    auto kbuf = [&](int b) { return smem + b * TL::K_BYTES; };
-    auto vbuf = [&](int b) { return smem + TL::K_STAGES * TL::K_BYTES + b * TL::V_BYTES; };
+    // ---- LDS read offsets ----------------------------------------------------
+    // K fragment kk (d-step kk): row l32, unit 2 kk + hlf, stored at
+    // (2 kk + hlf) ^ swz(l32), i.e. at byte k_rd ^ 32 kk.
+    const uint32_t k_rd = uint32_t(l32 * TL::ROW_BYTES + 16 * (hlf ^ swz_k<D>(l32)));
+    // V^T fragment gi (16-key chunk gi / EB, output block m = gi % EB) via two
+    // transposed reads: in each 16-lane group lane j addresses row
+    // 16 cc + 4 hlf + j/4 (+8 for the second read) at dims
+    // 32m + 16*(group&1) + 4*(j&3); lane i then receives dim 32m + (lane&31)
+    // for 4 consecutive keys.  The swizzle of those rows depends only on j/4
+    // and is a multiple of 4 units, so output block m is stored at
+    // byte v_rd ^ 64 m.
+    const uint32_t v_rd = [&] {
+        const int vrow = 4 * hlf + ((lane & 15) >> 2);
+        const int vu = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        return uint32_t(vrow * TL::ROW_BYTES + 16 * (vu ^ swz_v<D>(vrow)) + 8 * (lane & 1));
+    }();
+    auto kfrag = [&](const unsigned char* kb, int kk) -> bf16x8_t {
+        return *reinterpret_cast<const bf16x8_t*>(kb + (k_rd ^ uint32_t(32 * kk)));
+    };
+    auto vfrag = [&](const unsigned char* vb, int gi) -> bf16x8_t {
+        const unsigned char* a = vb + (gi / EB) * 16 * TL::ROW_BYTES + (v_rd ^ uint32_t(64 * (gi % EB)));
+        const s16x4_t lo = lds_read_tr16_b64(a);
+        const s16x4_t hi = lds_read_tr16_b64(a + 8 * TL::ROW_BYTES);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
     bool first_segment = true;
-    for (int64_t it = range_begin(sch.W, g, p.G); it < it_end;) {
+    for (int64_t it = it_begin; it < it_end;) {
         // ---- the segment: one tile's key steps [kv0, kv1) -------------------
         // The segment is the same for every lane; readfirstlane says so, so
         // that the buffer resources and offsets below live in SGPRs.
@@ -319,14 +467,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
         const int tile = __builtin_amdgcn_readfirstlane(at.tile);
         const int kv0 = __builtin_amdgcn_readfirstlane(at.step);
         const int kv1 = __builtin_amdgcn_readfirstlane(int(min(int64_t(nkv), int64_t(kv0) + (it_end - it))));
+        const bool first_piece = it == it_begin;
         const int head = tile / nt;
         const int qtile = tile - head * nt;
         const int64_t tok0 = __builtin_amdgcn_readfirstlane(p.cu[seq]);
         const int L = __builtin_amdgcn_readfirstlane(p.cu[seq + 1]) - int(tok0);
-        // the last key tile of a sequence whose length is not a multiple of
-        // kBN has keys past the end: those scores are masked
-        const int masked_tile = (L % kBN) != 0 ? nkv - 1 : nkv;
+        // Key step j of a tile processes key tile (j + nkv - 1) % nkv: the
+        // sequence's last key tile, the only one with keys past the end
+        // (masked when L is not a multiple of kBN), comes first, so only the
+        // first step of a tile's first segment ever masks and the step loop
+        // has no mask branch (the softmax does not depend on key order).
+        const bool mask_first = kv0 == 0 && (L % kBN) != 0;
         it += kv1 - kv0;
+        const int n = kv1 - kv0;
 
         // Buffer resources over this sequence's rows of the head: loads of
         // rows at or past L return zeros (ragged q-tile and last key tile).
@@ -335,232 +488,339 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(KParams p) {
         const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(p.q + head_off, seq_bytes);
         const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(p.k + head_off, seq_bytes);
         const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(p.v + head_off, seq_bytes);
-
-        // Direct loads of key tile `t` into K buffer kb / V buffer vb
-        // (leading waves only).
-        auto dma_k = [&](int t, int kb) {
-            const uint32_t base = uint32_t(t) * kBN * row_bytes;
-#pragma unroll
-            for (int j = 0; j < TL::K_DMA_PER_WAVE; ++j) {
-                const int nidx = lw + kLoaders * j;
-                if (TL::K_DMA % kLoaders == 0 || nidx < TL::K_DMA)
-                    dma16(k_rs, kbuf(kb) + 1024 * nidx, k_dma_off[j], base);
-            }
+        // Scalar offset of key step j's tile, or an out-of-range offset for a
+        // step this segment does not take (the load then deposits zeros
+        // without touching memory; an offset that still lands inside a
+        // sequence of more than 2 GiB reads valid rows into a stage nobody
+        // reads).
+        auto tile_soff = [&](int j) -> uint32_t {
+            const int kt = j == 0 ? nkv - 1 : j - 1;
+            return j < kv1 ? uint32_t(kt) * uint32_t(kBN) * row_bytes : kOutOfRange;
         };
-        auto dma_v = [&](int t, int vb) {
-            const uint32_t base = uint32_t(t) * kBN * row_bytes;
-#pragma unroll
-            for (int j = 0; j < TL::V_DMA_PER_WAVE; ++j) {
-                const int nidx = lw + kLoaders * j;
-                if (TL::V_DMA % kLoaders == 0 || nidx < TL::V_DMA)
-                    dma16(v_rs, vbuf(vb) + 1024 * nidx, v_dma_off[j], base);
-            }
+        auto dma_k = [&](int stage, uint32_t so, int j) {
+            dma16_asm(k_rs, lds0 + stage * TL::TILE_BYTES + 1024 * (wave + kWaves * j), k_voff[j], so);
         };
-        auto dma = [&](int t, int kb, int vb) {
-            dma_k(t, kb);
-            dma_v(t, vb);
+        auto dma_v = [&](int stage, uint32_t so, int j) {
+            dma16_asm(v_rs, lds0 + (kKStages + stage) * TL::TILE_BYTES + 1024 * (wave + kWaves * j),
+                      v_voff[j], so);
         };
 
-        // Q^T fragments (B operand), kept in registers.
-        const int qrow = qtile * kBM + wave * 32 + l32;    // row inside the sequence
-        bf16x8_t qf[TL::KK];
-        {
+        // Q^T fragments (B operand) of the two row blocks, kept in registers.
+        bf16x8_t qf[2][KK];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int qrow = qtile * kBM + wave * kRows + 32 * b + l32;
             const uint32_t qoff = uint32_t(qrow) * row_bytes + 16u * hlf;
 #pragma unroll
-            for (int kk = 0; kk < TL::KK; ++kk)
-                qf[kk] = __builtin_bit_cast(bf16x8_t, bload16(q_rs, qoff, 32u * kk));
+            for (int kk = 0; kk < KK; ++kk)
+                qf[b][kk] = __builtin_bit_cast(bf16x8_t, bload16(q_rs, qoff, 32u * kk));
         }
 
-        f32x16_t oacc[TL::EB];
+        // Keys at or past L of the score tile s of the sequence's last key
+        // tile: -inf.
+        auto mask_scores = [&](Scores& s) {
+            const int lim = L - (nkv - 1) * kBN - 4 * hlf;   // key offsets >= lim are past the end
 #pragma unroll
-        for (int m = 0; m < TL::EB; ++m)
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[m][r] = 0.f;
-        float m_run = -INFINITY;
-        float l_run = 0.f;
-
-        // Operand fragments: S op i reads K fragment i (key block i&1, d-step
-        // i>>1); PV op j reads the V^T fragment of (chunk j/EB, output block
-        // j%EB) with two transposed reads (keys 4h..4h+3, 8+4h..8+4h+3).
-        auto kfrag = [&](int i, const unsigned char* kb) -> bf16x8_t {
-            return *reinterpret_cast<const bf16x8_t*>(kb + k_rd + (i & 1) * 32 * TL::K_ROW_BYTES + (i >> 1) * 32);
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + (r & 3) >= lim) s[b][r] = -INFINITY;
         };
-        auto vfrag = [&](int j, const unsigned char* vb) -> bf16x8_t {
-            const unsigned char* a = vb + v_rd + (j / TL::EB) * 16 * TL::V_ROW_BYTES + (j % TL::EB) * 64;
-            const s16x4_t lo = lds_read_tr16_b64(a);
-            const s16x4_t hi = lds_read_tr16_b64(a + 8 * TL::V_ROW_BYTES);
-            return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-
-        // S^T = K Q^T for one key tile held in K buffer kb.
-        f32x16_t s[2];
-        auto qk = [&](const unsigned char* __restrict__ kb) {
-            bf16x8_t fr[kPrefetch];
+        // S = K Q^T of the K tile in LDS at kb (no overlapped work).
+        auto scores = [&](Scores& s, const unsigned char* kb) {
 #pragma unroll
-            for (int i = 0; i < kPrefetch; ++i) fr[i] = kfrag(i, kb);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int kk = 0; kk < KK; ++kk) {
+                const bf16x8_t f = kfrag(kb, kk);
 #pragma unroll
-            for (int i = 0; i < TL::NQK; ++i) {
-                const bf16x8_t f = fr[i % kPrefetch];
-                if (i < 2)
-                    s[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[0], f32x16_t{}, 0, 0, 0);
-                else
-                    s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[i >> 1], s[i & 1], 0, 0, 0);
-                if (i + kPrefetch < TL::NQK) fr[i % kPrefetch] = kfrag(i + kPrefetch, kb);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int b = 0; b < 2; ++b)
+                    s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[b][kk], kk == 0 ? f32x16_t{} : s[b], 0, 0, 0);
             }
         };
 
-        // Online softmax of key tile t (scores in s) for this lane's query
-        // row, then O^T += V^T P^T with the tile's V in buffer vb.  The
-        // exponentials use a reference max m_run that is only raised when a
-        // row's block max exceeds it by more than kRescaleLog2 (so p <=
-        // 2^kRescaleLog2); numerator and denominator share m_run, so the
-        // result is the same softmax, and the output accumulator is rescaled
-        // only on those (rare, wave-uniform) occasions.
-        auto softmax_pv = [&](int t, const unsigned char* __restrict__ vb) {
-            if (t == masked_tile) {
-                const int key0 = t * kBN;
-#pragma unroll
-                for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + 32 * bb + 8 * (r >> 2) + 4 * hlf + (r & 3);
-                        if (key >= L) s[bb][r] = -INFINITY;
-                    }
-            }
-            float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int r = (bb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
-            mx = half_max(mx) * c;
-            const bool raise = mx > m_run + kRescaleLog2;
-            if (__any(raise)) {
-                const float m_new = raise ? mx : m_run;
-                const float alpha = exp2f(m_run - m_new);      // 1 where not raised, 0 at start
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int m = 0; m < TL::EB; ++m)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
-            }
-            float lsum = 0.f;
-            bf16x8_t pf[4];
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const int bb = cc >> 1, r0 = 8 * (cc & 1);
-                float e[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r0 + i], c, -m_run));
-                    lsum += e[i];
-                }
-                u32x4_t u;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) u[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
-                pf[cc] = __builtin_bit_cast(bf16x8_t, u);
-            }
-            l_run += lsum;
-
-            // O^T += V^T P^T over EB independent accumulators, chunk outer.
-            bf16x8_t fr[kPrefetch];
-#pragma unroll
-            for (int i = 0; i < kPrefetch; ++i) fr[i] = vfrag(i, vb);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < TL::NPV; ++i) {
-                const bf16x8_t f = fr[i % kPrefetch];
-                oacc[i % TL::EB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[i / TL::EB],
-                                                                          oacc[i % TL::EB], 0, 0, 0);
-                if (i + kPrefetch < TL::NPV) fr[i % kPrefetch] = vfrag(i + kPrefetch, vb);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-
-        // ---- key steps -----------------------------------------------------
-        // Iteration i (0 <= i <= n) runs softmax + PV of tile i-1, then S of
-        // tile i; the leading waves pass the step barrier between the two,
-        // the trailing waves after both.  Between two barriers a leading wave
-        // thus runs S(i), softmax(i), PV(i) while a trailing wave runs
-        // softmax(i), PV(i), S(i+1): on each SIMD one wave's softmax (VALU)
-        // overlaps the other wave's MFMAs instead of both alternating in
-        // lockstep.  In that interval K of tiles i and i+1 and V of tile i
-        // are read, so K of tile i+2 and V of tile i+1 are fetched into the
-        // third K buffer and the second V buffer (K of tile i in buffer i%3,
-        // V in buffer i%2).  Only the leading waves load; each barrier
-        // follows its wave's own loads landing.
-        const int n = kv1 - kv0;
-        if (lead) {
-            dma(kv0, 0, 0);
-            if (n > 1) dma_k(kv0 + 1, 1);
-        }
-        wait_dma();
-        __syncthreads();
-        int k0 = 0, k1 = 1, k2 = 2, v0 = 0;     // K buffers of tiles i, i+1, i+2; V of tile i
-        for (int i = 0; i <= n; ++i) {
-            if (i > 0) softmax_pv(kv0 + i - 1, vbuf(v0 ^ 1));
-            if (lead) {
-                wait_dma();
-                __syncthreads();
-                if (i + 2 < n) dma_k(kv0 + i + 2, k2);
-                if (i + 1 < n) dma_v(kv0 + i + 1, v0 ^ 1);
-            }
-            if (i < n) qk(kbuf(k0));
-            if (!lead) {
-                wait_dma();
+        // The reference max of each row (log2 units) is fixed by the first
+        // key step, and a step only records whether a row max has since
+        // grown past it by more than 2^kRescaleLog2 (raise).  If any row did,
+        // the whole workgroup redoes the segment once with every reference
+        // max preset to the row's exact maximum over the segment's keys
+        // (found by a scores-only pass), after which no raise is possible.
+        // So the output accumulators are only ever written by MFMAs.
+        bool preset = false;
+        float m_pre[2] = {-INFINITY, -INFINITY};
+        for (;;) {
+            // The previous segment's (or attempt's) LDS reads are done and its
+            // loads landed before its stages are refilled.
+            if (!first_segment) {
+                wait_vm<0>();
                 __syncthreads();
             }
-            const int kt = k0;
-            k0 = k1;
-            k1 = k2;
-            k2 = kt;
-            v0 ^= 1;
-        }
-
-        // ---- epilogue ----------------------------------------------------
-        const float l_tot = half_sum(l_run);
-        if (kv0 == 0 && kv1 == nkv) {
-            // whole tile: normalise and store O (bf16) and the LSE
-            if (qrow < L) {
-                const float inv = 1.0f / l_tot;
-                uint16_t* op = p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 4 * hlf;
+            first_segment = false;
+            if (preset) {
+                // exact row maxima over key steps kv0 .. kv1-1, one tile at a
+                // time through K stage 0
+                Scores sp;
+                for (int j = kv0; j < kv1; ++j) {
 #pragma unroll
-                for (int m = 0; m < TL::EB; ++m)
+                    for (int jj = 0; jj < NI_W; ++jj) dma_k(0, tile_soff(j), jj);
+                    wait_vm<0>();
+                    __syncthreads();
+                    scores(sp, kstage(0));
+                    if (j == 0 && mask_first) mask_scores(sp);
 #pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        u32x2_t val;
-                        val[0] = pack_bf16x2(oacc[m][4 * gq] * inv, oacc[m][4 * gq + 1] * inv);
-                        val[1] = pack_bf16x2(oacc[m][4 * gq + 2] * inv, oacc[m][4 * gq + 3] * inv);
-                        *reinterpret_cast<u32x2_t*>(op + 32 * m + 8 * gq) = val;
+                    for (int b = 0; b < 2; ++b) {
+                        float mxb = sp[b][0];
+#pragma unroll
+                        for (int r = 1; r < 16; ++r) mxb = fmaxf(mxb, sp[b][r]);
+                        m_pre[b] = fmaxf(m_pre[b], half_max(mxb) * c);
                     }
-                if (p.lse != nullptr && hlf == 0)
-                    p.lse[int64_t(head) * p.T + tok0 + qrow] = m_run * 0.69314718055994531f + logf(l_tot);
-            }
-        } else {
-            // piece of a tile shared with other workgroups: partial in slot
-            // 2g (this workgroup's first segment) or 2g+1 (its last)
-            unsigned char* slot = partials + size_t(2 * g + (first_segment ? 0 : 1)) * TL::SLOT_BYTES;
-            uint16_t* acc = reinterpret_cast<uint16_t*>(slot);
-            float* ml = reinterpret_cast<float*>(slot + size_t(kBM) * D * 2);
-            const int row = wave * 32 + l32;
-#pragma unroll
-            for (int m = 0; m < TL::EB; ++m)
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    u32x2_t val;
-                    val[0] = pack_bf16x2(oacc[m][4 * gq], oacc[m][4 * gq + 1]);
-                    val[1] = pack_bf16x2(oacc[m][4 * gq + 2], oacc[m][4 * gq + 3]);
-                    *reinterpret_cast<u32x2_t*>(acc + row * D + 32 * m + 8 * gq + 4 * hlf) = val;
+                    __syncthreads();
                 }
-            if (hlf == 0) {
-                ml[row] = m_run;
-                ml[kBM + row] = l_tot;
             }
+            // K stage i holds tiles kv0+i, kv0+i+kKStages, ...; V stage i holds
+            // tiles kv0+i, kv0+i+kVStages, ...  The prologue loads K of tiles
+            // kv0 .. kv0+kKStages-1 and V of tiles kv0 .. kv0+kVStages-2.
+#pragma unroll
+            for (int i = 0; i < kKStages; ++i)
+#pragma unroll
+                for (int j = 0; j < NI_W; ++j) dma_k(i, tile_soff(kv0 + i), j);
+#pragma unroll
+            for (int i = 0; i < kVStages - 1; ++i)
+#pragma unroll
+                for (int j = 0; j < NI_W; ++j) dma_v(i, tile_soff(kv0 + i), j);
+
+            f32x16_t o[2][EB];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int m = 0; m < EB; ++m)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[b][m][r] = 0.f;
+            float m_run[2], lsum[2] = {0.f, 0.f};
+            bool raised = false;
+
+            bf16x8_t kf[kPfK], vf[kPfV];
+            bf16x8_t pf[2][2];
+            Scores h0, h1;
+
+            wait_vm<0>();
+            __syncthreads();
+
+            // ---- phase 1: S(t+1) = K(t+1) Q^T || p = exp2(x(t)) (kExp) ------
+            // Slot i issues S MFMA i (d-step i/2, row block i % 2: each K
+            // fragment feeds the two row blocks) and the exponentials of x
+            // elements [E i, E i + E) (element e: row block e/16, register
+            // e%16); the bf16 rounding and row sums of slot i's pairs run in
+            // slot i+1.  The first V fragments of phase 2 are read in the last
+            // slots.
+            auto phase1 = [&]<bool kS>(Scores& x, Scores& s, const unsigned char* kb, const unsigned char* vb) {
+                constexpr int E = 32 / NS;
+                float ex[E];
+                static_for<NS + 1>([&](auto SI) {
+                    constexpr int sl = SI;
+                    if constexpr (kS && sl < NS) {
+                        constexpr int kk = sl / 2, b = sl % 2;
+                        if constexpr (kk == 0)
+                            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kPfK], qf[b][kk], f32x16_t{}, 0, 0, 0);
+                        else
+                            s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kPfK], qf[b][kk], s[b], 0, 0, 0);
+                        if constexpr (b == 1 && kk + kPfK < KK) kf[kk % kPfK] = kfrag(kb, kk + kPfK);
+                    }
+                    if constexpr (sl > 0) {
+                        // bf16 rounding and row sums of the previous slot's pairs
+#pragma unroll
+                        for (int i = 0; i < E; i += 2) {
+                            const int e = E * (sl - 1) + i;
+                            const int b = e / 16, r = e % 16;
+                            const uint32_t w = pack_bf16x2(ex[i], ex[i + 1]);
+                            const int cc = r / 8, dw = (r % 8) / 2;
+                            u32x4_t u = __builtin_bit_cast(u32x4_t, pf[b][cc]);
+                            u[dw] = w;
+                            pf[b][cc] = __builtin_bit_cast(bf16x8_t, u);
+                            lsum[b] += ex[i] + ex[i + 1];
+                        }
+                    }
+                    if constexpr (sl < NS) {
+#pragma unroll
+                        for (int i = 0; i < E; ++i) {
+                            const int e = E * sl + i;
+                            ex[i] = __builtin_amdgcn_exp2f(x[e / 16][e % 16]);
+                        }
+                    }
+                    if constexpr (sl >= NS + 1 - kPfV) vf[sl - (NS + 1 - kPfV)] = vfrag(vb, sl - (NS + 1 - kPfV));
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
+
+            // ---- phase 2: O += V(t)^T P(t)^T || front half of softmax(t+1) --
+            // Slot i issues PV MFMA i (chunk i / 2EB, output block (i/2) % EB,
+            // row block i % 2: each V fragment feeds the two row blocks).  With
+            // kNext the slots also carry the front half of the next tile's
+            // softmax: the row maxima of S(t+1), the raise check and
+            // x(t+1) = S(t+1) c - m, in place; they issue the step's direct
+            // loads (K of tile t+kKStages, V of tile t+kVStages-1) in slots
+            // 1 .. 2 NI_W and read the first K fragments of the next phase 1
+            // in the last slots.
+            auto phase2 = [&]<bool kNext>(Scores& s, const unsigned char* vb, const unsigned char* kb_next, int t,
+                                          int kdst, int vdst) {
+                constexpr int NMAX = 16;                 // 8 max ops per row block
+                constexpr int NFIN = 2;                  // raise check per row block
+                constexpr int NFMA = 32;
+                constexpr int NITEMS = kNext ? NMAX + NFIN + NFMA : 0;
+                float mx[2];
+                const uint32_t so_k = tile_soff(t + kKStages), so_v = tile_soff(t + kVStages - 1);
+                auto item = [&](auto II) {
+                    constexpr int I = II;
+                    if constexpr (I < NMAX) {
+                        constexpr int b = I / 8, j = I % 8;
+                        if constexpr (j == 0)
+                            mx[b] = fmaxf(s[b][0], s[b][1]);
+                        else
+                            mx[b] = fmaxf(mx[b], fmaxf(s[b][2 * j], s[b][2 * j + 1]));
+                    } else if constexpr (I < NMAX + NFIN) {
+                        constexpr int b = I - NMAX;
+                        raised |= __builtin_amdgcn_ballot_w64(half_max(mx[b]) * c > m_run[b] + kRescaleLog2) != 0;
+                    } else {
+                        constexpr int e = I - NMAX - NFIN;
+                        constexpr int b = e / 16, r = e % 16;
+                        s[b][r] = __builtin_fmaf(s[b][r], c, -m_run[b]);
+                    }
+                };
+                static_for<NP>([&](auto SI) {
+                    constexpr int sl = SI;
+                    constexpr int gi = sl / 2, b = sl % 2, cc = gi / EB, m = gi % EB;
+                    o[b][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[gi % kPfV], pf[b][cc], o[b][m], 0, 0, 0);
+                    if constexpr (b == 1 && gi + kPfV < TL::NV_FR) vf[gi % kPfV] = vfrag(vb, gi + kPfV);
+                    if constexpr (kNext && sl >= 1 && sl <= NI_W) dma_k(kdst, so_k, sl - 1);
+                    if constexpr (kNext && sl > NI_W && sl <= 2 * NI_W) dma_v(vdst, so_v, sl - NI_W - 1);
+                    constexpr int lo = NITEMS * sl / NP, hi = NITEMS * (sl + 1) / NP;
+                    static_for<hi - lo>([&](auto JI) { item(std::integral_constant<int, lo + int(JI)>{}); });
+                    if constexpr (kNext && sl >= NP - kPfK) kf[sl - (NP - kPfK)] = kfrag(kb_next, sl - (NP - kPfK));
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
+
+            // ---- first tile: S(kv0), its row maxima and x(kv0) -------------
+            scores(h0, kstage(0));
+            if (mask_first) mask_scores(h0);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                float mxb = fmaxf(h0[b][0], h0[b][1]);
+#pragma unroll
+                for (int r = 2; r < 16; r += 2) mxb = fmaxf(mxb, fmaxf(h0[b][r], h0[b][r + 1]));
+                m_run[b] = fmaxf(half_max(mxb) * c, m_pre[b]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) h0[b][r] = __builtin_fmaf(h0[b][r], c, -m_run[b]);
+            }
+#pragma unroll
+            for (int i = 0; i < kPfK; ++i) kf[i] = kfrag(kstage(1), i);
+            // every wavefront is done with K stage 0 before step 0 refills it
+            __syncthreads();
+
+            // ---- key steps ---------------------------------------------------
+            // Step i (tile t = kv0 + i) reads K(t+1) and V(t), refills the K
+            // stage of tile t with tile t+kKStages and the V stage of tile t-1
+            // with tile t+kVStages-1, waits until its own loads issued kSlack
+            // steps before or earlier have landed, and passes the step
+            // barrier.  A tile is read no earlier than the step after the
+            // barrier that published it, and a stage is refilled only after
+            // the barrier that ended its last reads.  x(t) and S(t+1)
+            // alternate between h0 and h1; the loop runs the steps in pairs
+            // (an odd first step is peeled) so that it has a single exit.
+            int ks = 1 % kKStages;         // K stage of tile t+1
+            int vs = 0;                    // V stage of tile t
+            auto step = [&](Scores& x, Scores& s, int i) {
+                const int t = kv0 + i;
+                const int ks2 = ks + 1 == kKStages ? 0 : ks + 1;       // K stage of tile t+2
+                const int kd = ks == 0 ? kKStages - 1 : ks - 1;         // K stage of tile t
+                const int vd = vs == 0 ? kVStages - 1 : vs - 1;         // V stage of tile t-1
+                phase1.template operator()<true>(x, s, kstage(ks), vstage(vs));
+                phase2.template operator()<true>(s, vstage(vs), kstage(ks2), t, kd, vd);
+                wait_vm<2 * NI_W * kSlack>();
+                __syncthreads();
+                ks = ks2;
+                vs = vs + 1 == kVStages ? 0 : vs + 1;
+            };
+            const int m_steps = n - 1;     // steps followed by another step
+            int i = 0;
+            if (m_steps & 1) {
+                step(h0, h1, i++);
+                h0[0] = h1[0];
+                h0[1] = h1[1];
+            }
+            for (; i < m_steps; i += 2) {
+                step(h0, h1, i);
+                step(h1, h0, i + 1);
+            }
+            phase1.template operator()<false>(h0, h0, kstage(0), vstage(vs));
+            phase2.template operator()<false>(h0, vstage(vs), kstage(0), kv1, 0, 0);
+
+            // ---- redo decision (workgroup-wide) --------------------------------
+            if (!preset) {
+                if (lane == 0) redo_flag[wave] = raised;
+                __syncthreads();
+                bool any = false;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) any |= redo_flag[w] != 0;
+                if (__builtin_amdgcn_readfirstlane(any)) {
+                    preset = true;
+                    continue;
+                }
+            }
+
+            // ---- epilogue --------------------------------------------------
+            float l_tot[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) l_tot[b] = half_sum(lsum[b]);
+            if (kv0 == 0 && kv1 == nkv) {
+                // whole tile: normalise and store O (bf16) and the LSE
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int qrow = qtile * kBM + wave * kRows + 32 * b + l32;
+                    if (qrow < L) {
+                        const float inv = 1.0f / l_tot[b];
+                        uint16_t* op = p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 4 * hlf;
+#pragma unroll
+                        for (int m = 0; m < EB; ++m)
+#pragma unroll
+                            for (int gq = 0; gq < 4; ++gq) {
+                                u32x2_t val;
+                                val[0] = pack_bf16x2(o[b][m][4 * gq] * inv, o[b][m][4 * gq + 1] * inv);
+                                val[1] = pack_bf16x2(o[b][m][4 * gq + 2] * inv, o[b][m][4 * gq + 3] * inv);
+                                *reinterpret_cast<u32x2_t*>(op + 32 * m + 8 * gq) = val;
+                            }
+                        if (p.lse != nullptr && hlf == 0)
+                            p.lse[int64_t(head) * p.T + tok0 + qrow] =
+                                m_run[b] * 0.69314718055994531f + logf(l_tot[b]);
+                    }
+                }
+            } else {
+                // piece of a tile shared with other workgroups: partial in slot
+                // 2g (this workgroup's first segment) or 2g+1 (its last)
+                unsigned char* slot = partials + size_t(2 * g + (first_piece ? 0 : 1)) * TL::SLOT_BYTES;
+                uint16_t* acc = reinterpret_cast<uint16_t*>(slot);
+                float* ml = reinterpret_cast<float*>(slot + size_t(kBM) * D * 2);
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int row = wave * kRows + 32 * b + l32;
+#pragma unroll
+                    for (int m = 0; m < EB; ++m)
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq) {
+                            u32x2_t val;
+                            val[0] = pack_bf16x2(o[b][m][4 * gq], o[b][m][4 * gq + 1]);
+                            val[1] = pack_bf16x2(o[b][m][4 * gq + 2], o[b][m][4 * gq + 3]);
+                            *reinterpret_cast<u32x2_t*>(acc + row * D + 32 * m + 8 * gq + 4 * hlf) = val;
+                        }
+                    if (hlf == 0) {
+                        ml[row] = m_run[b];
+                        ml[kBM + row] = l_tot[b];
+                    }
+                }
+            }
+            break;
         }
-        first_segment = false;
     }
+    // no direct load may still be in flight when the wavefront ends
+    wait_vm<0>();
 }
 
 // Merge the partial pieces of every tile that a range boundary cut.  Block
@@ -658,7 +918,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
     if (G <= 0) return hipErrorInvalidDevice;
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     if (a.n_seq > kInlineSeqs) {
-        hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens,
+        hipLaunchKernelGGL(attn_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a.cu_seqlens,
                            a.n_seq, a.H, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
