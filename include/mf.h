@@ -172,6 +172,16 @@ mf_status mf_varlen_attn_fwd(void* stream,
                              int64_t T, int32_t H, int32_t D, int64_t ld_qkv, int64_t ld_o,
                              float softmax_scale, void* workspace, size_t workspace_bytes);
 
+/* Test hook: the persistent grid of mf_varlen_attn_fwd.
+ * g > 0 runs the attention forward on g persistent workgroups instead of one
+ * per compute unit, which moves the cut points of its stream-K work split
+ * (tests use it to show that results do not depend on them); g = 0 restores
+ * the default.  The setting is process-wide and also changes
+ * mf_varlen_attn_workspace_bytes, so set it before sizing a workspace and
+ * not while attention calls are in flight.
+ * Errors: MF_ERR_SHAPE for g < 0 or g > 65536. */
+mf_status mf_set_attn_fwd_grid(int32_t g);
+
 /* ------------------------------------------------------------------------
  * Backward of the block-diagonal attention (training).
  *

@@ -180,6 +180,12 @@ mf_status mf_varlen_attn_fwd(void* stream, const void* q, const void* k, const v
     return finish(mf::launch_varlen_attn_fwd(a, s), s);
 }
 
+mf_status mf_set_attn_fwd_grid(int32_t g) {
+    if (g < 0 || g > 65536) return MF_ERR_SHAPE;
+    mf::set_attn_fwd_grid(g);
+    return MF_OK;
+}
+
 size_t mf_varlen_attn_bwd_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D) {
     return mf::attn_bwd_workspace_bytes(n_seq, T, H, D);
 }

@@ -9,7 +9,7 @@
 // "Resumo Tecnico: Mage-Flow", Metodologia > 2. NR-MMDiT.
 //
 // Design (MI355X, CDNA4):
-//  * Work = (sequence, head, 256-query tile, 64-key step).  Sequences are
+//  * Work = (sequence, head, 256-query tile, 32-key step).  Sequences are
 //    ordered by descending octave of their key-step count, ties by index
 //    (in-kernel for packs of up to 64 sequences, otherwise by a one-workgroup
 //    O(n) prologue kernel writing into the caller's workspace); within a
@@ -27,31 +27,32 @@
 //    two 32-row blocks, so every K or V fragment read from LDS feeds two
 //    MFMAs.  Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: every lane holds 16 keys of one query row, so
-//    the online-softmax max/sum need one v_permlane32_swap and the rescale of
-//    the output accumulator is a per-lane scalar.  The fp32 probabilities are
-//    rounded to bf16 in registers and used directly as the B operand of
-//    O^T += V^T P^T: the S^T accumulator layout gives each lane keys
-//    {4h..4h+3, 8+4h..8+4h+3} of every 16-key chunk, which is exactly what
-//    two transposed LDS reads (ds_read_b64_tr_b16) of the row-major V tile
-//    deliver as the V^T operand.
-//  * The 128 output accumulators of a wavefront live in AGPRs: the PV MFMA is
-//    issued from inline assembly with its accumulator bound to AGPRs, which
-//    leaves the 256 VGPRs to the score tiles (VALU reads them), the
-//    probabilities and the Q fragments.  The accumulators are read or
-//    written by VALU only in the rare rescale and the epilogue, each behind
-//    explicit wait states.
-//  * Per 64-key step t a wavefront runs two phases of 32 MFMAs each, with the
+//    a row's statistics combine lanes l and l+32 with one v_permlane32_swap.
+//    The fp32 probabilities are rounded to bf16 in registers and used
+//    directly as the B operand of O^T += V^T P^T: the S^T accumulator layout
+//    gives each lane keys {4h..4h+3, 8+4h..8+4h+3} of every 16-key chunk,
+//    which is exactly what two transposed LDS reads (ds_read_b64_tr_b16) of
+//    the row-major V tile deliver as the V^T operand.  The 128 output
+//    accumulators and the score tiles are VGPRs; the Q fragments sit in AGPRs
+//    and feed the MFMAs from there.
+//  * Per step t a wavefront runs two phases of 16 MFMAs each, with the
 //    softmax VALU work threaded between the MFMAs of the same wavefront:
 //      phase 1: S(t+1) = K(t+1) Q^T   ||  p = exp2(x(t)), bf16 rounding, row sums
-//      phase 2: O += V(t)^T P(t)^T     ||  max of S(t+1), reference-max update,
-//                                          x(t+1) = S(t+1) * scale*log2e - max
-//    Operand fragments are read from LDS three MFMAs ahead.
+//      phase 2: O += V(t)^T P(t)^T     ||  x(t+1) = S(t+1) * scale*log2e - m
+//    Operand fragments are read from LDS three MFMAs ahead.  On gfx950 a
+//    wavefront hides only a few VALU instructions behind each of its own
+//    MFMAs, so the step carries no other VALU work: the reference max m of
+//    each row is fixed by the segment's first key step (numerator and
+//    denominator share it, so the softmax is unchanged), and a row sum above
+//    2^64 at the segment's end -- the only way a probability can have
+//    overflowed -- makes the workgroup redo the segment with exact row
+//    maxima from a scores-only pass.
 //  * K and V arrive by direct global->LDS buffer loads (no staging registers,
 //    no LDS stores), issued by all four wavefronts from inline assembly (the
 //    compiler would otherwise order every transposed LDS read behind all
 //    outstanding direct loads); completion is tracked with explicit vmcnt
-//    waits.  K of tiles t+1..t+4 and V of tiles t..t+2 are resident (4 + 3
-//    stages of 16 KB), loads run two steps ahead, and one barrier per step
+//    waits.  K of tiles t+1..t+5 and V of tiles t..t+3 are resident (5 + 4
+//    stages of 8 KB), loads have two steps to land, and one barrier per step
 //    publishes them.  Every step issues the same number of loads (a tile past
 //    the segment is addressed out of range, which returns zeros without
 //    memory traffic), so the wait count is a constant.  LDS rows are not
@@ -59,12 +60,12 @@
 //    LDS read cycle of the K reads and of the transposed V reads touches 64
 //    distinct banks.
 //  * Q/K/V are read through raw buffer resources that end at the sequence's
-//    last row, so ragged tiles read zeros without branches; only the last
-//    key tile of a sequence masks its scores.
-//  * exp2 with the softmax scale folded into one FMA (scale * log2 e); the
-//    reference max is raised lazily (only when a row max grows by more than
-//    2^8), so the output accumulator is rarely rescaled; all softmax state
-//    in fp32, row sums of the fp32 probabilities.
+//    last row, so ragged tiles read zeros without branches.  A tile's key
+//    steps take the sequence's last (ragged) key tile first, so only that
+//    first step masks its scores and the step loop has no mask branch.
+//  * exp2 with the softmax scale folded into one FMA (scale * log2 e); all
+//    softmax state in fp32, row sums of the fp32 probabilities.
+#include <atomic>
 #include <cmath>
 #include <utility>
 
@@ -80,7 +81,7 @@ constexpr int kBM = kWaves * kRows;  // query rows per tile
 constexpr int kBN = 32;              // keys per K/V step (one 32-key MFMA block)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;             // XCDs of an MI355X; blockIdx round-robins over them
-constexpr float kRescaleLog2 = 8.0f; // lazy-rescale threshold (log2 units)
+constexpr float kSumLimit = 1.8446744e19f;  // 2^64: bound on a row sum before the exact-max redo
 constexpr int kInlineSeqs = 64;      // packs up to this many sequences schedule in-kernel
 constexpr int kSlack = 2;            // steps a direct load may stay in flight
 constexpr int kKStages = 3 + kSlack; // K of tiles t+1 .. t+kKStages
@@ -537,13 +538,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
             }
         };
 
-        // The reference max of each row (log2 units) is fixed by the first
-        // key step, and a step only records whether a row max has since
-        // grown past it by more than 2^kRescaleLog2 (raise).  If any row did,
-        // the whole workgroup redoes the segment once with every reference
+        // The reference max m of each row (log2 units) is fixed by the first
+        // key step of the segment, so p = 2^(x - m) may exceed 1 on later
+        // steps; numerator and denominator share m, so the result is the same
+        // softmax.  No step checks anything: at the end, a row sum above
+        // 2^64 (or not finite) means that some p may have overflowed, and the
+        // whole workgroup then redoes the segment once with every reference
         // max preset to the row's exact maximum over the segment's keys
-        // (found by a scores-only pass), after which no raise is possible.
-        // So the output accumulators are only ever written by MFMAs.
+        // (found by a scores-only pass), after which every p <= 1.  So the
+        // output accumulators are only ever written by MFMAs, and the step
+        // loop carries no max or rescale work.
         bool preset = false;
         float m_pre[2] = {-INFINITY, -INFINITY};
         for (;;) {
@@ -594,8 +598,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
                 for (int m = 0; m < EB; ++m)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[b][m][r] = 0.f;
-            float m_run[2], lsum[2] = {0.f, 0.f};
-            bool raised = false;
+            float m_run[2], negm[2], lsum[2] = {0.f, 0.f};
 
             bf16x8_t kf[kPfK], vf[kPfV];
             bf16x8_t pf[2][2];
@@ -661,28 +664,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
             // in the last slots.
             auto phase2 = [&]<bool kNext>(Scores& s, const unsigned char* vb, const unsigned char* kb_next, int t,
                                           int kdst, int vdst) {
-                constexpr int NMAX = 16;                 // 8 max ops per row block
-                constexpr int NFIN = 2;                  // raise check per row block
-                constexpr int NFMA = 32;
-                constexpr int NITEMS = kNext ? NMAX + NFIN + NFMA : 0;
-                float mx[2];
+                constexpr int NITEMS = kNext ? 32 : 0;   // x = S c - m, in place
                 const uint32_t so_k = tile_soff(t + kKStages), so_v = tile_soff(t + kVStages - 1);
                 auto item = [&](auto II) {
-                    constexpr int I = II;
-                    if constexpr (I < NMAX) {
-                        constexpr int b = I / 8, j = I % 8;
-                        if constexpr (j == 0)
-                            mx[b] = fmaxf(s[b][0], s[b][1]);
-                        else
-                            mx[b] = fmaxf(mx[b], fmaxf(s[b][2 * j], s[b][2 * j + 1]));
-                    } else if constexpr (I < NMAX + NFIN) {
-                        constexpr int b = I - NMAX;
-                        raised |= __builtin_amdgcn_ballot_w64(half_max(mx[b]) * c > m_run[b] + kRescaleLog2) != 0;
-                    } else {
-                        constexpr int e = I - NMAX - NFIN;
-                        constexpr int b = e / 16, r = e % 16;
-                        s[b][r] = __builtin_fmaf(s[b][r], c, -m_run[b]);
-                    }
+                    constexpr int e = II;
+                    constexpr int b = e / 16, r = e % 16;
+                    s[b][r] = __builtin_fmaf(s[b][r], c, negm[b]);
                 };
                 static_for<NP>([&](auto SI) {
                     constexpr int sl = SI;
@@ -707,8 +694,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
 #pragma unroll
                 for (int r = 2; r < 16; r += 2) mxb = fmaxf(mxb, fmaxf(h0[b][r], h0[b][r + 1]));
                 m_run[b] = fmaxf(half_max(mxb) * c, m_pre[b]);
+                negm[b] = -m_run[b];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) h0[b][r] = __builtin_fmaf(h0[b][r], c, -m_run[b]);
+                for (int r = 0; r < 16; ++r) h0[b][r] = __builtin_fmaf(h0[b][r], c, negm[b]);
             }
 #pragma unroll
             for (int i = 0; i < kPfK; ++i) kf[i] = kfrag(kstage(1), i);
@@ -754,7 +742,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
             phase2.template operator()<false>(h0, vstage(vs), kstage(0), kv1, 0, 0);
 
             // ---- redo decision (workgroup-wide) --------------------------------
+            // A row sum is at least every one of its terms, so a sum within
+            // the limit (and finite) shows that no probability overflowed.
             if (!preset) {
+                const bool raised = __builtin_amdgcn_ballot_w64(!(lsum[0] <= kSumLimit) || !(lsum[1] <= kSumLimit)) != 0;
                 if (lane == 0) redo_flag[wave] = raised;
                 __syncthreads();
                 bool any = false;
@@ -912,9 +903,17 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     }
 }
 
+std::atomic<int> g_grid_override{0};
+
+// Persistent workgroups of a call: one per CU unless a test overrides it.
+int attn_grid() {
+    const int o = g_grid_override.load(std::memory_order_relaxed);
+    return o > 0 ? o : device_cu_count();
+}
+
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
-    const int G = device_cu_count();
+    const int G = attn_grid();
     if (G <= 0) return hipErrorInvalidDevice;
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     if (a.n_seq > kInlineSeqs) {
@@ -947,11 +946,13 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
 
 size_t attn_workspace_bytes(int32_t n_seq, int64_t /*T*/, int32_t /*H*/, int32_t D) {
     const int n = n_seq < 0 ? 0 : n_seq;
-    int G = device_cu_count();
+    int G = attn_grid();
     if (G <= 0) G = 256;   // no device visible: size for an MI355X
     const size_t slot = D == 64 ? Tile<64>::SLOT_BYTES : Tile<128>::SLOT_BYTES;
     return sched_bytes(n) + size_t(2) * G * slot;
 }
+
+void set_attn_fwd_grid(int g) { g_grid_override.store(g, std::memory_order_relaxed); }
 
 hipError_t launch_varlen_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     if (a.D == 128) return launch_d<128>(a, stream);

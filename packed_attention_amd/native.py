@@ -28,7 +28,8 @@ EXPORTS = ("mf_status_string", "mf_abi_version", "mf_pack_count", "mf_pack_table
            "mf_modulate_rope_bwd", "mf_gated_residual_bwd", "mf_modulate_rope_bwd_workspace_bytes",
            "mf_gated_residual_bwd_workspace_bytes", "mf_block_qkv_workspace_bytes", "mf_block_qkv",
            "mf_block_out", "mf_cfg_pair_count", "mf_cfg_pair_rows", "mf_cfg_euler_step", "mf_qk_norm_rope",
-           "mf_varlen_attn_causal_workspace_bytes", "mf_varlen_attn_causal_fwd", "mf_prompt_tables")
+           "mf_varlen_attn_causal_workspace_bytes", "mf_varlen_attn_causal_fwd", "mf_prompt_tables",
+           "mf_set_attn_fwd_grid")
 
 
 class MFError(RuntimeError):
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.mf_varlen_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i64, i64,
                                      f32, vp, sz]
     L.mf_varlen_attn_fwd.restype = i32
+    L.mf_set_attn_fwd_grid.argtypes = [i32]
+    L.mf_set_attn_fwd_grid.restype = i32
     L.mf_gated_residual.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, f32]
     L.mf_gated_residual.restype = i32
     L.mf_varlen_attn_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32]
@@ -201,6 +204,12 @@ def modulate_rope(q_in, k_in, q_out, k_out, pos, rope_dims, rope_base=10000.0,
     check(lib().mf_modulate_rope(_stream(stream), _ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out),
                                  T, H, D, ld_in, ld_out, _ptr(shift), _ptr(scale), _ptr(mod_row),
                                  _ptr(pos), f, r, c, float(rope_base), float(eps)))
+
+
+def set_attn_fwd_grid(g: int) -> None:
+    """Test hook: run the attention forward on g persistent workgroups (0 =
+    one per CU).  Process-wide; size workspaces after setting it."""
+    check(lib().mf_set_attn_fwd_grid(int(g)))
 
 
 def attn_workspace_bytes(n_seq: int, T: int, H: int, D: int) -> int:

@@ -300,3 +300,123 @@ def test_graph_replay_matches_eager(which):
                 f"replay {rep}: {name} differs from the eager result"
         runner.run_chain(other)          # unrelated eager work between replays
         torch.cuda.synchronize()
+
+
+def _attn_inputs(lens, H, D, seed, q_shift=0.0):
+    """Seeded bf16 q, k, v ~ N(0,1) for a pack of the given lengths."""
+    import torch
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    mk = lambda: torch.from_numpy(rng.standard_normal((T, H, D)).astype(np.float32)).to(torch.bfloat16)  # noqa: E731
+    q, k, v = mk(), mk(), mk()
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return q, k, v, cu
+
+
+def _run_attn(q, k, v, cu, grid=0):
+    """One attention call on the GPU with the persistent grid set to `grid`
+    (0 = one workgroup per CU); returns O (f64) and LSE (f64)."""
+    import torch
+    native.set_attn_fwd_grid(grid)
+    try:
+        T, H, D = q.shape
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        o = torch.empty_like(qd)
+        lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+        cud = torch.from_numpy(cu).cuda()
+        ws = torch.empty(native.attn_workspace_bytes(len(cu) - 1, T, H, D), dtype=torch.uint8, device="cuda")
+        native.varlen_attn_fwd(qd, kd, vd, o, cud, int(np.diff(cu).max()), lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        return G.f64(o), lse.cpu().numpy().astype(np.float64), ws
+    finally:
+        native.set_attn_fwd_grid(0)
+
+
+def test_grid_size_invariance():
+    """The stream-K cut points move with the number of persistent
+    workgroups (1: every tile whole; 37, 128, 300, one per CU: different
+    cuts).  Every grid matches the oracle, and all agree with each other:
+    LSE within fp32 rounding, O within a fraction of the bf16 rounding of the
+    probabilities (each piece of a cut tile takes its reference max from its
+    own first key step, so its probabilities round differently; the pieces'
+    unnormalised O is also rounded to bf16 before the merge)."""
+    lens = [1300, 41, 700, 2]
+    q, k, v, cu = _attn_inputs(lens, H=3, D=128, seed=4242)
+    f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+    O_ref, L_ref = R.attention(f(q), f(k), f(v), cu)
+    results, err = {}, {}
+    for grid in (0, 1, 37, 128, 300):
+        G.say("grid size", grid, "lens", lens)
+        O, lse, _ = _run_attn(q, k, v, cu, grid)
+        G.check_attention(O, O_ref, f"grid{grid}", lse, L_ref)
+        results[grid] = (O, lse)
+        err[grid] = np.linalg.norm(O - O_ref) / np.linalg.norm(O_ref)
+    # Each grid's O carries its own bf16 rounding of the probabilities
+    # (relative RMS near 2^-9 / sqrt(3) per term) and of its cut pieces, so
+    # two grids differ by about sqrt(2) times one grid's error to the oracle.
+    O0, L0 = results[0]
+    for grid, (O, lse) in results.items():
+        d = np.abs(O - O0)
+        rel = np.linalg.norm(O - O0) / np.linalg.norm(O0)
+        assert rel <= 5e-3 and d.max() <= 1e-2, (grid, rel, d.max(), err)
+        np.testing.assert_allclose(lse, L0, rtol=0, atol=2e-5)
+
+
+@pytest.mark.parametrize("grid", [1, 0])
+def test_score_spike_redo(grid):
+    """One key per (sequence, head) scores about 260 (log2 units) above the
+    rest, and it does not sit in the tile a segment starts with: the
+    probabilities overflow against the reference max taken from the first
+    key step, the row sums show it, and the workgroup redoes the segment with
+    exact row maxima.  O (then close to that key's value row) and LSE match
+    the oracle; grid 1 takes whole tiles, the default grid cut ones."""
+    import torch
+    lens = [1000, 700]
+    H, D = 4, 128
+    q, k, v, cu = _attn_inputs(lens, H=H, D=D, seed=777)
+    q[:, :, :64] = (q[:, :, :64].float() * 0.5 + 2.0).to(torch.bfloat16)
+    k[:, :, :64] = (k[:, :, :64].float() * 0.5).to(torch.bfloat16)
+    for s, (a0, L) in enumerate(zip(cu[:-1], lens)):
+        for h in range(H):
+            j = int(a0) + 100 + 37 * h + 151 * s          # key tiles 3.. of the sequence
+            assert j < a0 + L - 32
+            k[j, h, :64] = 16.0
+    f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+    O_ref, L_ref = R.attention(f(q), f(k), f(v), cu)
+    assert L_ref.max() > 150.0                             # the spikes dominate
+    G.say("score spike redo, grid", grid)
+    O, lse, _ = _run_attn(q, k, v, cu, grid)
+    G.check_attention(O, O_ref, f"spike_grid{grid}", lse, L_ref)
+
+
+def test_prologue_schedule_exact():
+    """Packs of more than 64 sequences take their work schedule from the
+    prologue kernel, in the caller's workspace: sequences ranked by
+    descending octave of their 32-key step count (empty sequences last),
+    ties by index, with tiles = ceil(L/256), steps = ceil(L/32) and the
+    exclusive prefix of tiles*H*steps.  Read back, it equals this host
+    computation exactly."""
+    rng = np.random.default_rng(2718)
+    lens = [int(x) for x in rng.integers(0, 3000, size=150)]
+    lens[7] = lens[40] = 0
+    H, D = 2, 64
+    q, k, v, cu = _attn_inputs(lens, H=H, D=D, seed=11)
+    G.say("prologue schedule, n", len(lens))
+    _, _, ws = _run_attn(q, k, v, cu, 0)
+    raw = ws.cpu().numpy()
+    n = len(lens)
+    W_got = int(raw[0:8].view(np.int64)[0])
+    ints = raw[8:8 + 4 * (1 + 3 * n)].view(np.int32)
+    assert ints[0] == n
+    seq, tiles, nkv = ints[1:1 + n], ints[1 + n:1 + 2 * n], ints[1 + 2 * n:1 + 3 * n]
+    off = (12 + 12 * n + 7) // 8 * 8
+    it_start = raw[off:off + 8 * (n + 1)].view(np.int64)
+    steps = [(L + 31) // 32 for L in lens]
+    octave = [0 if s == 0 else int(s).bit_length() for s in steps]
+    order = sorted(range(n), key=lambda i: (-octave[i], i))
+    np.testing.assert_array_equal(seq, order)
+    np.testing.assert_array_equal(tiles, [(lens[i] + 255) // 256 for i in order])
+    np.testing.assert_array_equal(nkv, [steps[i] for i in order])
+    work = [((lens[i] + 255) // 256) * H * steps[i] for i in order]
+    np.testing.assert_array_equal(it_start, np.concatenate([[0], np.cumsum(work)]))
+    assert W_got == sum(work)
