@@ -39,8 +39,19 @@ cover their submission), divided by K.  Prints one JSON line:
               norm + 1D RoPE of q and k (mf_qk_norm_rope, GB/s of its
               algorithmic bytes) and causal grouped-head attention
               (mf_varlen_attn_causal_fwd, TFLOP/s at 4*D*Hq*sum L(L+1)/2);
+  configs     the other workload shapes of the pages (the tiny pack, the
+              eight native-resolution budget packs, packed CFG, the edit pack
+              with 3D RoPE), each with tensors drawn on the GPU from a seeded
+              generator: attention TFLOP/s and fraction of the bf16 peak,
+              modulate+RoPE and gated residual (y alone, y with the fused
+              next adaLN) GB/s and fraction of the HBM peak;
+  sclk        the shader clock sampled (amdsmi) while attention calls run
+              back to back;
   cpu_baseline the fp64 oracle's whole step over the same workload, repeated
-              for about 10 s, timed on the host cores.
+              for about 10 s on the host cores of the process's affinity
+              mask, and one pass of a bounded sample on one core.
+
+  --only attention   time attention calls only (for profiler runs).
 """
 from __future__ import annotations
 
@@ -88,9 +99,9 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed counter summary, if it
-    was taken on the current kernel source; otherwise None."""
+def committed_counters():
+    """The committed counter summary of the attention call, if it was taken on
+    the current kernel source; otherwise None."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
@@ -98,7 +109,53 @@ def measured_traffic():
         return None
     if c.get("source_hash") != source_hash():
         return None
-    return c.get("hbm_bytes_per_launch")
+    return c
+
+
+class ClockSampler:
+    """Samples the GFX clock (MHz) with amdsmi from a thread while work runs."""
+
+    def __init__(self, period_s=0.005):
+        self.period_s, self.samples, self._stop, self._th = period_s, [], False, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:   # noqa: BLE001 -- clock sampling is best effort
+            self._smi = None
+
+    def _read(self):
+        info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+        return float(info.get("clk", info.get("cur_clk", 0)))
+
+    def __enter__(self):
+        import threading
+        if self._smi is None:
+            return self
+
+        def loop():
+            while not self._stop:
+                try:
+                    self.samples.append(self._read())
+                except Exception:   # noqa: BLE001
+                    return
+                time.sleep(self.period_s)
+        self._th = threading.Thread(target=loop, daemon=True)
+        self._th.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop = True
+        if self._th is not None:
+            self._th.join()
+
+    def summary(self):
+        xs = [x for x in self.samples if x > 0]
+        if not xs:
+            return None
+        return {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": min(xs), "max_mhz": max(xs),
+                "samples": len(xs)}
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -109,11 +166,12 @@ def cpu_baseline(w, budget_s=10.0):
     import numpy as np  # noqa: F401
     from oracle import reference as R
     from packed_attention_amd.workloads import bf16_bits_to_f64 as f
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        threadpool_limits, blas_threads = None, None
     g = lambda a: None if a is None else f(a)  # noqa: E731
     args = (w.descs, f(w.q), f(w.k), f(w.v), w.rope_dims, w.rope_base, g(w.shift), g(w.scale),
             g(w.x), g(w.gate), g(w.shift2), g(w.scale2), w.eps)
@@ -123,11 +181,66 @@ def cpu_baseline(w, budget_s=10.0):
         R.forward(*args)
         passes += 1
     dt = time.perf_counter() - t0
-    return {"value": round(w.attn_flops() * passes / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, whole step (modulate+RoPE, attention with LSE, gated "
-                      f"residual + LN) over all of {w.name} (T={w.T}, H={w.H}), {passes} pass(es) "
-                      f"in {dt:.1f} s wall"}
+    out = {"value": round(w.attn_flops() * passes / dt / 1e12, 6), "unit": "TFLOP/s",
+           "cores": int(cores), "blas_threads": blas_threads, "kind": "oracle",
+           "sample": f"fp64 numpy oracle, whole step (modulate+RoPE, attention with LSE, gated "
+                     f"residual + LN) over all of {w.name} (T={w.T}, H={w.H}), {passes} pass(es) "
+                     f"in {dt:.1f} s wall on the {cores} cores of the affinity mask"}
+    if threadpool_limits is not None:
+        # one core: the oracle's attention over 2 of the heads (1/12 of the
+        # step's attention work), one pass
+        hs = slice(0, 2)
+        cu, _, _, _ = R.pack_tables(w.descs)
+        qh, kh, vh = f(w.q)[:, hs], f(w.k)[:, hs], f(w.v)[:, hs]
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            R.attention(qh, kh, vh, cu)
+            d1 = time.perf_counter() - t1
+        fl1 = 4.0 * w.D * 2 * w.sum_sq_len
+        out["one_core"] = {"value": round(fl1 / d1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                           "sample": f"fp64 oracle attention of 2 of the {w.H} heads of {w.name}, one pass "
+                                     f"in {d1:.1f} s with BLAS limited to one thread"}
+    return out
+
+
+def _gbs(nbytes, ms):
+    g = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 5), "algorithmic_bytes": int(nbytes), "GB/s": round(g, 1),
+            "frac_hbm_peak": round(g / PEAK_HBM_GBS, 4)}
+
+
+def config_lines(args, timed, torch, runner, W):
+    """Per-config throughput: each shape's tensors drawn on the GPU (seeded),
+    enough input sets rotated to leave the 256 MB Infinity Cache, each call
+    kind timed back to back."""
+    out = {}
+    for shape in W.shapes_of_configs():
+        T, C, n = shape.T, shape.C, shape.n_seq
+        set_bytes = T * C * 2 * 6
+        n_sets = max(2, min(4, -(-600 * (1 << 20) // max(set_bytes, 1))))
+        sets = [runner.to_device_synthetic(shape, seed=i) for i in range(n_sets)]
+        for b in sets:
+            runner.run_chain(b)
+        torch.cuda.synchronize()
+        ms_mod = timed(lambda i: runner.run_modulate_rope(sets[i % n_sets]))[0]
+        ms_att = timed(lambda i: runner.run_attention(sets[i % n_sets]))[0]
+        fl = shape.attn_flops()
+        tf = fl / (ms_att * 1e-3) / 1e12
+        e = {"T": T, "n_seq": n, "H": shape.H, "D": shape.D, "rope_dims": list(shape.rope_dims),
+             "seq_lens": [W.sample_len(d) for d in shape.descs], "input_sets": n_sets,
+             "varlen_attn_fwd": {"ms": round(ms_att, 5), "flops": fl, "TFLOP/s": round(tf, 2),
+                                 "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}}
+        mod_bytes = T * (2 * 2 * C * 2) + T * 16 + (2 * n * C * 2 if shape.modulate else 0)
+        e["modulate_rope"] = _gbs(mod_bytes, ms_mod)
+        if shape.residual:
+            ms_y = timed(lambda i: runner.run_gated_residual_y(sets[i % n_sets]))[0]
+            ms_yz = timed(lambda i: runner.run_gated_residual(sets[i % n_sets]))[0]
+            e["gated_residual_y"] = _gbs(T * (3 * C * 2 + 4) + n * C * 2, ms_y)
+            e["gated_residual_y_z"] = _gbs(T * (4 * C * 2 + 4) + 3 * n * C * 2, ms_yz)
+        out[shape.name] = e
+        del sets
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -142,6 +255,9 @@ def main():
                     help="skip the HIP-graph replay timing of the step")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--only", choices=["attention"], default=None,
+                    help="time only this call on the headline workload (profiler runs)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config lines")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -163,6 +279,28 @@ def main():
 
     def step(b):
         runner.run_chain(b)
+
+    if args.only == "attention":
+        # profiler runs: the attention call alone, back to back
+        for b in sets:
+            runner.run_modulate_rope(b)
+        for i in range(args.warmup):
+            runner.run_attention(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            runner.run_attention(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        if args.copy_calib_mb:
+            n = args.copy_calib_mb * (1 << 20) // 4
+            src = torch.ones(n, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"only": "attention", "workload": w.name, "calls": args.steps,
+                          "wall_ms_per_call": round(ms, 4)}), flush=True)
+        return
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
@@ -294,6 +432,16 @@ def main():
                                        "TFLOP/s": round(ct, 2), "frac_bf16_peak": round(ct / PEAK_BF16_TFLOPS, 4)}}}
     del tsets
 
+    # Shader clock while attention calls run back to back (about 0.2 s).
+    with ClockSampler() as clk:
+        reps = max(1, int(200.0 / max(kern_ms["varlen_attn_fwd"], 1e-3)))
+        for i in range(reps):
+            runner.run_attention(sets[i % len(sets)])
+        torch.cuda.synchronize()
+    sclk = clk.summary()
+
+    configs = None if args.no_configs else config_lines(args, timed, torch, runner, W)
+
     if args.copy_calib_mb:
         n = args.copy_calib_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -340,7 +488,7 @@ def main():
         block["kernels"][n] = {"ms": round(blk_ms[n], 5), "gemm_flops": bflop[n], "TFLOP/s": round(tf, 2),
                                "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
-    traffic = measured_traffic() if args.workload == "single_1024" else None
+    counters = committed_counters() if args.workload == "single_1024" else None
     out = {
         "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
@@ -361,14 +509,19 @@ def main():
                    "attn_gflop": round(flops / 1e9, 3), "input_sets": len(sets)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic,
+                     "traffic": None if counters is None else counters.get("hbm_bytes_per_launch"),
                      "kernel": f"mf_varlen_attn_fwd call (attn_fwd_kernel<{w.D}> + attn_fixup_kernel<{w.D}>)",
-                     "flops_per_launch": flops, "launch_ms": round(kern_ms["varlen_attn_fwd"], 5)},
+                     "flops_per_launch": flops, "launch_ms": round(kern_ms["varlen_attn_fwd"], 5),
+                     "mfma_busy": None if counters is None else counters.get("mfma_busy_frac"),
+                     "counters": None if counters is None else os.path.relpath(COUNTERS_FILE, ROOT),
+                     "sclk_mhz": None if sclk is None else sclk["mean_mhz"]},
         "kernels": kernels,
         "backward": backward,
         "block": block,
         "sampler": sampler,
         "text_encoder": text_encoder,
+        "configs": configs,
+        "sclk": sclk,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:

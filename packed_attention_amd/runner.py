@@ -81,6 +81,40 @@ def to_device(w: Workload, device="cuda", with_lse=True) -> DeviceBatch:
     )
 
 
+def to_device_synthetic(shape: "workloads.Shape", device="cuda", seed: int = 0) -> DeviceBatch:
+    """A device batch of the given shape whose tensors are drawn on the GPU
+    from a seeded generator with the workloads' distributions (q, k, v, x
+    ~ N(0,1), adaLN rows ~ N(0,0.1), bf16): for timing the large packs
+    without building them on the host; tables from the library's builder."""
+    import torch
+    cu, pos, _sid, mr = native.pack_tables(shape.descs)
+    T, H, D, n = shape.T, shape.H, shape.D, len(shape.descs)
+    C = H * D
+    g = torch.Generator(device=device)
+    g.manual_seed(int(shape.seed) * 7919 + seed)
+    rn = lambda *sz, s=1.0: (torch.randn(*sz, generator=g, device=device) * s).to(torch.bfloat16)  # noqa: E731
+    q, k, v = rn(T, H, D), rn(T, H, D), rn(T, H, D)
+    x = rn(T, C) if shape.residual else None
+    shift = rn(n, C, s=0.1) if shape.modulate else None
+    scale = rn(n, C, s=0.1) if shape.modulate else None
+    gate = rn(n, C, s=0.1) if shape.residual else None
+    shift2 = rn(n, C, s=0.1) if shape.residual else None
+    scale2 = rn(n, C, s=0.1) if shape.residual else None
+    lens = np.diff(cu)
+    return DeviceBatch(
+        w=shape, cu_host=cu, pos_host=pos, mod_row_host=mr,
+        cu=torch.from_numpy(cu).to(device), pos=torch.from_numpy(pos).to(device),
+        mod_row=torch.from_numpy(mr).to(device),
+        q=q, k=k, v=v, x=x, shift=shift, scale=scale, gate=gate, shift2=shift2, scale2=scale2,
+        qr=torch.empty_like(q), kr=torch.empty_like(k), o=torch.empty_like(q),
+        lse=torch.empty((H, T), dtype=torch.float32, device=device),
+        y=torch.empty((T, C), dtype=torch.bfloat16, device=device) if x is not None else None,
+        z=torch.empty((T, C), dtype=torch.bfloat16, device=device) if x is not None else None,
+        workspace=torch.empty(native.attn_workspace_bytes(n, T, H, D), dtype=torch.uint8, device=device),
+        max_seqlen=int(lens.max()) if len(lens) else 0,
+    )
+
+
 def run_modulate_rope(b: DeviceBatch, stream=None):
     w = b.w
     native.modulate_rope(b.q, b.k, b.qr, b.kr, b.pos, w.rope_dims, w.rope_base,
@@ -98,6 +132,13 @@ def run_gated_residual(b: DeviceBatch, stream=None):
         return
     native.gated_residual(b.x, b.o.view(b.w.T, -1), b.y, b.gate, b.mod_row, b.shift2, b.scale2,
                           b.z, b.w.eps, stream=stream)
+
+
+def run_gated_residual_y(b: DeviceBatch, stream=None):
+    """The gated residual alone (y = x + gate * o, no fused next adaLN)."""
+    if b.x is None:
+        return
+    native.gated_residual(b.x, b.o.view(b.w.T, -1), b.y, b.gate, b.mod_row, stream=stream)
 
 
 def run_chain(b: DeviceBatch, stream=None):

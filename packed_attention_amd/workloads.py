@@ -356,6 +356,56 @@ def edit_pack(seed: int = 1004) -> Workload:
     return _draw_tensors("edit_pack", seed, rng, descs, 24, 128, (16, 56, 56), True, True)
 
 
+@dataclasses.dataclass
+class Shape:
+    """A workload's shape without its tensors: descriptors and parameters."""
+    name: str
+    seed: int
+    descs: List[Desc]
+    H: int
+    D: int
+    rope_dims: Tuple[int, int, int]
+    modulate: bool
+    residual: bool
+    rope_base: float = ROPE_BASE
+    eps: float = LN_EPS
+
+    @property
+    def T(self) -> int:
+        return int(sum(sample_len(d) for d in self.descs))
+
+    @property
+    def C(self) -> int:
+        return self.H * self.D
+
+    @property
+    def n_seq(self) -> int:
+        return len(self.descs)
+
+    @property
+    def sum_sq_len(self) -> int:
+        return int(sum(sample_len(d) ** 2 for d in self.descs))
+
+    def attn_flops(self) -> float:
+        return 4.0 * self.D * self.H * self.sum_sq_len
+
+
+def shapes_of_configs() -> List[Shape]:
+    """The measured configurations other than the 1024^2 pack, with the same
+    seeded descriptor draws as their named workloads: the tiny pack, the
+    eight native-resolution budget packs (seeds 2000..2007), packed CFG and
+    the edit pack with 3D RoPE."""
+    out = [Shape("tiny", 1000, descs_tiny(), 2, 64, (0, 32, 32), False, False)]
+    for seed in range(2000, 2008):
+        out.append(Shape(f"native_pack_{seed}", seed, descs_native_budget(np.random.default_rng(seed)),
+                         24, 128, (0, 64, 64), True, True))
+    out.append(Shape("cfg_pack", CFG_SEED, descs_cfg(np.random.default_rng(CFG_SEED)), 24, 128, (0, 64, 64),
+                     True, True))
+    out.append(Shape("edit_pack", 1004, descs_edit(np.random.default_rng(1004)), 24, 128, (16, 56, 56),
+                     True, True))
+    return out
+
+
 def custom(descs: Sequence[Desc], H: int, D: int, rope_dims=(0, 0, 0), modulate=False,
            residual=False, seed: int = 0, qk_sigma: float = 1.0, name: str = "custom") -> Workload:
     """Arbitrary descriptor list (edge cases, stress packs)."""
