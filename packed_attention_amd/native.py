@@ -170,6 +170,18 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _temp_workspace(nbytes: int, device, stream):
+    """A workspace for one call when the caller passed none.  It is allocated
+    on the stream the kernels run on, so the caching allocator hands its bytes
+    to later work only in that stream's order (a block allocated on another
+    stream could be reused while the kernels still read it)."""
+    import torch
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def _check_bf16_rows(name, t, cols):
     import torch
     if t.dtype != torch.bfloat16 or not t.is_cuda:
@@ -238,7 +250,7 @@ def varlen_attn_fwd(q, k, v, o, cu_seqlens, max_seqlen, lse=None, softmax_scale=
         softmax_scale = 1.0 / math.sqrt(D)
     need = attn_workspace_bytes(n_seq, T, H, D)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _temp_workspace(need, q.device, stream)
     check(lib().mf_varlen_attn_fwd(_stream(stream), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                    _ptr(cu_seqlens), n_seq, int(max_seqlen), T, H, D, ld, ld_o,
                                    float(softmax_scale), _ptr(workspace), workspace.numel()))
@@ -292,7 +304,7 @@ def varlen_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, max_seqlen, s
         softmax_scale = 1.0 / math.sqrt(D)
     need = attn_bwd_workspace_bytes(n_seq, T, H, D)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _temp_workspace(need, q.device, stream)
     check(lib().mf_varlen_attn_bwd(_stream(stream), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
                                    _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), n_seq,
                                    int(max_seqlen), T, H, D, ld, ld_o, ld_d, float(softmax_scale),
@@ -324,8 +336,8 @@ def modulate_rope_bwd(q_in, k_in, dq_out, dk_out, dq_in, dk_in, pos, rope_dims, 
                 raise ValueError(f"{n}: expected float32 [n_rows][H*D]")
     f, r, c = (int(x) for x in rope_dims)
     if workspace is None and scale is not None:
-        workspace = torch.empty(int(lib().mf_modulate_rope_bwd_workspace_bytes(T, H, D)),
-                                dtype=torch.uint8, device=q_in.device)
+        workspace = _temp_workspace(int(lib().mf_modulate_rope_bwd_workspace_bytes(T, H, D)), q_in.device,
+                                    stream)
     check(lib().mf_modulate_rope_bwd(_stream(stream), _ptr(q_in), _ptr(k_in), ld_in, _ptr(dq_out),
                                      _ptr(dk_out), ld_gout, _ptr(dq_in), _ptr(dk_in), ld_gin, T, H, D,
                                      _ptr(scale), _ptr(mod_row), n_rows, _ptr(dshift), _ptr(dscale),
@@ -350,8 +362,7 @@ def gated_residual_bwd(x, o, gate, mod_row, dy, dx, dout, dgate, scale2=None, dz
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (n_rows, C)):
             raise ValueError(f"{n}: expected float32 [n_rows][C]")
     if workspace is None:
-        workspace = torch.empty(int(lib().mf_gated_residual_bwd_workspace_bytes(T, C)),
-                                dtype=torch.uint8, device=x.device)
+        workspace = _temp_workspace(int(lib().mf_gated_residual_bwd_workspace_bytes(T, C)), x.device, stream)
     check(lib().mf_gated_residual_bwd(_stream(stream), _ptr(x), _ptr(o), _ptr(gate), _ptr(mod_row),
                                       n_rows, _ptr(dy), _ptr(scale2), _ptr(dz), _ptr(dx), _ptr(dout),
                                       _ptr(dgate), _ptr(dshift2), _ptr(dscale2), T, C, float(eps),
@@ -377,7 +388,7 @@ def block_qkv(x, w_qkv, qkv, pos, H, rope_dims, rope_base=10000.0, shift=None, s
     if qkv.dim() != 2 or qkv.shape[0] != T or qkv.shape[1] != 3 * C:
         raise ValueError("qkv: expected [T][3C]")
     if workspace is None:
-        workspace = torch.empty(block_qkv_workspace_bytes(T, H, D), dtype=torch.uint8, device=x.device)
+        workspace = _temp_workspace(block_qkv_workspace_bytes(T, H, D), x.device, stream)
     f, r, c = (int(v) for v in rope_dims)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().mf_block_qkv(_stream(stream), _ptr(x), _token_stride(x, C), _ptr(w_qkv), _ptr(qkv),
@@ -463,7 +474,7 @@ def varlen_attn_causal_fwd(q, k, v, o, cu_seqlens, lse=None, softmax_scale=None,
         softmax_scale = 1.0 / math.sqrt(D)
     need = int(lib().mf_varlen_attn_causal_workspace_bytes(n_seq, T))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _temp_workspace(max(need, 16), q.device, stream)
     check(lib().mf_varlen_attn_causal_fwd(_stream(stream), _ptr(q), _token_stride(q, Hq * D), _ptr(k), _ptr(v),
                                           ld_kv, _ptr(o), _token_stride(o, Hq * D), _ptr(lse), _ptr(cu_seqlens),
                                           n_seq, T, Hq, Hkv, D, float(softmax_scale), _ptr(workspace),

@@ -420,3 +420,28 @@ def test_prologue_schedule_exact():
     work = [((lens[i] + 255) // 256) * H * steps[i] for i in order]
     np.testing.assert_array_equal(it_start, np.concatenate([[0], np.cumsum(work)]))
     assert W_got == sum(work)
+
+
+def test_side_stream_without_workspace():
+    """stream= given and no workspace: the binding allocates the call's
+    workspace on that stream, so memory allocated and filled on the current
+    stream right after the call cannot land on it while the kernels run."""
+    import torch
+    lens = [2000, 900]
+    q, k, v, cu = _attn_inputs(lens, H=8, D=128, seed=99)
+    f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+    O_ref, L_ref = R.attention(f(q), f(k), f(v), cu)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(qd)
+    lse = torch.empty((8, int(sum(lens))), dtype=torch.float32, device="cuda")
+    cud = torch.from_numpy(cu).cuda()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    G.say("attention on a side stream without a workspace")
+    for _ in range(3):
+        native.varlen_attn_fwd(qd, kd, vd, o, cud, max(lens), lse=lse, stream=side)
+        junk = [torch.full((1 << 22,), 3.0, device="cuda") for _ in range(8)]   # current stream
+        del junk
+        side.synchronize()
+        torch.cuda.synchronize()
+        G.check_attention(G.f64(o), O_ref, "side_stream", lse.cpu().numpy().astype(np.float64), L_ref)
