@@ -172,6 +172,24 @@ mf_status mf_varlen_attn_fwd(void* stream,
                              int64_t T, int32_t H, int32_t D, int64_t ld_qkv, int64_t ld_o,
                              float softmax_scale, void* workspace, size_t workspace_bytes);
 
+/* Allocation-free mf_varlen_attn_fwd, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same computation, arguments and errors as
+ * mf_varlen_attn_fwd without the workspace: the workspace is a 40 MiB scratch
+ * array inside the library, one per GPU, held until the process ends (its
+ * device address is looked up once per device, on the first call there; the
+ * call allocates nothing).  Every call on a GPU uses that GPU's array, which
+ * keeps the last call's contents: calls that overlap on one GPU (several
+ * streams or host threads) race, and the caller must serialise them.  A call
+ * whose workspace would exceed 40 MiB (mf_varlen_attn_workspace_bytes above
+ * 41943040: D = 128 with a persistent grid above 300 workgroups, or more than
+ * about 360 000 sequences) returns MF_ERR_UNSUPPORTED and enqueues nothing. */
+mf_status mf_varlen_attn_fwd_noalloc(void* stream,
+                                     const void* q, const void* k, const void* v, void* o, float* lse,
+                                     const int32_t* cu_seqlens, int32_t n_seq, int32_t max_seqlen,
+                                     int64_t T, int32_t H, int32_t D, int64_t ld_qkv, int64_t ld_o,
+                                     float softmax_scale);
+
 /* Test hook: the persistent grid of mf_varlen_attn_fwd.
  * g > 0 runs the attention forward on g persistent workgroups instead of one
  * per compute unit, which moves the cut points of its stream-K work split

@@ -135,10 +135,15 @@ size_t mf_varlen_attn_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32
     return mf::attn_workspace_bytes(n_seq, T, H, D);
 }
 
-mf_status mf_varlen_attn_fwd(void* stream, const void* q, const void* k, const void* v, void* o,
-                             float* lse, const int32_t* cu_seqlens, int32_t n_seq, int32_t max_seqlen,
-                             int64_t T, int32_t H, int32_t D, int64_t ld_qkv, int64_t ld_o,
-                             float softmax_scale, void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the two forward-attention entry points (all on
+// the host, before any HIP call); fills the launch arguments.
+mf_status attn_fwd_args(void* stream, const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens, int32_t n_seq, int32_t max_seqlen, int64_t T, int32_t H,
+                        int32_t D, int64_t ld_qkv, int64_t ld_o, float softmax_scale, mf::AttnArgs& a) {
     if (T < 0 || T > INT32_MAX || H <= 0 || H > 4096) return MF_ERR_SHAPE;
     if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
     if (n_seq < 0 || (T > 0 && n_seq < 1) || n_seq > (1 << 24)) return MF_ERR_SHAPE;
@@ -149,35 +154,78 @@ mf_status mf_varlen_attn_fwd(void* stream, const void* q, const void* k, const v
     if ((int64_t(max_seqlen) + 256) * ld_qkv * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
     // work units must fit a 1D grid
     if (int64_t(H) * (T / 128 + 1 + n_seq) > (int64_t(1) << 30)) return MF_ERR_SHAPE;
-    if (T == 0) return MF_OK;
-    if (!q || !k || !v || !o || !cu_seqlens) return MF_ERR_NULL;
-    if (ld_qkv % 8 || ld_o % 8) return MF_ERR_ALIGN;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4)))
-        return MF_ERR_ALIGN;
-    const size_t need = mf::attn_workspace_bytes(n_seq, T, H, D);
-    if (workspace == nullptr || workspace_bytes < need) return MF_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return MF_ERR_ALIGN;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (debug_mode()) {
-        std::vector<int32_t> cu;
-        if (!fetch(cu_seqlens, size_t(n_seq) + 1, cu, s)) return MF_ERR_HIP;
-        if (cu[0] != 0 || cu[n_seq] != T) return MF_ERR_TABLE;
-        for (int32_t i = 0; i < n_seq; ++i) {
-            const int64_t L = int64_t(cu[i + 1]) - cu[i];
-            if (L < 0 || L > max_seqlen) return MF_ERR_TABLE;
-        }
+    if (T > 0) {
+        if (!q || !k || !v || !o || !cu_seqlens) return MF_ERR_NULL;
+        if (ld_qkv % 8 || ld_o % 8) return MF_ERR_ALIGN;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+            !aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4)))
+            return MF_ERR_ALIGN;
     }
-    mf::AttnArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.o = static_cast<uint16_t*>(o);
     a.lse = lse; a.cu_seqlens = cu_seqlens; a.n_seq = n_seq; a.max_seqlen = max_seqlen;
     a.T = T; a.H = H; a.D = D; a.ld_qkv = ld_qkv; a.ld_o = ld_o;
-    a.softmax_scale = softmax_scale; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.softmax_scale = softmax_scale; a.workspace = nullptr; a.workspace_bytes = 0;
+    (void)stream;
+    return MF_OK;
+}
+
+// MF_DEBUG table checks of the forward attention.
+mf_status attn_fwd_debug_tables(const mf::AttnArgs& a, hipStream_t s) {
+    std::vector<int32_t> cu;
+    if (!fetch(a.cu_seqlens, size_t(a.n_seq) + 1, cu, s)) return MF_ERR_HIP;
+    if (cu[0] != 0 || cu[a.n_seq] != a.T) return MF_ERR_TABLE;
+    for (int32_t i = 0; i < a.n_seq; ++i) {
+        const int64_t L = int64_t(cu[i + 1]) - cu[i];
+        if (L < 0 || L > a.max_seqlen) return MF_ERR_TABLE;
+    }
+    return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mf_status mf_varlen_attn_fwd(void* stream, const void* q, const void* k, const void* v, void* o,
+                             float* lse, const int32_t* cu_seqlens, int32_t n_seq, int32_t max_seqlen,
+                             int64_t T, int32_t H, int32_t D, int64_t ld_qkv, int64_t ld_o,
+                             float softmax_scale, void* workspace, size_t workspace_bytes) {
+    mf::AttnArgs a;
+    mf_status st = attn_fwd_args(stream, q, k, v, o, lse, cu_seqlens, n_seq, max_seqlen, T, H, D, ld_qkv,
+                                 ld_o, softmax_scale, a);
+    if (st != MF_OK) return st;
+    if (T == 0) return MF_OK;
+    const size_t need = mf::attn_workspace_bytes(n_seq, T, H, D);
+    if (workspace == nullptr || workspace_bytes < need) return MF_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MF_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        st = attn_fwd_debug_tables(a, s);
+        if (st != MF_OK) return st;
+    }
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
     return finish(mf::launch_varlen_attn_fwd(a, s), s);
+}
+
+mf_status mf_varlen_attn_fwd_noalloc(void* stream, const void* q, const void* k, const void* v, void* o,
+                                     float* lse, const int32_t* cu_seqlens, int32_t n_seq,
+                                     int32_t max_seqlen, int64_t T, int32_t H, int32_t D, int64_t ld_qkv,
+                                     int64_t ld_o, float softmax_scale) {
+    mf::AttnArgs a;
+    mf_status st = attn_fwd_args(stream, q, k, v, o, lse, cu_seqlens, n_seq, max_seqlen, T, H, D, ld_qkv,
+                                 ld_o, softmax_scale, a);
+    if (st != MF_OK) return st;
+    if (T == 0) return MF_OK;
+    if (mf::attn_workspace_bytes(n_seq, T, H, D) > mf::kAttnNoAllocScratchBytes) return MF_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+        st = attn_fwd_debug_tables(a, s);
+        if (st != MF_OK) return st;
+    }
+    return finish(mf::launch_varlen_attn_fwd_noalloc(a, s), s);
 }
 
 mf_status mf_set_attn_fwd_grid(int32_t g) {

@@ -67,6 +67,7 @@
 //    softmax state in fp32, row sums of the fp32 probabilities.
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <utility>
 
 #include "mf_device.h"
@@ -953,6 +954,48 @@ size_t attn_workspace_bytes(int32_t n_seq, int64_t /*T*/, int32_t /*H*/, int32_t
 }
 
 void set_attn_fwd_grid(int g) { g_grid_override.store(g, std::memory_order_relaxed); }
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward.  Its workspace (schedule and partial slots, none
+// of which needs to start zeroed) is this file-scope array: one copy per GPU,
+// allocated with the code object and held until the process ends.  Host code
+// never passes the array's name to a kernel (that is a host-side stand-in);
+// it looks up the device address once per device and passes that.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kAttnNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's scratch array.
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_varlen_attn_fwd_noalloc(const AttnArgs& args, hipStream_t stream) {
+    void* p = nullptr;
+    const hipError_t e = scratch_address(&p);
+    if (e != hipSuccess) return e;
+    AttnArgs a = args;
+    a.workspace = p;
+    a.workspace_bytes = kAttnNoAllocScratchBytes;
+    return launch_varlen_attn_fwd(a, stream);
+}
 
 hipError_t launch_varlen_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     if (a.D == 128) return launch_d<128>(a, stream);

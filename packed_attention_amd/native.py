@@ -29,7 +29,7 @@ EXPORTS = ("mf_status_string", "mf_abi_version", "mf_pack_count", "mf_pack_table
            "mf_gated_residual_bwd_workspace_bytes", "mf_block_qkv_workspace_bytes", "mf_block_qkv",
            "mf_block_out", "mf_cfg_pair_count", "mf_cfg_pair_rows", "mf_cfg_euler_step", "mf_qk_norm_rope",
            "mf_varlen_attn_causal_workspace_bytes", "mf_varlen_attn_causal_fwd", "mf_prompt_tables",
-           "mf_set_attn_fwd_grid")
+           "mf_set_attn_fwd_grid", "mf_varlen_attn_fwd_noalloc")
 
 
 class MFError(RuntimeError):
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.mf_varlen_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i64, i64,
                                      f32, vp, sz]
     L.mf_varlen_attn_fwd.restype = i32
+    L.mf_varlen_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i64, i64, f32]
+    L.mf_varlen_attn_fwd_noalloc.restype = i32
     L.mf_set_attn_fwd_grid.argtypes = [i32]
     L.mf_set_attn_fwd_grid.restype = i32
     L.mf_gated_residual.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, f32]
@@ -254,6 +256,30 @@ def varlen_attn_fwd(q, k, v, o, cu_seqlens, max_seqlen, lse=None, softmax_scale=
     check(lib().mf_varlen_attn_fwd(_stream(stream), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                    _ptr(cu_seqlens), n_seq, int(max_seqlen), T, H, D, ld, ld_o,
                                    float(softmax_scale), _ptr(workspace), workspace.numel()))
+
+
+def varlen_attn_fwd_noalloc(q, k, v, o, cu_seqlens, max_seqlen, lse=None, softmax_scale=None, stream=None):
+    """mf_varlen_attn_fwd_noalloc: mf_varlen_attn_fwd with the library's
+    per-GPU scratch array as its workspace (nothing is allocated; calls that
+    overlap on one GPU race)."""
+    import torch
+    T, H, D = q.shape
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bf16_rows(n, t, H * D)
+        if tuple(t.shape) != (T, H, D):
+            raise ValueError(f"{n}: shape {tuple(t.shape)} != {(T, H, D)}")
+    ld = _token_stride(q, H * D)
+    if _token_stride(k, H * D) != ld or _token_stride(v, H * D) != ld:
+        raise ValueError("q, k and v must share a token stride")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+        raise TypeError("cu_seqlens: expected an int32 CUDA tensor")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (H, T)):
+        raise ValueError("lse: expected float32 [H][T]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    check(lib().mf_varlen_attn_fwd_noalloc(_stream(stream), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                           _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), T, H, D,
+                                           ld, _token_stride(o, H * D), float(softmax_scale)))
 
 
 def gated_residual(x, o, y, gate, mod_row, shift2=None, scale2=None, z=None, eps=1e-6, stream=None):
