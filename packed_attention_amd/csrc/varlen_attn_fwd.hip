@@ -23,42 +23,45 @@
 //    The partition is fixed by (W, G), so results are deterministic.
 //    Logical workgroups map to blockIdx so that consecutive ranges (same
 //    sequence and head, hence the same K/V) run on one XCD and share its L2.
-//  * One wavefront per SIMD (4 per workgroup), each owning 64 query rows as
-//    two 32-row blocks, so every K or V fragment read from LDS feeds two
-//    MFMAs.  Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: every lane holds 16 keys of one query row, so
-//    a row's statistics combine lanes l and l+32 with one v_permlane32_swap.
-//    The fp32 probabilities are rounded to bf16 in registers and used
-//    directly as the B operand of O^T += V^T P^T: the S^T accumulator layout
-//    gives each lane keys {4h..4h+3, 8+4h..8+4h+3} of every 16-key chunk,
-//    which is exactly what two transposed LDS reads (ds_read_b64_tr_b16) of
-//    the row-major V tile deliver as the V^T operand.  The 128 output
-//    accumulators and the score tiles are VGPRs; the Q fragments sit in AGPRs
-//    and feed the MFMAs from there.
-//  * Per step t a wavefront runs two phases of 16 MFMAs each, with the
-//    softmax VALU work threaded between the MFMAs of the same wavefront:
+//  * A workgroup owns a 256-row query tile.  For d = 128 it runs eight
+//    wavefronts of 32 query rows, two per SIMD, so that one wavefront's
+//    MFMAs run while the other issues its softmax work or waits; for d = 64
+//    it runs four wavefronts of 64 rows as two 32-row blocks (each K or V
+//    fragment then feeds two MFMAs).  Scores are computed transposed,
+//    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: every lane holds 16 keys of
+//    one query row, so a row's statistics combine lanes l and l+32 with one
+//    v_permlane32_swap.  The fp32 probabilities are rounded to bf16 in
+//    registers and used directly as the B operand of O^T += V^T P^T: the S^T
+//    accumulator layout gives each lane keys {4h..4h+3, 8+4h..8+4h+3} of
+//    every 16-key chunk, which is exactly what two transposed LDS reads
+//    (ds_read_b64_tr_b16) of the row-major V tile deliver as the V^T operand.
+//  * Per step t a wavefront runs two phases, with the softmax VALU work
+//    threaded between the MFMAs of the same wavefront:
 //      phase 1: S(t+1) = K(t+1) Q^T   ||  p = exp2(x(t)), bf16 rounding, row sums
 //      phase 2: O += V(t)^T P(t)^T     ||  x(t+1) = S(t+1) * scale*log2e - m
-//    Operand fragments are read from LDS three MFMAs ahead.  On gfx950 a
-//    wavefront hides only a few VALU instructions behind each of its own
-//    MFMAs, so the step carries no other VALU work: the reference max m of
-//    each row is fixed by the segment's first key step (numerator and
-//    denominator share it, so the softmax is unchanged), and a row sum above
-//    2^64 at the segment's end -- the only way a probability can have
-//    overflowed -- makes the workgroup redo the segment with exact row
-//    maxima from a scores-only pass.
+//    Operand fragments are read from LDS three MFMAs ahead.  The step carries
+//    no other VALU work: the reference max m of each row is fixed by the
+//    segment's first key step (numerator and denominator share it, so the
+//    softmax is unchanged), and a row sum above 2^64 at the segment's end --
+//    the only way a probability can have overflowed -- makes the workgroup
+//    redo the segment with exact row maxima from a scores-only pass.
 //  * K and V arrive by direct global->LDS buffer loads (no staging registers,
-//    no LDS stores), issued by all four wavefronts from inline assembly (the
+//    no LDS stores), issued by every wavefront from inline assembly (the
 //    compiler would otherwise order every transposed LDS read behind all
 //    outstanding direct loads); completion is tracked with explicit vmcnt
-//    waits.  K of tiles t+1..t+5 and V of tiles t..t+3 are resident (5 + 4
-//    stages of 8 KB), loads have two steps to land, and one barrier per step
-//    publishes them.  Every step issues the same number of loads (a tile past
-//    the segment is addressed out of range, which returns zeros without
-//    memory traffic), so the wait count is a constant.  LDS rows are not
-//    padded: the 16-byte units of each row are XOR-swizzled so that every
-//    LDS read cycle of the K reads and of the transposed V reads touches 64
-//    distinct banks.
+//    waits.  K and V each have a ring of 8 stages of 32 rows: during step t,
+//    K of tiles t+1..t+7 and V of tiles t..t+6 are resident and K(t+8) and
+//    V(t+7) are loading, so a load has five steps to land, and one barrier
+//    per step publishes them.  The step loop runs in groups of 8 steps with
+//    the ring positions known at compile time, so every LDS stage address
+//    is an immediate offset from per-lane base registers and the loop
+//    carries almost no address arithmetic; the steps that do not fill a
+//    group run first.  Every step issues the same number of loads (a tile
+//    past the segment is addressed out of range, which returns zeros
+//    without memory traffic), so the wait count is a constant.  LDS rows are
+//    not padded: the 16-byte units of each row are XOR-swizzled so that
+//    every LDS read cycle of the K reads and of the transposed V reads
+//    touches 64 distinct banks.
 //  * Q/K/V are read through raw buffer resources that end at the sequence's
 //    last row, so ragged tiles read zeros without branches.  A tile's key
 //    steps take the sequence's last (ragged) key tile first, so only that
@@ -76,23 +79,34 @@
 namespace mf {
 namespace {
 
-constexpr int kWaves = 4;            // wavefronts per workgroup: one per SIMD
-constexpr int kRows = 64;            // query rows per wavefront (two 32-row blocks)
-constexpr int kBM = kWaves * kRows;  // query rows per tile
+constexpr int kBM = 256;             // query rows per tile (one workgroup)
 constexpr int kBN = 32;              // keys per K/V step (one 32-key MFMA block)
-constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;             // XCDs of an MI355X; blockIdx round-robins over them
 constexpr float kSumLimit = 1.8446744e19f;  // 2^64: bound on a row sum before the exact-max redo
 constexpr int kInlineSeqs = 64;      // packs up to this many sequences schedule in-kernel
-constexpr int kSlack = 2;            // steps a direct load may stay in flight
-constexpr int kKStages = 3 + kSlack; // K of tiles t+1 .. t+kKStages
-constexpr int kVStages = 2 + kSlack; // V of tiles t .. t+kVStages-1
+// K and V stages in LDS: rings of kRing tiles (tile j lives in stage
+// (j + phase offset) mod kRing).  During step t, K of tiles t+1 .. t+7 and V
+// of tiles t .. t+6 are resident and the loads of K(t+8) and V(t+7) fill the
+// stages freed by tiles t and t-1.
+constexpr int kRing = 8;
+constexpr int kKStages = kRing;
+constexpr int kVStages = kRing;
+constexpr int kSlack = kRing - 3;    // steps a direct load may stay in flight
+static_assert((kRing & (kRing - 1)) == 0, "ring positions are taken mod kRing with a mask");
 constexpr int kPfK = 3;              // K fragments read ahead of their MFMA
 constexpr int kPfV = 3;              // V fragments read ahead of their MFMA
 constexpr uint32_t kOutOfRange = 0x80000000u;  // scalar offset past any sequence's rows
 
 template <int D>
 struct Tile {
+    // 32-row blocks per wavefront: d = 128 runs eight wavefronts of 32 rows
+    // (two per SIMD, so one wavefront's MFMAs cover the other's softmax and
+    // waits); d = 64 runs four wavefronts of 64 rows, since its 4 KB K/V tile
+    // takes only four direct-load instructions.
+    static constexpr int NB = D == 128 ? 1 : 2;
+    static constexpr int ROWS_W = 32 * NB;         // query rows per wavefront
+    static constexpr int WAVES = kBM / ROWS_W;     // wavefronts per workgroup
+    static constexpr int THREADS = 64 * WAVES;
     static constexpr int KK = D / 16;              // QK^T MFMA steps along d
     static constexpr int EB = D / 32;              // 32-wide blocks of the output dim
     static constexpr int U = D / 8;                // 16-byte units per K or V row
@@ -100,16 +114,16 @@ struct Tile {
     static constexpr int ROW_BYTES = 2 * D;        // K/V rows are stored unpadded
     static constexpr int TILE_BYTES = kBN * ROW_BYTES;
     static constexpr int NI = TILE_BYTES / 1024;   // direct-load instructions per tile
-    static constexpr int NI_W = NI / kWaves;       // ... issued by each wavefront
-    static constexpr int NS = 2 * KK;              // S MFMAs per step (KK d-steps x 2 row blocks)
-    static constexpr int NP = 4 * EB;              // PV MFMAs per step (2 chunks x EB x 2 row blocks)
+    static constexpr int NI_W = NI / WAVES;        // ... issued by each wavefront
+    static constexpr int NS = KK * NB;             // S MFMAs per step (KK d-steps x NB row blocks)
+    static constexpr int NP = 2 * EB * NB;         // PV MFMAs per step (2 chunks x EB x NB row blocks)
     static constexpr int NV_FR = 2 * EB;           // V fragments per step
     static constexpr int LDS_BYTES = (kKStages + kVStages) * TILE_BYTES;
     // One partial-result slot of the workspace: unnormalised O (rounded to
     // bf16, kBM x D), then the reference max (log2 units) and sum of each
     // row in fp32.
     static constexpr size_t SLOT_BYTES = size_t(kBM) * D * 2 + size_t(kBM) * 8;
-    static_assert(NI % kWaves == 0, "whole direct-load instructions per wavefront");
+    static_assert(NI % WAVES == 0, "whole direct-load instructions per wavefront");
 };
 
 // XOR swizzles of the 16-byte units of LDS row `row` (unit u is stored at
@@ -366,6 +380,13 @@ __device__ __forceinline__ void dma16_asm(__amdgpu_buffer_rsrc_t r, uint32_t lds
                  : "memory");
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16, lane layout as lds_read_tr16_b64)
+// at LDS byte address a.
+__device__ __forceinline__ s16x4_t lds_tr16_at(uint32_t a) {
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(uintptr_t(a)));
+}
+
 // vmcnt waits (expcnt and lgkmcnt unconstrained); vmcnt is 6 bits, split
 // over bits [3:0] and [15:14] of the immediate.
 template <int N>
@@ -385,14 +406,14 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Score tile of one 32-key step for the lane's query row: 16 keys per lane,
-// for both 32-row blocks of the wavefront.
-typedef f32x16_t Scores[2];
-
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p) {
     using TL = Tile<D>;
-    constexpr int KK = TL::KK, EB = TL::EB, NI_W = TL::NI_W, NS = TL::NS, NP = TL::NP;
+    constexpr int KK = TL::KK, EB = TL::EB, NI_W = TL::NI_W, NS = TL::NS, NP = TL::NP, NB = TL::NB;
+    constexpr int kWaves = TL::WAVES, kRows = TL::ROWS_W;
+    // Score tile of one 32-key step for the lane's query row: 16 keys per
+    // lane, for each 32-row block of the wavefront.
+    typedef f32x16_t Scores[NB];
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ SchedLds sched_lds;
     __shared__ int redo_flag[kWaves];
@@ -414,14 +435,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
 
     // LDS: K stages 0 .. kKStages-1, then V stages 0 .. kVStages-1.
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-    auto kstage = [&](int s) -> const unsigned char* { return smem + s * TL::TILE_BYTES; };
-    auto vstage = [&](int s) -> const unsigned char* { return smem + (kKStages + s) * TL::TILE_BYTES; };
+    auto kstage = [&](int s) -> uint32_t { return uint32_t(s * TL::TILE_BYTES); };
+    auto vstage = [&](int s) -> uint32_t { return uint32_t(s * TL::TILE_BYTES); };
 
     // ---- direct-load source offsets (same for every tile) ------------------
     // Instruction n of a tile fills LDS units [64n, 64n+64) of the stage;
     // lane i fills unit 64n+i = (row, stored unit) and so fetches the row's
     // unit (stored unit ^ swizzle).  Wavefront w issues instructions
-    // w, w+4, ...
+    // w, w + kWaves, ...
     uint32_t k_voff[NI_W], v_voff[NI_W];
 #pragma unroll
     for (int j = 0; j < NI_W; ++j) {
@@ -446,13 +467,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
         const int vu = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
         return uint32_t(vrow * TL::ROW_BYTES + 16 * (vu ^ swz_v<D>(vrow)) + 8 * (lane & 1));
     }();
-    auto kfrag = [&](const unsigned char* kb, int kk) -> bf16x8_t {
-        return *reinterpret_cast<const bf16x8_t*>(kb + (k_rd ^ uint32_t(32 * kk)));
+    // Per-lane LDS byte addresses of the fragments in stage 0 of each ring,
+    // kept in registers (opaque to the compiler, which would otherwise
+    // recompute them before every read): a stage and a key chunk then add
+    // only an immediate offset (every such offset stays below 64 KB).
+    uint32_t ka[KK], va[EB];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        ka[kk] = lds0 + (k_rd ^ uint32_t(32 * kk));
+        asm volatile("" : "+v"(ka[kk]));
+    }
+#pragma unroll
+    for (int m = 0; m < EB; ++m) {
+        va[m] = lds0 + kKStages * TL::TILE_BYTES + (v_rd ^ uint32_t(64 * m));
+        asm volatile("" : "+v"(va[m]));
+    }
+    typedef __attribute__((address_space(3))) const bf16x8_t* lds_b128_ptr;
+    // kb, vb: byte offsets of a stage from the start of its ring
+    auto kfrag = [&](uint32_t kb, int kk) -> bf16x8_t {
+        return *reinterpret_cast<lds_b128_ptr>(uintptr_t(ka[kk] + kb));
     };
-    auto vfrag = [&](const unsigned char* vb, int gi) -> bf16x8_t {
-        const unsigned char* a = vb + (gi / EB) * 16 * TL::ROW_BYTES + (v_rd ^ uint32_t(64 * (gi % EB)));
-        const s16x4_t lo = lds_read_tr16_b64(a);
-        const s16x4_t hi = lds_read_tr16_b64(a + 8 * TL::ROW_BYTES);
+    auto vfrag = [&](uint32_t vb, int gi) -> bf16x8_t {
+        const uint32_t a = va[gi % EB] + vb + (gi / EB) * 16 * TL::ROW_BYTES;
+        const s16x4_t lo = lds_tr16_at(a);
+        const s16x4_t hi = lds_tr16_at(a + 8 * TL::ROW_BYTES);
         return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
@@ -499,6 +537,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
             const int kt = j == 0 ? nkv - 1 : j - 1;
             return j < kv1 ? uint32_t(kt) * uint32_t(kBN) * row_bytes : kOutOfRange;
         };
+        // ... for a key step j >= 1 (all steps the step loop loads)
+        auto tile_soff_pos = [&](int j) -> uint32_t {
+            return j < kv1 ? uint32_t(j - 1) * uint32_t(kBN) * row_bytes : kOutOfRange;
+        };
+        // The step loop runs its steps in groups of kRing with every ring
+        // position a compile-time constant (so LDS stage addresses are
+        // immediates); the m % kRing steps that do not fill a group run first,
+        // with run-time ring positions.  Tile kv0 is placed at ring position
+        // ph0 so that the groups start at position 0 and the last step of
+        // the segment (tile kv1 - 1) sits at position 0.
+        const int m_steps = n - 1;     // steps followed by another step
+        const int r_steps = m_steps & (kRing - 1);
+        const int ph0 = (kRing - r_steps) & (kRing - 1);
         auto dma_k = [&](int stage, uint32_t so, int j) {
             dma16_asm(k_rs, lds0 + stage * TL::TILE_BYTES + 1024 * (wave + kWaves * j), k_voff[j], so);
         };
@@ -507,10 +558,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
                       v_voff[j], so);
         };
 
-        // Q^T fragments (B operand) of the two row blocks, kept in registers.
-        bf16x8_t qf[2][KK];
+        // Q^T fragments (B operand) of the row blocks, kept in registers.
+        bf16x8_t qf[NB][KK];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < NB; ++b) {
             const int qrow = qtile * kBM + wave * kRows + 32 * b + l32;
             const uint32_t qoff = uint32_t(qrow) * row_bytes + 16u * hlf;
 #pragma unroll
@@ -523,18 +574,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
         auto mask_scores = [&](Scores& s) {
             const int lim = L - (nkv - 1) * kBN - 4 * hlf;   // key offsets >= lim are past the end
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (8 * (r >> 2) + (r & 3) >= lim) s[b][r] = -INFINITY;
         };
         // S = K Q^T of the K tile in LDS at kb (no overlapped work).
-        auto scores = [&](Scores& s, const unsigned char* kb) {
+        auto scores = [&](Scores& s, uint32_t kb) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 const bf16x8_t f = kfrag(kb, kk);
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < NB; ++b)
                     s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[b][kk], kk == 0 ? f32x16_t{} : s[b], 0, 0, 0);
             }
         };
@@ -550,7 +601,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
         // output accumulators are only ever written by MFMAs, and the step
         // loop carries no max or rescale work.
         bool preset = false;
-        float m_pre[2] = {-INFINITY, -INFINITY};
+        float m_pre[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) m_pre[b] = -INFINITY;
         for (;;) {
             // The previous segment's (or attempt's) LDS reads are done and its
             // loads landed before its stages are refilled.
@@ -571,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
                     scores(sp, kstage(0));
                     if (j == 0 && mask_first) mask_scores(sp);
 #pragma unroll
-                    for (int b = 0; b < 2; ++b) {
+                    for (int b = 0; b < NB; ++b) {
                         float mxb = sp[b][0];
 #pragma unroll
                         for (int r = 1; r < 16; ++r) mxb = fmaxf(mxb, sp[b][r]);
@@ -580,53 +633,64 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
                     __syncthreads();
                 }
             }
-            // K stage i holds tiles kv0+i, kv0+i+kKStages, ...; V stage i holds
-            // tiles kv0+i, kv0+i+kVStages, ...  The prologue loads K of tiles
-            // kv0 .. kv0+kKStages-1 and V of tiles kv0 .. kv0+kVStages-2.
+            // Tile kv0+i lives in stage (ph0 + i) mod kRing of each ring.  The
+            // prologue loads K of tiles kv0 .. kv0+7 and V of tiles kv0 ..
+            // kv0+6 in the order they are first read: K0 K1 K2 V0 (before step
+            // 0), then K(i+2) and V(i) for step i = 1 .. 5, then V6, so that
+            // the constant vmcnt wait at the end of each step also covers them.
+            {
+                auto pk = [&](int i) {
 #pragma unroll
-            for (int i = 0; i < kKStages; ++i)
+                    for (int j = 0; j < NI_W; ++j) dma_k((ph0 + i) & (kRing - 1), tile_soff(kv0 + i), j);
+                };
+                auto pv = [&](int i) {
 #pragma unroll
-                for (int j = 0; j < NI_W; ++j) dma_k(i, tile_soff(kv0 + i), j);
+                    for (int j = 0; j < NI_W; ++j) dma_v((ph0 + i) & (kRing - 1), tile_soff(kv0 + i), j);
+                };
+                pk(0); pk(1); pk(2); pv(0);
 #pragma unroll
-            for (int i = 0; i < kVStages - 1; ++i)
-#pragma unroll
-                for (int j = 0; j < NI_W; ++j) dma_v(i, tile_soff(kv0 + i), j);
+                for (int i = 1; i <= 5; ++i) { pk(i + 2); pv(i); }
+                pv(6);
+            }
 
-            f32x16_t o[2][EB];
+            f32x16_t o[NB][EB];
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int m = 0; m < EB; ++m)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[b][m][r] = 0.f;
-            float m_run[2], negm[2], lsum[2] = {0.f, 0.f};
+            float m_run[NB], negm[NB], lsum[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) lsum[b] = 0.f;
 
             bf16x8_t kf[kPfK], vf[kPfV];
-            bf16x8_t pf[2][2];
+            bf16x8_t pf[NB][2];
             Scores h0, h1;
 
-            wait_vm<0>();
+            // K0 K1 K2 V0 have landed (11 later prologue tiles may be in flight)
+            wait_vm<11 * NI_W>();
             __syncthreads();
 
             // ---- phase 1: S(t+1) = K(t+1) Q^T || p = exp2(x(t)) (kExp) ------
-            // Slot i issues S MFMA i (d-step i/2, row block i % 2: each K
-            // fragment feeds the two row blocks) and the exponentials of x
+            // Slot i issues S MFMA i (d-step i / NB, row block i % NB: each K
+            // fragment feeds the NB row blocks) and the exponentials of x
             // elements [E i, E i + E) (element e: row block e/16, register
             // e%16); the bf16 rounding and row sums of slot i's pairs run in
             // slot i+1.  The first V fragments of phase 2 are read in the last
             // slots.
-            auto phase1 = [&]<bool kS>(Scores& x, Scores& s, const unsigned char* kb, const unsigned char* vb) {
-                constexpr int E = 32 / NS;
+            auto phase1 = [&]<bool kS>(Scores& x, Scores& s, uint32_t kb, uint32_t vb) {
+                constexpr int E = 16 * NB / NS;
                 float ex[E];
                 static_for<NS + 1>([&](auto SI) {
                     constexpr int sl = SI;
                     if constexpr (kS && sl < NS) {
-                        constexpr int kk = sl / 2, b = sl % 2;
+                        constexpr int kk = sl / NB, b = sl % NB;
                         if constexpr (kk == 0)
                             s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kPfK], qf[b][kk], f32x16_t{}, 0, 0, 0);
                         else
                             s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % kPfK], qf[b][kk], s[b], 0, 0, 0);
-                        if constexpr (b == 1 && kk + kPfK < KK) kf[kk % kPfK] = kfrag(kb, kk + kPfK);
+                        if constexpr (b == NB - 1 && kk + kPfK < KK) kf[kk % kPfK] = kfrag(kb, kk + kPfK);
                     }
                     if constexpr (sl > 0) {
                         // bf16 rounding and row sums of the previous slot's pairs
@@ -655,18 +719,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
             };
 
             // ---- phase 2: O += V(t)^T P(t)^T || front half of softmax(t+1) --
-            // Slot i issues PV MFMA i (chunk i / 2EB, output block (i/2) % EB,
-            // row block i % 2: each V fragment feeds the two row blocks).  With
+            // Slot i issues PV MFMA i (chunk i / (NB EB), output block
+            // (i / NB) % EB, row block i % NB: each V fragment feeds the NB
+            // row blocks).  With
             // kNext the slots also carry the front half of the next tile's
             // softmax: the row maxima of S(t+1), the raise check and
             // x(t+1) = S(t+1) c - m, in place; they issue the step's direct
             // loads (K of tile t+kKStages, V of tile t+kVStages-1) in slots
             // 1 .. 2 NI_W and read the first K fragments of the next phase 1
             // in the last slots.
-            auto phase2 = [&]<bool kNext>(Scores& s, const unsigned char* vb, const unsigned char* kb_next, int t,
+            auto phase2 = [&]<bool kNext>(Scores& s, uint32_t vb, uint32_t kb_next, int t,
                                           int kdst, int vdst) {
-                constexpr int NITEMS = kNext ? 32 : 0;   // x = S c - m, in place
-                const uint32_t so_k = tile_soff(t + kKStages), so_v = tile_soff(t + kVStages - 1);
+                constexpr int NITEMS = kNext ? 16 * NB : 0;   // x = S c - m, in place
+                const uint32_t so_k = tile_soff_pos(t + kKStages), so_v = tile_soff_pos(t + kVStages - 1);
                 auto item = [&](auto II) {
                     constexpr int e = II;
                     constexpr int b = e / 16, r = e % 16;
@@ -674,9 +739,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
                 };
                 static_for<NP>([&](auto SI) {
                     constexpr int sl = SI;
-                    constexpr int gi = sl / 2, b = sl % 2, cc = gi / EB, m = gi % EB;
+                    constexpr int gi = sl / NB, b = sl % NB, cc = gi / EB, m = gi % EB;
                     o[b][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[gi % kPfV], pf[b][cc], o[b][m], 0, 0, 0);
-                    if constexpr (b == 1 && gi + kPfV < TL::NV_FR) vf[gi % kPfV] = vfrag(vb, gi + kPfV);
+                    if constexpr (b == NB - 1 && gi + kPfV < TL::NV_FR) vf[gi % kPfV] = vfrag(vb, gi + kPfV);
                     if constexpr (kNext && sl >= 1 && sl <= NI_W) dma_k(kdst, so_k, sl - 1);
                     if constexpr (kNext && sl > NI_W && sl <= 2 * NI_W) dma_v(vdst, so_v, sl - NI_W - 1);
                     constexpr int lo = NITEMS * sl / NP, hi = NITEMS * (sl + 1) / NP;
@@ -687,10 +752,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
             };
 
             // ---- first tile: S(kv0), its row maxima and x(kv0) -------------
-            scores(h0, kstage(0));
+            scores(h0, kstage(ph0));
             if (mask_first) mask_scores(h0);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 float mxb = fmaxf(h0[b][0], h0[b][1]);
 #pragma unroll
                 for (int r = 2; r < 16; r += 2) mxb = fmaxf(mxb, fmaxf(h0[b][r], h0[b][r + 1]));
@@ -700,53 +765,53 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
                 for (int r = 0; r < 16; ++r) h0[b][r] = __builtin_fmaf(h0[b][r], c, negm[b]);
             }
 #pragma unroll
-            for (int i = 0; i < kPfK; ++i) kf[i] = kfrag(kstage(1), i);
-            // every wavefront is done with K stage 0 before step 0 refills it
+            for (int i = 0; i < kPfK; ++i) kf[i] = kfrag(kstage((ph0 + 1) & (kRing - 1)), i);
+            // every wavefront is done with K of tile kv0 before step 0 refills it
             __syncthreads();
 
             // ---- key steps ---------------------------------------------------
-            // Step i (tile t = kv0 + i) reads K(t+1) and V(t), refills the K
-            // stage of tile t with tile t+kKStages and the V stage of tile t-1
-            // with tile t+kVStages-1, waits until its own loads issued kSlack
-            // steps before or earlier have landed, and passes the step
-            // barrier.  A tile is read no earlier than the step after the
-            // barrier that published it, and a stage is refilled only after
-            // the barrier that ended its last reads.  x(t) and S(t+1)
-            // alternate between h0 and h1; the loop runs the steps in pairs
-            // (an odd first step is peeled) so that it has a single exit.
-            int ks = 1 % kKStages;         // K stage of tile t+1
-            int vs = 0;                    // V stage of tile t
-            auto step = [&](Scores& x, Scores& s, int i) {
-                const int t = kv0 + i;
-                const int ks2 = ks + 1 == kKStages ? 0 : ks + 1;       // K stage of tile t+2
-                const int kd = ks == 0 ? kKStages - 1 : ks - 1;         // K stage of tile t
-                const int vd = vs == 0 ? kVStages - 1 : vs - 1;         // V stage of tile t-1
-                phase1.template operator()<true>(x, s, kstage(ks), vstage(vs));
-                phase2.template operator()<true>(s, vstage(vs), kstage(ks2), t, kd, vd);
+            // Step t (tile t at ring position ph) reads K(t+1) and V(t),
+            // refills the K stage of tile t with tile t+8 and the V stage of
+            // tile t-1 with tile t+7, waits until the loads it and the other
+            // steps issued kSlack steps before or earlier have landed, and
+            // passes the step barrier.  A tile is read no earlier than the step
+            // after the barrier that published it, and a stage is refilled only
+            // after the barrier that ended its last reads.  x(t) and S(t+1)
+            // alternate between h0 and h1 (even ring positions read x from h0).
+            auto step = [&](Scores& x, Scores& s, int t, int ph) {
+                const int ks = (ph + 1) & (kRing - 1);       // K stage of tile t+1
+                const int ks2 = (ph + 2) & (kRing - 1);      // K stage of tile t+2
+                const int vd = (ph + kRing - 1) & (kRing - 1);  // V stage of tile t-1
+                phase1.template operator()<true>(x, s, kstage(ks), vstage(ph));
+                phase2.template operator()<true>(s, vstage(ph), kstage(ks2), t, ph, vd);
                 wait_vm<2 * NI_W * kSlack>();
                 __syncthreads();
-                ks = ks2;
-                vs = vs + 1 == kVStages ? 0 : vs + 1;
             };
-            const int m_steps = n - 1;     // steps followed by another step
             int i = 0;
-            if (m_steps & 1) {
-                step(h0, h1, i++);
-                h0[0] = h1[0];
-                h0[1] = h1[1];
+            for (; i < r_steps; ++i) {
+                step(h0, h1, kv0 + i, (ph0 + i) & (kRing - 1));
+#pragma unroll
+                for (int b = 0; b < NB; ++b) h0[b] = h1[b];
             }
-            for (; i < m_steps; i += 2) {
-                step(h0, h1, i);
-                step(h1, h0, i + 1);
+            for (; i < m_steps; i += kRing) {
+                static_for<kRing>([&](auto P) {
+                    constexpr int ph = P;
+                    if constexpr (ph % 2 == 0) step(h0, h1, kv0 + i + ph, ph);
+                    else step(h1, h0, kv0 + i + ph, ph);
+                });
             }
-            phase1.template operator()<false>(h0, h0, kstage(0), vstage(vs));
-            phase2.template operator()<false>(h0, vstage(vs), kstage(0), kv1, 0, 0);
+            // the segment's last tile, at ring position 0
+            phase1.template operator()<false>(h0, h0, kstage(1), vstage(0));
+            phase2.template operator()<false>(h0, vstage(0), kstage(2), kv1, 0, 0);
 
             // ---- redo decision (workgroup-wide) --------------------------------
             // A row sum is at least every one of its terms, so a sum within
             // the limit (and finite) shows that no probability overflowed.
             if (!preset) {
-                const bool raised = __builtin_amdgcn_ballot_w64(!(lsum[0] <= kSumLimit) || !(lsum[1] <= kSumLimit)) != 0;
+                bool big = false;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) big |= !(lsum[b] <= kSumLimit);
+                const bool raised = __builtin_amdgcn_ballot_w64(big) != 0;
                 if (lane == 0) redo_flag[wave] = raised;
                 __syncthreads();
                 bool any = false;
@@ -759,13 +824,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
             }
 
             // ---- epilogue --------------------------------------------------
-            float l_tot[2];
+            float l_tot[NB];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) l_tot[b] = half_sum(lsum[b]);
+            for (int b = 0; b < NB; ++b) l_tot[b] = half_sum(lsum[b]);
             if (kv0 == 0 && kv1 == nkv) {
                 // whole tile: normalise and store O (bf16) and the LSE
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
+                for (int b = 0; b < NB; ++b) {
                     const int qrow = qtile * kBM + wave * kRows + 32 * b + l32;
                     if (qrow < L) {
                         const float inv = 1.0f / l_tot[b];
@@ -791,7 +856,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(KParams p) {
                 uint16_t* acc = reinterpret_cast<uint16_t*>(slot);
                 float* ml = reinterpret_cast<float*>(slot + size_t(kBM) * D * 2);
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
+                for (int b = 0; b < NB; ++b) {
                     const int row = wave * kRows + 32 * b + l32;
 #pragma unroll
                     for (int m = 0; m < EB; ++m)
@@ -933,7 +998,7 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
         reinterpret_cast<const void*>(&attn_fwd_kernel<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
         int(smem));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(G), dim3(kThreads), smem, stream, p);
+    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(G), dim3(Tile<D>::THREADS), smem, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (G > 1) {
