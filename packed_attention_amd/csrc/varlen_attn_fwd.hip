@@ -163,6 +163,8 @@ struct Sched {
     const int32_t* tiles;
     const int32_t* nkv;
     const int64_t* it_start;
+    const int32_t* tok0;   // first token and length of each rank's sequence
+    const int32_t* len;    // (in-LDS schedules only; nullptr otherwise)
     int n;
     int64_t W;
 };
@@ -185,7 +187,8 @@ __device__ __forceinline__ int octave_class(int L) {
 // In-kernel schedule of a small pack (n <= kInlineSeqs), built in LDS by
 // every thread of the block.
 __device__ void build_schedule_small(const int32_t* __restrict__ cu, int n, int H, int32_t* seq,
-                                     int32_t* tiles, int32_t* nkv, int64_t* it_start) {
+                                     int32_t* tiles, int32_t* nkv, int64_t* it_start, int32_t* tok0,
+                                     int32_t* len) {
     for (int s = threadIdx.x; s < n; s += blockDim.x) {
         const int Ls = cu[s + 1] - cu[s];
         const int cs = octave_class(Ls);
@@ -197,6 +200,8 @@ __device__ void build_schedule_small(const int32_t* __restrict__ cu, int n, int 
         seq[rank] = s;
         tiles[rank] = (Ls + kBM - 1) / kBM;
         nkv[rank] = (Ls + kBN - 1) / kBN;
+        tok0[rank] = cu[s];
+        len[rank] = Ls;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(const int3
 
 // Schedule of this call: built in LDS for small packs, else the prologue's.
 struct SchedLds {
-    int32_t seq[kInlineSeqs], tiles[kInlineSeqs], nkv[kInlineSeqs];
+    int32_t seq[kInlineSeqs], tiles[kInlineSeqs], nkv[kInlineSeqs], tok0[kInlineSeqs], len[kInlineSeqs];
     int64_t it_start[kInlineSeqs + 1];
 };
 
@@ -295,13 +300,17 @@ __device__ Sched get_schedule(const int32_t* cu, int n, int H, const unsigned ch
     Sched s;
     s.n = n;
     if (n <= kInlineSeqs) {
-        build_schedule_small(cu, n, H, lds.seq, lds.tiles, lds.nkv, lds.it_start);
+        build_schedule_small(cu, n, H, lds.seq, lds.tiles, lds.nkv, lds.it_start, lds.tok0, lds.len);
+        s.tok0 = lds.tok0;
+        s.len = lds.len;
         s.seq = lds.seq;
         s.tiles = lds.tiles;
         s.nkv = lds.nkv;
         s.it_start = lds.it_start;
     } else {
         const int32_t* ints = reinterpret_cast<const int32_t*>(ws + 8);
+        s.tok0 = nullptr;
+        s.len = nullptr;
         s.seq = ints + 1;
         s.tiles = ints + 1 + n;
         s.nkv = ints + 1 + 2 * n;
@@ -510,8 +519,11 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
         const bool first_piece = it == it_begin;
         const int head = tile / nt;
         const int qtile = tile - head * nt;
-        const int64_t tok0 = __builtin_amdgcn_readfirstlane(p.cu[seq]);
-        const int L = __builtin_amdgcn_readfirstlane(p.cu[seq + 1]) - int(tok0);
+        // the sequence's first token and length (from the LDS schedule when
+        // there is one: no global load on the segment's critical path)
+        const int64_t tok0 = __builtin_amdgcn_readfirstlane(sch.tok0 ? sch.tok0[rank] : p.cu[seq]);
+        const int L = sch.len ? __builtin_amdgcn_readfirstlane(sch.len[rank])
+                              : __builtin_amdgcn_readfirstlane(p.cu[seq + 1]) - int(tok0);
         // Key step j of a tile processes key tile (j + nkv - 1) % nkv: the
         // sequence's last key tile, the only one with keys past the end
         // (masked when L is not a multiple of kBN), comes first, so only the
@@ -557,6 +569,12 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
             dma16_asm(v_rs, lds0 + (kKStages + stage) * TL::TILE_BYTES + 1024 * (wave + kWaves * j),
                       v_voff[j], so);
         };
+
+        // The previous segment's LDS reads are done before any of its stages
+        // is refilled.  (Its last direct loads need no wait: a wavefront's
+        // loads land in issue order, so they land before this segment's.)
+        if (!first_segment) __syncthreads();
+        first_segment = false;
 
         // Q^T fragments (B operand) of the row blocks, kept in registers.
         bf16x8_t qf[NB][KK];
@@ -605,14 +623,11 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
 #pragma unroll
         for (int b = 0; b < NB; ++b) m_pre[b] = -INFINITY;
         for (;;) {
-            // The previous segment's (or attempt's) LDS reads are done and its
-            // loads landed before its stages are refilled.
-            if (!first_segment) {
+            if (preset) {
+                // the failed attempt's loads have landed and its LDS reads
+                // are done before the scores-only pass refills K stage 0
                 wait_vm<0>();
                 __syncthreads();
-            }
-            first_segment = false;
-            if (preset) {
                 // exact row maxima over key steps kv0 .. kv1-1, one tile at a
                 // time through K stage 0
                 Scores sp;
