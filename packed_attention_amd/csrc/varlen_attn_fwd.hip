@@ -942,14 +942,24 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     auto slot_at = [&](int i) { return partials + size_t(slots[i]) * TL::SLOT_BYTES; };
     auto ml_at = [&](int i) { return reinterpret_cast<const float*>(slot_at(i) + size_t(kBM) * D * 2); };
 
-    // per row: the reference max M over the pieces and 1 / total weight
+    // per row: the reference max M over the pieces and 1 / total weight.
+    // Pieces are read two at a time with all their loads issued together
+    // (one memory round trip per pair instead of one per load); the sums
+    // keep the order of a piece-by-piece pass.
     __shared__ float row_m[kBM], row_inv[kBM];
     const int tid = threadIdx.x;
     if (tid < kBM) {
-        float M = -INFINITY;
-        for (int i = 0; i < ns; ++i) M = fmaxf(M, ml_at(i)[tid]);
-        float lt = 0.f;
-        for (int i = 0; i < ns; ++i) lt += exp2f(ml_at(i)[tid] - M) * ml_at(i)[kBM + tid];
+        float M = -INFINITY, lt = 0.f;
+        for (int i = 0; i < ns; i += 2) {
+            const bool has1 = i + 1 < ns;
+            const float m0 = ml_at(i)[tid], l0 = ml_at(i)[kBM + tid];
+            const float m1 = has1 ? ml_at(i + 1)[tid] : -INFINITY;
+            const float l1 = has1 ? ml_at(i + 1)[kBM + tid] : 0.f;
+            const float Mn = fmaxf(M, fmaxf(m0, m1));
+            lt = lt * exp2f(M - Mn) + exp2f(m0 - Mn) * l0;
+            if (has1) lt += exp2f(m1 - Mn) * l1;
+            M = Mn;
+        }
         row_m[tid] = M;
         row_inv[tid] = 1.0f / lt;
         const int qrow = qtile * kBM + tid;
@@ -958,29 +968,55 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     __syncthreads();
 
     // weighted sum of the pieces over the tile's 16-byte chunks (8 bf16) in
-    // memory order (consecutive lanes read consecutive chunks)
+    // memory order (consecutive lanes read consecutive chunks), the chunks
+    // of a pair of pieces loaded together
     constexpr int kRowChunks = D / 8;
     constexpr int kChunks = kBM * kRowChunks;
+    constexpr int kPer = kChunks / kFixThreads;
     static_assert(kChunks % kFixThreads == 0, "whole chunks per thread");
+    float acc[kPer][8];
 #pragma unroll
-    for (int j = 0; j < kChunks / kFixThreads; ++j) {
+    for (int j = 0; j < kPer; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+    for (int i = 0; i < ns; i += 2) {
+        u32x4_t raw[2][kPer];
+        float w[2][kPer];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const bool has = i + k < ns;
+            const unsigned char* sl = slot_at(has ? i + k : i);
+            const float* ml = ml_at(has ? i + k : i);
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int cidx = tid + kFixThreads * j;
+                const int row = cidx / kRowChunks;
+                raw[k][j] = reinterpret_cast<const u32x4_t*>(sl)[cidx];
+                w[k][j] = has ? exp2f(ml[row] - row_m[row]) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (i + k >= ns) break;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                float a8[8];
+                unpack8(raw[k][j], a8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[j][e] += w[k][j] * a8[e];
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
         const int cidx = tid + kFixThreads * j;
         const int row = cidx / kRowChunks;
         const int qrow = qtile * kBM + row;
         if (qrow >= L) continue;
-        const float M = row_m[row];
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int i = 0; i < ns; ++i) {
-            const float w = exp2f(ml_at(i)[row] - M);
-            float a8[8];
-            unpack8(reinterpret_cast<const u32x4_t*>(slot_at(i))[cidx], a8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += w * a8[e];
-        }
         const float inv = row_inv[row];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] *= inv;
-        st16(p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 8 * (cidx % kRowChunks), pack8(acc));
+        for (int e = 0; e < 8; ++e) acc[j][e] *= inv;
+        st16(p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 8 * (cidx % kRowChunks), pack8(acc[j]));
     }
 }
 

@@ -71,8 +71,10 @@ def to_device(w: Workload, device="cuda", with_lse=True) -> DeviceBatch:
         mod_row=torch.from_numpy(mr).to(device),
         q=q, k=k, v=v, x=dev(w.x), shift=dev(w.shift), scale=dev(w.scale), gate=dev(w.gate),
         shift2=dev(w.shift2), scale2=dev(w.scale2),
-        qr=torch.empty_like(q), kr=torch.empty_like(k), o=torch.empty_like(q),
-        lse=torch.empty((H, T), dtype=torch.float32, device=device) if with_lse else None,
+        # attention outputs start as NaN, so that a row the kernels never
+        # write cannot pass a check on values left in reused memory
+        qr=torch.empty_like(q), kr=torch.empty_like(k), o=torch.full_like(q, float("nan")),
+        lse=torch.full((H, T), float("nan"), dtype=torch.float32, device=device) if with_lse else None,
         y=torch.empty((T, H * D), dtype=torch.bfloat16, device=device) if w.x is not None else None,
         z=torch.empty((T, H * D), dtype=torch.bfloat16, device=device) if w.x is not None else None,
         workspace=torch.empty(native.attn_workspace_bytes(len(w.descs), T, H, D), dtype=torch.uint8,

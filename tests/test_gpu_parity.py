@@ -152,8 +152,8 @@ def test_packed_equals_alone_and_determinism():
     for s in range(len(descs)):
         a0, a1 = int(b.cu_host[s]), int(b.cu_host[s + 1])
         L = a1 - a0
-        o = torch.empty((L, w.H, w.D), dtype=torch.bfloat16, device="cuda")
-        lse = torch.empty((w.H, L), dtype=torch.float32, device="cuda")
+        o = torch.full((L, w.H, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((w.H, L), float("nan"), dtype=torch.float32, device="cuda")
         cu1 = torch.tensor([0, L], dtype=torch.int32, device="cuda")
         native.varlen_attn_fwd(b.qr[a0:a1], b.kr[a0:a1], b.v[a0:a1], o, cu1, L, lse=lse)
         torch.cuda.synchronize()
@@ -321,8 +321,10 @@ def _run_attn(q, k, v, cu, grid=0):
     try:
         T, H, D = q.shape
         qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-        o = torch.empty_like(qd)
-        lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+        # NaN-filled outputs: a row the kernels fail to write cannot pass on
+        # a previous call's values left at the same address
+        o = torch.full_like(qd, float("nan"))
+        lse = torch.full((H, T), float("nan"), dtype=torch.float32, device="cuda")
         cud = torch.from_numpy(cu).cuda()
         ws = torch.empty(native.attn_workspace_bytes(len(cu) - 1, T, H, D), dtype=torch.uint8, device="cuda")
         native.varlen_attn_fwd(qd, kd, vd, o, cud, int(np.diff(cu).max()), lse=lse, workspace=ws)
@@ -432,8 +434,8 @@ def test_side_stream_without_workspace():
     f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
     O_ref, L_ref = R.attention(f(q), f(k), f(v), cu)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    o = torch.empty_like(qd)
-    lse = torch.empty((8, int(sum(lens))), dtype=torch.float32, device="cuda")
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((8, int(sum(lens))), float("nan"), dtype=torch.float32, device="cuda")
     cud = torch.from_numpy(cu).cuda()
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
