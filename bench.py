@@ -45,8 +45,11 @@ cover their submission), divided by K.  Prints one JSON line:
               generator: attention TFLOP/s and fraction of the bf16 peak,
               modulate+RoPE and gated residual (y alone, y with the fused
               next adaLN) GB/s and fraction of the HBM peak;
-  sclk        the shader clock sampled (amdsmi) while attention calls run
-              back to back;
+  sclk        the shader clock while attention calls run back to back:
+              amdsmi's GFX clock reading, and the effective clock (shader
+              cycles per second of a spin running beside the calls), which
+              falls well below the clock setting under sustained MFMA load
+              with random operands;
   cpu_baseline the fp64 oracle's whole step over the same workload, repeated
               for about 10 s on the host cores of the process's affinity
               mask, and one pass of a bounded sample on one core.
@@ -432,13 +435,30 @@ def main():
                                        "TFLOP/s": round(ct, 2), "frac_bf16_peak": round(ct / PEAK_BF16_TFLOPS, 4)}}}
     del tsets
 
-    # Shader clock while attention calls run back to back (about 0.2 s).
+    # Shader clock while attention calls run back to back (about 0.3 s):
+    # amdsmi's GFX clock reading, and the effective clock, from a one-thread
+    # spin on a side stream that runs beside the attention calls for a
+    # fixed number of shader cycles (s_memtime), timed by HIP events.
+    side = torch.cuda.Stream()
+    spin_cycles = int(1.5e8)        # <= 0.15 s at any clock above 1 GHz
     with ClockSampler() as clk:
-        reps = max(1, int(200.0 / max(kern_ms["varlen_attn_fwd"], 1e-3)))
+        reps = max(1, int(300.0 / max(kern_ms["varlen_attn_fwd"], 1e-3)))
+        runner.run_attention(sets[0])
+        se0, se1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            se0.record(side)
+            torch.cuda._sleep(spin_cycles)
+            se1.record(side)
         for i in range(reps):
             runner.run_attention(sets[i % len(sets)])
         torch.cuda.synchronize()
     sclk = clk.summary()
+    spin_ms = se0.elapsed_time(se1)
+    if sclk is None:
+        sclk = {}
+    sclk["effective_mhz"] = round(spin_cycles / (spin_ms * 1e-3) / 1e6, 1)
+    sclk["effective_note"] = ("shader cycles counted by a one-thread spin beside the attention calls, "
+                              "per second of wall time")
 
     configs = None if args.no_configs else config_lines(args, timed, torch, runner, W)
 
@@ -514,7 +534,7 @@ def main():
                      "flops_per_launch": flops, "launch_ms": round(kern_ms["varlen_attn_fwd"], 5),
                      "mfma_busy": None if counters is None else counters.get("mfma_busy_frac"),
                      "counters": None if counters is None else os.path.relpath(COUNTERS_FILE, ROOT),
-                     "sclk_mhz": None if sclk is None else sclk["mean_mhz"]},
+                     "sclk_mhz": sclk.get("mean_mhz"), "sclk_effective_mhz": sclk.get("effective_mhz")},
         "kernels": kernels,
         "backward": backward,
         "block": block,
