@@ -100,7 +100,7 @@ mf_status mf_pack_count(const mf_sample_desc* descs, int32_t n, int64_t* total_t
  *   mod_row[T]     : adaLN row of every token (may be NULL).
  * Per-sample positions restart at every sample, as the per-sample 2D/3D
  * rotary embedding requires.  Errors as mf_pack_count, plus MF_ERR_NULL if
- * cu_seqlens or pos is NULL. */
+ * cu_seqlens is NULL, or pos is NULL while T > 0. */
 mf_status mf_pack_tables(const mf_sample_desc* descs, int32_t n, int32_t* cu_seqlens,
                          int32_t* pos, int32_t* seq_id, int32_t* mod_row);
 

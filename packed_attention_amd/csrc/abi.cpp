@@ -36,6 +36,16 @@ bool debug_mode() {
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Arguments a workspace-size query can size: anything its call would reject
+// for its sizes gets 0 bytes (and no arithmetic on out-of-range values).
+inline bool query_ok(int64_t T, int32_t H, int32_t D) {
+    return T >= 0 && T <= INT32_MAX && H > 0 && H <= 4096 && D > 0 && D <= 65536 && int64_t(H) * D <= 65536;
+}
+
+// Largest token stride (elements) any entry point takes: with T <= 2^31 every
+// offset T * stride * element size then fits in 64 bits.
+constexpr int64_t kMaxStride = int64_t(1) << 31;
+
 inline mf_status from_hip(hipError_t e) { return e == hipSuccess ? MF_OK : MF_ERR_HIP; }
 
 // Copy a device int32 array to the host (debug checks only).
@@ -93,6 +103,7 @@ mf_status mf_modulate_rope(void* stream, const void* q_in, const void* k_in, voi
         return MF_ERR_SHAPE;
     if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return MF_ERR_SHAPE;
     if (ld_in < int64_t(H) * D || ld_out < int64_t(H) * D) return MF_ERR_SHAPE;
+    if (ld_in > kMaxStride || ld_out > kMaxStride) return MF_ERR_UNSUPPORTED;
     if ((shift == nullptr) != (scale == nullptr)) return MF_ERR_NULL;
     const bool modulate = shift != nullptr;
     if (modulate && !(eps > 0.f)) return MF_ERR_SHAPE;
@@ -132,6 +143,7 @@ mf_status mf_modulate_rope(void* stream, const void* q_in, const void* k_in, voi
 }
 
 size_t mf_varlen_attn_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D) {
+    if (!query_ok(T, H, D) || n_seq < 0 || n_seq > (1 << 24)) return 0;
     return mf::attn_workspace_bytes(n_seq, T, H, D);
 }
 
@@ -149,6 +161,7 @@ mf_status attn_fwd_args(void* stream, const void* q, const void* k, const void* 
     if (n_seq < 0 || (T > 0 && n_seq < 1) || n_seq > (1 << 24)) return MF_ERR_SHAPE;
     if (max_seqlen < 0 || max_seqlen > T || (T > 0 && max_seqlen == 0)) return MF_ERR_SHAPE;
     if (ld_qkv < int64_t(H) * D || ld_o < int64_t(H) * D) return MF_ERR_SHAPE;
+    if (ld_qkv > kMaxStride || ld_o > kMaxStride) return MF_ERR_UNSUPPORTED;
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MF_ERR_SHAPE;
     // 32-bit buffer offsets inside one sequence's rows (plus a ragged tile)
     if ((int64_t(max_seqlen) + 256) * ld_qkv * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
@@ -235,6 +248,7 @@ mf_status mf_set_attn_fwd_grid(int32_t g) {
 }
 
 size_t mf_varlen_attn_bwd_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D) {
+    if (!query_ok(T, H, D) || n_seq < 0 || n_seq > (1 << 24)) return 0;
     return mf::attn_bwd_workspace_bytes(n_seq, T, H, D);
 }
 
@@ -248,6 +262,7 @@ mf_status mf_varlen_attn_bwd(void* stream, const void* q, const void* k, const v
     if (n_seq < 0 || (T > 0 && n_seq < 1) || n_seq > (1 << 24)) return MF_ERR_SHAPE;
     if (max_seqlen < 0 || max_seqlen > T || (T > 0 && max_seqlen == 0)) return MF_ERR_SHAPE;
     if (ld_qkv < int64_t(H) * D || ld_o < int64_t(H) * D || ld_dqkv < int64_t(H) * D) return MF_ERR_SHAPE;
+    if (ld_qkv > kMaxStride || ld_o > kMaxStride || ld_dqkv > kMaxStride) return MF_ERR_UNSUPPORTED;
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MF_ERR_SHAPE;
     // 32-bit buffer offsets inside one sequence's rows (plus a ragged tile)
     const int64_t ld_max = ld_qkv > ld_o ? ld_qkv : ld_o;
@@ -324,10 +339,12 @@ mf_status mf_gated_residual(void* stream, const void* x, const void* o, void* y,
 }
 
 size_t mf_modulate_rope_bwd_workspace_bytes(int64_t T, int32_t H, int32_t D) {
+    if (!query_ok(T, H, D)) return 0;
     return mf::elementwise_bwd_workspace_bytes(T, H * D, 2);
 }
 
 size_t mf_gated_residual_bwd_workspace_bytes(int64_t T, int32_t C) {
+    if (!query_ok(T, 1, C)) return 0;
     return mf::elementwise_bwd_workspace_bytes(T, C, 3);
 }
 
@@ -346,6 +363,7 @@ mf_status mf_modulate_rope_bwd(void* stream, const void* q_in, const void* k_in,
         return MF_ERR_SHAPE;
     if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return MF_ERR_SHAPE;
     if (ld_in < int64_t(H) * D || ld_gout < int64_t(H) * D || ld_gin < int64_t(H) * D) return MF_ERR_SHAPE;
+    if (ld_in > kMaxStride || ld_gout > kMaxStride || ld_gin > kMaxStride) return MF_ERR_UNSUPPORTED;
     const bool modulate = scale != nullptr;
     if (modulate && (!(eps > 0.f) || n_rows <= 0)) return MF_ERR_SHAPE;
     if (modulate && int64_t(n_rows) * H * D > (int64_t(1) << 31)) return MF_ERR_SHAPE;
@@ -444,6 +462,7 @@ mf_status mf_gated_residual_bwd(void* stream, const void* x, const void* o, cons
 }
 
 size_t mf_block_qkv_workspace_bytes(int64_t T, int32_t H, int32_t D) {
+    if (!query_ok(T, H, D)) return 0;
     return mf::block_qkv_workspace_bytes(T, H * D);
 }
 
@@ -460,6 +479,7 @@ mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_
         return MF_ERR_SHAPE;
     if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return MF_ERR_SHAPE;
     if (ld_x < C || ld_qkv < 3 * C) return MF_ERR_SHAPE;
+    if (ld_x > kMaxStride || ld_qkv > kMaxStride) return MF_ERR_UNSUPPORTED;
     // 32-bit buffer offsets over the activations and the weights
     if (T * ld_x * 2 >= (int64_t(1) << 32) || 3 * C * C * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
     if ((shift == nullptr) != (scale == nullptr)) return MF_ERR_NULL;
@@ -505,6 +525,7 @@ mf_status mf_block_out(void* stream, const void* o, int64_t ld_o, const void* w_
                        const void* gate, const int32_t* mod_row, void* y, int64_t T, int32_t C) {
     if (T < 0 || T > INT32_MAX || C <= 0 || C % 64 || C > 8192) return MF_ERR_SHAPE;
     if (ld_o < C) return MF_ERR_SHAPE;
+    if (ld_o > kMaxStride) return MF_ERR_UNSUPPORTED;
     if (T * ld_o * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
     if (T == 0) return MF_OK;
     if (!o || !w_o || !x || !gate || !mod_row || !y) return MF_ERR_NULL;
@@ -534,6 +555,7 @@ mf_status mf_cfg_euler_step(void* stream, const void* v, int64_t ld_v, const int
                             float guidance, float t, float t_next) {
     if (n_tokens < 0 || n_tokens > INT32_MAX || Cl <= 0 || Cl % 8 || Cl > 4096) return MF_ERR_SHAPE;
     if (ld_v < Cl || (x_next != nullptr && ld_x < Cl)) return MF_ERR_SHAPE;
+    if (ld_v > kMaxStride || ld_x > kMaxStride) return MF_ERR_UNSUPPORTED;
     if (!std::isfinite(guidance) || !std::isfinite(t) || !std::isfinite(t_next)) return MF_ERR_SHAPE;
     if (n_tokens == 0) return MF_OK;
     if (!v || !rows || !z || !z_out) return MF_ERR_NULL;
@@ -571,6 +593,7 @@ mf_status mf_qk_norm_rope(void* stream, const void* q_in, int64_t ld_q, const vo
     if (int64_t(Hq) * D > 8192 || int64_t(Hkv) * D > 8192) return MF_ERR_UNSUPPORTED;
     if (ld_q < int64_t(Hq) * D || ld_qo < int64_t(Hq) * D || ld_k < int64_t(Hkv) * D || ld_ko < int64_t(Hkv) * D)
         return MF_ERR_SHAPE;
+    if (ld_q > kMaxStride || ld_qo > kMaxStride || ld_k > kMaxStride || ld_ko > kMaxStride) return MF_ERR_UNSUPPORTED;
     if (!(rope_base > 0.f) || !std::isfinite(rope_base) || !(eps > 0.f)) return MF_ERR_SHAPE;
     if (T == 0) return MF_OK;
     if (!q_in || !k_in || !q_out || !k_out || !wq || !wk || !pos) return MF_ERR_NULL;
@@ -600,6 +623,7 @@ mf_status mf_qk_norm_rope(void* stream, const void* q_in, int64_t ld_q, const vo
 }
 
 size_t mf_varlen_attn_causal_workspace_bytes(int32_t n_seq, int64_t T) {
+    if (!query_ok(T, 1, 1) || n_seq < 0 || n_seq > (1 << 24)) return 0;
     return mf::causal_attn_workspace_bytes(n_seq, T);
 }
 
@@ -610,6 +634,7 @@ mf_status mf_varlen_attn_causal_fwd(void* stream, const void* q, int64_t ld_q, c
     if (T < 0 || T > INT32_MAX || n_seq < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return MF_ERR_SHAPE;
     if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
     if (ld_q < int64_t(Hq) * D || ld_o < int64_t(Hq) * D || ld_kv < int64_t(Hkv) * D) return MF_ERR_SHAPE;
+    if (ld_q > kMaxStride || ld_o > kMaxStride || ld_kv > kMaxStride) return MF_ERR_UNSUPPORTED;
     if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MF_ERR_SHAPE;
     if (T * ld_q * 2 >= (int64_t(1) << 32) || T * ld_kv * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
     if (T == 0 || n_seq == 0) return MF_OK;

@@ -25,7 +25,11 @@ mf_status count_tokens(const mf_sample_desc* d, int32_t n, int64_t* total) {
         if (e.text_len < 0 || e.n_frames < 0 || e.grid_h < 0 || e.grid_w < 0 ||
             e.mod_row_text < 0 || e.mod_row_image < 0)
             return MF_ERR_SHAPE;
-        const int64_t img = int64_t(e.n_frames) * int64_t(e.grid_h) * int64_t(e.grid_w);
+        // frames * rows * cols, checked after each product (each fits int64
+        // because its factors are below 2^31)
+        int64_t img = int64_t(e.n_frames) * int64_t(e.grid_h);
+        if (img > INT32_MAX && e.grid_w > 0) return MF_ERR_SHAPE;
+        img = e.grid_w == 0 ? 0 : img * int64_t(e.grid_w);
         if (img > INT32_MAX) return MF_ERR_SHAPE;
         T += int64_t(e.text_len) + img;
         if (T > INT32_MAX) return MF_ERR_SHAPE;
@@ -43,10 +47,11 @@ extern "C" mf_status mf_pack_count(const mf_sample_desc* descs, int32_t n, int64
 
 extern "C" mf_status mf_pack_tables(const mf_sample_desc* descs, int32_t n, int32_t* cu_seqlens,
                                     int32_t* pos, int32_t* seq_id, int32_t* mod_row) {
-    if (cu_seqlens == nullptr || pos == nullptr) return MF_ERR_NULL;
+    if (cu_seqlens == nullptr) return MF_ERR_NULL;
     int64_t T = 0;
     mf_status st = count_tokens(descs, n, &T);
     if (st != MF_OK) return st;
+    if (pos == nullptr && T > 0) return MF_ERR_NULL;
     int32_t t = 0;
     cu_seqlens[0] = 0;
     for (int32_t s = 0; s < n; ++s) {
@@ -58,7 +63,9 @@ extern "C" mf_status mf_pack_tables(const mf_sample_desc* descs, int32_t n, int3
             if (seq_id) seq_id[t] = s;
             if (mod_row) mod_row[t] = e.mod_row_text;
         }
-        // Frames in order, each frame's grid in row-major (raster) order.
+        // Frames in order, each frame's grid in row-major (raster) order (an
+        // empty grid has no tokens, whatever the frame count and other side).
+        if (e.grid_h > 0 && e.grid_w > 0)
         for (int32_t f = 0; f < e.n_frames; ++f)
             for (int32_t r = 0; r < e.grid_h; ++r)
                 for (int32_t c = 0; c < e.grid_w; ++c, ++t) {
