@@ -9,126 +9,98 @@
 //   y = x + gate[m(t)] * o                       (fp32, rounded to bf16)
 //   z = LN(y) * (1 + scale2[m(t)]) + shift2[m(t)] (LN of the fp32 y)
 //
-// One wavefront per token row of C channels; lane l owns the 16-byte chunks
-// l, l+64, ... so each access is a coalesced 1 KiB wavefront transaction.
-// HBM-bound: per token it reads x and o and writes y (and z).
+// One workgroup per token row of C channels, each thread one 16-byte chunk
+// (the workgroup is C/8 threads rounded up to whole wavefronts), so every
+// access is a coalesced 1 KiB wavefront transaction and the grid streams
+// reads and writes together (see the modulate + RoPE kernel for why this
+// beats one wavefront per row).  The LayerNorm of the fused form reduces
+// within wavefronts with DPP and across them through LDS.  HBM-bound: per
+// token it reads x and o and writes y (and z); the gate and adaLN rows are
+// shared by the tokens of a sample and stay in L2.
 #include "mf_device.h"
 #include "mf_internal.h"
 
 namespace mf {
 namespace {
 
-constexpr int kTokensPerBlock = 4;
+constexpr int kMaxWaves = 16;       // C <= 8192: at most 1024 chunks per row
 
-// Up to C = 3072: five wavefronts per SIMD (<= 96 VGPRs), so that all
-// tokens of a 1024^2 pack (17 per CU) are resident at once.
-template <int NCH, bool kFusedNorm>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH <= 6 ? 5 : 1))) void
-gated_residual_kernel(GatedResArgs a) {
-    const int lane = threadIdx.x & 63;
-    // wave-uniform (readfirstlane): the buffer resources below live in SGPRs
-    const int64_t t = int64_t(blockIdx.x) * kTokensPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (t >= a.T) return;
-    const int C = a.C;
-    const int nch = C >> 3;
-    const int64_t m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
-    // Raw buffer resources over the rows: chunks past the row (C not a
-    // multiple of 512) read zeros and their stores are dropped, so no load or
-    // store sits behind a branch and all loads of the row are in flight at once.
-    const uint32_t row_bytes = uint32_t(C) * 2u;
-    const __amdgpu_buffer_rsrc_t x_rs = make_rsrc(a.x + t * C, row_bytes);
-    const __amdgpu_buffer_rsrc_t o_rs = make_rsrc(a.o + t * C, row_bytes);
-    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(a.gate + m * C, row_bytes);
-    const __amdgpu_buffer_rsrc_t y_rs = make_rsrc(a.y + t * C, row_bytes);
-
-    u32x4_t px[NCH], po[NCH], pg[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const uint32_t off = 16u * uint32_t(lane + kWave * i);
-        px[i] = bload16(x_rs, off, 0);
-        po[i] = bload16(o_rs, off, 0);
-        pg[i] = bload16(g_rs, off, 0);
-    }
-    float y[NCH][8];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        float fx[8], fo[8], fg[8];
-        unpack8(px[i], fx);
-        unpack8(po[i], fo);
-        unpack8(pg[i], fg);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) y[i][j] = fx[j] + fg[j] * fo[j];
-        bstore16(y_rs, 16u * uint32_t(lane + kWave * i), 0, pack8(y[i]));
-    }
-    if constexpr (kFusedNorm) {
-        // LayerNorm of the fp32 y (population variance), two passes; the
-        // zero-filled chunks past the row hold y = 0 and are left out of the
-        // variance.
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s += y[i][j];
-        const float invC = 1.0f / float(C);
-        const float mean = wave_sum(s) * invC;
-        float v = 0.f;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const bool in = lane + kWave * i < nch;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float d = y[i][j] - mean;
-                v += in ? d * d : 0.f;
-            }
-        }
-        const float rstd = rsqrtf(wave_sum(v) * invC + a.eps);
-        const __amdgpu_buffer_rsrc_t sh_rs = make_rsrc(a.shift2 + m * C, row_bytes);
-        const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(a.scale2 + m * C, row_bytes);
-        const __amdgpu_buffer_rsrc_t z_rs = make_rsrc(a.z + t * C, row_bytes);
-        // adaLN chunks loaded one chunk ahead of the stores (a load written
-        // after a store would wait for it)
-        u32x4_t nsh = bload16(sh_rs, 16u * uint32_t(lane), 0), nsc = bload16(sc_rs, 16u * uint32_t(lane), 0);
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const uint32_t off = 16u * uint32_t(lane + kWave * i);
-            float fs[8], fc[8], r[8];
-            unpack8(nsh, fs);
-            unpack8(nsc, fc);
-            if (i + 1 < NCH) {
-                nsh = bload16(sh_rs, off + 16u * kWave, 0);
-                nsc = bload16(sc_rs, off + 16u * kWave, 0);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) r[j] = (y[i][j] - mean) * rstd * (1.0f + fc[j]) + fs[j];
-            bstore16(z_rs, off, 0, pack8(r));
-        }
-    }
+// Sum of v over the workgroup, in every thread (red: one float per wavefront
+// of LDS, free again when this returns).
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float s = 0.f;
+    for (int i = 0; i < nw; ++i) s += red[i];
+    __syncthreads();
+    return s;
 }
 
-template <int NCH>
-hipError_t launch_nch(const GatedResArgs& a, hipStream_t stream) {
-    const int64_t blocks = (a.T + kTokensPerBlock - 1) / kTokensPerBlock;
-    if (a.z != nullptr)
-        hipLaunchKernelGGL((gated_residual_kernel<NCH, true>), dim3(unsigned(blocks)), dim3(256), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((gated_residual_kernel<NCH, false>), dim3(unsigned(blocks)), dim3(256), 0,
-                           stream, a);
-    return hipGetLastError();
+template <bool kFusedNorm>
+__global__ __launch_bounds__(1024) void gated_residual_kernel(GatedResArgs a) {
+    __shared__ float red[kMaxWaves];
+    const int64_t t = blockIdx.x;
+    const int c = threadIdx.x;                // this thread's chunk of the row
+    const int C = a.C;
+    const bool in = c < (C >> 3);
+    const int64_t m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
+    // Raw buffer resources over the rows: a chunk past the row reads zeros
+    // and its store is dropped, so no load or store sits behind a branch.
+    const uint32_t row_bytes = uint32_t(C) * 2u;
+    const uint32_t off = 16u * uint32_t(c);
+    const u32x4_t px = bload16(make_rsrc(a.x + t * C, row_bytes), off, 0);
+    const u32x4_t po = bload16(make_rsrc(a.o + t * C, row_bytes), off, 0);
+    const u32x4_t pg = bload16(make_rsrc(a.gate + m * C, row_bytes), off, 0);
+    u32x4_t psh = {0u, 0u, 0u, 0u}, psc = {0u, 0u, 0u, 0u};
+    if constexpr (kFusedNorm) {
+        psh = bload16(make_rsrc(a.shift2 + m * C, row_bytes), off, 0);
+        psc = bload16(make_rsrc(a.scale2 + m * C, row_bytes), off, 0);
+    }
+    float y[8];
+    {
+        float fx[8], fo[8], fg[8];
+        unpack8(px, fx);
+        unpack8(po, fo);
+        unpack8(pg, fg);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = fx[j] + fg[j] * fo[j];
+    }
+    bstore16(make_rsrc(a.y + t * C, row_bytes), off, 0, pack8(y));
+    if constexpr (kFusedNorm) {
+        // LayerNorm of the fp32 y (population variance), two passes; chunks
+        // past the row hold y = 0 and are left out of the variance.
+        const float invC = 1.0f / float(C);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += y[j];
+        const float mean = block_sum(s, red) * invC;
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v += (y[j] - mean) * (y[j] - mean);
+        const float rstd = rsqrtf(block_sum(in ? v : 0.f, red) * invC + a.eps);
+        float fs[8], fc[8], r[8];
+        unpack8(psh, fs);
+        unpack8(psc, fc);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = (y[j] - mean) * rstd * (1.0f + fc[j]) + fs[j];
+        bstore16(make_rsrc(a.z + t * C, row_bytes), off, 0, pack8(r));
+    }
 }
 
 }  // namespace
 
 hipError_t launch_gated_residual(const GatedResArgs& a, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
     const int nch = a.C / 8;
-    const int per_lane = (nch + kWave - 1) / kWave;
-    if (per_lane <= 1) return launch_nch<1>(a, stream);
-    if (per_lane <= 2) return launch_nch<2>(a, stream);
-    if (per_lane <= 4) return launch_nch<4>(a, stream);
-    if (per_lane <= 6) return launch_nch<6>(a, stream);
-    if (per_lane <= 8) return launch_nch<8>(a, stream);
-    if (per_lane <= 12) return launch_nch<12>(a, stream);
-    return launch_nch<16>(a, stream);
+    const int threads = (nch + kWave - 1) / kWave * kWave;   // <= 1024 for C <= 8192
+    if (threads > kWave * kMaxWaves) return hipErrorInvalidConfiguration;
+    if (a.z != nullptr)
+        hipLaunchKernelGGL((gated_residual_kernel<true>), dim3(unsigned(a.T)), dim3(threads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gated_residual_kernel<false>), dim3(unsigned(a.T)), dim3(threads), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace mf
