@@ -216,8 +216,9 @@ __global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs 
             continue;
         }
         const int m = a.mod_row[t];
+        const bool mok = m >= 0 && m < a.n_rows;      // a row outside the table reads zeros, adds nothing
         if (m != cur) {
-            if (cur >= 0 && live) rows_to_output<2>(part, outs, cur, C, c0);
+            if (cur >= 0 && cur < a.n_rows && live) rows_to_output<2>(part, outs, cur, C, c0);
             cur = m;
         }
         float x[2][8];
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs 
         buf ^= 1;
         const float rs[2] = {rsqrtf(vr[0] * invC + a.eps), rsqrtf(vr[1] * invC + a.eps)};
         float sc[8];
-        unpack8(live ? ld16(a.scale + int64_t(m) * C + c0) : u32x4_t{}, sc);
+        unpack8(live && mok ? ld16(a.scale + int64_t(m) * C + c0) : u32x4_t{}, sc);
         float xh[2][8], gx[2][8];
         float ab[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs 
                                                slot_tags_bytes(n_slots_for(a.T))) +
                       int64_t(blockIdx.x) * 2 * C;
         if (live) rows_to_slot<2>(part, slot, C, c0);
-        if (threadIdx.x == 0) tags[blockIdx.x] = cur;
+        if (threadIdx.x == 0) tags[blockIdx.x] = cur < a.n_rows ? cur : -1;   // -1: nothing to add
     }
 }
 
@@ -322,8 +323,9 @@ __global__ __launch_bounds__(1024) void gated_residual_bwd_kernel(GatedResBwdArg
         for (int i = 0; i < 4; ++i) row[i] = nxt[i];
         if (t + 1 < t_end) load(t + 1, nxt);
         const int m = a.mod_row[t];
+        const bool mok = m >= 0 && m < a.n_rows;      // a row outside the table reads zeros, adds nothing
         if (m != cur) {
-            if (cur >= 0 && live) {
+            if (cur >= 0 && cur < a.n_rows && live) {
                 if (fused)
                     rows_to_output<3>(part, outs, cur, C, c0);
                 else
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(1024) void gated_residual_bwd_kernel(GatedResBwdArg
         float xv[8], ov[8], gv[8], dy[8], dz[8];
         unpack8(row[0], xv);
         unpack8(row[1], ov);
-        unpack8(live ? ld16(a.gate + int64_t(m) * C + c0) : u32x4_t{}, gv);
+        unpack8(live && mok ? ld16(a.gate + int64_t(m) * C + c0) : u32x4_t{}, gv);
         unpack8(has_dy ? row[2] : u32x4_t{}, dy);
         unpack8(fused ? row[3] : u32x4_t{}, dz);
         float y[8], dyt[8];
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(1024) void gated_residual_bwd_kernel(GatedResBwdArg
             buf ^= 1;
             const float rs = rsqrtf(v[0] * invC + a.eps);
             float s2[8];
-            unpack8(live ? ld16(a.scale2 + int64_t(m) * C + c0) : u32x4_t{}, s2);
+            unpack8(live && mok ? ld16(a.scale2 + int64_t(m) * C + c0) : u32x4_t{}, s2);
             float yh[8], gy[8];
             float ab[2] = {0.f, 0.f};
 #pragma unroll
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(1024) void gated_residual_bwd_kernel(GatedResBwdArg
         else
             rows_to_slot<1>(reinterpret_cast<float(&)[1][8]>(part), slot, C, c0);
     }
-    if (threadIdx.x == 0) tags[blockIdx.x] = cur;
+    if (threadIdx.x == 0) tags[blockIdx.x] = cur < a.n_rows ? cur : -1;   // -1: nothing to add
 }
 
 int block_threads(int C) { return ((C / 8 + 63) / 64) * 64; }
