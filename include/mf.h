@@ -59,7 +59,7 @@ enum {
     MF_ERR_HIP = -7          /* the HIP runtime reported an error              */
 };
 
-#define MF_ABI_VERSION 1
+#define MF_ABI_VERSION 2
 
 /* Human-readable name of a status code; static storage, never NULL. */
 const char* mf_status_string(mf_status s);
@@ -121,8 +121,12 @@ mf_status mf_pack_tables(const mf_sample_desc* descs, int32_t n, int32_t* cu_seq
  * q_in, k_in, q_out, k_out: bf16 [T][H][D] with token strides ld_in / ld_out
  *   (elements, >= H*D, multiple of 8).  q_out may equal q_in and k_out may
  *   equal k_in (in place); other overlaps are undefined.
- * shift, scale: bf16 [n_rows][H*D], both NULL (RoPE only) or both set.
- * mod_row: int32 [T]; required when shift/scale are set, ignored otherwise.
+ * shift, scale: bf16 [n_rows][H*D], both NULL (RoPE only) or both set;
+ *   when set, n_rows >= 1 (>= 0 when T = 0) and n_rows*H*D <= 2^31.
+ * mod_row: int32 [T], every entry in [0, n_rows); required when shift/scale
+ *   are set, ignored otherwise (n_rows too).  An entry outside [0, n_rows)
+ *   reads no table memory: that token is modulated with zero shift and
+ *   scale (MF_ERR_TABLE under MF_DEBUG).
  * pos: int32 [T][3] (frame, row, col).
  * rope_f + rope_r + rope_c == D, each a multiple of 8.  D in {64, 128},
  * H*D <= 8192.
@@ -133,8 +137,8 @@ mf_status mf_modulate_rope(void* stream,
                            const void* q_in, const void* k_in, void* q_out, void* k_out,
                            int64_t T, int32_t H, int32_t D, int64_t ld_in, int64_t ld_out,
                            const void* shift, const void* scale, const int32_t* mod_row,
-                           const int32_t* pos, int32_t rope_f, int32_t rope_r, int32_t rope_c,
-                           float rope_base, float eps);
+                           int32_t n_rows, const int32_t* pos, int32_t rope_f, int32_t rope_r,
+                           int32_t rope_c, float rope_base, float eps);
 
 /* ------------------------------------------------------------------------
  * Block-diagonal (varlen) joint softmax attention forward.
@@ -326,14 +330,18 @@ mf_status mf_gated_residual_bwd(void* stream,
  *   z[t] = LN(y[t]) * (1 + scale2[m(t)]) + shift2[m(t)]    (from fp32 y)
  * x, o, y, z: bf16 [T][C], contiguous rows (o is the attention output viewed
  *   as [T][H*D]).  y may equal x (in place); z must not overlap x, o or y.
- * gate, shift2, scale2: bf16 [n_rows][C]; mod_row: int32 [T].
+ * gate, shift2, scale2: bf16 [n_rows][C], n_rows >= 1 (>= 0 when T = 0),
+ *   n_rows*C <= 2^31.
+ * mod_row: int32 [T], every entry in [0, n_rows).  An entry outside reads no
+ *   table memory: that token takes zero gate, shift2 and scale2
+ *   (MF_ERR_TABLE under MF_DEBUG).
  * shift2, scale2 and z are all NULL (no fused adaLN) or all set.
  * C a multiple of 64 and at most 8192; eps > 0 when z is produced.
  * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_TABLE (MF_DEBUG
  * only), MF_ERR_HIP. */
 mf_status mf_gated_residual(void* stream,
                             const void* x, const void* o, void* y,
-                            const void* gate, const int32_t* mod_row,
+                            const void* gate, const int32_t* mod_row, int32_t n_rows,
                             const void* shift2, const void* scale2, void* z,
                             int64_t T, int32_t C, float eps);
 
@@ -357,9 +365,11 @@ mf_status mf_gated_residual(void* stream,
  * w_qkv: bf16 [3C][C] contiguous (output x input, no bias).
  * qkv: bf16 [T][3C] output (q', k', v side by side), token stride
  *   ld_qkv >= 3C, a multiple of 8; must not overlap x or w_qkv.
- * shift, scale: bf16 [n_rows][C], both NULL (no modulation: u = x) or both
- *   set with mod_row int32 [T]; pos: int32 [T][3]; rope dims as for
- *   mf_modulate_rope; eps > 0 when modulating.
+ * shift, scale: bf16 [n_rows][C], both NULL (no modulation: u = x; mod_row
+ *   and n_rows ignored) or both set with mod_row int32 [T] and n_rows as for
+ *   mf_modulate_rope (a row outside [0, n_rows) modulates with zeros);
+ *   pos: int32 [T][3]; rope dims as for mf_modulate_rope; eps > 0 when
+ *   modulating.
  * workspace: device memory of at least mf_block_qkv_workspace_bytes(T, H,
  *   D) bytes, 256-byte aligned: the modulated rows, then fp32 partial tiles
  *   of the split last round (when the last round of 256 x 256 output tiles
@@ -376,7 +386,7 @@ mf_status mf_block_qkv(void* stream,
                        const void* x, int64_t ld_x, const void* w_qkv,
                        void* qkv, int64_t ld_qkv,
                        const void* shift, const void* scale, const int32_t* mod_row,
-                       const int32_t* pos, int64_t T, int32_t H, int32_t D,
+                       int32_t n_rows, const int32_t* pos, int64_t T, int32_t H, int32_t D,
                        int32_t rope_f, int32_t rope_r, int32_t rope_c,
                        float rope_base, float eps, void* workspace, size_t workspace_bytes);
 
@@ -385,14 +395,17 @@ mf_status mf_block_qkv(void* stream,
  * o: bf16 [T][C] (the attention output viewed as [T][H*D]), token stride
  *   ld_o >= C, a multiple of 8.  w_o: bf16 [C][C] contiguous (output x
  *   input, no bias).  x, y: bf16 [T][C] contiguous; y must not overlap o,
- *   w_o or x.  gate: bf16 [n_rows][C]; mod_row: int32 [T].
+ *   w_o or x.  gate: bf16 [n_rows][C], n_rows >= 1 (>= 0 when T = 0),
+ *   n_rows*C <= 2^31;
+ *   mod_row: int32 [T], entries in [0, n_rows) (a row outside gates with
+ *   zeros, so y = x there; MF_ERR_TABLE under MF_DEBUG).
  * Limits: C a multiple of 64, at most 8192; T * ld_o * 2 below 2^32.
  * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
  * MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
 mf_status mf_block_out(void* stream,
                        const void* o, int64_t ld_o, const void* w_o,
                        const void* x, const void* gate, const int32_t* mod_row,
-                       void* y, int64_t T, int32_t C);
+                       int32_t n_rows, void* y, int64_t T, int32_t C);
 
 /* ------------------------------------------------------------------------
  * Packed classifier-free guidance + Euler sampler step after the last block.

@@ -56,11 +56,17 @@ bool fetch(const int32_t* dev, size_t n, std::vector<int32_t>& out, hipStream_t 
     return hipMemcpy(out.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost) == hipSuccess;
 }
 
-mf_status check_rows(const int32_t* mod_row, int64_t T, hipStream_t stream) {
+// An adaLN table read by a forward call: at least one row when there are
+// tokens, and every element offset below 2^31.
+bool rows_ok(int32_t n_rows, int64_t T, int64_t C) {
+    return n_rows >= (T > 0 ? 1 : 0) && int64_t(n_rows) * C <= (int64_t(1) << 31);
+}
+
+mf_status check_rows(const int32_t* mod_row, int64_t T, int32_t n_rows, hipStream_t stream) {
     std::vector<int32_t> h;
     if (!fetch(mod_row, size_t(T), h, stream)) return MF_ERR_HIP;
     for (int32_t m : h)
-        if (m < 0) return MF_ERR_TABLE;
+        if (m < 0 || m >= n_rows) return MF_ERR_TABLE;
     return MF_OK;
 }
 
@@ -92,7 +98,7 @@ int32_t mf_abi_version(void) { return MF_ABI_VERSION; }
 
 mf_status mf_modulate_rope(void* stream, const void* q_in, const void* k_in, void* q_out, void* k_out,
                            int64_t T, int32_t H, int32_t D, int64_t ld_in, int64_t ld_out,
-                           const void* shift, const void* scale, const int32_t* mod_row,
+                           const void* shift, const void* scale, const int32_t* mod_row, int32_t n_rows,
                            const int32_t* pos, int32_t rope_f, int32_t rope_r, int32_t rope_c,
                            float rope_base, float eps) {
     if (T < 0 || T > INT32_MAX || H <= 0) return MF_ERR_SHAPE;
@@ -107,6 +113,7 @@ mf_status mf_modulate_rope(void* stream, const void* q_in, const void* k_in, voi
     if ((shift == nullptr) != (scale == nullptr)) return MF_ERR_NULL;
     const bool modulate = shift != nullptr;
     if (modulate && !(eps > 0.f)) return MF_ERR_SHAPE;
+    if (modulate && !rows_ok(n_rows, T, int64_t(H) * D)) return MF_ERR_SHAPE;
     if (T == 0) return MF_OK;
     if (!q_in || !k_in || !q_out || !k_out || !pos) return MF_ERR_NULL;
     if (modulate && !mod_row) return MF_ERR_NULL;
@@ -124,7 +131,7 @@ mf_status mf_modulate_rope(void* stream, const void* q_in, const void* k_in, voi
         for (int32_t v : hp)
             if (v < 0) return MF_ERR_TABLE;
         if (modulate) {
-            mf_status st = check_rows(mod_row, T, s);
+            mf_status st = check_rows(mod_row, T, n_rows, s);
             if (st != MF_OK) return st;
         }
     }
@@ -136,7 +143,7 @@ mf_status mf_modulate_rope(void* stream, const void* q_in, const void* k_in, voi
     a.T = T; a.H = H; a.D = D; a.ld_in = ld_in; a.ld_out = ld_out;
     a.shift = static_cast<const uint16_t*>(shift);
     a.scale = static_cast<const uint16_t*>(scale);
-    a.mod_row = mod_row; a.pos = pos;
+    a.mod_row = mod_row; a.n_rows = modulate ? n_rows : 0; a.pos = pos;
     a.rope_f = rope_f; a.rope_r = rope_r; a.rope_c = rope_c;
     a.rope_base = rope_base; a.eps = eps;
     return finish(mf::launch_modulate_rope(a, s), s);
@@ -307,9 +314,10 @@ mf_status mf_varlen_attn_bwd(void* stream, const void* q, const void* k, const v
 }
 
 mf_status mf_gated_residual(void* stream, const void* x, const void* o, void* y, const void* gate,
-                            const int32_t* mod_row, const void* shift2, const void* scale2, void* z,
-                            int64_t T, int32_t C, float eps) {
+                            const int32_t* mod_row, int32_t n_rows, const void* shift2, const void* scale2,
+                            void* z, int64_t T, int32_t C, float eps) {
     if (T < 0 || T > INT32_MAX || C <= 0 || C % 64 || C > 8192) return MF_ERR_SHAPE;
+    if (!rows_ok(n_rows, T, C)) return MF_ERR_SHAPE;
     const int n_fused = (shift2 != nullptr) + (scale2 != nullptr) + (z != nullptr);
     if (n_fused != 0 && n_fused != 3) return MF_ERR_NULL;
     if (n_fused == 3 && !(eps > 0.f)) return MF_ERR_SHAPE;
@@ -322,7 +330,7 @@ mf_status mf_gated_residual(void* stream, const void* x, const void* o, void* y,
         return MF_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (debug_mode()) {
-        mf_status st = check_rows(mod_row, T, s);
+        mf_status st = check_rows(mod_row, T, n_rows, s);
         if (st != MF_OK) return st;
     }
     mf::GatedResArgs a;
@@ -331,6 +339,7 @@ mf_status mf_gated_residual(void* stream, const void* x, const void* o, void* y,
     a.y = static_cast<uint16_t*>(y);
     a.gate = static_cast<const uint16_t*>(gate);
     a.mod_row = mod_row;
+    a.n_rows = n_rows;
     a.shift2 = static_cast<const uint16_t*>(shift2);
     a.scale2 = static_cast<const uint16_t*>(scale2);
     a.z = static_cast<uint16_t*>(z);
@@ -468,7 +477,7 @@ size_t mf_block_qkv_workspace_bytes(int64_t T, int32_t H, int32_t D) {
 
 mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_qkv, void* qkv,
                        int64_t ld_qkv, const void* shift, const void* scale, const int32_t* mod_row,
-                       const int32_t* pos, int64_t T, int32_t H, int32_t D, int32_t rope_f, int32_t rope_r,
+                       int32_t n_rows, const int32_t* pos, int64_t T, int32_t H, int32_t D, int32_t rope_f, int32_t rope_r,
                        int32_t rope_c, float rope_base, float eps, void* workspace, size_t workspace_bytes) {
     if (T < 0 || T > INT32_MAX || H <= 0) return MF_ERR_SHAPE;
     if (D != 64 && D != 128) return MF_ERR_UNSUPPORTED;
@@ -485,6 +494,7 @@ mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_
     if ((shift == nullptr) != (scale == nullptr)) return MF_ERR_NULL;
     const bool modulate = shift != nullptr;
     if (modulate && !(eps > 0.f)) return MF_ERR_SHAPE;
+    if (modulate && !rows_ok(n_rows, T, C)) return MF_ERR_SHAPE;
     if (T == 0) return MF_OK;
     if (!x || !w_qkv || !qkv || !pos) return MF_ERR_NULL;
     if (modulate && !mod_row) return MF_ERR_NULL;
@@ -501,7 +511,7 @@ mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_
         for (int32_t v : hp)
             if (v < 0) return MF_ERR_TABLE;
         if (modulate) {
-            mf_status st = check_rows(mod_row, T, s);
+            mf_status st = check_rows(mod_row, T, n_rows, s);
             if (st != MF_OK) return st;
         }
     }
@@ -513,7 +523,7 @@ mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_
     a.ld_qkv = ld_qkv;
     a.shift = static_cast<const uint16_t*>(shift);
     a.scale = static_cast<const uint16_t*>(scale);
-    a.mod_row = mod_row; a.pos = pos;
+    a.mod_row = mod_row; a.n_rows = modulate ? n_rows : 0; a.pos = pos;
     a.T = T; a.H = H; a.D = D;
     a.rope_f = rope_f; a.rope_r = rope_r; a.rope_c = rope_c;
     a.rope_base = rope_base; a.eps = eps;
@@ -522,8 +532,9 @@ mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_
 }
 
 mf_status mf_block_out(void* stream, const void* o, int64_t ld_o, const void* w_o, const void* x,
-                       const void* gate, const int32_t* mod_row, void* y, int64_t T, int32_t C) {
+                       const void* gate, const int32_t* mod_row, int32_t n_rows, void* y, int64_t T, int32_t C) {
     if (T < 0 || T > INT32_MAX || C <= 0 || C % 64 || C > 8192) return MF_ERR_SHAPE;
+    if (!rows_ok(n_rows, T, C)) return MF_ERR_SHAPE;
     if (ld_o < C) return MF_ERR_SHAPE;
     if (ld_o > kMaxStride) return MF_ERR_UNSUPPORTED;
     if (T * ld_o * 2 >= (int64_t(1) << 32)) return MF_ERR_UNSUPPORTED;
@@ -535,7 +546,7 @@ mf_status mf_block_out(void* stream, const void* o, int64_t ld_o, const void* w_
         return MF_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (debug_mode()) {
-        mf_status st = check_rows(mod_row, T, s);
+        mf_status st = check_rows(mod_row, T, n_rows, s);
         if (st != MF_OK) return st;
     }
     mf::BlockOutArgs a;
@@ -545,6 +556,7 @@ mf_status mf_block_out(void* stream, const void* o, int64_t ld_o, const void* w_
     a.x = static_cast<const uint16_t*>(x);
     a.gate = static_cast<const uint16_t*>(gate);
     a.mod_row = mod_row;
+    a.n_rows = n_rows;
     a.y = static_cast<uint16_t*>(y);
     a.T = T; a.C = C;
     return finish(mf::launch_block_out(a, s), s);

@@ -99,6 +99,7 @@ struct GemmParams {
     const uint16_t* resid;
     const uint16_t* gate;
     const int32_t* mod_row;
+    int n_rows;              // a row outside [0, n_rows) gates with zeros
     int tiles_t, tiles_f;
     // split tail: tiles [n_full, tiles) run as `split` K-ranges each, fp32
     // partial tiles in `partial` (kTileAcc floats per piece)
@@ -158,7 +159,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&ac
         const int tl = 128 * wt + 32 * tb + l32;   // token row inside the tile
         const int64_t t = t0 + tl;
         int64_t m = 0;
-        if constexpr (MODE == kModeOut) m = t < p.T ? p.mod_row[t] : 0;
+        if constexpr (MODE == kModeOut) m = t < p.T ? p.mod_row[t] : -1;
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb) {
             const int fl = 64 * wf + 32 * fb;      // first feature of the block inside the tile
@@ -190,7 +191,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&ac
                     if (t < p.T && f0 + f < p.N) {
                         const int64_t n0 = f0 + f;
                         const u32x2_t xr = *reinterpret_cast<const u32x2_t*>(p.resid + t * int64_t(p.N) + n0);
-                        const u32x2_t gr = *reinterpret_cast<const u32x2_t*>(p.gate + m * int64_t(p.N) + n0);
+                        const u32x2_t gr = m >= 0 && m < p.n_rows
+                                               ? *reinterpret_cast<const u32x2_t*>(p.gate + m * int64_t(p.N) + n0)
+                                               : u32x2_t{0u, 0u};
                         v0 = bf_lo(xr[0]) + bf_lo(gr[0]) * v0;
                         v1 = bf_hi(xr[0]) + bf_hi(gr[0]) * v1;
                         v2 = bf_lo(xr[1]) + bf_lo(gr[1]) * v2;
@@ -402,7 +405,7 @@ template <int NCH>
 __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                     const uint16_t* __restrict__ shift,
                                                     const uint16_t* __restrict__ scale,
-                                                    const int32_t* __restrict__ mod_row,
+                                                    const int32_t* __restrict__ mod_row, int n_rows,
                                                     uint16_t* __restrict__ u, int64_t T, int C, float eps) {
     const int lane = threadIdx.x & 63;
     const int64_t t = int64_t(blockIdx.x) * kLnTokensPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -431,9 +434,11 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__
         }
     }
     const float rstd = rsqrtf(wave_sum(v) * invC + eps);
+    // a row outside [0, n_rows) gets empty resources: its loads read zeros
     const int64_t m = __builtin_amdgcn_readfirstlane(mod_row[t]);
-    const __amdgpu_buffer_rsrc_t sh_rs = make_rsrc(shift + m * C, row_bytes);
-    const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(scale + m * C, row_bytes);
+    const bool mok = m >= 0 && m < n_rows;
+    const __amdgpu_buffer_rsrc_t sh_rs = make_rsrc(shift + (mok ? m : 0) * C, mok ? row_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(scale + (mok ? m : 0) * C, mok ? row_bytes : 0u);
     const __amdgpu_buffer_rsrc_t u_rs = make_rsrc(u + t * C, row_bytes);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -452,7 +457,7 @@ template <int NCH>
 hipError_t launch_adaln_nch(const BlockQkvArgs& a, uint16_t* u, hipStream_t stream) {
     const int64_t blocks = (a.T + kLnTokensPerBlock - 1) / kLnTokensPerBlock;
     hipLaunchKernelGGL(adaln_kernel<NCH>, dim3(unsigned(blocks)), dim3(256), 0, stream, a.x, a.ld_x, a.shift,
-                       a.scale, a.mod_row, u, a.T, a.H * a.D, a.eps);
+                       a.scale, a.mod_row, a.n_rows, u, a.T, a.H * a.D, a.eps);
     return hipGetLastError();
 }
 
@@ -580,6 +585,7 @@ hipError_t launch_block_out(const BlockOutArgs& a, hipStream_t stream) {
     p.resid = a.x;
     p.gate = a.gate;
     p.mod_row = a.mod_row;
+    p.n_rows = a.n_rows;
     return launch_gemm<kModeOut>(p, stream);
 }
 

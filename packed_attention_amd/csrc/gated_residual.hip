@@ -45,18 +45,22 @@ __global__ __launch_bounds__(1024) void gated_residual_kernel(GatedResArgs a) {
     const int c = threadIdx.x;                // this thread's chunk of the row
     const int C = a.C;
     const bool in = c < (C >> 3);
-    const int64_t m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
+    // a row outside [0, n_rows) gets empty resources: its loads read zeros
+    const int64_t m0 = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
+    const bool mok = m0 >= 0 && m0 < a.n_rows;
+    const int64_t m = mok ? m0 : 0;
     // Raw buffer resources over the rows: a chunk past the row reads zeros
     // and its store is dropped, so no load or store sits behind a branch.
     const uint32_t row_bytes = uint32_t(C) * 2u;
+    const uint32_t mrow_bytes = mok ? row_bytes : 0u;
     const uint32_t off = 16u * uint32_t(c);
     const u32x4_t px = bload16(make_rsrc(a.x + t * C, row_bytes), off, 0);
     const u32x4_t po = bload16(make_rsrc(a.o + t * C, row_bytes), off, 0);
-    const u32x4_t pg = bload16(make_rsrc(a.gate + m * C, row_bytes), off, 0);
+    const u32x4_t pg = bload16(make_rsrc(a.gate + m * C, mrow_bytes), off, 0);
     u32x4_t psh = {0u, 0u, 0u, 0u}, psc = {0u, 0u, 0u, 0u};
     if constexpr (kFusedNorm) {
-        psh = bload16(make_rsrc(a.shift2 + m * C, row_bytes), off, 0);
-        psc = bload16(make_rsrc(a.scale2 + m * C, row_bytes), off, 0);
+        psh = bload16(make_rsrc(a.shift2 + m * C, mrow_bytes), off, 0);
+        psc = bload16(make_rsrc(a.scale2 + m * C, mrow_bytes), off, 0);
     }
     float y[8];
     {

@@ -28,6 +28,7 @@ struct ModRopeArgs {
     const uint16_t* shift;   // nullptr: RoPE only
     const uint16_t* scale;
     const int32_t* mod_row;
+    int32_t n_rows;          // rows of shift/scale; a row outside [0, n_rows) reads zeros
     const int32_t* pos;
     int32_t rope_f, rope_r, rope_c;
     float rope_base, eps;
@@ -91,6 +92,7 @@ struct GatedResArgs {
     uint16_t* y;
     const uint16_t* gate;
     const int32_t* mod_row;
+    int32_t n_rows;          // rows of gate/shift2/scale2; a row outside [0, n_rows) reads zeros
     const uint16_t* shift2;  // nullptr: no fused adaLN
     const uint16_t* scale2;
     uint16_t* z;
@@ -159,6 +161,7 @@ struct BlockQkvArgs {
     const uint16_t* shift;    // nullptr: no modulation
     const uint16_t* scale;
     const int32_t* mod_row;
+    int32_t n_rows;           // rows of shift/scale; a row outside [0, n_rows) reads zeros
     const int32_t* pos;
     int64_t T;
     int32_t H, D;
@@ -177,6 +180,7 @@ struct BlockOutArgs {
     const uint16_t* x;        // [T][C] residual
     const uint16_t* gate;     // [n_rows][C]
     const int32_t* mod_row;
+    int32_t n_rows;           // a row outside [0, n_rows) reads zeros
     uint16_t* y;              // [T][C]
     int64_t T;
     int32_t C;

@@ -52,9 +52,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH <= 6 ? 
     const bool mod = a.shift != nullptr;
     u32x4_t ush[NCH], usc[NCH];
     if (mod) {
+        // a row outside [0, n_rows) gets empty resources: its loads read zeros
         const int64_t m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
-        const __amdgpu_buffer_rsrc_t sh_rs = make_rsrc(a.shift + m * C, row_bytes);
-        const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(a.scale + m * C, row_bytes);
+        const bool mok = m >= 0 && m < a.n_rows;
+        const __amdgpu_buffer_rsrc_t sh_rs = make_rsrc(a.shift + (mok ? m : 0) * C, mok ? row_bytes : 0u);
+        const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(a.scale + (mok ? m : 0) * C, mok ? row_bytes : 0u);
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             ush[i] = bload16(sh_rs, 16u * uint32_t(lane + kWave * i), 0);

@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
     L.mf_pack_count.restype = i32
     L.mf_pack_tables.argtypes = [vp, i32, vp, vp, vp, vp]
     L.mf_pack_tables.restype = i32
-    L.mf_modulate_rope.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, vp, vp, vp, vp,
+    L.mf_modulate_rope.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i64, vp, vp, vp, i32, vp,
                                    i32, i32, i32, f32, f32]
     L.mf_modulate_rope.restype = i32
     L.mf_varlen_attn_workspace_bytes.argtypes = [i32, i64, i32, i32]
@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
     L.mf_varlen_attn_fwd_noalloc.restype = i32
     L.mf_set_attn_fwd_grid.argtypes = [i32]
     L.mf_set_attn_fwd_grid.restype = i32
-    L.mf_gated_residual.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, f32]
+    L.mf_gated_residual.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, i64, i32, f32]
     L.mf_gated_residual.restype = i32
     L.mf_varlen_attn_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32]
     L.mf_varlen_attn_bwd_workspace_bytes.restype = sz
@@ -97,10 +97,10 @@ def lib() -> ctypes.CDLL:
     L.mf_gated_residual_bwd.restype = i32
     L.mf_block_qkv_workspace_bytes.argtypes = [i64, i32, i32]
     L.mf_block_qkv_workspace_bytes.restype = sz
-    L.mf_block_qkv.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
-                               f32, f32, vp, sz]
+    L.mf_block_qkv.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, vp, i32, vp, i64, i32, i32, i32, i32,
+                               i32, f32, f32, vp, sz]
     L.mf_block_qkv.restype = i32
-    L.mf_block_out.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, i32]
+    L.mf_block_out.argtypes = [vp, vp, i64, vp, vp, vp, vp, i32, vp, i64, i32]
     L.mf_block_out.restype = i32
     L.mf_cfg_pair_count.argtypes = [vp, i32, vp, vp, i32, ctypes.POINTER(i64)]
     L.mf_cfg_pair_count.restype = i32
@@ -192,6 +192,20 @@ def _check_bf16_rows(name, t, cols):
         raise ValueError(f"{name}: last dimension must be contiguous")
 
 
+def _table_rows(name, t, cols, rows=None):
+    """Row count of a contiguous bf16 [n_rows][cols] adaLN table (0 for None);
+    with rows given, the table must have that many."""
+    if t is None:
+        return 0 if rows is None else rows
+    _check_bf16_rows(name, t, cols)
+    if not t.is_contiguous() or t.numel() % cols:
+        raise ValueError(f"{name}: expected a contiguous [n_rows][{cols}] tensor")
+    n = t.numel() // cols
+    if rows is not None and n != rows:
+        raise ValueError(f"{name}: {n} rows, expected {rows}")
+    return n
+
+
 def _token_stride(t, inner):
     """Token stride (elements) of a [T][H][D] or [T][C] view whose inner dims are packed."""
     if t.dim() == 3:
@@ -215,8 +229,9 @@ def modulate_rope(q_in, k_in, q_out, k_out, pos, rope_dims, rope_base=10000.0,
     if _token_stride(k_out, H * D) != ld_out:
         raise ValueError("q_out and k_out must share a token stride")
     f, r, c = (int(x) for x in rope_dims)
+    n_rows = _table_rows("scale", scale, H * D, _table_rows("shift", shift, H * D) if shift is not None else None)
     check(lib().mf_modulate_rope(_stream(stream), _ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out),
-                                 T, H, D, ld_in, ld_out, _ptr(shift), _ptr(scale), _ptr(mod_row),
+                                 T, H, D, ld_in, ld_out, _ptr(shift), _ptr(scale), _ptr(mod_row), n_rows,
                                  _ptr(pos), f, r, c, float(rope_base), float(eps)))
 
 
@@ -292,8 +307,11 @@ def gated_residual(x, o, y, gate, mod_row, shift2=None, scale2=None, z=None, eps
         _check_bf16_rows(n, t, C)
         if not t.is_contiguous() or t.numel() != T * C:
             raise ValueError(f"{n}: expected a contiguous [T][C] tensor")
+    n_rows = _table_rows("gate", gate, C)
+    _table_rows("shift2", shift2, C, n_rows)
+    _table_rows("scale2", scale2, C, n_rows)
     check(lib().mf_gated_residual(_stream(stream), _ptr(x), _ptr(o), _ptr(y), _ptr(gate),
-                                  _ptr(mod_row), _ptr(shift2), _ptr(scale2), _ptr(z), T, C,
+                                  _ptr(mod_row), n_rows, _ptr(shift2), _ptr(scale2), _ptr(z), T, C,
                                   float(eps)))
 
 
@@ -417,8 +435,9 @@ def block_qkv(x, w_qkv, qkv, pos, H, rope_dims, rope_base=10000.0, shift=None, s
         workspace = _temp_workspace(block_qkv_workspace_bytes(T, H, D), x.device, stream)
     f, r, c = (int(v) for v in rope_dims)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    n_rows = _table_rows("scale", scale, C, _table_rows("shift", shift, C) if shift is not None else None)
     check(lib().mf_block_qkv(_stream(stream), _ptr(x), _token_stride(x, C), _ptr(w_qkv), _ptr(qkv),
-                             _token_stride(qkv, 3 * C), _ptr(shift), _ptr(scale), _ptr(mod_row), _ptr(pos),
+                             _token_stride(qkv, 3 * C), _ptr(shift), _ptr(scale), _ptr(mod_row), n_rows, _ptr(pos),
                              T, H, D, f, r, c, float(rope_base), float(eps), _ptr(workspace), nbytes))
 
 
@@ -432,8 +451,9 @@ def block_out(o, w_o, x, gate, mod_row, y, stream=None):
             raise ValueError(f"{n}: expected a contiguous tensor")
     if tuple(w_o.shape) != (C, C):
         raise ValueError("w_o: expected [C][C]")
+    n_rows = _table_rows("gate", gate, C)
     check(lib().mf_block_out(_stream(stream), _ptr(o), _token_stride(o, C), _ptr(w_o), _ptr(x), _ptr(gate),
-                             _ptr(mod_row), _ptr(y), T, C))
+                             _ptr(mod_row), n_rows, _ptr(y), T, C))
 
 
 def cfg_pair_rows(descs, cond, uncond) -> np.ndarray:

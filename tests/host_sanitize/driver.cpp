@@ -165,8 +165,8 @@ void abi() {
     const int N = 3000;
     fuzz("mf_modulate_rope", 11, N, [](Rng& r) {
         return mf_modulate_rope(nullptr, r.ptr(), r.ptr(), r.wptr(), r.wptr(), r.i64(), r.i32(), r.i32(), r.i64(),
-                                r.i64(), r.ptr(), r.ptr(), r.i32p(), r.i32p(), r.i32(), r.i32(), r.i32(), r.f(),
-                                r.f());
+                                r.i64(), r.ptr(), r.ptr(), r.i32p(), r.i32(), r.i32p(), r.i32(), r.i32(), r.i32(),
+                                r.f(), r.f());
     });
     fuzz("mf_varlen_attn_workspace_bytes", 12, N, [](Rng& r) {
         (void)mf_varlen_attn_workspace_bytes(r.i32(), r.i64(), r.i32(), r.i32());
@@ -201,17 +201,17 @@ void abi() {
                                      r.f(), r.wptr(), r.sz());
     });
     fuzz("mf_gated_residual", 19, N, [](Rng& r) {
-        return mf_gated_residual(nullptr, r.ptr(), r.ptr(), r.wptr(), r.ptr(), r.i32p(), r.ptr(), r.ptr(), r.wptr(),
-                                 r.i64(), r.i32(), r.f());
+        return mf_gated_residual(nullptr, r.ptr(), r.ptr(), r.wptr(), r.ptr(), r.i32p(), r.i32(), r.ptr(), r.ptr(),
+                                 r.wptr(), r.i64(), r.i32(), r.f());
     });
     fuzz("mf_block_qkv", 20, N, [](Rng& r) {
         return mf_block_qkv(nullptr, r.ptr(), r.i64(), r.ptr(), r.wptr(), r.i64(), r.ptr(), r.ptr(), r.i32p(),
-                            r.i32p(), r.i64(), r.i32(), r.i32(), r.i32(), r.i32(), r.i32(), r.f(), r.f(), r.wptr(),
-                            r.sz());
+                            r.i32(), r.i32p(), r.i64(), r.i32(), r.i32(), r.i32(), r.i32(), r.i32(), r.f(), r.f(),
+                            r.wptr(), r.sz());
     });
     fuzz("mf_block_out", 21, N, [](Rng& r) {
-        return mf_block_out(nullptr, r.ptr(), r.i64(), r.ptr(), r.ptr(), r.ptr(), r.i32p(), r.wptr(), r.i64(),
-                            r.i32());
+        return mf_block_out(nullptr, r.ptr(), r.i64(), r.ptr(), r.ptr(), r.ptr(), r.i32p(), r.i32(), r.wptr(),
+                            r.i64(), r.i32());
     });
     fuzz("mf_cfg_euler_step", 22, N, [](Rng& r) {
         return mf_cfg_euler_step(nullptr, r.ptr(), r.i64(), r.i32p(), static_cast<const float*>(r.ptr()), r.f32p(),
@@ -252,10 +252,10 @@ void valid_calls() {
             const int32_t H = 3;
             const int64_t ld = int64_t(H) * D;
             expect_launch("valid mf_modulate_rope",
-                          mf_modulate_rope(nullptr, b, b, b, b, T, H, D, ld, ld, b, b, ip, ip, 0, D / 2, D / 2,
+                          mf_modulate_rope(nullptr, b, b, b, b, T, H, D, ld, ld, b, b, ip, 2, ip, 0, D / 2, D / 2,
                                            10000.f, 1e-6f));
             expect_launch("valid mf_modulate_rope (RoPE only)",
-                          mf_modulate_rope(nullptr, b, b, b, b, T, H, D, ld, ld, nullptr, nullptr, nullptr, ip,
+                          mf_modulate_rope(nullptr, b, b, b, b, T, H, D, ld, ld, nullptr, nullptr, nullptr, 0, ip,
                                            D / 4, D / 4 + (D / 4) % 2, D / 2 - (D / 4) % 2, 10000.f, 1e-6f));
             expect_launch("valid mf_varlen_attn_fwd",
                           mf_varlen_attn_fwd(nullptr, b, b, b, b, fp, ip, 1, int32_t(T), T, H, D, 3 * ld, ld,
@@ -276,10 +276,11 @@ void valid_calls() {
                                                     b, size_t(1) << 40));
         }
         expect_launch("valid mf_block_qkv",
-                      mf_block_qkv(nullptr, b, 256, b, b, 768, b, b, ip, ip, T, 2, 128, 0, 64, 64, 10000.f, 1e-6f, b,
-                                   size_t(1) << 40));
+                      mf_block_qkv(nullptr, b, 256, b, b, 768, b, b, ip, 2, ip, T, 2, 128, 0, 64, 64, 10000.f, 1e-6f,
+                                   b, size_t(1) << 40));
         expect_launch("valid mf_gated_residual",
-                      mf_gated_residual(nullptr, b, b, b, b, ip, b, b, b, T, 256, 1e-6f));
+                      mf_gated_residual(nullptr, b, b, b, b, ip, 2, b, b, b, T, 256, 1e-6f));
+        expect_launch("valid mf_block_out", mf_block_out(nullptr, b, 256, b, b, b, ip, 2, b, T, 256));
     }
 }
 

@@ -32,7 +32,7 @@ def test_exports_match_header():
 
 def test_version_and_strings():
     lib = native.lib()
-    assert lib.mf_abi_version() == 1
+    assert lib.mf_abi_version() == 2
     for code in range(-7, 1):
         s = lib.mf_status_string(code).decode()
         assert s.startswith(native.STATUS_NAMES[code])
@@ -41,7 +41,8 @@ def test_version_and_strings():
 
 def modrope(**kw):
     a = dict(stream=None, q_in=P, k_in=P, q_out=P, k_out=P, T=4, H=2, D=64, ld_in=128, ld_out=128,
-             shift=None, scale=None, mod_row=None, pos=P, f=0, r=32, c=32, base=10000.0, eps=1e-6)
+             shift=None, scale=None, mod_row=None, n_rows=2, pos=P, f=0, r=32, c=32, base=10000.0,
+             eps=1e-6)
     a.update(kw)
     return native.lib().mf_modulate_rope(*a.values())
 
@@ -57,7 +58,11 @@ def test_modulate_rope_validation():
     assert modrope(base=0.0) == SHAPE
     assert modrope(ld_in=120) == SHAPE
     assert modrope(shift=P) == NULL              # shift without scale
-    assert modrope(shift=P, scale=P, mod_row=P, eps=0.0) == SHAPE
+    assert modrope(shift=P, scale=P, mod_row=P, n_rows=2, eps=0.0) == SHAPE
+    assert modrope(shift=P, scale=P, mod_row=P, n_rows=0) == SHAPE         # no rows for 4 tokens
+    assert modrope(shift=P, scale=P, mod_row=P, n_rows=-1) == SHAPE
+    assert modrope(shift=P, scale=P, mod_row=P, n_rows=(1 << 31) // 128 + 1) == SHAPE
+    assert modrope(T=0, shift=P, scale=P, mod_row=P, n_rows=0) == 0          # no tokens, no rows
     assert modrope(q_in=None) == NULL
     assert modrope(pos=None) == NULL
     assert modrope(shift=P, scale=P, mod_row=None) == NULL
@@ -191,8 +196,8 @@ def test_gated_residual_bwd_validation():
 
 
 def gres(**kw):
-    a = dict(stream=None, x=P, o=P, y=P, gate=P, mod_row=P, shift2=None, scale2=None, z=None, T=4,
-             C=256, eps=1e-6)
+    a = dict(stream=None, x=P, o=P, y=P, gate=P, mod_row=P, n_rows=2, shift2=None, scale2=None, z=None,
+             T=4, C=256, eps=1e-6)
     a.update(kw)
     return native.lib().mf_gated_residual(*a.values())
 
@@ -208,17 +213,21 @@ def test_gated_residual_validation():
     assert gres(o=PODD) == ALIGN
     assert gres(shift2=P, scale2=P, z=PODD) == ALIGN
     assert gres(T=0, x=None, o=None, y=None, gate=None, mod_row=None) == 0
+    assert gres(T=0, x=None, o=None, y=None, gate=None, mod_row=None, n_rows=0) == 0
+    assert gres(n_rows=0) == SHAPE
+    assert gres(n_rows=-2) == SHAPE
+    assert gres(n_rows=(1 << 31) // 256 + 1) == SHAPE
 
 
 def bqkv(**kw):
     a = dict(stream=None, x=P, ld_x=128, w=P, qkv=P, ld_qkv=384, shift=None, scale=None, mod_row=None,
-             pos=P, T=4, H=2, D=64, f=0, r=32, c=32, base=10000.0, eps=1e-6, ws=None, ws_bytes=0)
+             n_rows=2, pos=P, T=4, H=2, D=64, f=0, r=32, c=32, base=10000.0, eps=1e-6, ws=None, ws_bytes=0)
     a.update(kw)
     return native.lib().mf_block_qkv(*a.values())
 
 
 def bout(**kw):
-    a = dict(stream=None, o=P, ld_o=256, w=P, x=P, gate=P, mod_row=P, y=P, T=4, C=256)
+    a = dict(stream=None, o=P, ld_o=256, w=P, x=P, gate=P, mod_row=P, n_rows=2, y=P, T=4, C=256)
     a.update(kw)
     return native.lib().mf_block_out(*a.values())
 
@@ -231,6 +240,8 @@ def test_block_projection_validation():
     assert bqkv(ld_qkv=256) == SHAPE
     assert bqkv(shift=P) == NULL
     assert bqkv(shift=P, scale=P, mod_row=P, eps=0.0) == SHAPE
+    assert bqkv(shift=P, scale=P, mod_row=P, n_rows=0) == SHAPE
+    assert bqkv(shift=P, scale=P, mod_row=P, n_rows=(1 << 31) // 128 + 1) == SHAPE
     assert bqkv(x=None) == NULL
     assert bqkv(pos=None) == NULL
     assert bqkv(shift=P, scale=P, mod_row=None) == NULL
@@ -247,6 +258,8 @@ def test_block_projection_validation():
     assert bout(ld_o=260) == ALIGN
     assert bout(o=None) == NULL
     assert bout(gate=None) == NULL
+    assert bout(n_rows=0) == SHAPE
+    assert bout(n_rows=(1 << 31) // 256 + 1) == SHAPE
     assert bout(y=PODD) == ALIGN
     assert bout(T=1 << 22, C=1024, ld_o=1024) == UNSUP
     assert bout(T=0, o=None, w=None, x=None, gate=None, mod_row=None, y=None) == 0

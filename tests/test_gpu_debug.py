@@ -6,10 +6,11 @@ it set.  Each case breaks exactly one table entry of an otherwise valid call:
   * attention (forward, allocation-free forward, backward): cu_seqlens not
     starting at 0, not ending at T, decreasing, or a sequence longer than
     max_seqlen;
-  * modulate + RoPE (forward and backward): a negative position; a negative
-    adaLN row (forward) or a row >= n_rows (backward);
-  * gated residual (forward and backward): a negative row, or a row >= n_rows
-    (backward).
+  * modulate + RoPE (forward and backward): a negative position; an adaLN
+    row that is negative (forward) or >= n_rows;
+  * gated residual (forward and backward): a negative row, or a row >= n_rows;
+  * block projections (QKV with modulation, out with the gate): a negative
+    row, or a row >= n_rows.
 Every rejected call must leave its NaN-filled output untouched (nothing ran),
 and the same calls with valid tables must succeed."""
 import json
@@ -92,7 +93,8 @@ qo, ko = nan_bf(T, H, D), nan_bf(T, H, D)
 record("modrope_ok", lambda: native.modulate_rope(q, k, qo, ko, pos, dims, 10000.0, shift, scale, rows), [])
 bad_pos = pos.clone(); bad_pos[37, 2] = -1
 bad_row = rows.clone(); bad_row[80] = -1
-for name, p, r in (("pos", bad_pos, rows), ("row", pos, bad_row)):
+big_row = rows.clone(); big_row[99] = 2        # n_rows = 2
+for name, p, r in (("pos", bad_pos, rows), ("row", pos, bad_row), ("big_row", pos, big_row)):
     a, b_ = nan_bf(T, H, D), nan_bf(T, H, D)
     record("modrope_" + name, lambda: native.modulate_rope(q, k, a, b_, p, dims, 10000.0, shift, scale, r), [a, b_])
 dqo, dko = bf(T, H, D), bf(T, H, D)
@@ -100,7 +102,6 @@ dsh, dsc = nan_f(2, C), nan_f(2, C)
 a, b_ = nan_bf(T, H, D), nan_bf(T, H, D)
 record("modrope_bwd_ok", lambda: native.modulate_rope_bwd(q, k, dqo, dko, a, b_, pos, dims, 10000.0, scale, rows,
                                                           dsh, dsc), [])
-big_row = rows.clone(); big_row[99] = 2        # n_rows = 2
 for name, p, r in (("pos", bad_pos, rows), ("row", pos, big_row)):
     a, b_, s1, s2 = nan_bf(T, H, D), nan_bf(T, H, D), nan_f(2, C), nan_f(2, C)
     record("modrope_bwd_" + name, lambda: native.modulate_rope_bwd(q, k, dqo, dko, a, b_, p, dims, 10000.0, scale, r,
@@ -110,8 +111,9 @@ for name, p, r in (("pos", bad_pos, rows), ("row", pos, big_row)):
 x, og, gate = bf(T, C), bf(T, C), bf(2, C)
 y, z = nan_bf(T, C), nan_bf(T, C)
 record("gres_ok", lambda: native.gated_residual(x, og, y, gate, rows, shift, scale, z), [])
-a, b_ = nan_bf(T, C), nan_bf(T, C)
-record("gres_row", lambda: native.gated_residual(x, og, a, gate, bad_row, shift, scale, b_), [a, b_])
+for name, r in (("row", bad_row), ("big_row", big_row)):
+    a, b_ = nan_bf(T, C), nan_bf(T, C)
+    record("gres_" + name, lambda: native.gated_residual(x, og, a, gate, r, shift, scale, b_), [a, b_])
 dy, dz = bf(T, C), bf(T, C)
 dx, do = nan_bf(T, C), nan_bf(T, C)
 dg, ds2, dc2 = nan_f(2, C), nan_f(2, C), nan_f(2, C)
@@ -120,6 +122,18 @@ for name, r in (("neg_row", bad_row), ("big_row", big_row)):
     a, b_, c1, c2, c3 = nan_bf(T, C), nan_bf(T, C), nan_f(2, C), nan_f(2, C), nan_f(2, C)
     record("gres_bwd_" + name, lambda: native.gated_residual_bwd(x, og, gate, r, dy, a, b_, c1, scale, dz, c2, c3),
            [a, b_, c1, c2, c3])
+
+# ---- block projections
+w_qkv, w_o = bf(3 * C, C), bf(C, C)
+qkv = nan_bf(T, 3 * C)
+record("bqkv_ok", lambda: native.block_qkv(x, w_qkv, qkv, pos, H, dims, 10000.0, shift, scale, rows), [])
+yo = nan_bf(T, C)
+record("bout_ok", lambda: native.block_out(og, w_o, x, gate, rows, yo), [])
+for name, r in (("neg_row", bad_row), ("big_row", big_row)):
+    a = nan_bf(T, 3 * C)
+    record("bqkv_" + name, lambda: native.block_qkv(x, w_qkv, a, pos, H, dims, 10000.0, shift, scale, r), [a])
+    b_ = nan_bf(T, C)
+    record("bout_" + name, lambda: native.block_out(og, w_o, x, gate, r, b_), [b_])
 print("RESULT " + json.dumps(out), flush=True)
 '''
 
@@ -137,4 +151,4 @@ def test_debug_table_checks():
         else:
             assert v["status"] == -6, (name, v)          # MF_ERR_TABLE
             assert v["untouched"], (name, "a rejected call wrote its outputs")
-    assert len([n for n in res if not n.endswith("_ok")]) == 18
+    assert len([n for n in res if not n.endswith("_ok")]) == 24

@@ -447,3 +447,57 @@ def test_side_stream_without_workspace():
         side.synchronize()
         torch.cuda.synchronize()
         G.check_attention(G.f64(o), O_ref, "side_stream", lse.cpu().numpy().astype(np.float64), L_ref)
+
+
+def test_rows_outside_table_read_as_zero():
+    """An adaLN row outside [0, n_rows) reads no table memory and acts as a
+    row of zeros: every forward entry point gives, bit for bit, what it gives
+    with a third, all-zero table row that those tokens select."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    T, H, D = 100, 2, 64
+    C = H * D
+    bf = lambda *s: torch.randn(*s, generator=g, device="cuda").to(torch.bfloat16)
+    pos = torch.zeros((T, 3), dtype=torch.int32, device="cuda")
+    pos[:, 1] = torch.arange(T, device="cuda", dtype=torch.int32) // 10
+    pos[:, 2] = torch.arange(T, device="cuda", dtype=torch.int32) % 10
+    rows = torch.zeros(T, dtype=torch.int32, device="cuda")
+    rows[40:] = 1
+    rows[7], rows[55], rows[99] = 2, -1, 1 << 30       # outside a 2-row table
+    rows_ref = torch.where((rows < 0) | (rows >= 2), torch.full_like(rows, 2), rows)
+    zero_row = torch.zeros((1, C), dtype=torch.bfloat16, device="cuda")
+    shift, scale, gate = bf(2, C), bf(2, C), bf(2, C)
+    shift3, scale3, gate3 = (torch.cat([t, zero_row]) for t in (shift, scale, gate))
+    q, k, x, o = bf(T, H, D), bf(T, H, D), bf(T, C), bf(T, C)
+    dims = (0, 32, 32)
+
+    def same(a, b, name):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+
+    outs = [torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    native.modulate_rope(q, k, outs[0], outs[1], pos, dims, 10000.0, shift, scale, rows)
+    native.modulate_rope(q, k, outs[2], outs[3], pos, dims, 10000.0, shift3, scale3, rows_ref)
+    torch.cuda.synchronize()
+    same(outs[0], outs[2], "modulate_rope q")
+    same(outs[1], outs[3], "modulate_rope k")
+
+    y, z, y3, z3 = (torch.empty((T, C), dtype=torch.bfloat16, device="cuda") for _ in range(4))
+    native.gated_residual(x, o, y, gate, rows, shift, scale, z)
+    native.gated_residual(x, o, y3, gate3, rows_ref, shift3, scale3, z3)
+    torch.cuda.synchronize()
+    same(y, y3, "gated_residual y")
+    same(z, z3, "gated_residual z")
+    same(y[7], x[7], "gated_residual: zero gate keeps x")
+
+    w_qkv, w_o = (bf(3 * C, C) * 0.1).to(torch.bfloat16), (bf(C, C) * 0.1).to(torch.bfloat16)
+    qkv, qkv3 = (torch.empty((T, 3 * C), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    native.block_qkv(x, w_qkv, qkv, pos, H, dims, 10000.0, shift, scale, rows)
+    native.block_qkv(x, w_qkv, qkv3, pos, H, dims, 10000.0, shift3, scale3, rows_ref)
+    yo, yo3 = (torch.empty((T, C), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    native.block_out(o, w_o, x, gate, rows, yo)
+    native.block_out(o, w_o, x, gate3, rows_ref, yo3)
+    torch.cuda.synchronize()
+    same(qkv, qkv3, "block_qkv")
+    same(yo, yo3, "block_out")
+    same(yo[55], x[55], "block_out: zero gate keeps x")
