@@ -179,15 +179,16 @@ mf_status mf_varlen_attn_fwd(void* stream,
 /* Allocation-free mf_varlen_attn_fwd, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation.  Same computation, arguments and errors as
- * mf_varlen_attn_fwd without the workspace: the workspace is a 40 MiB scratch
+ * mf_varlen_attn_fwd without the workspace: the workspace is an 80 MiB scratch
  * array inside the library, one per GPU, held until the process ends (its
  * device address is looked up once per device, on the first call there; the
  * call allocates nothing).  Every call on a GPU uses that GPU's array, which
  * keeps the last call's contents: calls that overlap on one GPU (several
  * streams or host threads) race, and the caller must serialise them.  A call
- * whose workspace would exceed 40 MiB (mf_varlen_attn_workspace_bytes above
- * 41943040: D = 128 with a persistent grid above 300 workgroups, or more than
- * about 360 000 sequences) returns MF_ERR_UNSUPPORTED and enqueues nothing. */
+ * whose workspace would exceed 80 MiB (mf_varlen_attn_workspace_bytes above
+ * 83886080: D = 128 with a persistent grid above 315 workgroups, or more than
+ * about 780 000 sequences at D = 128 on 256 CUs) returns MF_ERR_UNSUPPORTED
+ * and enqueues nothing. */
 mf_status mf_varlen_attn_fwd_noalloc(void* stream,
                                      const void* q, const void* k, const void* v, void* o, float* lse,
                                      const int32_t* cu_seqlens, int32_t n_seq, int32_t max_seqlen,

@@ -121,7 +121,7 @@ size_t attn_workspace_bytes(int32_t n_seq, int64_t T, int32_t H, int32_t D);
 hipError_t launch_varlen_attn_fwd(const AttnArgs& a, hipStream_t stream);
 // Allocation-free forward: the workspace is the library's per-GPU scratch
 // array of kAttnNoAllocScratchBytes.
-constexpr size_t kAttnNoAllocScratchBytes = size_t(40) << 20;
+constexpr size_t kAttnNoAllocScratchBytes = size_t(80) << 20;
 hipError_t launch_varlen_attn_fwd_noalloc(const AttnArgs& a, hipStream_t stream);
 // Persistent grid of the attention forward: g > 0 overrides one workgroup
 // per CU (tests move the stream-K cut points with it); 0 restores it.

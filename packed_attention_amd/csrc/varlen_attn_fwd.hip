@@ -18,7 +18,7 @@
 //    the contiguous range [g*W/G, (g+1)*W/G) of the W (tile, key-step)
 //    iterations, so mixed lengths and tile counts that are not a multiple of
 //    the CU count leave no CU idle.  A tile cut by a range boundary leaves
-//    partial results (unnormalised O in bf16, reference max and sum in fp32)
+//    partial results (unnormalised O, reference max and sum, all in fp32)
 //    in the workspace; a fix-up kernel merges them with the log-sum-exp rule.
 //    The partition is fixed by (W, G), so results are deterministic.
 //    Logical workgroups map to blockIdx so that consecutive ranges (same
@@ -119,10 +119,10 @@ struct Tile {
     static constexpr int NP = 2 * EB * NB;         // PV MFMAs per step (2 chunks x EB x NB row blocks)
     static constexpr int NV_FR = 2 * EB;           // V fragments per step
     static constexpr int LDS_BYTES = (kKStages + kVStages) * TILE_BYTES;
-    // One partial-result slot of the workspace: unnormalised O (rounded to
-    // bf16, kBM x D), then the reference max (log2 units) and sum of each
-    // row in fp32.
-    static constexpr size_t SLOT_BYTES = size_t(kBM) * D * 2 + size_t(kBM) * 8;
+    // One partial-result slot of the workspace: unnormalised O (fp32, kBM x
+    // D, so a cut tile's O is rounded to bf16 once, as a whole tile's), then
+    // the reference max (log2 units) and sum of each row in fp32.
+    static constexpr size_t SLOT_BYTES = size_t(kBM) * D * 4 + size_t(kBM) * 8;
     static_assert(NI % WAVES == 0, "whole direct-load instructions per wavefront");
 };
 
@@ -868,8 +868,8 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
                 // piece of a tile shared with other workgroups: partial in slot
                 // 2g (this workgroup's first segment) or 2g+1 (its last)
                 unsigned char* slot = partials + size_t(2 * g + (first_piece ? 0 : 1)) * TL::SLOT_BYTES;
-                uint16_t* acc = reinterpret_cast<uint16_t*>(slot);
-                float* ml = reinterpret_cast<float*>(slot + size_t(kBM) * D * 2);
+                float* acc = reinterpret_cast<float*>(slot);
+                float* ml = reinterpret_cast<float*>(slot + size_t(kBM) * D * 4);
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     const int row = wave * kRows + 32 * b + l32;
@@ -877,10 +877,9 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
                     for (int m = 0; m < EB; ++m)
 #pragma unroll
                         for (int gq = 0; gq < 4; ++gq) {
-                            u32x2_t val;
-                            val[0] = pack_bf16x2(o[b][m][4 * gq], o[b][m][4 * gq + 1]);
-                            val[1] = pack_bf16x2(o[b][m][4 * gq + 2], o[b][m][4 * gq + 3]);
-                            *reinterpret_cast<u32x2_t*>(acc + row * D + 32 * m + 8 * gq + 4 * hlf) = val;
+                            const f32x4_t val = {o[b][m][4 * gq], o[b][m][4 * gq + 1], o[b][m][4 * gq + 2],
+                                                 o[b][m][4 * gq + 3]};
+                            *reinterpret_cast<f32x4_t*>(acc + row * D + 32 * m + 8 * gq + 4 * hlf) = val;
                         }
                     if (hlf == 0) {
                         ml[row] = m_run[b];
@@ -940,7 +939,7 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     const unsigned char* partials = p.ws + sched_bytes(p.n_seq);
     const int ns = n_slots;
     auto slot_at = [&](int i) { return partials + size_t(slots[i]) * TL::SLOT_BYTES; };
-    auto ml_at = [&](int i) { return reinterpret_cast<const float*>(slot_at(i) + size_t(kBM) * D * 2); };
+    auto ml_at = [&](int i) { return reinterpret_cast<const float*>(slot_at(i) + size_t(kBM) * D * 4); };
 
     // per row: the reference max M over the pieces and 1 / total weight.
     // Pieces are read two at a time with all their loads issued together
@@ -967,20 +966,20 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     }
     __syncthreads();
 
-    // weighted sum of the pieces over the tile's 16-byte chunks (8 bf16) in
+    // weighted sum of the pieces over the tile's 16-byte chunks (4 fp32) in
     // memory order (consecutive lanes read consecutive chunks), the chunks
     // of a pair of pieces loaded together
-    constexpr int kRowChunks = D / 8;
+    constexpr int kRowChunks = D / 4;
     constexpr int kChunks = kBM * kRowChunks;
     constexpr int kPer = kChunks / kFixThreads;
     static_assert(kChunks % kFixThreads == 0, "whole chunks per thread");
-    float acc[kPer][8];
+    float acc[kPer][4];
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+        for (int e = 0; e < 4; ++e) acc[j][e] = 0.f;
     for (int i = 0; i < ns; i += 2) {
-        u32x4_t raw[2][kPer];
+        f32x4_t raw[2][kPer];
         float w[2][kPer];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -991,7 +990,7 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
             for (int j = 0; j < kPer; ++j) {
                 const int cidx = tid + kFixThreads * j;
                 const int row = cidx / kRowChunks;
-                raw[k][j] = reinterpret_cast<const u32x4_t*>(sl)[cidx];
+                raw[k][j] = reinterpret_cast<const f32x4_t*>(sl)[cidx];
                 w[k][j] = has ? exp2f(ml[row] - row_m[row]) : 0.f;
             }
         }
@@ -999,12 +998,9 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
         for (int k = 0; k < 2; ++k) {
             if (i + k >= ns) break;
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                float a8[8];
-                unpack8(raw[k][j], a8);
+            for (int j = 0; j < kPer; ++j)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[j][e] += w[k][j] * a8[e];
-            }
+                for (int e = 0; e < 4; ++e) acc[j][e] += w[k][j] * raw[k][j][e];
         }
     }
 #pragma unroll
@@ -1014,9 +1010,10 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
         const int qrow = qtile * kBM + row;
         if (qrow >= L) continue;
         const float inv = row_inv[row];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] *= inv;
-        st16(p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 8 * (cidx % kRowChunks), pack8(acc[j]));
+        u32x2_t val;
+        val[0] = pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv);
+        val[1] = pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv);
+        *reinterpret_cast<u32x2_t*>(p.o + (tok0 + qrow) * p.ld_o + int64_t(head) * D + 4 * (cidx % kRowChunks)) = val;
     }
 }
 

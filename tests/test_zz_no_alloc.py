@@ -5,7 +5,7 @@ Both run the same kernels with the same schedule and persistent grid, so the
 allocation-free call must reproduce the regular call's O and LSE bit for bit.
 Two calls in a row share the library's scratch array, the second with a
 smaller input (fewer sequences, fewer heads, D = 64).  A call whose workspace
-would exceed the 40 MiB array is rejected before anything is enqueued."""
+would exceed the 80 MiB array is rejected before anything is enqueued."""
 import numpy as np
 import pytest
 
@@ -51,13 +51,13 @@ def test_noalloc_matches_workspace_entry_point():
 
 def test_noalloc_rejects_oversized_workspace():
     """A persistent grid of 400 workgroups needs 2 x 400 partial slots of
-    67.6 KB at D = 128, beyond the 40 MiB array: MF_ERR_UNSUPPORTED, and the
+    133 KB at D = 128, beyond the 80 MiB array: MF_ERR_UNSUPPORTED, and the
     output is left untouched."""
     import torch
     q, k, v, cu = _inputs([600], 2, 128, 13)
     native.set_attn_fwd_grid(400)
     try:
-        assert native.attn_workspace_bytes(1, 600, 2, 128) > 40 * (1 << 20)
+        assert native.attn_workspace_bytes(1, 600, 2, 128) > 80 * (1 << 20)
         o = torch.full_like(q, 7.0)
         with pytest.raises(native.MFError) as exc:
             native.varlen_attn_fwd_noalloc(q, k, v, o, cu, 600)
