@@ -75,6 +75,10 @@ int32_t mf_abi_version(void);
  * target or the edit source, frame 1 the edit target).  A 1024x1024 image at
  * 16x downsampling is a 64x64 grid.  mod_row_text / mod_row_image select the
  * adaLN table row used by that sample's text / image tokens.
+ * Pages: picx.dev summary of Mage-Flow, Methodology > Native-Resolution MMDiT
+ * (packing under a token budget, cumulative offsets, frame axis); gist.science
+ * "Resumo Tecnico: Mage-Flow", Metodologia > 2. NR-MMDiT (per-sample 2D
+ * positions).
  * ---------------------------------------------------------------------- */
 typedef struct mf_sample_desc {
     int32_t text_len;
@@ -106,6 +110,10 @@ mf_status mf_pack_tables(const mf_sample_desc* descs, int32_t n, int32_t* cu_seq
 
 /* ------------------------------------------------------------------------
  * Fused adaLN modulation + multi-axis rotary embedding of q and k.
+ * Pages: picx.dev summary, Methodology > Training Infrastructure (adaptive
+ * normalisation and RoPE as one fused kernel); gist.science "Resumo Tecnico",
+ * Metodologia > 2. NR-MMDiT (per-sample 2D rotary embedding); picx.dev,
+ * Methodology > Native-Resolution MMDiT (frame coordinate for editing).
  *
  * For X in {q, k} and every token t (row of C = H*D channels, c = h*D + e):
  *   if shift != NULL:  u = LN(X[t]) * (1 + scale[m(t)]) + shift[m(t)]
@@ -142,6 +150,10 @@ mf_status mf_modulate_rope(void* stream,
 
 /* ------------------------------------------------------------------------
  * Block-diagonal (varlen) joint softmax attention forward.
+ * Pages: gist.science "Resumo Tecnico", Metodologia > 2. NR-MMDiT
+ * (variable-length attention kernels over packed samples); picx.dev summary,
+ * Methodology > Native-Resolution MMDiT (joint text + image attention kept
+ * inside each sample by the cumulative offsets).
  *
  * For every packed sequence s (tokens cu_seqlens[s] .. cu_seqlens[s+1]-1)
  * and head h, with Q, K, V that sequence's L_s x D slices:
@@ -326,6 +338,9 @@ mf_status mf_gated_residual_bwd(void* stream,
 
 /* ------------------------------------------------------------------------
  * Gated residual, optionally fused with the next sub-layer's adaLN.
+ * Pages: picx.dev summary, Methodology > Training Infrastructure (fused
+ * gating / residual chains); gist.science "Resumo Tecnico", Metodologia > 3.
+ * Otimizacao de Nivel de Sistema > Kernels Fundidos.
  *
  *   y[t] = x[t] + gate[m(t)] * o[t]                        (fp32, then bf16)
  *   z[t] = LN(y[t]) * (1 + scale2[m(t)]) + shift2[m(t)]    (from fp32 y)
