@@ -82,7 +82,8 @@ def algorithmic_bytes(w):
     mod = T * (2 * 2 * C * 2) + T * 16 + (2 * n_rows * C * 2 if w.modulate else 0)
     attn = 4 * T * C * 2 + 4 * w.H * T + 4 * (w.n_seq + 1)
     gres = (T * (4 * C * 2 + 4) + 3 * n_rows * C * 2) if w.x is not None else 0
-    return dict(modulate_rope=mod, varlen_attn_fwd=attn, gated_residual=gres)
+    gres_y = (T * (3 * C * 2 + 4) + n_rows * C * 2) if w.x is not None else 0
+    return dict(modulate_rope=mod, varlen_attn_fwd=attn, gated_residual=gres, gated_residual_y=gres_y)
 
 
 def backward_bytes(w):
@@ -351,8 +352,8 @@ def main():
 
     # Per-call durations: K calls of one kind back to back between two HIP
     # events on the stream the kernels run on.
-    names = ("modulate_rope", "varlen_attn_fwd", "gated_residual")
-    fns = (runner.run_modulate_rope, runner.run_attention, runner.run_gated_residual)
+    names = ("modulate_rope", "varlen_attn_fwd", "gated_residual", "gated_residual_y")
+    fns = (runner.run_modulate_rope, runner.run_attention, runner.run_gated_residual, runner.run_gated_residual_y)
     kern_ms = {n: timed(lambda i, fn=fn: fn(sets[i % len(sets)]))[0] for n, fn in zip(names, fns)}
 
     # Backward pass of the same step (training): gated residual -> attention

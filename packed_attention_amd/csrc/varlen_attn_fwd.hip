@@ -978,29 +978,36 @@ __global__ __launch_bounds__(kFixThreads) void attn_fixup_kernel(KParams p) {
     for (int j = 0; j < kPer; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[j][e] = 0.f;
-    for (int i = 0; i < ns; i += 2) {
-        f32x4_t raw[2][kPer];
-        float w[2][kPer];
+    // a thread's chunks in rounds of kRound, so that a pair's loads (2 x
+    // kRound x 16 bytes) stay within the 128 registers of 1024 threads
+    constexpr int kRound = kPer > 4 ? 4 : kPer;
+    static_assert(kPer % kRound == 0, "whole rounds of chunks");
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const bool has = i + k < ns;
-            const unsigned char* sl = slot_at(has ? i + k : i);
-            const float* ml = ml_at(has ? i + k : i);
+    for (int j0 = 0; j0 < kPer; j0 += kRound) {
+        for (int i = 0; i < ns; i += 2) {
+            f32x4_t raw[2][kRound];
+            float w[2][kRound];
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                const int cidx = tid + kFixThreads * j;
-                const int row = cidx / kRowChunks;
-                raw[k][j] = reinterpret_cast<const f32x4_t*>(sl)[cidx];
-                w[k][j] = has ? exp2f(ml[row] - row_m[row]) : 0.f;
+            for (int k = 0; k < 2; ++k) {
+                const bool has = i + k < ns;
+                const unsigned char* sl = slot_at(has ? i + k : i);
+                const float* ml = ml_at(has ? i + k : i);
+#pragma unroll
+                for (int j = 0; j < kRound; ++j) {
+                    const int cidx = tid + kFixThreads * (j0 + j);
+                    const int row = cidx / kRowChunks;
+                    raw[k][j] = reinterpret_cast<const f32x4_t*>(sl)[cidx];
+                    w[k][j] = has ? exp2f(ml[row] - row_m[row]) : 0.f;
+                }
             }
-        }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (i + k >= ns) break;
+            for (int k = 0; k < 2; ++k) {
+                if (i + k >= ns) break;
 #pragma unroll
-            for (int j = 0; j < kPer; ++j)
+                for (int j = 0; j < kRound; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[j][e] += w[k][j] * raw[k][j][e];
+                    for (int e = 0; e < 4; ++e) acc[j0 + j][e] += w[k][j] * raw[k][j][e];
+            }
         }
     }
 #pragma unroll
