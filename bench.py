@@ -21,7 +21,8 @@ cover their submission), divided by K.  Prints one JSON line:
               committed FETCH_SIZE/WRITE_SIZE summary when it matches the
               kernel source;
   kernels     per-call durations, algorithmic bytes and GB/s against the HBM
-              peak (the two elementwise kernels are HBM-bound);
+              peak (the elementwise kernels are HBM-bound; the gated
+              residual with the fused next adaLN and with y alone);
   backward    the training backward of the same step (gated residual ->
               attention -> modulate+RoPE), per-call durations; attention at
               2.5x the forward's flops (five products), the elementwise
