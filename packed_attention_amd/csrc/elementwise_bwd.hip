@@ -286,6 +286,213 @@ __global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs 
 }
 
 // ---------------------------------------------------------------------------
+// modulate + RoPE backward in two kernels (C <= 3072)
+// ---------------------------------------------------------------------------
+// Kernel A, the per-token outputs, with the forward kernel's mapping: one
+// wavefront per row (q or k) of a token, two tokens per workgroup; lane l
+// owns the 16-byte chunks l, l+64, ... (all at in-head offset 8l mod D, so
+// its four rotation angles serve every chunk); the row statistics are
+// reductions inside the wavefront.  It writes dq, dk and each row's mean and
+// 1/sigma (fp32).  Kernel B, the per-row sums: lane = one 8-channel chunk of
+// a run of kSumRun tokens; it reads the rows again, turns dq', dk' back and
+// normalises q, k with kernel A's statistics, and writes one tagged slot
+// per run (a row change inside a run adds the finished sums with atomics, as
+// above); slot_reduce_kernel then adds the slots.  Reading the four rows
+// twice costs less than keeping 2 x 8 fp32 sums per chunk in every
+// wavefront, which does not fit two wavefronts per SIMD at C = 3072.
+constexpr int kRowsTokens = 2;    // tokens per kernel-A workgroup
+constexpr int kSumRun = 8;        // tokens per kernel-B slot
+__host__ __device__ constexpr int64_t sum_slots_for(int64_t T) { return (T + kSumRun - 1) / kSumRun; }
+
+template <int NCH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH >= 6 ? 3 : 4))) void modrope_bwd_dx_kernel(
+    ModRopeBwdArgs a, float* __restrict__ stats) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t = int64_t(blockIdx.x) * kRowsTokens + (wave >> 1);
+    const bool is_k = (wave & 1) != 0;
+    if (t >= a.T) return;
+    const int C = a.H * a.D;
+    const int nch = C >> 3;
+    const uint32_t row_bytes = uint32_t(C) * 2u;
+    const bool mod = a.scale != nullptr;
+    auto off = [&](int i) { return 16u * uint32_t(lane + kWave * i); };
+    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc((is_k ? a.dk_out : a.dq_out) + t * a.ld_gout, row_bytes);
+    u32x4_t pg[NCH], px[NCH], usc[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) pg[i] = bload16(g_rs, off(i), 0);
+    if (mod) {
+        const __amdgpu_buffer_rsrc_t x_rs = make_rsrc((is_k ? a.k_in : a.q_in) + t * a.ld_in, row_bytes);
+        // a row outside [0, n_rows) reads zeros
+        const int m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
+        const bool mok = m >= 0 && m < a.n_rows;
+        const __amdgpu_buffer_rsrc_t sc_rs = make_rsrc(a.scale + int64_t(mok ? m : 0) * C, mok ? row_bytes : 0u);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            px[i] = bload16(x_rs, off(i), 0);
+            usc[i] = bload16(sc_rs, off(i), 0);
+        }
+    }
+    const int e0 = (8 * lane) % a.D;
+    const int axis = e0 < a.rope_f ? 0 : (e0 < a.rope_f + a.rope_r ? 1 : 2);
+    float cs[4], sn[4];
+    {
+        const double p = double(a.pos[3 * t + axis]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double turns = p * a.theta_turns[e0 / 2 + j];
+            const float f = float(turns - rint(turns));
+            sn[j] = __builtin_amdgcn_sinf(f);
+            cs[j] = __builtin_amdgcn_cosf(f);
+        }
+    }
+    // gradient with respect to the RoPE input: each pair turned back
+    auto rot_back = [&](int i, float (&g)[8]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float h0 = bf_lo(pg[i][j]), h1 = bf_hi(pg[i][j]);
+            g[2 * j] = h0 * cs[j] + h1 * sn[j];
+            g[2 * j + 1] = -h0 * sn[j] + h1 * cs[j];
+        }
+    };
+    const __amdgpu_buffer_rsrc_t d_rs = make_rsrc((is_k ? a.dk_in : a.dq_in) + t * a.ld_gin, row_bytes);
+    if (!mod) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            float g[8];
+            rot_back(i, g);
+            bstore16(d_rs, off(i), 0, pack8(g));
+        }
+        return;
+    }
+    const float invC = 1.0f / float(C);
+    // Register pins between the passes: the packed rows count as redefined
+    // at each pin, so every pass widens them again instead of keeping the
+    // widened fp32 copies live across the reductions.
+    auto pin = [&] {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) asm volatile("" : "+v"(px[i]), "+v"(pg[i]), "+v"(usc[i]));
+    };
+    float sx = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) sx += bf_lo(px[i][w]) + bf_hi(px[i][w]);
+    pin();
+    const float mu = wave_sum(sx) * invC;
+    float vx = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const bool inr = lane + kWave * i < nch;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float x0 = bf_lo(px[i][w]) - mu, x1 = bf_hi(px[i][w]) - mu;
+            vx += inr ? x0 * x0 + x1 * x1 : 0.f;
+        }
+    }
+    pin();
+    const float rs = rsqrtf(wave_sum(vx) * invC + a.eps);
+    // mean(gx) and mean(gx xh), gx = g (1 + scale); chunks past the row have g = 0
+    float sa = 0.f, sb = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        float g[8], x[8], sc[8];
+        rot_back(i, g);
+        unpack8(px[i], x);
+        unpack8(usc[i], sc);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float gx = g[j] * (1.0f + sc[j]);
+            sa += gx;
+            sb += gx * ((x[j] - mu) * rs);
+        }
+    }
+    pin();
+    const float ma = wave_sum(sa) * invC, mb = wave_sum(sb) * invC;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        float g[8], x[8], sc[8], dx[8];
+        rot_back(i, g);
+        unpack8(px[i], x);
+        unpack8(usc[i], sc);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dx[j] = (g[j] * (1.0f + sc[j]) - ma - (x[j] - mu) * rs * mb) * rs;
+        bstore16(d_rs, off(i), 0, pack8(dx));
+    }
+    if (lane == 0) *reinterpret_cast<float2*>(stats + 4 * t + 2 * (is_k ? 1 : 0)) = float2{mu, rs};
+}
+
+// Kernel B: blockIdx.y = run of kSumRun tokens, blockIdx.x = group of 64
+// chunks; lane = one chunk (in-head offset 8l mod D, as in kernel A).
+__global__ __launch_bounds__(64) void modrope_bwd_sums_kernel(ModRopeBwdArgs a, const float* __restrict__ stats,
+                                                              int32_t* __restrict__ tags, float* __restrict__ slots) {
+    const int lane = threadIdx.x;
+    const int C = a.H * a.D;
+    const int nch = C >> 3;
+    const int c = blockIdx.x * kWave + lane;
+    const bool live = c < nch;
+    const uint32_t row_bytes = uint32_t(C) * 2u;
+    const uint32_t voff = 16u * uint32_t(c);
+    const int e0 = (8 * lane) % a.D;
+    const int axis = e0 < a.rope_f ? 0 : (e0 < a.rope_f + a.rope_r ? 1 : 2);
+    double th[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) th[j] = a.theta_turns[e0 / 2 + j];
+    const int64_t t_begin = int64_t(blockIdx.y) * kSumRun;
+    const int64_t t_end = t_begin + kSumRun < a.T ? t_begin + kSumRun : a.T;
+    float s0[8], s1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s0[j] = s1[j] = 0.f;
+    int cur = -1;
+    auto flush = [&](int row) {
+        if (row < 0 || row >= a.n_rows || !live) return;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            atomic_add_f32(a.dshift + int64_t(row) * C + 8 * c + j, s0[j]);
+            atomic_add_f32(a.dscale + int64_t(row) * C + 8 * c + j, s1[j]);
+            s0[j] = s1[j] = 0.f;
+        }
+    };
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
+        if (m != cur) {
+            flush(cur);
+            cur = m;
+        }
+        const u32x4_t gq = bload16(make_rsrc(a.dq_out + t * a.ld_gout, row_bytes), voff, 0);
+        const u32x4_t gk = bload16(make_rsrc(a.dk_out + t * a.ld_gout, row_bytes), voff, 0);
+        const u32x4_t xq = bload16(make_rsrc(a.q_in + t * a.ld_in, row_bytes), voff, 0);
+        const u32x4_t xk = bload16(make_rsrc(a.k_in + t * a.ld_in, row_bytes), voff, 0);
+        const f32x4_t st = *reinterpret_cast<const f32x4_t*>(stats + 4 * t);   // mu_q, rs_q, mu_k, rs_k
+        const double p = double(a.pos[3 * t + axis]);
+        if (m < 0 || m >= a.n_rows) continue;   // a row outside the table adds nothing
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double turns = p * th[j];
+            const float f = float(turns - rint(turns));
+            const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+            const float q0 = bf_lo(gq[j]), q1 = bf_hi(gq[j]), k0 = bf_lo(gk[j]), k1 = bf_hi(gk[j]);
+            const float gq0 = q0 * cs + q1 * sn, gq1 = -q0 * sn + q1 * cs;
+            const float gk0 = k0 * cs + k1 * sn, gk1 = -k0 * sn + k1 * cs;
+            const float hq0 = (bf_lo(xq[j]) - st[0]) * st[1], hq1 = (bf_hi(xq[j]) - st[0]) * st[1];
+            const float hk0 = (bf_lo(xk[j]) - st[2]) * st[3], hk1 = (bf_hi(xk[j]) - st[2]) * st[3];
+            s0[2 * j] += gq0 + gk0;
+            s0[2 * j + 1] += gq1 + gk1;
+            s1[2 * j] += gq0 * hq0 + gk0 * hk0;
+            s1[2 * j + 1] += gq1 * hq1 + gk1 * hk1;
+        }
+    }
+    float* slot = slots + int64_t(blockIdx.y) * 2 * C;
+    if (live) {
+        *reinterpret_cast<f32x4_t*>(slot + 8 * c) = f32x4_t{s0[0], s0[1], s0[2], s0[3]};
+        *reinterpret_cast<f32x4_t*>(slot + 8 * c + 4) = f32x4_t{s0[4], s0[5], s0[6], s0[7]};
+        *reinterpret_cast<f32x4_t*>(slot + C + 8 * c) = f32x4_t{s1[0], s1[1], s1[2], s1[3]};
+        *reinterpret_cast<f32x4_t*>(slot + C + 8 * c + 4) = f32x4_t{s1[4], s1[5], s1[6], s1[7]};
+    }
+    if (blockIdx.x == 0 && lane == 0) tags[blockIdx.y] = cur >= 0 && cur < a.n_rows ? cur : -1;
+}
+
+// ---------------------------------------------------------------------------
 // gated residual (+ fused next adaLN) backward
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void gated_residual_bwd_kernel(GatedResBwdArgs a) {
@@ -420,8 +627,12 @@ hipError_t reduce_slots(void* ws, int64_t T, int C, float* o0, float* o1, float*
 }  // namespace
 
 size_t elementwise_bwd_workspace_bytes(int64_t T, int32_t C, int32_t n_arrays) {
-    const int64_t ns = n_slots_for(T < 0 ? 0 : T);
-    return slot_tags_bytes(ns) + size_t(ns) * size_t(n_arrays) * size_t(C) * 4;
+    const int64_t Tn = T < 0 ? 0 : T;
+    const int64_t ns = n_slots_for(Tn);
+    // slots of kRun tokens (the single-kernel form), plus 16 bytes of row
+    // statistics per token; the two-kernel form's fewer, larger-run slots and
+    // its statistics fit the same bytes
+    return slot_tags_bytes(ns) + size_t(ns) * size_t(n_arrays) * size_t(C) * 4 + size_t(Tn) * 16;
 }
 
 hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& args, hipStream_t stream) {
@@ -440,11 +651,40 @@ hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& args, hipStream_t stre
         if (e != hipSuccess) return e;
     }
     if (a.T == 0) return hipSuccess;
-    hipLaunchKernelGGL(modulate_rope_bwd_kernel, dim3(unsigned(n_slots_for(a.T))), dim3(block_threads(C)), 0,
-                       stream, a);
+    const int nch_w = (C / 8 + kWave - 1) / kWave;     // 16-byte chunks per lane of a row
+    if (nch_w > 6) {
+        hipLaunchKernelGGL(modulate_rope_bwd_kernel, dim3(unsigned(n_slots_for(a.T))), dim3(block_threads(C)), 0,
+                           stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || !mod) return e;
+        return reduce_slots<2>(a.workspace, a.T, C, a.dshift, a.dscale, nullptr, stream);
+    }
+    // two kernels: workspace = tags, slots of kSumRun tokens, then the rows'
+    // statistics (4 floats per token); it fits the size the single kernel's
+    // slots need (C >= 64)
+    const int64_t ns = sum_slots_for(a.T);
+    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+    int32_t* tags = reinterpret_cast<int32_t*>(ws);
+    float* slots = reinterpret_cast<float*>(ws + slot_tags_bytes(ns));
+    float* stats = slots + ns * 2 * C;
+    const dim3 grid_a(unsigned((a.T + kRowsTokens - 1) / kRowsTokens));
+    switch (nch_w) {
+        case 1: hipLaunchKernelGGL(modrope_bwd_dx_kernel<1>, grid_a, dim3(256), 0, stream, a, stats); break;
+        case 2: hipLaunchKernelGGL(modrope_bwd_dx_kernel<2>, grid_a, dim3(256), 0, stream, a, stats); break;
+        case 3: hipLaunchKernelGGL(modrope_bwd_dx_kernel<3>, grid_a, dim3(256), 0, stream, a, stats); break;
+        case 4: hipLaunchKernelGGL(modrope_bwd_dx_kernel<4>, grid_a, dim3(256), 0, stream, a, stats); break;
+        case 5: hipLaunchKernelGGL(modrope_bwd_dx_kernel<5>, grid_a, dim3(256), 0, stream, a, stats); break;
+        default: hipLaunchKernelGGL(modrope_bwd_dx_kernel<6>, grid_a, dim3(256), 0, stream, a, stats); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !mod) return e;
-    return reduce_slots<2>(a.workspace, a.T, C, a.dshift, a.dscale, nullptr, stream);
+    hipLaunchKernelGGL(modrope_bwd_sums_kernel, dim3(unsigned((C / 8 + kWave - 1) / kWave), unsigned(ns)), dim3(64),
+                       0, stream, a, stats, tags, slots);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dim3 grid(unsigned((C + 255) / 256), unsigned((ns + kSlotGroup - 1) / kSlotGroup));
+    hipLaunchKernelGGL(slot_reduce_kernel<2>, grid, dim3(256), 0, stream, tags, slots, ns, C, a.dshift, a.dscale,
+                       nullptr);
+    return hipGetLastError();
 }
 
 hipError_t launch_gated_residual_bwd(const GatedResBwdArgs& a, hipStream_t stream) {

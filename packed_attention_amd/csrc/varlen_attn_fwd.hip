@@ -186,9 +186,13 @@ __device__ __forceinline__ int octave_class(int L) {
 
 // In-kernel schedule of a small pack (n <= kInlineSeqs), built in LDS by
 // every thread of the block.
-__device__ void build_schedule_small(const int32_t* __restrict__ cu, int n, int H, int32_t* seq,
+__device__ void build_schedule_small(const int32_t* __restrict__ cu_g, int n, int H, int32_t* seq,
                                      int32_t* tiles, int32_t* nkv, int64_t* it_start, int32_t* tok0,
-                                     int32_t* len) {
+                                     int32_t* len, int32_t* cu) {
+    // the offsets are staged in LDS once, so the O(n) rank loop below makes
+    // no global loads
+    for (int i = threadIdx.x; i <= n; i += blockDim.x) cu[i] = cu_g[i];
+    __syncthreads();
     for (int s = threadIdx.x; s < n; s += blockDim.x) {
         const int Ls = cu[s + 1] - cu[s];
         const int cs = octave_class(Ls);
@@ -293,6 +297,7 @@ __global__ __launch_bounds__(kSchedThreads) void attn_schedule_kernel(const int3
 // Schedule of this call: built in LDS for small packs, else the prologue's.
 struct SchedLds {
     int32_t seq[kInlineSeqs], tiles[kInlineSeqs], nkv[kInlineSeqs], tok0[kInlineSeqs], len[kInlineSeqs];
+    int32_t cu[kInlineSeqs + 1];
     int64_t it_start[kInlineSeqs + 1];
 };
 
@@ -300,7 +305,7 @@ __device__ Sched get_schedule(const int32_t* cu, int n, int H, const unsigned ch
     Sched s;
     s.n = n;
     if (n <= kInlineSeqs) {
-        build_schedule_small(cu, n, H, lds.seq, lds.tiles, lds.nkv, lds.it_start, lds.tok0, lds.len);
+        build_schedule_small(cu, n, H, lds.seq, lds.tiles, lds.nkv, lds.it_start, lds.tok0, lds.len, lds.cu);
         s.tok0 = lds.tok0;
         s.len = lds.len;
         s.seq = lds.seq;
