@@ -14,27 +14,29 @@
 //              do = gate dyt, dgate[r] += dyt o, dshift2[r] += dz,
 //              dscale2[r] += dz yh.
 //
-// Layout and mapping.  A workgroup processes a run of kRun consecutive
-// tokens, one token row at a time; thread i owns the 16-byte chunk i of the
-// row (8 channels), so every row access is one coalesced pass and each
-// thread's per-row gradient sums are 8 registers per summed array.  Row
-// statistics (LayerNorm mean and variance, then mean(gx) and mean(gx xh))
-// are workgroup reductions: DPP within each wavefront, then the wavefront
-// partials through LDS.  The next token's rows are loaded while the current
-// one is reduced.
-//
-// Per-row sums over tokens (dshift, dscale, dgate, ...) without global
-// contention: each workgroup keeps the sums of its current adaLN row in
-// registers; a row change inside the run (a sample or modality boundary)
-// adds the finished sums to the output with fp32 global atomics (rare), and
-// at the end of the run the workgroup writes its sums once to its own slot
-// of the caller's workspace, tagged with the row.  A second kernel then walks
-// the slots in order, one thread per channel and group of slots, and adds
-// each run of equal tags to the output row.  Each output row is touched by a
-// handful of atomic adds instead of one per token, so a pack whose tokens all
-// share one row (one sample) does not serialise on it.  The order of the fp32
-// additions into the outputs varies between calls (the row sums are not
-// bitwise reproducible; dx and the other per-token outputs are).
+// Layout and mapping.  Each call runs two kernels and a reduction:
+//  * the per-token outputs (dq, dk; dx, do) with the forward kernels'
+//    mappings (modulate + RoPE: one wavefront per q or k row, statistics
+//    inside the wavefront; gated residual: one workgroup per token, one
+//    16-byte chunk per thread, LayerNorm reductions through LDS), which also
+//    write each row's fp32 statistics (4 floats per token);
+//  * the per-row sums over tokens (dshift, dscale; dgate, dshift2,
+//    dscale2): one lane per 8-channel chunk walks a run of kSumRun tokens,
+//    reads the rows again and recomputes the fp32 gradients from them and
+//    the statistics, so the sums see the same fp32 values as the outputs;
+//  * slot_reduce_kernel: each run leaves its sums in its own slot of the
+//    caller's workspace, tagged with its adaLN row, and the reduction walks
+//    the slots in order, one thread per channel and group of slots, adding
+//    each run of equal tags to the output row with one fp32 atomic add.  A
+//    row change inside a run adds the finished sums with atomics too.  Each
+//    output row is touched by a handful of atomic adds instead of one per
+//    token, so a pack whose tokens all share one row does not serialise on
+//    it; the order of those additions varies between calls (the row sums
+//    are not bitwise reproducible; every per-token output is).
+// Modulate + RoPE rows of more than 3072 channels keep a single kernel: a
+// workgroup walks a run of kRun tokens one row at a time (thread per chunk,
+// statistics by workgroup reductions), keeps the sums of its current adaLN
+// row in registers and writes them to its slot at the end of the run.
 #include <cmath>
 
 #include "mf_device.h"
@@ -492,126 +494,6 @@ __global__ __launch_bounds__(64) void modrope_bwd_sums_kernel(ModRopeBwdArgs a, 
     if (blockIdx.x == 0 && lane == 0) tags[blockIdx.y] = cur >= 0 && cur < a.n_rows ? cur : -1;
 }
 
-// ---------------------------------------------------------------------------
-// gated residual (+ fused next adaLN) backward
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void gated_residual_bwd_kernel(GatedResBwdArgs a) {
-    __shared__ float red[2 * 2 * 16];
-    const int C = a.C;
-    const int ci = threadIdx.x;
-    const bool live = ci < (C >> 3);
-    const int c0 = 8 * ci;
-    const bool fused = a.dz != nullptr;
-    const bool has_dy = a.dy != nullptr;
-    const float invC = 1.0f / float(C);
-    const int64_t t_begin = int64_t(blockIdx.x) * kRun;
-    const int64_t t_end = t_begin + kRun < a.T ? t_begin + kRun : a.T;
-    float* const outs[3] = {a.dgate, a.dshift2, a.dscale2};
-    float part[3][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) part[0][j] = part[1][j] = part[2][j] = 0.f;
-    int cur = -1;
-    int buf = 0;
-
-    // rows of token t: x, o, dy, dz
-    auto load = [&](int64_t t, u32x4_t (&r)[4]) {
-        if (live) {
-            r[0] = ld16(a.x + t * C + c0);
-            r[1] = ld16(a.o + t * C + c0);
-            if (has_dy) r[2] = ld16(a.dy + t * C + c0);
-            if (fused) r[3] = ld16(a.dz + t * C + c0);
-        }
-    };
-    u32x4_t nxt[4] = {};
-    load(t_begin, nxt);
-    for (int64_t t = t_begin; t < t_end; ++t) {
-        u32x4_t row[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) row[i] = nxt[i];
-        if (t + 1 < t_end) load(t + 1, nxt);
-        const int m = a.mod_row[t];
-        const bool mok = m >= 0 && m < a.n_rows;      // a row outside the table reads zeros, adds nothing
-        if (m != cur) {
-            if (cur >= 0 && cur < a.n_rows && live) {
-                if (fused)
-                    rows_to_output<3>(part, outs, cur, C, c0);
-                else
-                    rows_to_output<1>(reinterpret_cast<float(&)[1][8]>(part),
-                                      reinterpret_cast<float* const(&)[1]>(outs), cur, C, c0);
-            }
-            cur = m;
-        }
-        float xv[8], ov[8], gv[8], dy[8], dz[8];
-        unpack8(row[0], xv);
-        unpack8(row[1], ov);
-        unpack8(live && mok ? ld16(a.gate + int64_t(m) * C + c0) : u32x4_t{}, gv);
-        unpack8(has_dy ? row[2] : u32x4_t{}, dy);
-        unpack8(fused ? row[3] : u32x4_t{}, dz);
-        float y[8], dyt[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            y[j] = xv[j] + gv[j] * ov[j];
-            dyt[j] = dy[j];
-        }
-        if (fused) {
-            float s[2] = {0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s[0] += y[j];          // dead chunks hold y = 0
-            wg_sum<2>(s, red, buf);
-            buf ^= 1;
-            const float mu = s[0] * invC;
-            float v[2] = {0.f, 0.f};
-            if (live)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) v[0] += (y[j] - mu) * (y[j] - mu);
-            wg_sum<2>(v, red, buf);
-            buf ^= 1;
-            const float rs = rsqrtf(v[0] * invC + a.eps);
-            float s2[8];
-            unpack8(live && mok ? ld16(a.scale2 + int64_t(m) * C + c0) : u32x4_t{}, s2);
-            float yh[8], gy[8];
-            float ab[2] = {0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                yh[j] = (y[j] - mu) * rs;
-                gy[j] = dz[j] * (1.0f + s2[j]);
-                ab[0] += gy[j];
-                ab[1] += gy[j] * yh[j];
-            }
-            wg_sum<2>(ab, red, buf);
-            buf ^= 1;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                dyt[j] += (gy[j] - ab[0] * invC - yh[j] * ab[1] * invC) * rs;
-                part[1][j] += dz[j];
-                part[2][j] += dz[j] * yh[j];
-            }
-        }
-        if (live) {
-            float dov[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                dov[j] = gv[j] * dyt[j];
-                part[0][j] += dyt[j] * ov[j];
-            }
-            st16(a.dx + t * C + c0, pack8(dyt));
-            st16(a.dout + t * C + c0, pack8(dov));
-        }
-    }
-    const int na = fused ? 3 : 1;
-    int32_t* tags = static_cast<int32_t*>(a.workspace);
-    float* slot = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) +
-                                           slot_tags_bytes(n_slots_for(a.T))) +
-                  int64_t(blockIdx.x) * na * C;
-    if (live) {
-        if (fused)
-            rows_to_slot<3>(part, slot, C, c0);
-        else
-            rows_to_slot<1>(reinterpret_cast<float(&)[1][8]>(part), slot, C, c0);
-    }
-    if (threadIdx.x == 0) tags[blockIdx.x] = cur < a.n_rows ? cur : -1;   // -1: nothing to add
-}
-
 int block_threads(int C) { return ((C / 8 + 63) / 64) * 64; }
 
 template <int NA>
@@ -622,6 +504,150 @@ hipError_t reduce_slots(void* ws, int64_t T, int C, float* o0, float* o1, float*
     dim3 grid(unsigned((C + 255) / 256), unsigned((ns + kSlotGroup - 1) / kSlotGroup));
     hipLaunchKernelGGL(slot_reduce_kernel<NA>, grid, dim3(256), 0, stream, tags, slots, ns, C, o0, o1, o2);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// gated residual backward in two kernels
+// ---------------------------------------------------------------------------
+// Kernel A: one workgroup per token, one 16-byte chunk per thread (the
+// forward kernel's mapping), LayerNorm reductions through LDS; it writes dx,
+// do and, with the fused adaLN, the token's mean and 1/sigma of y and the
+// means of g2 and g2 yh (g2 = dz (1 + scale2)).  Kernel B: lane = one
+// 8-channel chunk of a run of kSumRun tokens; it recomputes dyt in fp32 from
+// the rows and those statistics and writes one tagged slot of dgate (and
+// dshift2, dscale2) per run, as the modulate + RoPE sums kernel does.
+template <bool FUSED>
+__global__ __launch_bounds__(1024) void gres_bwd_rows_kernel(GatedResBwdArgs a, float* __restrict__ stats) {
+    __shared__ float red[2 * 2 * 16];
+    const int64_t t = blockIdx.x;
+    const int c = threadIdx.x;
+    const int C = a.C;
+    const bool in = c < (C >> 3);
+    const int m0 = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
+    const bool mok = m0 >= 0 && m0 < a.n_rows;      // a row outside the table reads zeros
+    const int64_t m = mok ? m0 : 0;
+    const uint32_t row_bytes = uint32_t(C) * 2u;
+    const uint32_t mrow_bytes = mok ? row_bytes : 0u;
+    const uint32_t off = 16u * uint32_t(c);
+    float xv[8], ov[8], gv[8], dy[8], y[8];
+    unpack8(bload16(make_rsrc(a.x + t * C, row_bytes), off, 0), xv);
+    unpack8(bload16(make_rsrc(a.o + t * C, row_bytes), off, 0), ov);
+    unpack8(bload16(make_rsrc(a.gate + m * C, mrow_bytes), off, 0), gv);
+    unpack8(a.dy != nullptr ? bload16(make_rsrc(a.dy + t * C, row_bytes), off, 0) : u32x4_t{}, dy);
+    u32x4_t pz = {0u, 0u, 0u, 0u}, ps2 = {0u, 0u, 0u, 0u};
+    if constexpr (FUSED) {
+        pz = bload16(make_rsrc(a.dz + t * C, row_bytes), off, 0);
+        ps2 = bload16(make_rsrc(a.scale2 + m * C, mrow_bytes), off, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = xv[j] + gv[j] * ov[j];
+    if constexpr (FUSED) {
+        const float invC = 1.0f / float(C);
+        float s[2] = {0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[0] += y[j];        // chunks past the row hold y = 0
+        wg_sum<2>(s, red, 0);
+        const float mu = s[0] * invC;
+        float v[2] = {0.f, 0.f};
+        if (in)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[0] += (y[j] - mu) * (y[j] - mu);
+        wg_sum<2>(v, red, 1);
+        const float rs = rsqrtf(v[0] * invC + a.eps);
+        float dz[8], s2[8], yh[8], g2[8];
+        unpack8(pz, dz);
+        unpack8(ps2, s2);
+        float ab[2] = {0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            yh[j] = (y[j] - mu) * rs;
+            g2[j] = dz[j] * (1.0f + s2[j]);
+            ab[0] += g2[j];
+            ab[1] += g2[j] * yh[j];
+        }
+        wg_sum<2>(ab, red, 0);
+        const float ma = ab[0] * invC, mb = ab[1] * invC;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dy[j] += (g2[j] - ma - yh[j] * mb) * rs;
+        if (c == 0) *reinterpret_cast<f32x4_t*>(stats + 4 * t) = f32x4_t{mu, rs, ma, mb};
+    }
+    float dov[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dov[j] = gv[j] * dy[j];
+    bstore16(make_rsrc(a.dx + t * C, row_bytes), off, 0, pack8(dy));
+    bstore16(make_rsrc(a.dout + t * C, row_bytes), off, 0, pack8(dov));
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(64) void gres_bwd_sums_kernel(GatedResBwdArgs a, const float* __restrict__ stats,
+                                                           int32_t* __restrict__ tags, float* __restrict__ slots) {
+    constexpr int NA = FUSED ? 3 : 1;
+    const int lane = threadIdx.x;
+    const int C = a.C;
+    const int c = blockIdx.x * kWave + lane;
+    const bool live = c < (C >> 3);
+    const uint32_t row_bytes = uint32_t(C) * 2u;
+    const uint32_t voff = 16u * uint32_t(c);
+    const int64_t t_begin = int64_t(blockIdx.y) * kSumRun;
+    const int64_t t_end = t_begin + kSumRun < a.T ? t_begin + kSumRun : a.T;
+    float* const outs[3] = {a.dgate, a.dshift2, a.dscale2};
+    float sm[NA][8];
+#pragma unroll
+    for (int k = 0; k < NA; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sm[k][j] = 0.f;
+    int cur = -1;
+    float gv[8], s2[8];
+    auto flush = [&](int row) {
+        if (row < 0 || row >= a.n_rows || !live) return;
+#pragma unroll
+        for (int k = 0; k < NA; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                atomic_add_f32(outs[k] + int64_t(row) * C + 8 * c + j, sm[k][j]);
+                sm[k][j] = 0.f;
+            }
+    };
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
+        if (m != cur) {
+            flush(cur);
+            cur = m;
+            const bool mok = m >= 0 && m < a.n_rows;
+            const int64_t mm = mok ? m : 0;
+            unpack8(bload16(make_rsrc(a.gate + mm * C, mok ? row_bytes : 0u), voff, 0), gv);
+            if constexpr (FUSED) unpack8(bload16(make_rsrc(a.scale2 + mm * C, mok ? row_bytes : 0u), voff, 0), s2);
+        }
+        float xv[8], ov[8], dy[8], dz[8];
+        unpack8(bload16(make_rsrc(a.x + t * C, row_bytes), voff, 0), xv);
+        unpack8(bload16(make_rsrc(a.o + t * C, row_bytes), voff, 0), ov);
+        unpack8(a.dy != nullptr ? bload16(make_rsrc(a.dy + t * C, row_bytes), voff, 0) : u32x4_t{}, dy);
+        f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FUSED) {
+            unpack8(bload16(make_rsrc(a.dz + t * C, row_bytes), voff, 0), dz);
+            st = *reinterpret_cast<const f32x4_t*>(stats + 4 * t);   // mu, rs, mean g2, mean g2 yh
+        }
+        if (m < 0 || m >= a.n_rows) continue;    // a row outside the table adds nothing
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float dyt = dy[j];
+            if constexpr (FUSED) {
+                const float yh = (xv[j] + gv[j] * ov[j] - st[0]) * st[1];
+                dyt += (dz[j] * (1.0f + s2[j]) - st[2] - yh * st[3]) * st[1];
+                sm[1][j] += dz[j];
+                sm[2][j] += dz[j] * yh;
+            }
+            sm[0][j] += dyt * ov[j];
+        }
+    }
+    float* slot = slots + int64_t(blockIdx.y) * NA * C;
+    if (live)
+#pragma unroll
+        for (int k = 0; k < NA; ++k) {
+            *reinterpret_cast<f32x4_t*>(slot + k * C + 8 * c) = f32x4_t{sm[k][0], sm[k][1], sm[k][2], sm[k][3]};
+            *reinterpret_cast<f32x4_t*>(slot + k * C + 8 * c + 4) = f32x4_t{sm[k][4], sm[k][5], sm[k][6], sm[k][7]};
+        }
+    if (blockIdx.x == 0 && lane == 0) tags[blockIdx.y] = cur >= 0 && cur < a.n_rows ? cur : -1;
 }
 
 }  // namespace
@@ -695,11 +721,35 @@ hipError_t launch_gated_residual_bwd(const GatedResBwdArgs& a, hipStream_t strea
     if (e == hipSuccess && fused) e = zero_f32(a.dscale2, n, stream);
     if (e != hipSuccess) return e;
     if (a.T == 0) return hipSuccess;
-    hipLaunchKernelGGL(gated_residual_bwd_kernel, dim3(unsigned(n_slots_for(a.T))), dim3(block_threads(a.C)),
-                       0, stream, a);
+    // workspace: tags, slots of kSumRun tokens (1 or 3 arrays), then the rows'
+    // statistics (4 floats per token); it fits the size the query returns
+    const int na = fused ? 3 : 1;
+    const int64_t ns = sum_slots_for(a.T);
+    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+    int32_t* tags = reinterpret_cast<int32_t*>(ws);
+    float* slots = reinterpret_cast<float*>(ws + slot_tags_bytes(ns));
+    float* stats = slots + ns * na * a.C;
+    const dim3 grid_b(unsigned((a.C / 8 + kWave - 1) / kWave), unsigned(ns));
+    if (fused) {
+        hipLaunchKernelGGL(gres_bwd_rows_kernel<true>, dim3(unsigned(a.T)), dim3(block_threads(a.C)), 0, stream, a,
+                           stats);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(gres_bwd_sums_kernel<true>, grid_b, dim3(64), 0, stream, a, stats, tags, slots);
+    } else {
+        hipLaunchKernelGGL(gres_bwd_rows_kernel<false>, dim3(unsigned(a.T)), dim3(block_threads(a.C)), 0, stream, a,
+                           stats);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(gres_bwd_sums_kernel<false>, grid_b, dim3(64), 0, stream, a, stats, tags, slots);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (fused) return reduce_slots<3>(a.workspace, a.T, a.C, a.dgate, a.dshift2, a.dscale2, stream);
-    return reduce_slots<1>(a.workspace, a.T, a.C, a.dgate, nullptr, nullptr, stream);
+    dim3 grid(unsigned((a.C + 255) / 256), unsigned((ns + kSlotGroup - 1) / kSlotGroup));
+    if (fused)
+        hipLaunchKernelGGL(slot_reduce_kernel<3>, grid, dim3(256), 0, stream, tags, slots, ns, a.C, a.dgate,
+                           a.dshift2, a.dscale2);
+    else
+        hipLaunchKernelGGL(slot_reduce_kernel<1>, grid, dim3(256), 0, stream, tags, slots, ns, a.C, a.dgate,
+                           nullptr, nullptr);
+    return hipGetLastError();
 }
 
 }  // namespace mf
