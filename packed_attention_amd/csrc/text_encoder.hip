@@ -139,10 +139,9 @@ hipError_t launch_qknorm_d(const QkNormRopeArgs& a, hipStream_t stream) {
 constexpr int kCW = 4;                 // wavefronts per workgroup
 constexpr int kCN = 64;                // keys per tile
 constexpr int kSlabMin = 32;           // smallest query slab (four grouped heads)
-// Workgroups per CU in the grid.  The LDS holds two, but the D = 128
-// kernel's registers (241 VGPRs + 96 AGPRs) leave one wavefront per SIMD, so
-// a CU's second workgroup runs after its first; forcing two resident
-// (244 VGPRs, no AGPRs) measured slower.
+// Workgroups per CU in the grid.  The LDS holds two, and the D = 128 kernel
+// stays within 256 registers per lane (249 VGPRs), so both are resident, two
+// wavefronts per SIMD; every register more than that would leave one.
 constexpr int kWgPerCu = 2;
 constexpr int kClasses = 1024;         // work classes (key-tile counts) of the longest-first order
 static_assert(kClasses % 256 == 0, "whole classes per prologue thread");
