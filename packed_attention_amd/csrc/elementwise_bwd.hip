@@ -46,18 +46,22 @@ namespace mf {
 namespace {
 
 constexpr int kRun = 4;          // tokens per workgroup
-constexpr int kSlotGroup = 32;   // slots summed per thread of the reduction kernel
+constexpr int kSlotGroup = 8;    // slots summed per thread of the reduction kernel
 
 __device__ __forceinline__ void atomic_add_f32(float* p, float v) { unsafeAtomicAdd(p, v); }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+// Zeros n floats at each of up to three arrays (blockIdx.y picks the array;
+// nullptr entries are skipped), one launch for all of a call's row sums.
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p0, float* __restrict__ p1,
+                                                        float* __restrict__ p2, int64_t n) {
+    float* const p = blockIdx.y == 0 ? p0 : blockIdx.y == 1 ? p1 : p2;
     const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (i < n) p[i] = 0.f;
+    if (p != nullptr && i < n) p[i] = 0.f;
 }
 
-hipError_t zero_f32(float* p, int64_t n, hipStream_t stream) {
-    if (p == nullptr || n == 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, p, n);
+hipError_t zero_f32(float* p0, float* p1, float* p2, int64_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned((n + 255) / 256), 3), dim3(256), 0, stream, p0, p1, p2, n);
     return hipGetLastError();
 }
 
@@ -97,10 +101,10 @@ template <int NA>
 __global__ __launch_bounds__(256) void slot_reduce_kernel(const int32_t* __restrict__ tags,
                                                           const float* __restrict__ slots, int64_t n_slots,
                                                           int C, float* o0, float* o1, float* o2) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int c = blockIdx.y * 256 + threadIdx.x;
     if (c >= C) return;
     float* const outs[3] = {o0, o1, o2};
-    const int64_t s0 = int64_t(blockIdx.y) * kSlotGroup;
+    const int64_t s0 = int64_t(blockIdx.x) * kSlotGroup;
     const int64_t s1 = s0 + kSlotGroup < n_slots ? s0 + kSlotGroup : n_slots;
     int cur = -1;
     float acc[NA];
@@ -424,14 +428,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH >= 6 ? 
     if (lane == 0) *reinterpret_cast<float2*>(stats + 4 * t + 2 * (is_k ? 1 : 0)) = float2{mu, rs};
 }
 
-// Kernel B: blockIdx.y = run of kSumRun tokens, blockIdx.x = group of 64
+// Kernel B: blockIdx.x = run of kSumRun tokens, blockIdx.y = group of 64
 // chunks; lane = one chunk (in-head offset 8l mod D, as in kernel A).
 __global__ __launch_bounds__(64) void modrope_bwd_sums_kernel(ModRopeBwdArgs a, const float* __restrict__ stats,
                                                               int32_t* __restrict__ tags, float* __restrict__ slots) {
     const int lane = threadIdx.x;
     const int C = a.H * a.D;
     const int nch = C >> 3;
-    const int c = blockIdx.x * kWave + lane;
+    const int c = blockIdx.y * kWave + lane;
     const bool live = c < nch;
     const uint32_t row_bytes = uint32_t(C) * 2u;
     const uint32_t voff = 16u * uint32_t(c);
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(64) void modrope_bwd_sums_kernel(ModRopeBwdArgs a, 
     double th[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) th[j] = a.theta_turns[e0 / 2 + j];
-    const int64_t t_begin = int64_t(blockIdx.y) * kSumRun;
+    const int64_t t_begin = int64_t(blockIdx.x) * kSumRun;
     const int64_t t_end = t_begin + kSumRun < a.T ? t_begin + kSumRun : a.T;
     float s0[8], s1[8];
 #pragma unroll
@@ -484,14 +488,14 @@ __global__ __launch_bounds__(64) void modrope_bwd_sums_kernel(ModRopeBwdArgs a, 
             s1[2 * j + 1] += gq1 * hq1 + gk1 * hk1;
         }
     }
-    float* slot = slots + int64_t(blockIdx.y) * 2 * C;
+    float* slot = slots + int64_t(blockIdx.x) * 2 * C;
     if (live) {
         *reinterpret_cast<f32x4_t*>(slot + 8 * c) = f32x4_t{s0[0], s0[1], s0[2], s0[3]};
         *reinterpret_cast<f32x4_t*>(slot + 8 * c + 4) = f32x4_t{s0[4], s0[5], s0[6], s0[7]};
         *reinterpret_cast<f32x4_t*>(slot + C + 8 * c) = f32x4_t{s1[0], s1[1], s1[2], s1[3]};
         *reinterpret_cast<f32x4_t*>(slot + C + 8 * c + 4) = f32x4_t{s1[4], s1[5], s1[6], s1[7]};
     }
-    if (blockIdx.x == 0 && lane == 0) tags[blockIdx.y] = cur >= 0 && cur < a.n_rows ? cur : -1;
+    if (blockIdx.y == 0 && lane == 0) tags[blockIdx.x] = cur >= 0 && cur < a.n_rows ? cur : -1;
 }
 
 int block_threads(int C) { return ((C / 8 + 63) / 64) * 64; }
@@ -501,7 +505,7 @@ hipError_t reduce_slots(void* ws, int64_t T, int C, float* o0, float* o1, float*
     const int64_t ns = n_slots_for(T);
     const int32_t* tags = static_cast<const int32_t*>(ws);
     const float* slots = reinterpret_cast<const float*>(static_cast<const unsigned char*>(ws) + slot_tags_bytes(ns));
-    dim3 grid(unsigned((C + 255) / 256), unsigned((ns + kSlotGroup - 1) / kSlotGroup));
+    dim3 grid(unsigned((ns + kSlotGroup - 1) / kSlotGroup), unsigned((C + 255) / 256));
     hipLaunchKernelGGL(slot_reduce_kernel<NA>, grid, dim3(256), 0, stream, tags, slots, ns, C, o0, o1, o2);
     return hipGetLastError();
 }
@@ -584,11 +588,11 @@ __global__ __launch_bounds__(64) void gres_bwd_sums_kernel(GatedResBwdArgs a, co
     constexpr int NA = FUSED ? 3 : 1;
     const int lane = threadIdx.x;
     const int C = a.C;
-    const int c = blockIdx.x * kWave + lane;
+    const int c = blockIdx.y * kWave + lane;
     const bool live = c < (C >> 3);
     const uint32_t row_bytes = uint32_t(C) * 2u;
     const uint32_t voff = 16u * uint32_t(c);
-    const int64_t t_begin = int64_t(blockIdx.y) * kSumRun;
+    const int64_t t_begin = int64_t(blockIdx.x) * kSumRun;
     const int64_t t_end = t_begin + kSumRun < a.T ? t_begin + kSumRun : a.T;
     float* const outs[3] = {a.dgate, a.dshift2, a.dscale2};
     float sm[NA][8];
@@ -640,14 +644,14 @@ __global__ __launch_bounds__(64) void gres_bwd_sums_kernel(GatedResBwdArgs a, co
             sm[0][j] += dyt * ov[j];
         }
     }
-    float* slot = slots + int64_t(blockIdx.y) * NA * C;
+    float* slot = slots + int64_t(blockIdx.x) * NA * C;
     if (live)
 #pragma unroll
         for (int k = 0; k < NA; ++k) {
             *reinterpret_cast<f32x4_t*>(slot + k * C + 8 * c) = f32x4_t{sm[k][0], sm[k][1], sm[k][2], sm[k][3]};
             *reinterpret_cast<f32x4_t*>(slot + k * C + 8 * c + 4) = f32x4_t{sm[k][4], sm[k][5], sm[k][6], sm[k][7]};
         }
-    if (blockIdx.x == 0 && lane == 0) tags[blockIdx.y] = cur >= 0 && cur < a.n_rows ? cur : -1;
+    if (blockIdx.y == 0 && lane == 0) tags[blockIdx.x] = cur >= 0 && cur < a.n_rows ? cur : -1;
 }
 
 }  // namespace
@@ -672,8 +676,7 @@ hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& args, hipStream_t stre
     const int C = a.H * a.D;
     const bool mod = a.scale != nullptr;
     if (mod) {
-        hipError_t e = zero_f32(a.dshift, int64_t(a.n_rows) * C, stream);
-        if (e == hipSuccess) e = zero_f32(a.dscale, int64_t(a.n_rows) * C, stream);
+        const hipError_t e = zero_f32(a.dshift, a.dscale, nullptr, int64_t(a.n_rows) * C, stream);
         if (e != hipSuccess) return e;
     }
     if (a.T == 0) return hipSuccess;
@@ -704,10 +707,10 @@ hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& args, hipStream_t stre
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !mod) return e;
-    hipLaunchKernelGGL(modrope_bwd_sums_kernel, dim3(unsigned((C / 8 + kWave - 1) / kWave), unsigned(ns)), dim3(64),
+    hipLaunchKernelGGL(modrope_bwd_sums_kernel, dim3(unsigned(ns), unsigned((C / 8 + kWave - 1) / kWave)), dim3(64),
                        0, stream, a, stats, tags, slots);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 grid(unsigned((C + 255) / 256), unsigned((ns + kSlotGroup - 1) / kSlotGroup));
+    dim3 grid(unsigned((ns + kSlotGroup - 1) / kSlotGroup), unsigned((C + 255) / 256));
     hipLaunchKernelGGL(slot_reduce_kernel<2>, grid, dim3(256), 0, stream, tags, slots, ns, C, a.dshift, a.dscale,
                        nullptr);
     return hipGetLastError();
@@ -716,9 +719,7 @@ hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& args, hipStream_t stre
 hipError_t launch_gated_residual_bwd(const GatedResBwdArgs& a, hipStream_t stream) {
     const int64_t n = int64_t(a.n_rows) * a.C;
     const bool fused = a.dz != nullptr;
-    hipError_t e = zero_f32(a.dgate, n, stream);
-    if (e == hipSuccess && fused) e = zero_f32(a.dshift2, n, stream);
-    if (e == hipSuccess && fused) e = zero_f32(a.dscale2, n, stream);
+    hipError_t e = zero_f32(a.dgate, fused ? a.dshift2 : nullptr, fused ? a.dscale2 : nullptr, n, stream);
     if (e != hipSuccess) return e;
     if (a.T == 0) return hipSuccess;
     // workspace: tags, slots of kSumRun tokens (1 or 3 arrays), then the rows'
@@ -729,7 +730,7 @@ hipError_t launch_gated_residual_bwd(const GatedResBwdArgs& a, hipStream_t strea
     int32_t* tags = reinterpret_cast<int32_t*>(ws);
     float* slots = reinterpret_cast<float*>(ws + slot_tags_bytes(ns));
     float* stats = slots + ns * na * a.C;
-    const dim3 grid_b(unsigned((a.C / 8 + kWave - 1) / kWave), unsigned(ns));
+    const dim3 grid_b(unsigned(ns), unsigned((a.C / 8 + kWave - 1) / kWave));
     if (fused) {
         hipLaunchKernelGGL(gres_bwd_rows_kernel<true>, dim3(unsigned(a.T)), dim3(block_threads(a.C)), 0, stream, a,
                            stats);
@@ -742,7 +743,7 @@ hipError_t launch_gated_residual_bwd(const GatedResBwdArgs& a, hipStream_t strea
         hipLaunchKernelGGL(gres_bwd_sums_kernel<false>, grid_b, dim3(64), 0, stream, a, stats, tags, slots);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 grid(unsigned((a.C + 255) / 256), unsigned((ns + kSlotGroup - 1) / kSlotGroup));
+    dim3 grid(unsigned((ns + kSlotGroup - 1) / kSlotGroup), unsigned((a.C + 255) / 256));
     if (fused)
         hipLaunchKernelGGL(slot_reduce_kernel<3>, grid, dim3(256), 0, stream, tags, slots, ns, a.C, a.dgate,
                            a.dshift2, a.dscale2);
