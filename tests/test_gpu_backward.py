@@ -77,6 +77,7 @@ def test_tiny_modulated_bwd():
 RAGGED = [(1, 1, 0, 0), (1, 1, 1, 1), (3, 1, 6, 10), (0, 1, 8, 8), (1, 1, 8, 8), (0, 1, 0, 0),
           (7, 1, 8, 15), (0, 1, 8, 16), (1, 1, 8, 16), (12, 1, 16, 18), (5, 2, 4, 6),
           (1, 1, 15, 17)]
+RAGGED_DESCS = [(t, f, h, ww, s, s) for s, (t, f, h, ww) in enumerate(RAGGED)]
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -304,3 +305,66 @@ def test_backward_chain_end_to_end():
         r = ref[name]
         rel = float(np.linalg.norm(got - r) / max(np.linalg.norm(r), 1e-30))
         assert rel <= CHAIN_REL_RMS, f"chain {name}: relative RMS {rel:.3e}"
+
+
+@pytest.mark.parametrize("H", [32, 64])
+def test_elementwise_bwd_wide_rows(H):
+    """Rows of 4096 and 8192 channels: the modulate+RoPE backward's form for
+    rows of more than 3072 channels, and the gated residual backward's
+    per-token kernel at its largest workgroups."""
+    descs = [(13, 1, 9, 10, 0, 0), (7, 1, 5, 6, 1, 1)]
+    w = W.custom(descs, H=H, D=128, rope_dims=(0, 64, 64), modulate=True, residual=True, seed=80 + H,
+                 name=f"wide_bwd_h{H}")
+    modrope_bwd_check(w)
+    gres_bwd_check(w)
+
+
+def test_elementwise_bwd_rows_outside_table():
+    """An adaLN row outside [0, n_rows) reads zeros and adds nothing: the
+    per-token gradients equal, bit for bit, those of the same call with an
+    explicit all-zero row for those tokens, and the table's rows sum the
+    same tokens as in that call (within fp32 ordering)."""
+    import torch
+    w = W.custom(RAGGED_DESCS[:6], H=3, D=64, rope_dims=(0, 32, 32), modulate=True, residual=True, seed=83,
+                 name="bwd_rows_outside")
+    b = runner.to_device(w)
+    runner.run_chain(b)
+    g = W.upstream_grads(w)
+    T, C = w.T, w.H * w.D
+    n = len(w.descs)
+    bad = b.mod_row.clone()
+    bad[3], bad[T // 2], bad[T - 1] = n, -1, 1 << 20
+    sub = torch.where((bad < 0) | (bad >= n), torch.full_like(bad, n), bad)
+    zero = torch.zeros((1, C), dtype=torch.bfloat16, device="cuda")
+    same = lambda a, c, name: torch.equal(a.view(torch.int16), c.view(torch.int16)) or pytest.fail(name)  # noqa
+
+    dq_out, dk_out = runner.bf16_tensor(g["dq"]), runner.bf16_tensor(g["dk"])
+    outs = []
+    for rows, scale in ((bad, b.scale), (sub, torch.cat([b.scale, zero]))):
+        dq, dk = torch.empty_like(b.q), torch.empty_like(b.k)
+        dsh = torch.empty((scale.shape[0], C), dtype=torch.float32, device="cuda")
+        dsc = torch.empty_like(dsh)
+        native.modulate_rope_bwd(b.q, b.k, dq_out, dk_out, dq, dk, b.pos, w.rope_dims, w.rope_base, scale,
+                                 rows, dsh, dsc, w.eps)
+        outs.append((dq, dk, dsh, dsc))
+    torch.cuda.synchronize()
+    same(outs[0][0], outs[1][0], "dq")
+    same(outs[0][1], outs[1][1], "dk")
+    for i, name in ((2, "dshift"), (3, "dscale")):
+        np.testing.assert_allclose(_f32(outs[0][i]), _f32(outs[1][i][:n]), rtol=1e-5, atol=1e-5, err_msg=name)
+
+    dy, dz = runner.bf16_tensor(g["dy"]), runner.bf16_tensor(g["dz"])
+    o2 = b.o.view(T, C)
+    outs = []
+    for rows, gate, scale2 in ((bad, b.gate, b.scale2), (sub, torch.cat([b.gate, zero]), torch.cat([b.scale2, zero]))):
+        dx, do = torch.empty((T, C), dtype=torch.bfloat16, device="cuda"), torch.empty((T, C), dtype=torch.bfloat16,
+                                                                                        device="cuda")
+        r = lambda: torch.empty((gate.shape[0], C), dtype=torch.float32, device="cuda")  # noqa: E731
+        dg, ds2, dc2 = r(), r(), r()
+        native.gated_residual_bwd(b.x, o2, gate, rows, dy, dx, do, dg, scale2, dz, ds2, dc2, w.eps)
+        outs.append((dx, do, dg, ds2, dc2))
+    torch.cuda.synchronize()
+    same(outs[0][0], outs[1][0], "dx")
+    same(outs[0][1], outs[1][1], "do")
+    for i, name in ((2, "dgate"), (3, "dshift2"), (4, "dscale2")):
+        np.testing.assert_allclose(_f32(outs[0][i]), _f32(outs[1][i][:n]), rtol=1e-5, atol=1e-5, err_msg=name)
