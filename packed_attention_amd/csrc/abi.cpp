@@ -472,7 +472,7 @@ mf_status mf_gated_residual_bwd(void* stream, const void* x, const void* o, cons
 
 size_t mf_block_qkv_workspace_bytes(int64_t T, int32_t H, int32_t D) {
     if (!query_ok(T, H, D)) return 0;
-    return mf::block_qkv_workspace_bytes(T, H * D);
+    return mf::block_qkv_workspace_bytes(T, H * D, D);
 }
 
 mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_qkv, void* qkv,
@@ -501,7 +501,7 @@ mf_status mf_block_qkv(void* stream, const void* x, int64_t ld_x, const void* w_
     if (ld_x % 8 || ld_qkv % 8) return MF_ERR_ALIGN;
     if (!aligned(x, 16) || !aligned(w_qkv, 16) || !aligned(qkv, 16) || !aligned(pos, 4)) return MF_ERR_ALIGN;
     if (modulate && (!aligned(shift, 16) || !aligned(scale, 16) || !aligned(mod_row, 4))) return MF_ERR_ALIGN;
-    if (workspace == nullptr || workspace_bytes < mf::block_qkv_workspace_bytes(T, int32_t(C)))
+    if (workspace == nullptr || workspace_bytes < mf::block_qkv_workspace_bytes(T, int32_t(C), D))
         return MF_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return MF_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);

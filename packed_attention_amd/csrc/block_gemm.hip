@@ -32,8 +32,18 @@
 //    chunks swizzled, so the fragment reads are conflict-free without
 //    padding.
 //    Transposed output: each lane holds one token and 16 features, so the
-//    RoPE pairs (adjacent features) sit in one lane and each lane stores 4
-//    consecutive features (8 bytes) per register group.
+//    RoPE pairs (adjacent features) sit in one lane.
+//  * Rotation table: the modulation pass (or, without modulation, a small
+//    kernel) writes (cos, sin) of every head pair of every token once, T*D/2
+//    fp32 pairs in the workspace.  The epilogue then turns a pair with one
+//    load per two pairs and four multiply-adds, instead of forming the fp64
+//    angle and the sine and cosine for each of the 3C/2 x T pairs again in
+//    each of the 2C/256 q and k feature tiles (the per-pair angle work was
+//    most of the epilogue's instructions).
+//  * Out projection epilogue: the gated residual needs x and gate along the
+//    features, while a lane holds one token, so the fp32 tile goes through
+//    LDS in two halves and every global access is a 512-byte row segment;
+//    the residual and gate rows are loaded before the staging.
 //  * Tiles are numbered so that the tiles one XCD runs are consecutive and
 //    share their weight tile (its L2 serves the re-reads).
 //  * Split tail (QKV projection): one workgroup per CU, so the tiles run in
@@ -92,9 +102,11 @@ struct GemmParams {
     int N, K;
     uint16_t* out;           // [T][N], token stride ld_out
     int64_t ld_out;
-    // QKV: RoPE on the features below rope_limit (q and k)
-    int rope_limit, D, rope_f, rope_r;
-    const int32_t* pos;
+    // QKV: RoPE on the features below rope_limit (q and k), from the
+    // rotation table: (cos, sin) of pair i of a head at token t in
+    // rope_cs[t * D/2 + i]
+    int rope_limit, D;
+    const f32x2_t* rope_cs;
     // out projection: y = resid + gate[m] * acc
     const uint16_t* resid;
     const uint16_t* gate;
@@ -105,8 +117,29 @@ struct GemmParams {
     // partial tiles in `partial` (kTileAcc floats per piece)
     int n_full, split;
     float* partial;
+};
+
+// The rotation table: for token t and pair i of a head (dims 2i, 2i+1 on
+// the axis their block belongs to), cs[t * D/2 + i] = (cos, sin) of
+// pos_axis(t) * theta_i.  The angle is formed in fp64 in turns and reduced to
+// [-1/2, 1/2] before the hardware sine and cosine.
+struct RopeTableParams {
+    f32x2_t* cs;
+    const int32_t* pos;
+    int D, rope_f, rope_r;
     double theta_turns[64];
 };
+
+__device__ __forceinline__ void rope_table_row(const RopeTableParams& rp, int64_t t, int lane) {
+    const int half = rp.D >> 1;
+    for (int i = lane; i < half; i += kWave) {
+        const int e = 2 * i;
+        const int axis = e < rp.rope_f ? 0 : (e < rp.rope_f + rp.rope_r ? 1 : 2);
+        const double turns = double(rp.pos[3 * t + axis]) * rp.theta_turns[i];
+        const float f = float(turns - rint(turns));
+        rp.cs[t * half + i] = f32x2_t{__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f)};
+    }
+}
 
 constexpr int kTileAcc = kBF * kBT;        // fp32 accumulators of one tile
 
@@ -137,12 +170,21 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Epilogue of one tile from its fp32 accumulators (lane = token, register r
-// of block fb = feature 8(r/4) + 4h + r%4 of the block).  The finished bf16
-// values go to an LDS image of the output tile (rows = tokens, 512 bytes;
+// of block fb = feature 8(r/4) + 4h + r%4 of the block).
+//
+// QKV projection: q and k pairs are turned by the table's rotation (register
+// pair (4j + 2c, 4j + 2c + 1) is head pair hp + 4j + c, hp = (nblk mod D)/2
+// + 2h, so one 16-byte table load serves two pairs), the values rounded to
+// bf16 go to an LDS image of the output tile (rows = tokens, 512 bytes;
 // 16-byte chunk c of row t in slot c ^ (t % 32), so the 8-byte writes of 32
-// consecutive rows and the 16-byte reads along a row are both
-// conflict-free), then out to global memory one 512-byte row segment per 32
-// lanes.
+// consecutive rows and the 16-byte reads along a row are both conflict-free)
+// and out one 512-byte row segment per 32 lanes.
+//
+// Out projection: y = x + gate * acc needs x and gate along the features, so
+// the fp32 tile goes through LDS in two halves of 128 tokens (rows of 1 KiB,
+// 16-byte chunk c of row t in slot c ^ (t % 16)); each wavefront then takes
+// whole rows, lane = 4 consecutive features, and every global load and store
+// is a 512-byte row segment.
 template <int MODE>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&acc)[2][4], const int f0,
                                               const int64_t t0, unsigned char* smem) {
@@ -154,69 +196,118 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&ac
     const int wf = wave & 3;
     const int wt = wave >> 2;
     __syncthreads();                       // every wavefront is done with the stages
+    if constexpr (MODE == kModeQkv) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const int tl = 128 * wt + 32 * tb + l32;   // token row inside the tile
-        const int64_t t = t0 + tl;
-        int64_t m = 0;
-        if constexpr (MODE == kModeOut) m = t < p.T ? p.mod_row[t] : -1;
+        for (int tb = 0; tb < 4; ++tb) {
+            const int tl = 128 * wt + 32 * tb + l32;   // token row inside the tile
+            const int64_t t = t0 + tl;
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb) {
-            const int fl = 64 * wf + 32 * fb;      // first feature of the block inside the tile
-            const int nblk = f0 + fl;
-            f32x16_t& a = acc[fb][tb];
-            if constexpr (MODE == kModeQkv) {
+            for (int fb = 0; fb < 2; ++fb) {
+                const int fl = 64 * wf + 32 * fb;      // first feature of the block inside the tile
+                const int nblk = f0 + fl;
+                f32x16_t& a = acc[fb][tb];
                 if (nblk < p.rope_limit && t < p.T) {
-                    // q or k: turn each adjacent pair (r, r+1) by pos_axis *
-                    // theta; the angle is formed in fp64 in turns and reduced
-                    // to [-1/2, 1/2] before the hardware sine and cosine
+                    const int hp = ((nblk % p.D) >> 1) + 2 * hlf;
+                    const f32x4_t* cs = reinterpret_cast<const f32x4_t*>(p.rope_cs + t * (p.D >> 1) + hp);
+                    f32x4_t c[4];
 #pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        const int e = (nblk + 8 * (r >> 2) + 4 * hlf + (r & 3)) % p.D;
-                        const int axis = e < p.rope_f ? 0 : (e < p.rope_f + p.rope_r ? 1 : 2);
-                        const double turns = double(p.pos[3 * t + axis]) * p.theta_turns[e >> 1];
-                        const float f = float(turns - rint(turns));
-                        const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
-                        const float x0 = a[r], x1 = a[r + 1];
-                        a[r] = x0 * cs - x1 * sn;
-                        a[r + 1] = x0 * sn + x1 * cs;
-                    }
-                }
-            }
+                    for (int j = 0; j < 4; ++j) c[j] = cs[2 * j];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int f = fl + 8 * g + 4 * hlf;        // feature inside the tile
-                float v0 = a[4 * g], v1 = a[4 * g + 1], v2 = a[4 * g + 2], v3 = a[4 * g + 3];
-                if constexpr (MODE == kModeOut) {
-                    if (t < p.T && f0 + f < p.N) {
-                        const int64_t n0 = f0 + f;
-                        const u32x2_t xr = *reinterpret_cast<const u32x2_t*>(p.resid + t * int64_t(p.N) + n0);
-                        const u32x2_t gr = m >= 0 && m < p.n_rows
-                                               ? *reinterpret_cast<const u32x2_t*>(p.gate + m * int64_t(p.N) + n0)
-                                               : u32x2_t{0u, 0u};
-                        v0 = bf_lo(xr[0]) + bf_lo(gr[0]) * v0;
-                        v1 = bf_hi(xr[0]) + bf_hi(gr[0]) * v1;
-                        v2 = bf_lo(xr[1]) + bf_lo(gr[1]) * v2;
-                        v3 = bf_hi(xr[1]) + bf_hi(gr[1]) * v3;
-                    }
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int r = 4 * j + 2 * h;
+                            const float co = c[j][2 * h], sn = c[j][2 * h + 1];
+                            const float x0 = a[r], x1 = a[r + 1];
+                            a[r] = x0 * co - x1 * sn;
+                            a[r + 1] = x0 * sn + x1 * co;
+                        }
                 }
-                u32x2_t val;
-                val[0] = pack_bf16x2(v0, v1);
-                val[1] = pack_bf16x2(v2, v3);
-                const int slot = (f >> 3) ^ (tl & 31);
-                *reinterpret_cast<u32x2_t*>(smem + tl * 512 + 16 * slot + 8 * ((f >> 2) & 1)) = val;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int f = fl + 8 * g + 4 * hlf;        // feature inside the tile
+                    u32x2_t val;
+                    val[0] = pack_bf16x2(a[4 * g], a[4 * g + 1]);
+                    val[1] = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+                    const int slot = (f >> 3) ^ (tl & 31);
+                    *reinterpret_cast<u32x2_t*>(smem + tl * 512 + 16 * slot + 8 * ((f >> 2) & 1)) = val;
+                }
             }
         }
-    }
-    __syncthreads();
-    // rows 2 (i kGW + wave) + h, chunk l32: 32 lanes per 512-byte row segment
+        __syncthreads();
+        // rows 2 (i kGW + wave) + h, chunk l32: 32 lanes per 512-byte row segment
 #pragma unroll 4
-    for (int i = 0; i < kBT / (2 * kGW); ++i) {
-        const int tl = 2 * (i * kGW + wave) + hlf;
-        const int64_t t = t0 + tl;
-        const int n = f0 + 8 * l32;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + tl * 512 + 16 * (l32 ^ (tl & 31)));
-        if (t < p.T && n < p.N) st16(p.out + t * p.ld_out + n, v);
+        for (int i = 0; i < kBT / (2 * kGW); ++i) {
+            const int tl = 2 * (i * kGW + wave) + hlf;
+            const int64_t t = t0 + tl;
+            const int n = f0 + 8 * l32;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + tl * 512 + 16 * (l32 ^ (tl & 31)));
+            if (t < p.T && n < p.N) st16(p.out + t * p.ld_out + n, v);
+        }
+    } else {
+        // Rows i kGW + wave of each half, lane = 4 consecutive features.  The
+        // residual and gate values of the first half are loaded before the
+        // staging; each register is reloaded for the second half as soon as
+        // the first half has used it, so the load latency overlaps the work.
+        constexpr int kRows = 128 / kGW;
+        const int n = f0 + 4 * lane;
+        u32x2_t xr[kRows], gr[kRows];
+        int32_t mr[kRows];
+        // the rows' adaLN table entries first (one value per wavefront), so
+        // no residual or gate load waits behind another one's
+        // (loaded unconditionally at a clamped row, masked where used, so
+        // the loads are all in flight together)
+        auto load_mod = [&](int half) {
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                const int64_t t = t0 + 128 * half + i * kGW + wave;
+                mr[i] = p.mod_row[t < p.T ? t : p.T - 1];
+            }
+        };
+        auto load_rows = [&](int half, int i) {
+            const int64_t t = t0 + 128 * half + i * kGW + wave;
+            const int64_t m = t < p.T ? mr[i] : -1;
+            xr[i] = u32x2_t{0u, 0u};
+            gr[i] = u32x2_t{0u, 0u};
+            if (t < p.T && n < p.N) xr[i] = *reinterpret_cast<const u32x2_t*>(p.resid + t * int64_t(p.N) + n);
+            if (m >= 0 && m < p.n_rows && n < p.N)
+                gr[i] = *reinterpret_cast<const u32x2_t*>(p.gate + m * int64_t(p.N) + n);
+        };
+        load_mod(0);
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) load_rows(0, i);
+        load_mod(1);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (half == 1) __syncthreads();    // every wavefront is done reading the first half
+            if (wt == half) {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const int row = 32 * tb + l32;
+#pragma unroll
+                    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int c = 16 * wf + 8 * fb + 2 * g + hlf;   // 4-feature chunk of the row
+                            const f32x4_t v = {acc[fb][tb][4 * g], acc[fb][tb][4 * g + 1], acc[fb][tb][4 * g + 2],
+                                               acc[fb][tb][4 * g + 3]};
+                            *reinterpret_cast<f32x4_t*>(smem + row * 1024 + 16 * (c ^ (row & 15))) = v;
+                        }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                const int row = i * kGW + wave;
+                const int64_t t = t0 + 128 * half + row;
+                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(smem + row * 1024 + 16 * (lane ^ (row & 15)));
+                u32x2_t val;
+                val[0] = pack_bf16x2(bf_lo(xr[i][0]) + bf_lo(gr[i][0]) * v[0], bf_hi(xr[i][0]) + bf_hi(gr[i][0]) * v[1]);
+                val[1] = pack_bf16x2(bf_lo(xr[i][1]) + bf_lo(gr[i][1]) * v[2], bf_hi(xr[i][1]) + bf_hi(gr[i][1]) * v[3]);
+                if (t < p.T && n < p.N) *reinterpret_cast<u32x2_t*>(p.out + t * p.ld_out + n) = val;
+                if (half == 0) load_rows(1, i);
+            }
+        }
     }
 }
 
@@ -401,15 +492,18 @@ __global__ __launch_bounds__(kGT) void gemm_fixup_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 constexpr int kLnTokensPerBlock = 4;
 
+// The same wavefront also writes the token's row of the rotation table.
 template <int NCH>
 __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__ x, int64_t ld_x,
                                                     const uint16_t* __restrict__ shift,
                                                     const uint16_t* __restrict__ scale,
                                                     const int32_t* __restrict__ mod_row, int n_rows,
-                                                    uint16_t* __restrict__ u, int64_t T, int C, float eps) {
+                                                    uint16_t* __restrict__ u, int64_t T, int C, float eps,
+                                                    RopeTableParams rp) {
     const int lane = threadIdx.x & 63;
     const int64_t t = int64_t(blockIdx.x) * kLnTokensPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t >= T) return;
+    rope_table_row(rp, t, lane);
     const int nch = C >> 3;
     const uint32_t row_bytes = uint32_t(C) * 2u;
     const __amdgpu_buffer_rsrc_t x_rs = make_rsrc(x + t * ld_x, row_bytes);
@@ -453,23 +547,31 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t* __restrict__
     }
 }
 
+// The rotation table alone (no modulation pass to carry it): one wavefront
+// per token.
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeTableParams rp, int64_t T) {
+    const int64_t t = int64_t(blockIdx.x) * kLnTokensPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (t >= T) return;
+    rope_table_row(rp, t, threadIdx.x & 63);
+}
+
 template <int NCH>
-hipError_t launch_adaln_nch(const BlockQkvArgs& a, uint16_t* u, hipStream_t stream) {
+hipError_t launch_adaln_nch(const BlockQkvArgs& a, uint16_t* u, const RopeTableParams& rp, hipStream_t stream) {
     const int64_t blocks = (a.T + kLnTokensPerBlock - 1) / kLnTokensPerBlock;
     hipLaunchKernelGGL(adaln_kernel<NCH>, dim3(unsigned(blocks)), dim3(256), 0, stream, a.x, a.ld_x, a.shift,
-                       a.scale, a.mod_row, a.n_rows, u, a.T, a.H * a.D, a.eps);
+                       a.scale, a.mod_row, a.n_rows, u, a.T, a.H * a.D, a.eps, rp);
     return hipGetLastError();
 }
 
-hipError_t launch_adaln(const BlockQkvArgs& a, uint16_t* u, hipStream_t stream) {
+hipError_t launch_adaln(const BlockQkvArgs& a, uint16_t* u, const RopeTableParams& rp, hipStream_t stream) {
     const int per_lane = (a.H * a.D / 8 + kWave - 1) / kWave;
-    if (per_lane <= 1) return launch_adaln_nch<1>(a, u, stream);
-    if (per_lane <= 2) return launch_adaln_nch<2>(a, u, stream);
-    if (per_lane <= 4) return launch_adaln_nch<4>(a, u, stream);
-    if (per_lane <= 6) return launch_adaln_nch<6>(a, u, stream);
-    if (per_lane <= 8) return launch_adaln_nch<8>(a, u, stream);
-    if (per_lane <= 12) return launch_adaln_nch<12>(a, u, stream);
-    return launch_adaln_nch<16>(a, u, stream);
+    if (per_lane <= 1) return launch_adaln_nch<1>(a, u, rp, stream);
+    if (per_lane <= 2) return launch_adaln_nch<2>(a, u, rp, stream);
+    if (per_lane <= 4) return launch_adaln_nch<4>(a, u, rp, stream);
+    if (per_lane <= 6) return launch_adaln_nch<6>(a, u, rp, stream);
+    if (per_lane <= 8) return launch_adaln_nch<8>(a, u, rp, stream);
+    if (per_lane <= 12) return launch_adaln_nch<12>(a, u, rp, stream);
+    return launch_adaln_nch<16>(a, u, rp, stream);
 }
 
 // Whole tiles run in rounds of `cus` (one workgroup per CU); a last round
@@ -491,8 +593,10 @@ SplitPlan split_plan(int n_tiles, int nks, int cus) {
 
 int qkv_tiles(int64_t T, int C) { return ((3 * C + kBF - 1) / kBF) * int((T + kBT - 1) / kBT); }
 
-// Bytes of the modulated rows (256-byte aligned) and of the partial tiles.
+// Bytes of the modulated rows and of the rotation table (each 256-byte
+// aligned) and of the partial tiles.
 size_t qkv_rows_bytes(int64_t T, int C) { return (size_t(T) * size_t(C) * 2 + 255) & ~size_t(255); }
+size_t qkv_table_bytes(int64_t T, int D) { return (size_t(T) * size_t(D) * 4 + 255) & ~size_t(255); }
 size_t qkv_partial_bytes(int64_t T, int C, int cus) {
     const int tiles = qkv_tiles(T, C);
     const SplitPlan sp = split_plan(tiles, (C + kBK - 1) / kBK, cus);
@@ -527,24 +631,43 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
 
 }  // namespace
 
-size_t block_qkv_workspace_bytes(int64_t T, int32_t C) {
-    if (T <= 0 || C <= 0) return 0;
+size_t block_qkv_workspace_bytes(int64_t T, int32_t C, int32_t D) {
+    if (T <= 0 || C <= 0 || D <= 0) return 0;
     int cus = device_cu_count();
     if (cus <= 0) cus = 256;   // no device visible: size for an MI355X
-    return qkv_rows_bytes(T, C) + qkv_partial_bytes(T, C, cus);
+    return qkv_rows_bytes(T, C) + qkv_table_bytes(T, D) + qkv_partial_bytes(T, C, cus);
 }
 
 hipError_t launch_block_qkv(const BlockQkvArgs& args, hipStream_t stream) {
     if (args.T == 0) return hipSuccess;
     const int C = args.H * args.D;
+    unsigned char* ws = static_cast<unsigned char*>(args.workspace);
+    // workspace: modulated rows, rotation table, partial tiles of the split tail
+    RopeTableParams rp = {};
+    rp.cs = reinterpret_cast<f32x2_t*>(ws + qkv_rows_bytes(args.T, C));
+    rp.pos = args.pos;
+    rp.D = args.D;
+    rp.rope_f = args.rope_f;
+    rp.rope_r = args.rope_r;
+    const int dims[3] = {args.rope_f, args.rope_r, args.rope_c};
+    int pair = 0;
+    for (int ax = 0; ax < 3; ++ax)
+        for (int j = 0; j < dims[ax] / 2; ++j)
+            rp.theta_turns[pair++] = std::pow(double(args.rope_base), -2.0 * j / double(dims[ax])) *
+                                     0.15915494309189535;   // radians -> turns (1 / 2 pi)
     const uint16_t* act = args.x;
     int64_t ld_act = args.ld_x;
     if (args.shift != nullptr) {
-        uint16_t* u = static_cast<uint16_t*>(args.workspace);   // the modulated rows
-        const hipError_t e = launch_adaln(args, u, stream);
+        uint16_t* u = reinterpret_cast<uint16_t*>(ws);   // the modulated rows
+        const hipError_t e = launch_adaln(args, u, rp, stream);
         if (e != hipSuccess) return e;
         act = u;
         ld_act = C;
+    } else {
+        const int64_t blocks = (args.T + kLnTokensPerBlock - 1) / kLnTokensPerBlock;
+        hipLaunchKernelGGL(rope_table_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, rp, args.T);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     GemmParams p = {};
     p.w = args.w;
@@ -557,17 +680,8 @@ hipError_t launch_block_qkv(const BlockQkvArgs& args, hipStream_t stream) {
     p.ld_out = args.ld_qkv;
     p.rope_limit = 2 * C;
     p.D = args.D;
-    p.rope_f = args.rope_f;
-    p.rope_r = args.rope_r;
-    p.pos = args.pos;
-    // the split tail's partial tiles follow the modulated rows
-    p.partial = reinterpret_cast<float*>(static_cast<unsigned char*>(args.workspace) + qkv_rows_bytes(args.T, C));
-    const int dims[3] = {args.rope_f, args.rope_r, args.rope_c};
-    int pair = 0;
-    for (int ax = 0; ax < 3; ++ax)
-        for (int j = 0; j < dims[ax] / 2; ++j)
-            p.theta_turns[pair++] = std::pow(double(args.rope_base), -2.0 * j / double(dims[ax])) *
-                                    0.15915494309189535;   // radians -> turns (1 / 2 pi)
+    p.rope_cs = rp.cs;
+    p.partial = reinterpret_cast<float*>(ws + qkv_rows_bytes(args.T, C) + qkv_table_bytes(args.T, args.D));
     return launch_gemm<kModeQkv>(p, stream);
 }
 

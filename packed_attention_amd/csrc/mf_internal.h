@@ -167,10 +167,9 @@ struct BlockQkvArgs {
     int32_t H, D;
     int32_t rope_f, rope_r, rope_c;
     float rope_base, eps;
-    void* workspace;          // the modulated rows, bf16 [T][C]
-    double theta_turns[64];   // filled by the launcher, as for the forward
+    void* workspace;          // modulated rows bf16 [T][C], rotation table fp32 [T][D/2][2], partial tiles
 };
-size_t block_qkv_workspace_bytes(int64_t T, int32_t C);
+size_t block_qkv_workspace_bytes(int64_t T, int32_t C, int32_t D);
 hipError_t launch_block_qkv(const BlockQkvArgs& a, hipStream_t stream);
 
 struct BlockOutArgs {

@@ -21,8 +21,9 @@ size_t attn_workspace_bytes(int32_t n_seq, int64_t, int32_t, int32_t) {
 size_t attn_bwd_workspace_bytes(int32_t n_seq, int64_t T, int32_t, int32_t) {
     return 4096 + 16 * size_t(n_seq > 0 ? n_seq : 0) + size_t(T > 0 && T < (1 << 20) ? T : 0);
 }
-size_t block_qkv_workspace_bytes(int64_t T, int32_t C) {
-    return T > 0 && C > 0 && T < (1 << 20) && C < (1 << 16) ? size_t(T) * size_t(C) * 2 : 256;
+size_t block_qkv_workspace_bytes(int64_t T, int32_t C, int32_t D) {
+    return T > 0 && C > 0 && T < (1 << 20) && C < (1 << 16) ? size_t(T) * size_t(C) * 2 + size_t(T) * size_t(D > 0 ? D : 0) * 4
+                                                             : 256;
 }
 size_t causal_attn_workspace_bytes(int32_t n_seq, int64_t) { return 256 + 16 * size_t(n_seq > 0 ? n_seq : 0); }
 size_t elementwise_bwd_workspace_bytes(int64_t T, int32_t C, int32_t n) {
