@@ -23,20 +23,23 @@
 //  * the per-row sums over tokens (dshift, dscale; dgate, dshift2,
 //    dscale2): one lane per 8-channel chunk walks a run of kSumRun tokens,
 //    reads the rows again and recomputes the fp32 gradients from them and
-//    the statistics, so the sums see the same fp32 values as the outputs;
-//  * slot_reduce_kernel: each run leaves its sums in its own slot of the
-//    caller's workspace, tagged with its adaLN row, and the reduction walks
-//    the slots in order, one thread per channel and group of slots, adding
-//    each run of equal tags to the output row with one fp32 atomic add.  A
-//    row change inside a run adds the finished sums with atomics too.  Each
-//    output row is touched by a handful of atomic adds instead of one per
-//    token, so a pack whose tokens all share one row does not serialise on
-//    it; the order of those additions varies between calls (the row sums
-//    are not bitwise reproducible; every per-token output is).
+//    the statistics, so the sums see the same fp32 values as the outputs.
+//    A run's tokens in order split into segments of equal adaLN row; each
+//    segment's sums are one entry (row tag + NA x C fp32) at the run's next
+//    entry position (run r owns positions r R .. r R + R - 1);
+//  * a segmented reduction over the entries in token order: each level
+//    adds the entries of kFanIn consecutive groups of the level below,
+//    merging neighbours of equal row, and writes the merged entries
+//    compactly at the start of its own range; the last level (at most
+//    kRootFan groups below it) adds its entries to the zeroed output rows.
+//    One thread per channel and each level a launch of its own, so every
+//    row sum is added in one fixed order: the row sums are bitwise
+//    reproducible, as every per-token output is.  A row whose tokens are not
+//    contiguous gets one entry per stretch, added in token order.
 // Modulate + RoPE rows of more than 3072 channels keep a single kernel: a
 // workgroup walks a run of kRun tokens one row at a time (thread per chunk,
-// statistics by workgroup reductions), keeps the sums of its current adaLN
-// row in registers and writes them to its slot at the end of the run.
+// statistics by workgroup reductions) and writes its segment entries the
+// same way.
 #include <cmath>
 
 #include "mf_device.h"
@@ -45,10 +48,11 @@
 namespace mf {
 namespace {
 
-constexpr int kRun = 4;          // tokens per workgroup
-constexpr int kSlotGroup = 8;    // slots summed per thread of the reduction kernel
-
-__device__ __forceinline__ void atomic_add_f32(float* p, float v) { unsafeAtomicAdd(p, v); }
+constexpr int kRun = 4;          // tokens per workgroup (wide rows)
+constexpr int kFanIn = 16;       // groups merged per reduction level
+constexpr int kRootFan = 128;    // at most this many groups below the last level
+constexpr int kMaxLevels = 6;     // 128 x 16^5 runs
+constexpr int kRedThreads = 256; // channels per reduction workgroup
 
 // Zeros n floats at each of up to three arrays (blockIdx.y picks the array;
 // nullptr entries are skipped), one launch for all of a call's row sums.
@@ -87,76 +91,334 @@ __device__ __forceinline__ void wg_sum(float (&v)[N], float* red, int buf) {
     }
 }
 
-// Slot layout of the workspace: tags [n_slots] (int32, 256-aligned block),
-// then n_slots x NA x C floats.
-__host__ __device__ constexpr size_t slot_tags_bytes(int64_t n_slots) {
-    return (size_t(n_slots) * 4 + 255) / 256 * 256;
-}
-__host__ __device__ constexpr int64_t n_slots_for(int64_t T) { return (T + kRun - 1) / kRun; }
+// ---------------------------------------------------------------------------
+// Row sums: segment entries and their reduction
+// ---------------------------------------------------------------------------
+// Workspace of one call, each part 256-byte aligned:
+//   tag0 int32 [P], cnt0 int32 [n_runs]: the runs' entries (P = n_runs R);
+//   tags int32 [2][n_cb][P]: entry rows of the levels (odd / even levels);
+//   cnts int32 [n_cb][n_cnt]: entries per group of each level;
+//   vals fp32 [P][NA][C]: the entries' sums, reduced in place level by level;
+//   stats fp32 [T][4]: the per-token statistics of the two-kernel forms.
+struct SegLayout {
+    int64_t n_runs = 0, P = 0, n_cnt = 0;
+    int R = 0, NA = 0, C = 0, n_cb = 0, n_levels = 0;
+    int64_t groups[kMaxLevels + 1] = {};   // groups of level k (k = 0: the runs)
+    int64_t span[kMaxLevels + 1] = {};     // runs per group of level k
+    int64_t cnt_off[kMaxLevels + 1] = {};  // level k's counts in cnts
+    size_t off_tag0 = 0, off_cnt0 = 0, off_tags = 0, off_cnts = 0, off_vals = 0, off_stats = 0, total = 0;
+};
 
-// Add the workspace slots to the outputs, one thread per (channel, group of
-// kSlotGroup consecutive slots): runs of equal tags are summed in order and
-// added to their row with one atomic add each.
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+SegLayout seg_layout(int64_t T, int C, int NA, int R) {
+    SegLayout L;
+    L.R = R;
+    L.NA = NA;
+    L.C = C;
+    L.n_runs = (T + R - 1) / R;
+    L.P = L.n_runs * R;
+    L.n_cb = (C + kRedThreads - 1) / kRedThreads;
+    L.groups[0] = L.n_runs;
+    L.span[0] = 1;
+    int k = 0;
+    // levels of kFanIn until at most kRootFan groups remain, then the root
+    while (L.groups[k] > kRootFan && k + 1 < kMaxLevels) {
+        ++k;
+        L.groups[k] = (L.groups[k - 1] + kFanIn - 1) / kFanIn;
+        L.span[k] = L.span[k - 1] * kFanIn;
+        L.cnt_off[k] = L.n_cnt;
+        L.n_cnt += L.groups[k];
+    }
+    ++k;
+    L.groups[k] = L.n_runs > 0 ? 1 : 0;
+    L.span[k] = L.n_runs;
+    L.n_levels = k;
+    size_t b = 0;
+    L.off_tag0 = b;  b += align256(size_t(L.P) * 4);
+    L.off_cnt0 = b;  b += align256(size_t(L.n_runs) * 4);
+    L.off_tags = b;  b += align256(size_t(2) * L.n_cb * L.P * 4);
+    L.off_cnts = b;  b += align256(size_t(L.n_cb) * size_t(L.n_cnt > 0 ? L.n_cnt : 1) * 4);
+    L.off_vals = b;  b += align256(size_t(L.P) * NA * C * 4);
+    L.off_stats = b; b += align256(size_t(T) * 16);
+    L.total = b;
+    return L;
+}
+
+struct SegArgs {
+    const int32_t* tag0;
+    const int32_t* cnt0;
+    int32_t* tags;
+    int32_t* cnts;
+    float* vals;
+    float* out[3];
+    int64_t P;
+    int n_cnt, R, C, n_cb, n_levels, n_rows;
+    int32_t groups[kMaxLevels + 1];
+    int32_t span[kMaxLevels + 1];
+    int32_t cnt_off[kMaxLevels + 1];
+};
+
+SegArgs seg_args(const SegLayout& L, void* ws, int n_rows, float* o0, float* o1, float* o2) {
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    SegArgs a = {};
+    a.tag0 = reinterpret_cast<const int32_t*>(w + L.off_tag0);
+    a.cnt0 = reinterpret_cast<const int32_t*>(w + L.off_cnt0);
+    a.tags = reinterpret_cast<int32_t*>(w + L.off_tags);
+    a.cnts = reinterpret_cast<int32_t*>(w + L.off_cnts);
+    a.vals = reinterpret_cast<float*>(w + L.off_vals);
+    a.out[0] = o0;
+    a.out[1] = o1;
+    a.out[2] = o2;
+    a.P = L.P;
+    a.R = L.R;
+    a.C = L.C;
+    a.n_cb = L.n_cb;
+    a.n_levels = L.n_levels;
+    a.n_rows = n_rows;
+    a.n_cnt = int(L.n_cnt);
+    for (int k = 0; k <= kMaxLevels; ++k) {
+        a.groups[k] = int32_t(L.groups[k]);
+        a.span[k] = int32_t(L.span[k]);
+        a.cnt_off[k] = int32_t(L.cnt_off[k]);
+    }
+    return a;
+}
+
+// Level k of the reduction, one launch per level: workgroup (g, cb) merges,
+// in order, the entries of the groups of level k - 1 below group g (level 0:
+// the runs), channels [256 cb, 256 cb + 256).  Neighbouring entries of equal
+// row are added; the merged entries go compactly to the start of group g's
+// range (in place: each thread reads and writes only its own channel, and an
+// entry is written only after every entry before it has been read), or, at
+// the last level, are added to the output rows (zeroed by the kernel that
+// wrote the runs' entries), which only this thread writes for its channel.
+// A child's first entry sits at the start of its range whatever its count,
+// so the children are taken kB at a time: one round of loads brings child
+// j's count and first row to lane j of every wavefront (read back as scalars
+// with readlane) and every thread's values of the children's first entries;
+// further entries of a child (a row change inside it) are loaded one by one.
 template <int NA>
-__global__ __launch_bounds__(256) void slot_reduce_kernel(const int32_t* __restrict__ tags,
-                                                          const float* __restrict__ slots, int64_t n_slots,
-                                                          int C, float* o0, float* o1, float* o2) {
-    const int c = blockIdx.y * 256 + threadIdx.x;
-    if (c >= C) return;
-    float* const outs[3] = {o0, o1, o2};
-    const int64_t s0 = int64_t(blockIdx.x) * kSlotGroup;
-    const int64_t s1 = s0 + kSlotGroup < n_slots ? s0 + kSlotGroup : n_slots;
-    int cur = -1;
+constexpr int batch_children() { return NA >= 3 ? 16 : NA == 2 ? 32 : 64; }
+
+template <int NA>
+__global__ __launch_bounds__(kRedThreads) void seg_level_kernel(SegArgs a, int k) {
+    constexpr int kB = batch_children<NA>();   // children per round of loads
+    static_assert(kB <= kWave, "one child per lane");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int cb = blockIdx.y;
+    const int c = cb * kRedThreads + tid;
+    const bool live = c < a.C;
+    const int cc = live ? c : a.C - 1;     // the channel the loads use
+    const int64_t g = blockIdx.x;
+    const bool top = k == a.n_levels;
+    const int fan = top ? int(a.groups[k - 1]) : kFanIn;
+    const int64_t ch0 = g * fan;
+    const int n_ch = int((ch0 + fan < a.groups[k - 1] ? ch0 + fan : a.groups[k - 1]) - ch0);
+    const int64_t child_span = int64_t(a.span[k - 1]) * a.R;   // positions per child
+    const int64_t out_base = g * int64_t(a.span[k]) * a.R;
+    const int32_t* in_tags = k == 1 ? a.tag0 : a.tags + ((k - 1) & 1) * int64_t(a.n_cb) * a.P + cb * a.P;
+    int32_t* out_tags = a.tags + (k & 1) * int64_t(a.n_cb) * a.P + cb * a.P;
+    const int32_t* in_cnt = k == 1 ? a.cnt0 : a.cnts + int64_t(cb) * a.n_cnt + a.cnt_off[k - 1];
     float acc[NA];
 #pragma unroll
-    for (int a = 0; a < NA; ++a) acc[a] = 0.f;
-    for (int64_t s = s0; s < s1; ++s) {
-        const int tag = tags[s];
-        if (tag < 0) continue;
-        if (tag != cur) {
-            if (cur >= 0)
+    for (int x = 0; x < NA; ++x) acc[x] = 0.f;
+    int cur = -1;
+    int nout = 0;
+    auto emit = [&]() {
+        if (top) {
+            if (live)
 #pragma unroll
-                for (int a = 0; a < NA; ++a) atomic_add_f32(outs[a] + int64_t(cur) * C + c, acc[a]);
+                for (int x = 0; x < NA; ++x) a.out[x][int64_t(cur) * a.C + c] += acc[x];
+        } else {
+            const int64_t pos = out_base + nout;
+            if (live)
+#pragma unroll
+                for (int x = 0; x < NA; ++x) a.vals[(pos * NA + x) * a.C + c] = acc[x];
+            if (tid == 0) out_tags[pos] = cur;
+        }
+        ++nout;
+    };
+    auto merge = [&](int tag, const float (&v)[NA]) {
+        if (tag != cur) {
+            if (cur >= 0) emit();
             cur = tag;
 #pragma unroll
-            for (int a = 0; a < NA; ++a) acc[a] = 0.f;
+            for (int x = 0; x < NA; ++x) acc[x] = 0.f;
         }
 #pragma unroll
-        for (int a = 0; a < NA; ++a) acc[a] += slots[(s * NA + a) * C + c];
-    }
-    if (cur >= 0)
+        for (int x = 0; x < NA; ++x) acc[x] += v[x];
+    };
+    for (int b0 = 0; b0 < n_ch; b0 += kB) {
+        const int nb = n_ch - b0 < kB ? n_ch - b0 : kB;
+        int my_cnt = 0, my_tag = -1;
+        if (lane < nb) {
+            const int64_t ch = ch0 + b0 + lane;
+            my_cnt = in_cnt[ch];
+            my_tag = in_tags[ch * child_span];
+        }
+        // unconditional loads (a clamped child and channel past the ends;
+        // those values go unused), so the batch is one round of loads
+        float v[kB][NA];
 #pragma unroll
-        for (int a = 0; a < NA; ++a) atomic_add_f32(outs[a] + int64_t(cur) * C + c, acc[a]);
+        for (int j = 0; j < kB; ++j) {
+            const int64_t ch = ch0 + b0 + (j < nb ? j : nb - 1);
+#pragma unroll
+            for (int x = 0; x < NA; ++x) v[j][x] = a.vals[(ch * child_span * NA + x) * a.C + cc];
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int n = __builtin_amdgcn_readlane(my_cnt, j);   // 0 past the batch
+            if (n > 0) merge(__builtin_amdgcn_readlane(my_tag, j), v[j]);
+            for (int i = 1; i < n; ++i) {
+                const int64_t pos = (ch0 + b0 + j) * child_span + i;
+                float w[NA];
+#pragma unroll
+                for (int x = 0; x < NA; ++x) w[x] = a.vals[(pos * NA + x) * a.C + cc];
+                merge(in_tags[pos], w);
+            }
+        }
+    }
+    if (cur >= 0) emit();
+    if (!top && tid == 0) a.cnts[int64_t(cb) * a.n_cnt + a.cnt_off[k] + g] = nout;
 }
 
-// Finished row sums of this thread's 8 channels: to the output with
-// atomics (row change inside a run) or to the workgroup's slot (end of run).
 template <int NA>
-__device__ __forceinline__ void rows_to_output(float (&p)[NA][8], float* const (&outs)[NA], int row, int C, int c0) {
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            atomic_add_f32(outs[a] + int64_t(row) * C + c0 + j, p[a][j]);
-            p[a][j] = 0.f;
-        }
-}
-template <int NA>
-__device__ __forceinline__ void rows_to_slot(const float (&p)[NA][8], float* slot, int C, int c0) {
-#pragma unroll
-    for (int a = 0; a < NA; ++a) {
-        f32x4_t lo = {p[a][0], p[a][1], p[a][2], p[a][3]};
-        f32x4_t hi = {p[a][4], p[a][5], p[a][6], p[a][7]};
-        *reinterpret_cast<f32x4_t*>(slot + int64_t(a) * C + c0) = lo;
-        *reinterpret_cast<f32x4_t*>(slot + int64_t(a) * C + c0 + 4) = hi;
+hipError_t reduce_segments(const SegLayout& L, void* ws, int n_rows, float* o0, float* o1, float* o2,
+                           hipStream_t stream) {
+    // the last level stages at most kRootFan children (reached for any T
+    // below 128 x 16^5 runs)
+    if (L.groups[L.n_levels - 1] > kRootFan) return hipErrorInvalidValue;
+    const SegArgs args = seg_args(L, ws, n_rows, o0, o1, o2);
+    for (int k = 1; k <= L.n_levels; ++k) {
+        hipLaunchKernelGGL(seg_level_kernel<NA>, dim3(unsigned(L.groups[k]), unsigned(L.n_cb)), dim3(kRedThreads), 0,
+                           stream, args, k);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+// Where a run writes its entries: run r's entry i at position r R + i.
+// The same kernel zeroes the output rows (the reduction's last level adds
+// into them), spread over all its threads.
+struct SegLeaf {
+    int32_t* tag0;
+    int32_t* cnt0;
+    float* vals;
+    float* out[3];
+    int64_t n_out;      // floats per output array (n_rows x C)
+};
+
+SegLeaf seg_leaf(const SegLayout& L, void* ws, int n_rows, float* o0, float* o1, float* o2) {
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    return SegLeaf{reinterpret_cast<int32_t*>(w + L.off_tag0), reinterpret_cast<int32_t*>(w + L.off_cnt0),
+                   reinterpret_cast<float*>(w + L.off_vals), {o0, o1, o2}, int64_t(n_rows) * L.C};
+}
+
+__device__ __forceinline__ void zero_outputs(const SegLeaf& leaf) {
+    const int64_t nthreads = int64_t(gridDim.x) * gridDim.y * blockDim.x;
+    const int64_t i0 = (int64_t(blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    for (int x = 0; x < 3; ++x)
+        if (leaf.out[x] != nullptr)
+            for (int64_t i = i0; i < leaf.n_out; i += nthreads) leaf.out[x][i] = 0.f;
+}
+
+// One segment's sums (8 channels of NA arrays) to the run's next entry.
+template <int NA>
+__device__ __forceinline__ void put_entry(float (&p)[NA][8], float* vals, int64_t pos, int C, int c0, bool live) {
+    if (live)
+#pragma unroll
+        for (int x = 0; x < NA; ++x) {
+            float* v = vals + (pos * NA + x) * C + c0;
+            *reinterpret_cast<f32x4_t*>(v) = f32x4_t{p[x][0], p[x][1], p[x][2], p[x][3]};
+            *reinterpret_cast<f32x4_t*>(v + 4) = f32x4_t{p[x][4], p[x][5], p[x][6], p[x][7]};
+        }
+#pragma unroll
+    for (int x = 0; x < NA; ++x)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[x][j] = 0.f;
+}
+
+// The two-kernel forms' sums workgroups take kRunsPerBlock runs of kSumRun
+// tokens, one wavefront each, and merge them before they finish: each
+// wavefront writes its run's entries (positions of its run) and their rows
+// to LDS, then one thread per channel adds the workgroup's entries in token
+// order and writes the merged entries compactly at the workgroup's range
+// (kLeafSpan positions), so the reduction starts from one group per
+// kLeafSpan tokens.  The first entry of every run is loaded in one round;
+// further entries of a run (a row change inside it) one by one.  Lane w
+// holds run w's count and first row, read back as scalars.
+constexpr int kSumRun = 8;                            // tokens per sums wavefront
+constexpr int kRunsPerBlock = 16;                     // wavefronts per sums workgroup
+constexpr int kLeafSpan = kSumRun * kRunsPerBlock;    // positions (tokens) per sums workgroup
+constexpr int kSumChannels = kWave * 8;               // channels per sums workgroup
+
+template <int NA>
+__device__ __forceinline__ void merge_block_runs(const SegLeaf& leaf, const int* s_cnt,
+                                                 const int (*s_tag)[kSumRun], int C) {
+    const int t = threadIdx.x;
+    const int ch = blockIdx.y * kSumChannels + t;
+    const bool live = t < kSumChannels && ch < C;
+    const int cc = live ? ch : C - 1;      // the channel the loads use
+    const int64_t base = int64_t(blockIdx.x) * kLeafSpan;
+    // unconditional loads of every run's first entry (values of runs without
+    // entries go unused), so they are one round of loads
+    float v[kRunsPerBlock][NA];
+#pragma unroll
+    for (int w = 0; w < kRunsPerBlock; ++w)
+#pragma unroll
+        for (int x = 0; x < NA; ++x) v[w][x] = leaf.vals[((base + w * kSumRun) * NA + x) * C + cc];
+    float acc[NA];
+#pragma unroll
+    for (int x = 0; x < NA; ++x) acc[x] = 0.f;
+    int cur = -1;
+    int nout = 0;
+    auto emit = [&]() {
+        const int64_t pos = base + nout;
+        if (live)
+#pragma unroll
+            for (int x = 0; x < NA; ++x) leaf.vals[(pos * NA + x) * C + ch] = acc[x];
+        if (blockIdx.y == 0 && t == 0) leaf.tag0[pos] = cur;
+        ++nout;
+    };
+    auto merge = [&](int tag, const float (&w)[NA]) {
+        if (tag != cur) {
+            if (cur >= 0) emit();
+            cur = tag;
+#pragma unroll
+            for (int x = 0; x < NA; ++x) acc[x] = 0.f;
+        }
+#pragma unroll
+        for (int x = 0; x < NA; ++x) acc[x] += w[x];
+    };
+    // run w's count and first row in lane w, read back as scalars
+    const int lane = t & 63;
+    const int my_cnt = lane < kRunsPerBlock ? s_cnt[lane] : 0;
+    const int my_tag = lane < kRunsPerBlock ? s_tag[lane][0] : -1;
+#pragma unroll
+    for (int w = 0; w < kRunsPerBlock; ++w) {
+        const int n = __builtin_amdgcn_readlane(my_cnt, w);
+        if (n > 0) merge(__builtin_amdgcn_readlane(my_tag, w), v[w]);
+        for (int i = 1; i < n; ++i) {
+            const int64_t pos = base + w * kSumRun + i;
+            float u[NA];
+#pragma unroll
+            for (int x = 0; x < NA; ++x) u[x] = leaf.vals[(pos * NA + x) * C + cc];
+            merge(s_tag[w][i], u);
+        }
+    }
+    if (cur >= 0) emit();
+    if (blockIdx.y == 0 && t == 0) leaf.cnt0[blockIdx.x] = nout;
 }
 
 // ---------------------------------------------------------------------------
 // modulate + RoPE backward
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs a) {
+__global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs a, SegLeaf leaf) {
     __shared__ float red[2 * 4 * 16];
+    if (a.scale != nullptr) zero_outputs(leaf);   // RoPE only: no row sums
     const int C = a.H * a.D;
     const int ci = threadIdx.x;                 // this thread's chunk
     const bool live = ci < (C >> 3);
@@ -170,11 +432,24 @@ __global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs 
     for (int j = 0; j < 4; ++j) th[j] = a.theta_turns[e0 / 2 + j];
     const int64_t t_begin = int64_t(blockIdx.x) * kRun;
     const int64_t t_end = t_begin + kRun < a.T ? t_begin + kRun : a.T;
-    float* const outs[2] = {a.dshift, a.dscale};
     float part[2][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) part[0][j] = part[1][j] = 0.f;
     int cur = -1;
+    int n_ent = 0;
+    // the finished segment of row `row` becomes the run's next entry (a row
+    // outside the table adds nothing)
+    auto flush = [&](int row) {
+        if (row >= 0 && row < a.n_rows) {
+            const int64_t pos = int64_t(blockIdx.x) * kRun + n_ent;
+            put_entry<2>(part, leaf.vals, pos, C, c0, live);
+            if (threadIdx.x == 0) leaf.tag0[pos] = row;
+            ++n_ent;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) part[0][j] = part[1][j] = 0.f;
+        }
+    };
     int buf = 0;
 
     // rows of token t: output gradients of q and k, then q and k
@@ -224,7 +499,7 @@ __global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs 
         const int m = a.mod_row[t];
         const bool mok = m >= 0 && m < a.n_rows;      // a row outside the table reads zeros, adds nothing
         if (m != cur) {
-            if (cur >= 0 && cur < a.n_rows && live) rows_to_output<2>(part, outs, cur, C, c0);
+            flush(cur);
             cur = m;
         }
         float x[2][8];
@@ -282,12 +557,8 @@ __global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs 
         }
     }
     if (mod) {
-        int32_t* tags = static_cast<int32_t*>(a.workspace);
-        float* slot = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) +
-                                               slot_tags_bytes(n_slots_for(a.T))) +
-                      int64_t(blockIdx.x) * 2 * C;
-        if (live) rows_to_slot<2>(part, slot, C, c0);
-        if (threadIdx.x == 0) tags[blockIdx.x] = cur < a.n_rows ? cur : -1;   // -1: nothing to add
+        flush(cur);
+        if (threadIdx.x == 0) leaf.cnt0[blockIdx.x] = n_ent;
     }
 }
 
@@ -301,14 +572,12 @@ __global__ __launch_bounds__(1024) void modulate_rope_bwd_kernel(ModRopeBwdArgs 
 // reductions inside the wavefront.  It writes dq, dk and each row's mean and
 // 1/sigma (fp32).  Kernel B, the per-row sums: lane = one 8-channel chunk of
 // a run of kSumRun tokens; it reads the rows again, turns dq', dk' back and
-// normalises q, k with kernel A's statistics, and writes one tagged slot
-// per run (a row change inside a run adds the finished sums with atomics, as
-// above); slot_reduce_kernel then adds the slots.  Reading the four rows
-// twice costs less than keeping 2 x 8 fp32 sums per chunk in every
-// wavefront, which does not fit two wavefronts per SIMD at C = 3072.
+// normalises q, k with kernel A's statistics, and writes one entry per
+// segment of equal adaLN row in the run; the segmented reduction then adds
+// the entries.  Reading the four rows twice costs less than keeping 2 x 8
+// fp32 sums per chunk in every wavefront, which does not fit two wavefronts
+// per SIMD at C = 3072.
 constexpr int kRowsTokens = 2;    // tokens per kernel-A workgroup
-constexpr int kSumRun = 8;        // tokens per kernel-B slot
-__host__ __device__ constexpr int64_t sum_slots_for(int64_t T) { return (T + kSumRun - 1) / kSumRun; }
 
 template <int NCH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH >= 6 ? 3 : 4))) void modrope_bwd_dx_kernel(
@@ -428,11 +697,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NCH >= 6 ? 
     if (lane == 0) *reinterpret_cast<float2*>(stats + 4 * t + 2 * (is_k ? 1 : 0)) = float2{mu, rs};
 }
 
-// Kernel B: blockIdx.x = run of kSumRun tokens, blockIdx.y = group of 64
-// chunks; lane = one chunk (in-head offset 8l mod D, as in kernel A).
-__global__ __launch_bounds__(64) void modrope_bwd_sums_kernel(ModRopeBwdArgs a, const float* __restrict__ stats,
-                                                              int32_t* __restrict__ tags, float* __restrict__ slots) {
-    const int lane = threadIdx.x;
+// Kernel B: blockIdx.x = kRunsPerBlock runs of kSumRun tokens (one per
+// wavefront), blockIdx.y = group of 64 chunks; lane = one chunk (in-head
+// offset 8l mod D, as in kernel A).
+__global__ __launch_bounds__(kWave * kRunsPerBlock) void modrope_bwd_sums_kernel(ModRopeBwdArgs a,
+                                                                                const float* __restrict__ stats,
+                                                                                SegLeaf leaf) {
+    __shared__ int s_cnt[kRunsPerBlock];
+    __shared__ int s_tag[kRunsPerBlock][kSumRun];
+    zero_outputs(leaf);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t run = int64_t(blockIdx.x) * kRunsPerBlock + wave;
     const int C = a.H * a.D;
     const int nch = C >> 3;
     const int c = blockIdx.y * kWave + lane;
@@ -444,20 +720,21 @@ __global__ __launch_bounds__(64) void modrope_bwd_sums_kernel(ModRopeBwdArgs a, 
     double th[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) th[j] = a.theta_turns[e0 / 2 + j];
-    const int64_t t_begin = int64_t(blockIdx.x) * kSumRun;
+    const int64_t t_begin = run * kSumRun;
     const int64_t t_end = t_begin + kSumRun < a.T ? t_begin + kSumRun : a.T;
-    float s0[8], s1[8];
+    float sm[2][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s0[j] = s1[j] = 0.f;
+    for (int j = 0; j < 8; ++j) sm[0][j] = sm[1][j] = 0.f;
     int cur = -1;
+    int n_ent = 0;
+    // the finished segment of row `row` becomes the run's next entry (rows
+    // outside the table accumulate nothing)
     auto flush = [&](int row) {
-        if (row < 0 || row >= a.n_rows || !live) return;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            atomic_add_f32(a.dshift + int64_t(row) * C + 8 * c + j, s0[j]);
-            atomic_add_f32(a.dscale + int64_t(row) * C + 8 * c + j, s1[j]);
-            s0[j] = s1[j] = 0.f;
-        }
+        if (row < 0 || row >= a.n_rows) return;
+        const int64_t pos = run * kSumRun + n_ent;
+        put_entry<2>(sm, leaf.vals, pos, C, 8 * c, live);
+        if (lane == 0) s_tag[wave][n_ent] = row;
+        ++n_ent;
     };
     for (int64_t t = t_begin; t < t_end; ++t) {
         const int m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
@@ -482,33 +759,19 @@ __global__ __launch_bounds__(64) void modrope_bwd_sums_kernel(ModRopeBwdArgs a, 
             const float gk0 = k0 * cs + k1 * sn, gk1 = -k0 * sn + k1 * cs;
             const float hq0 = (bf_lo(xq[j]) - st[0]) * st[1], hq1 = (bf_hi(xq[j]) - st[0]) * st[1];
             const float hk0 = (bf_lo(xk[j]) - st[2]) * st[3], hk1 = (bf_hi(xk[j]) - st[2]) * st[3];
-            s0[2 * j] += gq0 + gk0;
-            s0[2 * j + 1] += gq1 + gk1;
-            s1[2 * j] += gq0 * hq0 + gk0 * hk0;
-            s1[2 * j + 1] += gq1 * hq1 + gk1 * hk1;
+            sm[0][2 * j] += gq0 + gk0;
+            sm[0][2 * j + 1] += gq1 + gk1;
+            sm[1][2 * j] += gq0 * hq0 + gk0 * hk0;
+            sm[1][2 * j + 1] += gq1 * hq1 + gk1 * hk1;
         }
     }
-    float* slot = slots + int64_t(blockIdx.x) * 2 * C;
-    if (live) {
-        *reinterpret_cast<f32x4_t*>(slot + 8 * c) = f32x4_t{s0[0], s0[1], s0[2], s0[3]};
-        *reinterpret_cast<f32x4_t*>(slot + 8 * c + 4) = f32x4_t{s0[4], s0[5], s0[6], s0[7]};
-        *reinterpret_cast<f32x4_t*>(slot + C + 8 * c) = f32x4_t{s1[0], s1[1], s1[2], s1[3]};
-        *reinterpret_cast<f32x4_t*>(slot + C + 8 * c + 4) = f32x4_t{s1[4], s1[5], s1[6], s1[7]};
-    }
-    if (blockIdx.y == 0 && lane == 0) tags[blockIdx.x] = cur >= 0 && cur < a.n_rows ? cur : -1;
+    flush(cur);
+    if (lane == 0) s_cnt[wave] = n_ent;
+    __syncthreads();   // the runs' entries are written (workgroup scope) and their rows are in LDS
+    merge_block_runs<2>(leaf, s_cnt, s_tag, C);
 }
 
 int block_threads(int C) { return ((C / 8 + 63) / 64) * 64; }
-
-template <int NA>
-hipError_t reduce_slots(void* ws, int64_t T, int C, float* o0, float* o1, float* o2, hipStream_t stream) {
-    const int64_t ns = n_slots_for(T);
-    const int32_t* tags = static_cast<const int32_t*>(ws);
-    const float* slots = reinterpret_cast<const float*>(static_cast<const unsigned char*>(ws) + slot_tags_bytes(ns));
-    dim3 grid(unsigned((ns + kSlotGroup - 1) / kSlotGroup), unsigned((C + 255) / 256));
-    hipLaunchKernelGGL(slot_reduce_kernel<NA>, grid, dim3(256), 0, stream, tags, slots, ns, C, o0, o1, o2);
-    return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // gated residual backward in two kernels
@@ -518,8 +781,8 @@ hipError_t reduce_slots(void* ws, int64_t T, int C, float* o0, float* o1, float*
 // do and, with the fused adaLN, the token's mean and 1/sigma of y and the
 // means of g2 and g2 yh (g2 = dz (1 + scale2)).  Kernel B: lane = one
 // 8-channel chunk of a run of kSumRun tokens; it recomputes dyt in fp32 from
-// the rows and those statistics and writes one tagged slot of dgate (and
-// dshift2, dscale2) per run, as the modulate + RoPE sums kernel does.
+// the rows and those statistics and writes the run's segment entries of
+// dgate (and dshift2, dscale2), as the modulate + RoPE sums kernel does.
 template <bool FUSED>
 __global__ __launch_bounds__(1024) void gres_bwd_rows_kernel(GatedResBwdArgs a, float* __restrict__ stats) {
     __shared__ float red[2 * 2 * 16];
@@ -583,34 +846,39 @@ __global__ __launch_bounds__(1024) void gres_bwd_rows_kernel(GatedResBwdArgs a, 
 }
 
 template <bool FUSED>
-__global__ __launch_bounds__(64) void gres_bwd_sums_kernel(GatedResBwdArgs a, const float* __restrict__ stats,
-                                                           int32_t* __restrict__ tags, float* __restrict__ slots) {
+__global__ __launch_bounds__(kWave * kRunsPerBlock) void gres_bwd_sums_kernel(GatedResBwdArgs a,
+                                                                             const float* __restrict__ stats,
+                                                                             SegLeaf leaf) {
+    __shared__ int s_cnt[kRunsPerBlock];
+    __shared__ int s_tag[kRunsPerBlock][kSumRun];
+    zero_outputs(leaf);
     constexpr int NA = FUSED ? 3 : 1;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t run = int64_t(blockIdx.x) * kRunsPerBlock + wave;
     const int C = a.C;
     const int c = blockIdx.y * kWave + lane;
     const bool live = c < (C >> 3);
     const uint32_t row_bytes = uint32_t(C) * 2u;
     const uint32_t voff = 16u * uint32_t(c);
-    const int64_t t_begin = int64_t(blockIdx.x) * kSumRun;
+    const int64_t t_begin = run * kSumRun;
     const int64_t t_end = t_begin + kSumRun < a.T ? t_begin + kSumRun : a.T;
-    float* const outs[3] = {a.dgate, a.dshift2, a.dscale2};
     float sm[NA][8];
 #pragma unroll
     for (int k = 0; k < NA; ++k)
 #pragma unroll
         for (int j = 0; j < 8; ++j) sm[k][j] = 0.f;
     int cur = -1;
+    int n_ent = 0;
     float gv[8], s2[8];
+    // the finished segment of row `row` becomes the run's next entry (rows
+    // outside the table accumulate nothing)
     auto flush = [&](int row) {
-        if (row < 0 || row >= a.n_rows || !live) return;
-#pragma unroll
-        for (int k = 0; k < NA; ++k)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                atomic_add_f32(outs[k] + int64_t(row) * C + 8 * c + j, sm[k][j]);
-                sm[k][j] = 0.f;
-            }
+        if (row < 0 || row >= a.n_rows) return;
+        const int64_t pos = run * kSumRun + n_ent;
+        put_entry<NA>(sm, leaf.vals, pos, C, 8 * c, live);
+        if (lane == 0) s_tag[wave][n_ent] = row;
+        ++n_ent;
     };
     for (int64_t t = t_begin; t < t_end; ++t) {
         const int m = __builtin_amdgcn_readfirstlane(a.mod_row[t]);
@@ -644,25 +912,22 @@ __global__ __launch_bounds__(64) void gres_bwd_sums_kernel(GatedResBwdArgs a, co
             sm[0][j] += dyt * ov[j];
         }
     }
-    float* slot = slots + int64_t(blockIdx.x) * NA * C;
-    if (live)
-#pragma unroll
-        for (int k = 0; k < NA; ++k) {
-            *reinterpret_cast<f32x4_t*>(slot + k * C + 8 * c) = f32x4_t{sm[k][0], sm[k][1], sm[k][2], sm[k][3]};
-            *reinterpret_cast<f32x4_t*>(slot + k * C + 8 * c + 4) = f32x4_t{sm[k][4], sm[k][5], sm[k][6], sm[k][7]};
-        }
-    if (blockIdx.y == 0 && lane == 0) tags[blockIdx.x] = cur >= 0 && cur < a.n_rows ? cur : -1;
+    flush(cur);
+    if (lane == 0) s_cnt[wave] = n_ent;
+    __syncthreads();   // the runs' entries are written (workgroup scope) and their rows are in LDS
+    merge_block_runs<NA>(leaf, s_cnt, s_tag, C);
 }
 
 }  // namespace
 
 size_t elementwise_bwd_workspace_bytes(int64_t T, int32_t C, int32_t n_arrays) {
     const int64_t Tn = T < 0 ? 0 : T;
-    const int64_t ns = n_slots_for(Tn);
-    // slots of kRun tokens (the single-kernel form), plus 16 bytes of row
-    // statistics per token; the two-kernel form's fewer, larger-run slots and
-    // its statistics fit the same bytes
-    return slot_tags_bytes(ns) + size_t(ns) * size_t(n_arrays) * size_t(C) * 4 + size_t(Tn) * 16;
+    if (Tn == 0 || C <= 0 || n_arrays <= 0) return 0;
+    // entries of runs of kRun (the single-kernel form) or kLeafSpan tokens,
+    // the reduction's tags and counts, and 16 bytes of statistics per token
+    const size_t a = seg_layout(Tn, C, n_arrays, kRun).total;
+    const size_t b = seg_layout(Tn, C, n_arrays, kLeafSpan).total;
+    return a > b ? a : b;
 }
 
 hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& args, hipStream_t stream) {
@@ -675,27 +940,20 @@ hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& args, hipStream_t stre
                                     0.15915494309189535;   // radians -> turns (1 / 2 pi)
     const int C = a.H * a.D;
     const bool mod = a.scale != nullptr;
-    if (mod) {
-        const hipError_t e = zero_f32(a.dshift, a.dscale, nullptr, int64_t(a.n_rows) * C, stream);
-        if (e != hipSuccess) return e;
-    }
-    if (a.T == 0) return hipSuccess;
+    if (a.T == 0)   // no tokens: the row sums are zero (otherwise the reduction's last level writes every row)
+        return mod ? zero_f32(a.dshift, a.dscale, nullptr, int64_t(a.n_rows) * C, stream) : hipSuccess;
     const int nch_w = (C / 8 + kWave - 1) / kWave;     // 16-byte chunks per lane of a row
     if (nch_w > 6) {
-        hipLaunchKernelGGL(modulate_rope_bwd_kernel, dim3(unsigned(n_slots_for(a.T))), dim3(block_threads(C)), 0,
-                           stream, a);
+        const SegLayout L = seg_layout(a.T, C, 2, kRun);
+        hipLaunchKernelGGL(modulate_rope_bwd_kernel, dim3(unsigned(L.n_runs)), dim3(block_threads(C)), 0, stream, a,
+                           seg_leaf(L, a.workspace, a.n_rows, a.dshift, a.dscale, nullptr));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || !mod) return e;
-        return reduce_slots<2>(a.workspace, a.T, C, a.dshift, a.dscale, nullptr, stream);
+        return reduce_segments<2>(L, a.workspace, a.n_rows, a.dshift, a.dscale, nullptr, stream);
     }
-    // two kernels: workspace = tags, slots of kSumRun tokens, then the rows'
-    // statistics (4 floats per token); it fits the size the single kernel's
-    // slots need (C >= 64)
-    const int64_t ns = sum_slots_for(a.T);
-    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-    int32_t* tags = reinterpret_cast<int32_t*>(ws);
-    float* slots = reinterpret_cast<float*>(ws + slot_tags_bytes(ns));
-    float* stats = slots + ns * 2 * C;
+    // two kernels: the rows' statistics and the entries in the workspace
+    const SegLayout L = seg_layout(a.T, C, 2, kLeafSpan);
+    float* stats = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + L.off_stats);
     const dim3 grid_a(unsigned((a.T + kRowsTokens - 1) / kRowsTokens));
     switch (nch_w) {
         case 1: hipLaunchKernelGGL(modrope_bwd_dx_kernel<1>, grid_a, dim3(256), 0, stream, a, stats); break;
@@ -707,50 +965,43 @@ hipError_t launch_modulate_rope_bwd(const ModRopeBwdArgs& args, hipStream_t stre
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !mod) return e;
-    hipLaunchKernelGGL(modrope_bwd_sums_kernel, dim3(unsigned(ns), unsigned((C / 8 + kWave - 1) / kWave)), dim3(64),
-                       0, stream, a, stats, tags, slots);
+    hipLaunchKernelGGL(modrope_bwd_sums_kernel, dim3(unsigned(L.n_runs), unsigned((C / 8 + kWave - 1) / kWave)),
+                       dim3(kWave * kRunsPerBlock), 0, stream, a, stats,
+                       seg_leaf(L, a.workspace, a.n_rows, a.dshift, a.dscale, nullptr));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 grid(unsigned((ns + kSlotGroup - 1) / kSlotGroup), unsigned((C + 255) / 256));
-    hipLaunchKernelGGL(slot_reduce_kernel<2>, grid, dim3(256), 0, stream, tags, slots, ns, C, a.dshift, a.dscale,
-                       nullptr);
-    return hipGetLastError();
+    return reduce_segments<2>(L, a.workspace, a.n_rows, a.dshift, a.dscale, nullptr, stream);
 }
 
 hipError_t launch_gated_residual_bwd(const GatedResBwdArgs& a, hipStream_t stream) {
-    const int64_t n = int64_t(a.n_rows) * a.C;
     const bool fused = a.dz != nullptr;
-    hipError_t e = zero_f32(a.dgate, fused ? a.dshift2 : nullptr, fused ? a.dscale2 : nullptr, n, stream);
-    if (e != hipSuccess) return e;
-    if (a.T == 0) return hipSuccess;
-    // workspace: tags, slots of kSumRun tokens (1 or 3 arrays), then the rows'
-    // statistics (4 floats per token); it fits the size the query returns
+    if (a.T == 0)   // no tokens: the row sums are zero (otherwise the reduction's last level writes every row)
+        return zero_f32(a.dgate, fused ? a.dshift2 : nullptr, fused ? a.dscale2 : nullptr, int64_t(a.n_rows) * a.C,
+                        stream);
+    hipError_t e = hipSuccess;
+    // the rows' statistics and the runs' entries (1 or 3 arrays) in the
+    // workspace; it fits the size the query returns (sized for 3 arrays)
     const int na = fused ? 3 : 1;
-    const int64_t ns = sum_slots_for(a.T);
-    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-    int32_t* tags = reinterpret_cast<int32_t*>(ws);
-    float* slots = reinterpret_cast<float*>(ws + slot_tags_bytes(ns));
-    float* stats = slots + ns * na * a.C;
-    const dim3 grid_b(unsigned(ns), unsigned((a.C / 8 + kWave - 1) / kWave));
+    const SegLayout L = seg_layout(a.T, a.C, na, kLeafSpan);
+    float* stats = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + L.off_stats);
+    const SegLeaf leaf = seg_leaf(L, a.workspace, a.n_rows, a.dgate, fused ? a.dshift2 : nullptr,
+                                  fused ? a.dscale2 : nullptr);
+    const dim3 grid_b(unsigned(L.n_runs), unsigned((a.C / 8 + kWave - 1) / kWave));
     if (fused) {
         hipLaunchKernelGGL(gres_bwd_rows_kernel<true>, dim3(unsigned(a.T)), dim3(block_threads(a.C)), 0, stream, a,
                            stats);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(gres_bwd_sums_kernel<true>, grid_b, dim3(64), 0, stream, a, stats, tags, slots);
-    } else {
-        hipLaunchKernelGGL(gres_bwd_rows_kernel<false>, dim3(unsigned(a.T)), dim3(block_threads(a.C)), 0, stream, a,
-                           stats);
+        hipLaunchKernelGGL(gres_bwd_sums_kernel<true>, grid_b, dim3(kWave * kRunsPerBlock), 0, stream, a, stats,
+                           leaf);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(gres_bwd_sums_kernel<false>, grid_b, dim3(64), 0, stream, a, stats, tags, slots);
+        return reduce_segments<3>(L, a.workspace, a.n_rows, a.dgate, a.dshift2, a.dscale2, stream);
     }
+    hipLaunchKernelGGL(gres_bwd_rows_kernel<false>, dim3(unsigned(a.T)), dim3(block_threads(a.C)), 0, stream, a,
+                       stats);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 grid(unsigned((ns + kSlotGroup - 1) / kSlotGroup), unsigned((a.C + 255) / 256));
-    if (fused)
-        hipLaunchKernelGGL(slot_reduce_kernel<3>, grid, dim3(256), 0, stream, tags, slots, ns, a.C, a.dgate,
-                           a.dshift2, a.dscale2);
-    else
-        hipLaunchKernelGGL(slot_reduce_kernel<1>, grid, dim3(256), 0, stream, tags, slots, ns, a.C, a.dgate,
-                           nullptr, nullptr);
-    return hipGetLastError();
+    hipLaunchKernelGGL(gres_bwd_sums_kernel<false>, grid_b, dim3(kWave * kRunsPerBlock), 0, stream, a, stats,
+                       leaf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return reduce_segments<1>(L, a.workspace, a.n_rows, a.dgate, nullptr, nullptr, stream);
 }
 
 }  // namespace mf

@@ -188,10 +188,19 @@ def _f32(t):
     return t.detach().cpu().numpy().astype(np.float64)
 
 
-def modrope_bwd_check(w):
+def _use_rows(b, rows):
+    """Replace the pack's adaLN row table (device and host copies)."""
+    import torch
+    if rows is not None:
+        b.mod_row = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.int32)).to("cuda")
+        b.mod_row_host = np.ascontiguousarray(rows, dtype=np.int32)
+
+
+def modrope_bwd_check(w, rows=None):
     import torch
     G.say(w.name, "modulate_rope_bwd", "T", w.T, "H", w.H, "D", w.D)
     b = runner.to_device(w)
+    _use_rows(b, rows)
     g = W.upstream_grads(w)
     dq_out, dk_out = runner.bf16_tensor(g["dq"]), runner.bf16_tensor(g["dk"])
     dq, dk = torch.empty_like(b.q), torch.empty_like(b.k)
@@ -213,10 +222,11 @@ def modrope_bwd_check(w):
         check_rows(_f32(dsc), ref[3], w.name + ".dscale")
 
 
-def gres_bwd_check(w, fused=True, with_dy=True):
+def gres_bwd_check(w, fused=True, with_dy=True, rows=None):
     import torch
     G.say(w.name, "gated_residual_bwd", "fused", fused, "dy", with_dy)
     b = runner.to_device(w)
+    _use_rows(b, rows)
     runner.run_chain(b)
     g = W.upstream_grads(w)
     T, C = w.T, w.H * w.D
@@ -368,3 +378,75 @@ def test_elementwise_bwd_rows_outside_table():
     same(outs[0][1], outs[1][1], "do")
     for i, name in ((2, "dgate"), (3, "dshift2"), (4, "dscale2")):
         np.testing.assert_allclose(_f32(outs[0][i]), _f32(outs[1][i][:n]), rtol=1e-5, atol=1e-5, err_msg=name)
+
+
+def _interleaved_rows(T, n, seed):
+    """An adaLN row table whose row changes every one or two tokens and comes
+    back: the row sums' runs hold several segments, and a row's tokens are
+    not contiguous."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    while len(rows) < T:
+        rows += [int(rng.integers(0, n))] * int(rng.integers(1, 3))
+    return np.array(rows[:T], dtype=np.int32)
+
+
+@pytest.mark.parametrize("H,D,descs", [
+    (2, 64, [(40, 1, 24, 24, 0, 1), (9, 1, 7, 5, 2, 3)]),                    # runs of 8, one reduction level
+    (2, 64, [(64, 1, 64, 64, s, s) for s in range(5)]),                       # 20 800 tokens: three levels
+    (32, 128, [(31, 1, 16, 20, 0, 1), (5, 1, 9, 9, 2, 3)]),                   # 4096 channels: runs of 4
+])
+def test_elementwise_bwd_interleaved_rows(H, D, descs):
+    """Row sums when the adaLN row changes every one or two tokens and rows
+    recur: against the oracle, for both elementwise backward calls."""
+    w = W.custom(descs, H=H, D=D, rope_dims=(0, D // 2, D // 2), modulate=True, residual=True,
+                 seed=90 + H + len(descs), name=f"interleaved_h{H}_n{len(descs)}")
+    rows = _interleaved_rows(w.T, len(w.descs), seed=7 + H)
+    modrope_bwd_check(w, rows)
+    gres_bwd_check(w, rows=rows)
+    gres_bwd_check(w, fused=False, rows=rows)
+
+
+@pytest.mark.parametrize("name", ["single_1024", "wide", "interleaved"])
+def test_elementwise_bwd_row_sums_bitwise(name):
+    """The row sums (dshift, dscale; dgate, dshift2, dscale2) are bitwise
+    equal from call to call: every row sum is added in one fixed order."""
+    import torch
+    if name == "single_1024":
+        w = W.NAMED["single_1024"]()
+        rows = None
+    elif name == "wide":
+        w = W.custom([(60, 1, 24, 26, 0, 1), (11, 1, 13, 9, 2, 2)], H=32, D=128, rope_dims=(0, 64, 64),
+                     modulate=True, residual=True, seed=95, name="bitwise_wide")
+        rows = None
+    else:
+        w = W.custom([(64, 1, 40, 40, s, s) for s in range(3)], H=24, D=128, rope_dims=(0, 64, 64),
+                     modulate=True, residual=True, seed=96, name="bitwise_interleaved")
+        rows = _interleaved_rows(w.T, len(w.descs), seed=11)
+    G.say(w.name, "row sums bitwise", "T", w.T, "C", w.H * w.D)
+    b = runner.to_device(w)
+    _use_rows(b, rows)
+    runner.run_chain(b)
+    g = W.upstream_grads(w)
+    T, C, n = w.T, w.H * w.D, len(w.descs)
+    dq_out, dk_out = runner.bf16_tensor(g["dq"]), runner.bf16_tensor(g["dk"])
+    dy, dz = runner.bf16_tensor(g["dy"]), runner.bf16_tensor(g["dz"])
+    o2 = b.o.view(T, C)
+    f32 = lambda: torch.empty((n, C), dtype=torch.float32, device="cuda")  # noqa: E731
+    bf = lambda: torch.empty((T, C), dtype=torch.bfloat16, device="cuda")  # noqa: E731
+    runs = []
+    for _ in range(3):
+        dq, dk = torch.empty_like(b.q), torch.empty_like(b.k)
+        dsh, dsc = f32(), f32()
+        native.modulate_rope_bwd(b.q, b.k, dq_out, dk_out, dq, dk, b.pos, w.rope_dims, w.rope_base, b.scale,
+                                 b.mod_row, dsh, dsc, w.eps)
+        dx, do, dg, ds2, dc2 = bf(), bf(), f32(), f32(), f32()
+        native.gated_residual_bwd(b.x, o2, b.gate, b.mod_row, dy, dx, do, dg, b.scale2, dz, ds2, dc2, w.eps)
+        dx1, do1, dg1 = bf(), bf(), f32()
+        native.gated_residual_bwd(b.x, o2, b.gate, b.mod_row, dy, dx1, do1, dg1, None, None, None, None, w.eps)
+        runs.append((dsh, dsc, dg, ds2, dc2, dg1))
+    torch.cuda.synchronize()
+    names = ("dshift", "dscale", "dgate", "dshift2", "dscale2", "dgate (unfused)")
+    for r in runs[1:]:
+        for a, c, nm in zip(runs[0], r, names):
+            assert torch.equal(a.view(torch.int32), c.view(torch.int32)), f"{w.name}: {nm} differs between calls"
