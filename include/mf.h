@@ -278,15 +278,18 @@ mf_status mf_varlen_attn_bwd(void* stream,
  *   dq_out / dk_out (in place), other overlaps are undefined.
  * scale: bf16 [n_rows][H*D] or NULL (RoPE only; then mod_row, dshift and
  *   dscale are ignored).  shift is not needed.
- * dshift, dscale: fp32 [n_rows][H*D], overwritten (zeroed, then summed per
- *   run of tokens and added with fp32 atomics: the order of the additions
- *   varies between calls, so the row sums are not bitwise reproducible).
+ * dshift, dscale: fp32 [n_rows][H*D], overwritten.  Each row sum is added in
+ *   one fixed order (segments of equal row in runs of tokens, then groups of
+ *   them, in token order; no atomics), so the row sums are bitwise
+ *   reproducible from call to call; a row no token maps to is zero.
  * mod_row, pos, rope dims, rope_base, eps: as for mf_modulate_rope;
  *   0 <= mod_row[t] < n_rows.
  * workspace: device memory of at least mf_modulate_rope_bwd_workspace_bytes
- *   bytes, 256-byte aligned, when modulating (per-run partial row sums);
- *   unused (may be NULL) for RoPE only.  Concurrent calls need distinct
- *   workspaces.
+ *   bytes, 256-byte aligned, when modulating: the per-token statistics and
+ *   the partial row sums, room for 2 fp32 values per token and channel (a
+ *   run whose adaLN row changes at every token needs one partial per token;
+ *   in a pack about one per 128 tokens is written); unused (may be NULL) for
+ *   RoPE only.  Concurrent calls need distinct workspaces.
  * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_UNSUPPORTED,
  * MF_ERR_WORKSPACE, MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
 size_t mf_modulate_rope_bwd_workspace_bytes(int64_t T, int32_t H, int32_t D);
@@ -318,11 +321,13 @@ mf_status mf_modulate_rope_bwd(void* stream,
  * dy: bf16 [T][C] or NULL (zero); dz: bf16 [T][C] (fused) or NULL.
  * dx, dout: bf16 [T][C] outputs; dx may equal dy; no other overlap.
  * dgate, dshift2, dscale2: fp32 [n_rows][C], overwritten (row sums as
- *   above).
+ *   above, each added in one fixed order as for mf_modulate_rope_bwd:
+ *   bitwise reproducible).
  * C a multiple of 64 and at most 8192; eps > 0 when fused.
  * workspace: device memory of at least mf_gated_residual_bwd_workspace_bytes
- *   bytes, 256-byte aligned (per-run partial row sums); concurrent calls
- *   need distinct workspaces.
+ *   bytes, 256-byte aligned: the per-token statistics and the partial row
+ *   sums (room for 3 fp32 values per token and channel, as for
+ *   mf_modulate_rope_bwd); concurrent calls need distinct workspaces.
  * Errors: MF_ERR_NULL, MF_ERR_SHAPE, MF_ERR_ALIGN, MF_ERR_WORKSPACE,
  * MF_ERR_TABLE (MF_DEBUG only), MF_ERR_HIP. */
 size_t mf_gated_residual_bwd_workspace_bytes(int64_t T, int32_t C);
