@@ -57,12 +57,15 @@
 //    the residual and gate rows are loaded before the staging.
 //  * Tiles are numbered so that the tiles one XCD runs are consecutive and
 //    share their weight tile (its L2 serves the re-reads).
-//  * Split tail (QKV projection): one workgroup per CU, so the tiles run in
-//    rounds of #CUs; when the last round is less than half full, each of its
-//    tiles is cut into s K-ranges (s = #CUs / tail tiles) that run side by
-//    side and write fp32 partial tiles to the workspace, and
-//    gemm_fixup_kernel adds the pieces in a fixed order and runs the same
-//    epilogue.
+//  * Sliced tail (QKV projection): one workgroup per CU, so the tiles run in
+//    rounds of #CUs; when the last round is at most half full, each of its
+//    tiles is cut into two (or four) token slices of 128 (64) tokens that
+//    run side by side in the same launch (workgroups after the whole tiles'),
+//    each with the whole K and its own epilogue: the round takes about half
+//    (a quarter) of a tile's time and nothing is added afterwards.  (Run as
+//    a second launch, the slices measured slower: 241 -> 256 us at the
+//    1024^2 pack, the launch gap and the lost overlap with the last whole
+//    tiles.)
 //  * Ragged edges: buffer resources end at the last token / feature, so rows
 //    past them read as zeros; the epilogue stores only rows inside.
 #include <algorithm>
@@ -82,21 +85,14 @@ constexpr int kBT = 256;                   // tokens per tile
 constexpr int kBK = 64;                    // K per step
 constexpr int kChunks = kBK / 8;           // 16-byte chunks per LDS row (128 bytes, no padding)
 constexpr int kRowB = 16 * kChunks;
-constexpr int kStageRows = kBF + kBT;
-constexpr int kStageB = kStageRows * kRowB;
 constexpr int kStages = 2;
-constexpr int kLdsB = kStages * kStageB;   // 128 KiB
-static_assert(kStages >= 2 && kStages <= 4, "waits below cover up to two later groups");
+constexpr int kLdsB = kStages * (kBF + kBT) * kRowB;   // 128 KiB: two stages of a whole tile
 constexpr int kRowsPerDma = 64 / kChunks;  // LDS rows one direct-load instruction fills
-constexpr int kDma = kStageRows / kRowsPerDma;   // direct-load instructions per stage
-constexpr int kDmaW = kBF / kRowsPerDma;         // of which fill the weight rows
-constexpr int kDmaPerWave = kDma / kGW;
+constexpr int kDmaW = kBF / kRowsPerDma;   // direct-load instructions of a stage that fill the weight rows
 constexpr int kXcds = 8;
 constexpr int kGroupF = 4;                 // feature tiles per group of the tile order
-static_assert(kDma % kGW == 0, "whole direct-load instructions");
-// The epilogue stages the bf16 output tile [kBT tokens][kBF features]
-// through the (then free) LDS stages.
-static_assert(kBT * kBF * 2 <= kLdsB, "output tile fits the LDS stages");
+// The epilogue stages the bf16 output tile [tokens][kBF features] through the
+// (then free) LDS stages.
 
 // LDS rows are stored swizzled: chunk c of row r sits in slot c ^ sw(r),
 // sw(r) = (r / 2) % 8.  The 16 lanes one LDS cycle serves read 16-byte
@@ -133,10 +129,8 @@ struct GemmParams {
     const int32_t* mod_row;
     int n_rows;              // a row outside [0, n_rows) gates with zeros
     int tiles_t, tiles_f;
-    // split tail: tiles [n_full, tiles) run as `split` K-ranges each, fp32
-    // partial tiles in `partial` (kTileAcc floats per piece)
-    int n_full, split;
-    float* partial;
+    // tail: tiles [n_full, tiles) run as `slices` token slices each
+    int n_full, slices;
 };
 
 // The rotation table: for token t and pair i of a head (dims 2i, 2i+1 on
@@ -161,7 +155,20 @@ __device__ __forceinline__ void rope_table_row(const RopeTableParams& rp, int64_
     }
 }
 
-constexpr int kTileAcc = kBF * kBT;        // fp32 accumulators of one tile
+// Shape of a tile of BT tokens (256: the whole tiles; 128 and 64: slices of
+// the last round's tiles).  Wavefront (wf, wt) computes features
+// 64 wf .. 64 wf + 63 and tokens kWT wt .. kWT wt + kWT - 1.
+template <int BT>
+struct Tile {
+    static_assert(BT == 256 || BT == 128 || BT == 64, "tile tokens");
+    static constexpr int kTB = BT / 64;                     // 32-token blocks per wavefront
+    static constexpr int kWT = BT / 2;                      // tokens per wavefront
+    static constexpr int kStageRows = kBF + BT;
+    static constexpr int kStageB = kStageRows * kRowB;
+    static constexpr int kDmaPerWave = kStageRows / kRowsPerDma / kGW;
+    static_assert(kStageRows / kRowsPerDma % kGW == 0, "whole direct-load instructions");
+    static_assert(2 * kStageB <= kLdsB && BT * kBF * 2 <= 2 * kStageB, "stages and output image fit");
+};
 
 // Logical tile -> (feature tile, token tile): groups of kGroupF feature
 // tiles; consecutive tiles walk the group's feature tiles for one token tile,
@@ -205,9 +212,11 @@ __device__ __forceinline__ void wait_vm() {
 // 16-byte chunk c of row t in slot c ^ (t % 16)); each wavefront then takes
 // whole rows, lane = 4 consecutive features, and every global load and store
 // is a 512-byte row segment.
-template <int MODE>
-__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&acc)[2][4], const int f0,
-                                              const int64_t t0, unsigned char* smem) {
+template <int MODE, int BT>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&acc)[2][Tile<BT>::kTB],
+                                              const int f0, const int64_t t0, unsigned char* smem) {
+    constexpr int kTB = Tile<BT>::kTB;
+    constexpr int kWT = Tile<BT>::kWT;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -222,7 +231,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&ac
         // in flight across the barrier.
         f32x4_t cbuf[2][2][4];
         auto load_cs = [&](int buf, int tb) {
-            const int64_t t = t0 + 128 * wt + 32 * tb + l32;
+            const int64_t t = t0 + kWT * wt + 32 * tb + l32;
             const int64_t tc = t < p.T ? t : p.T - 1;
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb) {
@@ -238,9 +247,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&ac
         load_cs(0, 0);
         lds_barrier();                     // every wavefront is done with the stages
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            if (tb + 1 < 4) load_cs((tb + 1) & 1, tb + 1);
-            const int tl = 128 * wt + 32 * tb + l32;   // token row inside the tile
+        for (int tb = 0; tb < kTB; ++tb) {
+            if (tb + 1 < kTB) load_cs((tb + 1) & 1, tb + 1);
+            const int tl = kWT * wt + 32 * tb + l32;   // token row inside the tile
             const int64_t t = t0 + tl;
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb) {
@@ -274,7 +283,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&ac
         lds_barrier();
         // rows 2 (i kGW + wave) + h, chunk l32: 32 lanes per 512-byte row segment
 #pragma unroll 4
-        for (int i = 0; i < kBT / (2 * kGW); ++i) {
+        for (int i = 0; i < BT / (2 * kGW); ++i) {
             const int tl = 2 * (i * kGW + wave) + hlf;
             const int64_t t = t0 + tl;
             const int n = f0 + 8 * l32;
@@ -282,6 +291,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&ac
             if (t < p.T && n < p.N) st16(p.out + t * p.ld_out + n, v);
         }
     } else {
+        static_assert(BT == 256, "the out projection runs whole tiles");
         // Rows i kGW + wave of each half, lane = 4 consecutive features.  The
         // residual and gate values of the first half are loaded before the
         // staging; each register is reloaded for the second half as soon as
@@ -349,25 +359,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16_t (&ac
     }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int b = blockIdx.x;
-    // whole tiles first (blockIdx < n_full), then the pieces of the split
-    // tail tiles, which the dispatcher starts last
-    const bool piece = b >= p.n_full;
-    int lt, part = 0;
-    if (!piece) {
-        lt = xcd_order(b, p.n_full);
-    } else {
-        const int li = xcd_order(b - p.n_full, int(gridDim.x) - p.n_full);
-        lt = p.n_full + li / p.split;
-        part = li - (li / p.split) * p.split;
-    }
-    int ft, tt;
-    tile_of(p, lt, ft, tt);
+// One tile of BT tokens from token t0 and features 256 ft.
+template <int MODE, int BT>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const int ft, const int64_t t0, unsigned char* smem) {
+    using S = Tile<BT>;
+    constexpr int kTB = S::kTB;
+    constexpr int kDmaPerWave = S::kDmaPerWave;
+    constexpr int kStageB = S::kStageB;
     const int f0 = ft * kBF;
-    const int64_t t0 = int64_t(tt) * kBT;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -375,7 +374,7 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
     const int l32 = lane & 31;
     const int hlf = lane >> 5;
     const int wf = wave & 3;      // 64-feature quarter of the tile
-    const int wt = wave >> 2;     // 128-token half of the tile
+    const int wt = wave >> 2;     // token half of the tile
 
     const uint32_t kbytes = uint32_t(p.K) * 2u;
     const uint32_t abytes = uint32_t(p.ld_act) * 2u;
@@ -411,53 +410,52 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
         }
     };
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[2][kTB];
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < kTB; ++tb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fb][tb][r] = 0.f;
 
     // Fragment rows: weight rows 64 wf + 32 fb + l32, activation rows
-    // kBF + 128 wt + 32 tb + l32; their swizzle is sw(l32) for all of them
+    // kBF + kWT wt + 32 tb + l32; their swizzle is sw(l32) for all of them
     // (the row offsets are multiples of 16).  K sub-step kk reads chunk
     // 2 kk + h.
     const int sw = swz(l32);
     const int a_rd = (64 * wf + l32) * kRowB;
-    const int b_rd = (kBF + 128 * wt + l32) * kRowB;
+    const int b_rd = (kBF + S::kWT * wt + l32) * kRowB;
     int cofs[kBK / 16];
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) cofs[kk] = 16 * ((2 * kk + hlf) ^ sw);
-    // K steps [ks0, ks1): all of them, or this piece's share.  Stage s % 2
-    // holds step s.  The barrier of step s sits before the MFMAs of its last
-    // K sub-step: past it, every wavefront has finished reading stage s (so
-    // step s + 2 may refill it) and step s + 1 has landed, so the first
-    // fragments of step s + 1 and the loads of step s + 2 are issued while
-    // those MFMAs run.  The scheduling groups keep each sub-step's fragment
-    // reads ahead of the MFMAs of the sub-step before it (two fragment sets).
-    const int nks_all = (p.K + kBK - 1) / kBK;
-    const int ks0 = piece ? part * nks_all / p.split : 0;
-    const int ks1 = piece ? (part + 1) * nks_all / p.split : nks_all;
-    const int nks = ks1 - ks0;
+    // Stage s % 2 holds step s.  The barrier of step s sits before the MFMAs
+    // of its last K sub-step: past it, every wavefront has finished reading
+    // stage s (so step s + 2 may refill it) and step s + 1 has landed, so the
+    // first fragments of step s + 1 and the loads of step s + 2 are issued
+    // while those MFMAs run.  The scheduling groups keep each sub-step's
+    // fragment reads ahead of the MFMAs of the sub-step before it (two
+    // fragment sets).
+    const int nks = (p.K + kBK - 1) / kBK;
     constexpr int kSub = kBK / 16;
-    constexpr int kReads = 2 + 4;             // fragments per sub-step
-    constexpr int kMfma = 2 * 4;              // MFMAs per sub-step
-    static_assert(kSub % 2 == 0 && kDmaPerWave <= kMfma, "step layout");
-    bf16x8_t af[2][2], bf[2][4];
+    constexpr int kReads = 2 + kTB;           // fragments per sub-step
+    constexpr int kMfma = 2 * kTB;            // MFMAs per sub-step
+    static_assert(kSub % 2 == 0, "fragment sets alternate within a step");
+    // direct loads per MFMA after the barrier (the rest follow the last one)
+    constexpr int kLoadsPerMfma = kMfma > 1 ? (kDmaPerWave + kMfma - 2) / (kMfma - 1) : kDmaPerWave;
+    bf16x8_t af[2][2], bf[2][kTB];
     auto rd = [&](int buf, const unsigned char* st, int kk) {
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
             af[buf][fb] = *reinterpret_cast<const bf16x8_t*>(st + a_rd + 32 * fb * kRowB + cofs[kk]);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < kTB; ++tb)
             bf[buf][tb] = *reinterpret_cast<const bf16x8_t*>(st + b_rd + 32 * tb * kRowB + cofs[kk]);
     };
     auto mma = [&](int buf) {
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < kTB; ++tb)
                 acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][fb], bf[buf][tb], acc[fb][tb], 0, 0, 0);
     };
     auto substeps = [&](const unsigned char* st) {
@@ -481,18 +479,17 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
             wait_vm<0>();
             __syncthreads();
             rd(0, smem + ((s + 1) & 1) * kStageB, 0);
-            if constexpr (decltype(kLoad)::value) issue(ks0 + s + 2, s & 1);
+            if constexpr (decltype(kLoad)::value) issue(s + 2, s & 1);
             mma((kSub - 1) & 1);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);   // DS reads
             if constexpr (decltype(kLoad)::value) {
 #pragma unroll
-                for (int i = 0; i < kDmaPerWave; ++i) {
+                for (int i = 0; i + 1 < kMfma; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // direct load
+                    __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerMfma, 0);   // direct loads
                 }
-                if constexpr (kMfma - 1 - kDmaPerWave > 0)
-                    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - 1 - kDmaPerWave, 0);
+                if constexpr (kMfma == 1) __builtin_amdgcn_sched_group_barrier(0x020, kDmaPerWave, 0);
             } else {
                 __builtin_amdgcn_sched_group_barrier(0x008, kMfma - 1, 0);
             }
@@ -502,68 +499,47 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
     };
     using yes = std::true_type;
     using no = std::false_type;
-    if (nks > 0) {
-        issue(ks0, 0);
-        if (nks > 1) {
-            issue(ks0 + 1, 1);
-            wait_vm<kDmaPerWave>();
-        } else {
-            wait_vm<0>();
-        }
-        __syncthreads();   // step 0 has landed for every wavefront
-        rd(0, smem, 0);
-        int s = 0;
-        for (; s + 2 < nks; ++s) step(s, yes{}, yes{});
-        if (s + 1 < nks) step(s++, yes{}, no{});
-        step(s, no{}, no{});
+    issue(0, 0);
+    if (nks > 1) {
+        issue(1, 1);
+        wait_vm<kDmaPerWave>();
+    } else {
+        wait_vm<0>();
     }
+    __syncthreads();   // step 0 has landed for every wavefront
+    rd(0, smem, 0);
+    int s = 0;
+    for (; s + 2 < nks; ++s) step(s, yes{}, yes{});
+    if (s + 1 < nks) step(s++, yes{}, no{});
+    step(s, no{}, no{});
 
-    if (piece) {
-        // fp32 partial tile in fragment order: 16-byte groups of four
-        // registers, 64 lanes side by side (1 KiB per store instruction)
-        f32x4_t* dst = reinterpret_cast<f32x4_t*>(p.partial + size_t((lt - p.n_full) * p.split + part) * kTileAcc);
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4_t v = {acc[fb][tb][4 * g], acc[fb][tb][4 * g + 1], acc[fb][tb][4 * g + 2],
-                                       acc[fb][tb][4 * g + 3]};
-                    dst[(((wave * 2 + fb) * 4 + tb) * 4 + g) * 64 + lane] = v;
-                }
-        return;
-    }
-    gemm_epilogue<MODE>(p, acc, f0, t0, smem);
+    gemm_epilogue<MODE, BT>(p, acc, f0, t0, smem);
 }
 
-// Sum of the pieces of split tail tile n_full + blockIdx.x (in piece order),
-// then the same epilogue as a whole tile.
 template <int MODE>
-__global__ __launch_bounds__(kGT) void gemm_fixup_kernel(GemmParams p) {
+__global__ __launch_bounds__(kGT) void gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int lt = p.n_full + int(blockIdx.x);
+    const int b = blockIdx.x;
     int ft, tt;
-    tile_of(p, lt, ft, tt);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    f32x16_t acc[2][4];
-    for (int part = 0; part < p.split; ++part) {
-        const f32x4_t* src =
-            reinterpret_cast<const f32x4_t*>(p.partial + size_t((lt - p.n_full) * p.split + part) * kTileAcc);
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4_t v = src[(((wave * 2 + fb) * 4 + tb) * 4 + g) * 64 + lane];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[fb][tb][4 * g + e] = part == 0 ? v[e] : acc[fb][tb][4 * g + e] + v[e];
-                }
+    if (b < p.n_full) {
+        // whole tiles first, in the XCD-contiguous order
+        tile_of(p, xcd_order(b, p.n_full), ft, tt);
+        gemm_tile<MODE, kBT>(p, ft, int64_t(tt) * kBT, smem);
+        return;
     }
-    gemm_epilogue<MODE>(p, acc, ft * kBF, int64_t(tt) * kBT, smem);
+    if constexpr (MODE == kModeQkv) {
+        // then the last round's tiles, each cut into p.slices token slices
+        // (the dispatcher starts these last, as whole tiles free their CUs)
+        const int li = xcd_order(b - p.n_full, int(gridDim.x) - p.n_full);
+        const int part = li % p.slices;
+        tile_of(p, p.n_full + li / p.slices, ft, tt);
+        const int64_t t0 = int64_t(tt) * kBT + int64_t(part) * (kBT / p.slices);
+        if (t0 >= p.T) return;   // a slice past the last token (every wavefront leaves together)
+        if (p.slices == 4)
+            gemm_tile<MODE, kBT / 4>(p, ft, t0, smem);
+        else
+            gemm_tile<MODE, kBT / 2>(p, ft, t0, smem);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -653,34 +629,28 @@ hipError_t launch_adaln(const BlockQkvArgs& a, uint16_t* u, const RopeTableParam
     return launch_adaln_nch<16>(a, u, rp, stream);
 }
 
-// Whole tiles run in rounds of `cus` (one workgroup per CU); a last round
-// under half full is cut into K-ranges of at least four steps.
-struct SplitPlan {
-    int n_full, split;
+// Whole tiles run in rounds of `cus` (one workgroup per CU).  For the QKV
+// projection a last round at most half full is cut into token slices of the
+// same 256 features: two of 128 tokens, or four of 64 when that still fits
+// the CUs, so the round takes a half or a quarter of a tile's time with the
+// full K in each workgroup (no partial sums to add).
+struct TailPlan {
+    int n_full, slices;
 };
-SplitPlan split_plan(int n_tiles, int nks, int cus) {
-    SplitPlan sp{n_tiles, 1};
-    if (cus <= 0) return sp;
+TailPlan tail_plan(int n_tiles, int cus) {
+    TailPlan tp{n_tiles, 1};
+    if (cus <= 0) return tp;
     const int tail = n_tiles % cus;
-    if (tail == 0) return sp;
-    const int s = std::min(cus / tail, nks / 4);
-    if (s < 2) return sp;
-    sp.n_full = n_tiles - tail;
-    sp.split = s;
-    return sp;
+    if (tail == 0 || 2 * tail > cus) return tp;
+    tp.n_full = n_tiles - tail;
+    tp.slices = 4 * tail <= cus ? 4 : 2;
+    return tp;
 }
-
-int qkv_tiles(int64_t T, int C) { return ((3 * C + kBF - 1) / kBF) * int((T + kBT - 1) / kBT); }
 
 // Bytes of the modulated rows and of the rotation table (each 256-byte
-// aligned) and of the partial tiles.
+// aligned).
 size_t qkv_rows_bytes(int64_t T, int C) { return (size_t(T) * size_t(C) * 2 + 255) & ~size_t(255); }
 size_t qkv_table_bytes(int64_t T, int D) { return (size_t(T) * size_t(D) * 4 + 255) & ~size_t(255); }
-size_t qkv_partial_bytes(int64_t T, int C, int cus) {
-    const int tiles = qkv_tiles(T, C);
-    const SplitPlan sp = split_plan(tiles, (C + kBK - 1) / kBK, cus);
-    return sp.split > 1 ? size_t(tiles - sp.n_full) * sp.split * kTileAcc * sizeof(float) : 0;
-}
 
 template <int MODE>
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
@@ -691,20 +661,14 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
     p.tiles_t = int((p.T + kBT - 1) / kBT);
     const int n_tiles = p.tiles_f * p.tiles_t;
     p.n_full = n_tiles;
-    p.split = 1;
-    if (p.partial != nullptr) {
-        const SplitPlan sp = split_plan(n_tiles, (p.K + kBK - 1) / kBK, device_cu_count());
-        p.n_full = sp.n_full;
-        p.split = sp.split;
+    p.slices = 1;
+    if (MODE == kModeQkv) {
+        const TailPlan tp = tail_plan(n_tiles, device_cu_count());
+        p.n_full = tp.n_full;
+        p.slices = tp.slices;
     }
-    const int grid = p.n_full + (n_tiles - p.n_full) * p.split;
+    const int grid = p.n_full + (n_tiles - p.n_full) * p.slices;
     hipLaunchKernelGGL(gemm_kernel<MODE>, dim3(unsigned(grid)), dim3(kGT), kLdsB, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.split == 1) return e;
-    static const hipError_t attr_fix = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_fixup_kernel<MODE>), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsB);
-    if (attr_fix != hipSuccess) return attr_fix;
-    hipLaunchKernelGGL(gemm_fixup_kernel<MODE>, dim3(unsigned(n_tiles - p.n_full)), dim3(kGT), kLdsB, stream, p);
     return hipGetLastError();
 }
 
@@ -712,16 +676,14 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
 
 size_t block_qkv_workspace_bytes(int64_t T, int32_t C, int32_t D) {
     if (T <= 0 || C <= 0 || D <= 0) return 0;
-    int cus = device_cu_count();
-    if (cus <= 0) cus = 256;   // no device visible: size for an MI355X
-    return qkv_rows_bytes(T, C) + qkv_table_bytes(T, D) + qkv_partial_bytes(T, C, cus);
+    return qkv_rows_bytes(T, C) + qkv_table_bytes(T, D);
 }
 
 hipError_t launch_block_qkv(const BlockQkvArgs& args, hipStream_t stream) {
     if (args.T == 0) return hipSuccess;
     const int C = args.H * args.D;
     unsigned char* ws = static_cast<unsigned char*>(args.workspace);
-    // workspace: modulated rows, rotation table, partial tiles of the split tail
+    // workspace: modulated rows, rotation table
     RopeTableParams rp = {};
     rp.cs = reinterpret_cast<f32x2_t*>(ws + qkv_rows_bytes(args.T, C));
     rp.pos = args.pos;
@@ -760,7 +722,6 @@ hipError_t launch_block_qkv(const BlockQkvArgs& args, hipStream_t stream) {
     p.rope_limit = 2 * C;
     p.D = args.D;
     p.rope_cs = rp.cs;
-    p.partial = reinterpret_cast<float*>(ws + qkv_rows_bytes(args.T, C) + qkv_table_bytes(args.T, args.D));
     return launch_gemm<kModeQkv>(p, stream);
 }
 

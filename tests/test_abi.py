@@ -263,16 +263,10 @@ def test_block_projection_validation():
     assert bout(y=PODD) == ALIGN
     assert bout(T=1 << 22, C=1024, ld_o=1024) == UNSUP
     assert bout(T=0, o=None, w=None, x=None, gate=None, mod_row=None, y=None) == 0
-    # no device here: sized for 256 CUs.  The modulated rows (T C bf16), the
-    # rotation table (T D/2 pairs of fp32 cos, sin), then the partial tiles:
-    # 612 tiles of 256 x 256 leave a last round of 100 tiles, each cut in two
-    # K ranges (256 KiB fp32 per piece)
-    assert native.lib().mf_block_qkv_workspace_bytes(4352, 24, 128) == (4352 * 3072 * 2 + 4352 * 128 * 4
-                                                                        + 200 * 256 * 1024)
-    # 576 tiles: a tail of 64, cut in four
-    assert native.lib().mf_block_qkv_workspace_bytes(4096, 24, 128) == (4096 * 3072 * 2 + 4096 * 128 * 4
-                                                                        + 256 * 256 * 1024)
-    # 2304 tiles fill whole rounds: no split
+    # the modulated rows (T C bf16), then the rotation table (T D/2 pairs of
+    # fp32 cos, sin); no part depends on the device
+    assert native.lib().mf_block_qkv_workspace_bytes(4352, 24, 128) == 4352 * 3072 * 2 + 4352 * 128 * 4
+    assert native.lib().mf_block_qkv_workspace_bytes(4096, 24, 128) == 4096 * 3072 * 2 + 4096 * 128 * 4
     assert native.lib().mf_block_qkv_workspace_bytes(16384, 24, 128) == 16384 * 3072 * 2 + 16384 * 128 * 4
     # the table rows are 256-byte aligned: T D 4 = 3 * 64 * 4 rounds up to 768
     assert native.lib().mf_block_qkv_workspace_bytes(3, 1, 64) % 256 == 0

@@ -124,11 +124,15 @@ def test_block_qkv_ragged(D):
     check_qkv(w)
 
 
-# Small grids on a 256-CU device: every tile is cut into K ranges that run
-# side by side and are summed by the fix-up kernel (C = 512: 18 tiles, two
-# ranges of 4 steps; C = 1024: 24 tiles, four ranges of 4 steps).
-@pytest.mark.parametrize("H,descs", [(4, [(88, 1, 16, 32, 0, 0)]), (8, [(27, 1, 13, 21, 0, 0), (0, 1, 1, 1, 1, 1)])],
-                         ids=["C512", "C1024"])
+# Small grids on a 256-CU device: the last round's tiles are cut into token
+# slices that run side by side, each with the whole K (C = 512: 18 tiles, T =
+# 600, four slices of 64 tokens, the last tile's two upper slices past the
+# last token; C = 1024: 24 tiles, four slices; C = 3072: 108 tiles, T = 700,
+# two slices of 128 tokens).  The 1024^2 pack's 612 tiles (a last round of
+# 100, two slices) are in test_block_qkv_single_1024_sampled.
+@pytest.mark.parametrize("H,descs", [(4, [(88, 1, 16, 32, 0, 0)]), (8, [(27, 1, 13, 21, 0, 0), (0, 1, 1, 1, 1, 1)]),
+                                     (24, [(60, 1, 20, 32, 0, 0)])],
+                         ids=["C512", "C1024", "C3072"])
 def test_block_qkv_split_tail(H, descs):
     w = W.custom(descs, H=H, D=128, rope_dims=(0, 64, 64), modulate=True, residual=True, seed=41,
                  name=f"block_split_c{H * 128}")
