@@ -23,11 +23,12 @@
 //    The partition is fixed by (W, G), so results are deterministic.
 //    Logical workgroups map to blockIdx so that consecutive ranges (same
 //    sequence and head, hence the same K/V) run on one XCD and share its L2.
-//  * A workgroup owns a 256-row query tile.  For d = 128 it runs eight
-//    wavefronts of 32 query rows, two per SIMD, so that one wavefront's
-//    MFMAs run while the other issues its softmax work or waits; for d = 64
-//    it runs four wavefronts of 64 rows as two 32-row blocks (each K or V
-//    fragment then feeds two MFMAs).  Scores are computed transposed,
+//  * A workgroup owns a 256-row query tile and runs four wavefronts, one
+//    per SIMD, each owning 64 query rows as two 32-row blocks, so that each
+//    K or V fragment read from LDS feeds two MFMAs.  (Eight wavefronts of 32
+//    rows, two per SIMD, were faster on isolated calls but slower on calls
+//    back to back, where the clock settles lower: the four-wavefront form
+//    reads half the LDS bytes per MFMA.)  Scores are computed transposed,
 //    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: every lane holds 16 keys of
 //    one query row, so a row's statistics combine lanes l and l+32 with one
 //    v_permlane32_swap.  The fp32 probabilities are rounded to bf16 in
@@ -99,11 +100,8 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // scalar offset past any sequenc
 
 template <int D>
 struct Tile {
-    // 32-row blocks per wavefront: d = 128 runs eight wavefronts of 32 rows
-    // (two per SIMD, so one wavefront's MFMAs cover the other's softmax and
-    // waits); d = 64 runs four wavefronts of 64 rows, since its 4 KB K/V tile
-    // takes only four direct-load instructions.
-    static constexpr int NB = D == 128 ? 1 : 2;
+    // 32-row blocks per wavefront: each K or V fragment feeds NB MFMAs.
+    static constexpr int NB = 2;
     static constexpr int ROWS_W = 32 * NB;         // query rows per wavefront
     static constexpr int WAVES = kBM / ROWS_W;     // wavefronts per workgroup
     static constexpr int THREADS = 64 * WAVES;
