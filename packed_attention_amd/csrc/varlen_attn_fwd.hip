@@ -38,8 +38,8 @@
 //    (ds_read_b64_tr_b16) of the row-major V tile deliver as the V^T operand.
 //  * Per step t a wavefront runs two phases, with the softmax VALU work
 //    threaded between the MFMAs of the same wavefront:
-//      phase 1: S(t+1) = K(t+1) Q^T   ||  p = exp2(x(t)), bf16 rounding, row sums
-//      phase 2: O += V(t)^T P(t)^T     ||  x(t+1) = S(t+1) * scale*log2e - m
+//      phase 1: S(t+1) = K(t+1) Q^T   ||  p = exp2(x(t)) in place, bf16 rounding
+//      phase 2: O += V(t)^T P(t)^T     ||  row sums of p(t), x(t+1) = S(t+1) * scale*log2e - m
 //    Operand fragments are read from LDS three MFMAs ahead.  The step carries
 //    no other VALU work: the reference max m of each row is fixed by the
 //    segment's first key step (numerator and denominator share it, so the
@@ -699,7 +699,6 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
             // slots.
             auto phase1 = [&]<bool kS>(Scores& x, Scores& s, uint32_t kb, uint32_t vb) {
                 constexpr int E = 16 * NB / NS;
-                float ex[E];
                 static_for<NS + 1>([&](auto SI) {
                     constexpr int sl = SI;
                     if constexpr (kS && sl < NS) {
@@ -711,24 +710,23 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
                         if constexpr (b == NB - 1 && kk + kPfK < KK) kf[kk % kPfK] = kfrag(kb, kk + kPfK);
                     }
                     if constexpr (sl > 0) {
-                        // bf16 rounding and row sums of the previous slot's pairs
+                        // bf16 rounding of the previous slot's pairs
 #pragma unroll
                         for (int i = 0; i < E; i += 2) {
                             const int e = E * (sl - 1) + i;
                             const int b = e / 16, r = e % 16;
-                            const uint32_t w = pack_bf16x2(ex[i], ex[i + 1]);
+                            const uint32_t w = pack_bf16x2(x[b][r], x[b][r + 1]);
                             const int cc = r / 8, dw = (r % 8) / 2;
                             u32x4_t u = __builtin_bit_cast(u32x4_t, pf[b][cc]);
                             u[dw] = w;
                             pf[b][cc] = __builtin_bit_cast(bf16x8_t, u);
-                            lsum[b] += ex[i] + ex[i + 1];
                         }
                     }
                     if constexpr (sl < NS) {
 #pragma unroll
                         for (int i = 0; i < E; ++i) {
                             const int e = E * sl + i;
-                            ex[i] = __builtin_amdgcn_exp2f(x[e / 16][e % 16]);
+                            x[e / 16][e % 16] = __builtin_amdgcn_exp2f(x[e / 16][e % 16]);
                         }
                     }
                     if constexpr (sl >= NS + 1 - kPfV) vf[sl - (NS + 1 - kPfV)] = vfrag(vb, sl - (NS + 1 - kPfV));
@@ -746,9 +744,10 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
             // loads (K of tile t+kKStages, V of tile t+kVStages-1) in slots
             // 1 .. 2 NI_W and read the first K fragments of the next phase 1
             // in the last slots.
-            auto phase2 = [&]<bool kNext>(Scores& s, uint32_t vb, uint32_t kb_next, int t,
+            auto phase2 = [&]<bool kNext>(Scores& s, Scores& pr, uint32_t vb, uint32_t kb_next, int t,
                                           int kdst, int vdst) {
                 constexpr int NITEMS = kNext ? 16 * NB : 0;   // x = S c - m, in place
+                constexpr int NSUMS = 8 * NB;                  // pairs of p(t) added to the row sums
                 const uint32_t so_k = tile_soff_pos(t + kKStages), so_v = tile_soff_pos(t + kVStages - 1);
                 auto item = [&](auto II) {
                     constexpr int e = II;
@@ -764,6 +763,11 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
                     if constexpr (kNext && sl > NI_W && sl <= 2 * NI_W) dma_v(vdst, so_v, sl - NI_W - 1);
                     constexpr int lo = NITEMS * sl / NP, hi = NITEMS * (sl + 1) / NP;
                     static_for<hi - lo>([&](auto JI) { item(std::integral_constant<int, lo + int(JI)>{}); });
+                    constexpr int slo = NSUMS * sl / NP, shi = NSUMS * (sl + 1) / NP;
+                    static_for<shi - slo>([&](auto JI) {
+                        constexpr int e = 2 * (slo + int(JI)), b = e / 16, r = e % 16;
+                        lsum[b] += pr[b][r] + pr[b][r + 1];
+                    });
                     if constexpr (kNext && sl >= NP - kPfK) kf[sl - (NP - kPfK)] = kfrag(kb_next, sl - (NP - kPfK));
                     __builtin_amdgcn_sched_barrier(0);
                 });
@@ -801,7 +805,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
                 const int ks2 = (ph + 2) & (kRing - 1);      // K stage of tile t+2
                 const int vd = (ph + kRing - 1) & (kRing - 1);  // V stage of tile t-1
                 phase1.template operator()<true>(x, s, kstage(ks), vstage(ph));
-                phase2.template operator()<true>(s, vstage(ph), kstage(ks2), t, ph, vd);
+                phase2.template operator()<true>(s, x, vstage(ph), kstage(ks2), t, ph, vd);
                 wait_vm<2 * NI_W * kSlack>();
                 __syncthreads();
             };
@@ -820,7 +824,7 @@ __global__ __launch_bounds__(Tile<D>::THREADS, 1) void attn_fwd_kernel(KParams p
             }
             // the segment's last tile, at ring position 0
             phase1.template operator()<false>(h0, h0, kstage(1), vstage(0));
-            phase2.template operator()<false>(h0, vstage(0), kstage(2), kv1, 0, 0);
+            phase2.template operator()<false>(h0, h0, vstage(0), kstage(2), kv1, 0, 0);
 
             // ---- redo decision (workgroup-wide) --------------------------------
             // A row sum is at least every one of its terms, so a sum within
